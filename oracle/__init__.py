@@ -1,0 +1,152 @@
+"""fp64 CPU oracle for paged GQA decode, KV append + RoPE and chunked prefill.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The library under
+``paged_kv_gqa_append_amd`` never imports, links or calls it, and it shares no
+code with the HIP path: the arithmetic lives in ``oracle.c`` (plain loops,
+double precision), this file only marshals numpy arrays through ctypes.
+
+Inputs are numpy arrays: bf16 tensors as ``uint16`` bit patterns, page tables
+and lengths as ``int32``.  Layouts: see ``oracle.c``.
+
+Pins (tests/test_oracle_*.py): bf16 rounding against torch's float32 -> bf16
+and hand-built halfway cases; RoPE against complex multiplication and the
+Hugging Face Llama rotate-half routine; decode against torch's fp64
+``scaled_dot_product_attention`` on gathered contiguous K/V plus closed forms
+(single token, identical rows, q = 0, two-token logistic, ones column) and
+page-placement invariance; prefill against causal SDPA and decode.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, BAD_ARG, BAD_LEN, BAD_PAGE = 0, 1, 2, 3
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP) into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+               "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    dbl = ctypes.c_double
+    lib.oracle_bf16_to_f64.restype = dbl
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_f64_to_bf16.argtypes = [dbl]
+    lib.oracle_rope_head.restype = None
+    lib.oracle_rope_head.argtypes = [P, ctypes.c_int64, dbl, P]
+    lib.oracle_append_kv_rope.restype = ctypes.c_int
+    lib.oracle_append_kv_rope.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, dbl]
+    lib.oracle_decode_gqa.restype = ctypes.c_int
+    lib.oracle_decode_gqa.argtypes = [P, P, P, P, P, P, i32, i32, i32, dbl]
+    lib.oracle_prefill_chunk.restype = ctypes.c_int
+    lib.oracle_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, dbl, dbl]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"bf16 tensors are passed as uint16 bit patterns, got {a.dtype}")
+    return a
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def bf16_to_f64(b: int) -> float:
+    return float(_load().oracle_bf16_to_f64(int(b)))
+
+
+def f64_to_bf16(x: float) -> int:
+    """One-step round-to-nearest-even of a double to bf16 (bit pattern)."""
+    return int(_load().oracle_f64_to_bf16(float(x)))
+
+
+def rope_head(x_bits: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """Rotate one 64-wide bf16 head to fp64 at absolute position ``pos``."""
+    x = _u16(x_bits)
+    assert x.shape == (64,)
+    y = np.zeros(64, dtype=np.float64)
+    _load().oracle_rope_head(_ptr(x), int(pos), float(theta), _ptr(y))
+    return y
+
+
+def append_kv_rope(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, num_pages: int,
+                   theta: float) -> int:
+    """In place on ``q`` (may be None), ``k_pool`` and ``v_pool``; returns a status code."""
+    lib = _load()
+    qq = None if q is None else _u16(q)
+    for a in (k_pool, v_pool) + (() if q is None else (q,)):
+        if not (a.flags.c_contiguous and a.dtype == np.uint16):
+            raise TypeError("in-place arrays must be C-contiguous uint16")
+    kn, vn = _u16(k_new), _u16(v_new)
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    B = int(cl.shape[0])
+    return int(lib.oracle_append_kv_rope(_ptr(qq), _ptr(kn), _ptr(vn), _ptr(k_pool), _ptr(v_pool), _ptr(bt),
+                                         _ptr(cl), B, int(bt.shape[-1]), int(num_pages), float(theta)))
+
+
+def decode_gqa(q, k_pool, v_pool, block_tables, context_lens, num_pages: int, scale: float):
+    """Returns (out fp64 [B][32][64], status)."""
+    lib = _load()
+    qq, kp, vp = _u16(q), _u16(k_pool), _u16(v_pool)
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    B = int(cl.shape[0])
+    out = np.zeros((B, 32, 64), dtype=np.float64)
+    rc = lib.oracle_decode_gqa(_ptr(out), _ptr(qq), _ptr(kp), _ptr(vp), _ptr(bt), _ptr(cl), B,
+                               int(bt.shape[-1]), int(num_pages), float(scale))
+    return out, int(rc)
+
+
+def prefill_chunk(q, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens, num_pages: int,
+                  theta: float, scale: float):
+    """In place on ``q``, ``k_pool``, ``v_pool``; returns (out fp64 [B][C][32][64], status)."""
+    lib = _load()
+    for a in (q, k_pool, v_pool):
+        if not (a.flags.c_contiguous and a.dtype == np.uint16):
+            raise TypeError("in-place arrays must be C-contiguous uint16")
+    kc, vc = _u16(k_chunk), _u16(v_chunk)
+    bt, pl = _i32(block_tables), _i32(prefix_lens)
+    B, C = int(q.shape[0]), int(q.shape[1])
+    out = np.zeros((B, C, 32, 64), dtype=np.float64)
+    rc = lib.oracle_prefill_chunk(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(k_pool), _ptr(v_pool), _ptr(bt),
+                                  _ptr(pl), B, C, int(bt.shape[-1]), int(num_pages), float(theta), float(scale))
+    return out, int(rc)
