@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark: paged GQA decode with KV append on one MI355X.
+
+Default workload (one "step"): 64 sequences at context 2048 (2047 cached
+tokens + the one appended this step), 16 layers, 32 q / 8 KV heads, head dim
+64, bf16 K/V ~N(0,1) in a pool of 64 x 128 x 16 = 131072 pages whose ids are a
+random permutation.  A step runs, for every layer, the append of the new token
+(RoPE-rotated K and V written into its page, q rotated in place) and the paged
+decode attention: by default as one pa_append_decode_gqa launch per layer;
+the same step made of the two separate calls (pa_append_kv_rope, then
+pa_decode_gqa) is timed too and reported beside it.  Inputs are resident in
+HBM before timing starts.
+
+Prints ONE JSON line.  value = algorithmic KV bytes read per step (tokens
+attended x 2048 B x layers) / step time, in GB/s; tokens/s = sequences /
+step time.  The roofline object reports the decode kernel alone: its
+algorithmic bytes per launch over its mean duration from HIP events recorded
+around each launch, on the stream it runs on.  cpu_baseline times the fp64
+CPU oracle (append + decode) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged GQA decode: KV-read GB/s and % of HBM peak; decode tokens/s (1 GPU)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="batch64", choices=["batch64", "batch256", "batch8", "tiny"])
+    ap.add_argument("--path", default="fused", choices=["fused", "separate"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    return ap.parse_args()
+
+
+def build_workload(name, device):
+    import torch
+
+    from paged_kv_gqa_append_amd import workloads as W
+
+    if name == "batch64":
+        spec = W.batch64_spec()
+    elif name == "batch256":
+        spec = W.batch256_spec()
+    elif name == "batch8":
+        c = W.batch8_decode(poison=False)
+        spec = W.DeviceCaseSpec("batch8_decode", 1, c.num_seqs, c.max_blocks, c.num_pages, c.context_lens,
+                                c.block_tables, c.seed)
+    else:
+        c = W.tiny_decode(poison=False)
+        spec = W.DeviceCaseSpec("tiny_decode", 1, c.num_seqs, c.max_blocks, c.num_pages, c.context_lens,
+                                c.block_tables, c.seed)
+    k_pool = W.fill_pool_device(spec, device, "k")
+    v_pool = W.fill_pool_device(spec, device, "v")
+    rows = [spec.host_rows(l) for l in range(spec.num_layers)]
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+    layers = []
+    for l in range(spec.num_layers):
+        q, kn, vn = rows[l]
+        layers.append(dict(q=up(q), k_new=up(kn), v_new=up(vn),
+                           bt=torch.from_numpy(spec.block_tables[l]).to(device),
+                           out=torch.empty((spec.num_seqs, 32, 64), dtype=torch.bfloat16, device=device)))
+    lens = torch.from_numpy(spec.context_lens).to(device)
+    return spec, k_pool, v_pool, layers, lens, rows
+
+
+def cpu_baseline(spec, k_pool, v_pool, rows, target_s):
+    """Time the fp64 oracle's append + decode on whole layers of the workload (host cores)."""
+    import oracle
+    import torch
+
+    # sample: whole layers of the workload, in order, until the CPU budget is spent
+    def host_case(layer, seqs):
+        bt = spec.block_tables[layer][seqs]
+        used = np.unique(bt[bt >= 0])
+        remap = np.full(spec.num_pages, -1, np.int64)
+        remap[used] = np.arange(len(used))
+        idx = torch.from_numpy(used).to(k_pool.device)
+        kp = k_pool.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        vp = v_pool.index_select(0, idx).cpu().view(torch.int16).numpy().view(np.uint16).copy()
+        bt2 = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+        q, kn, vn = rows[layer]
+        return kp, vp, bt2, q[seqs].copy(), kn[seqs].copy(), vn[seqs].copy(), spec.context_lens[seqs].copy(), len(used)
+
+    def run(seqs, layer):
+        kp, vp, bt, q, kn, vn, lens, npg = host_case(layer, seqs)
+        t0 = time.perf_counter()
+        rc = oracle.append_kv_rope(q, kn, vn, kp, vp, bt, lens, npg, spec.theta)
+        out, rc2 = oracle.decode_gqa(q, kp, vp, bt, lens, npg, spec.scale)
+        dt = time.perf_counter() - t0
+        assert rc == oracle.OK and rc2 == oracle.OK
+        return dt, int(lens.astype(np.int64).sum())
+
+    B = spec.num_seqs
+    seqs = np.arange(B)
+    total_dt, total_tokens, layers_done = 0.0, 0, 0
+    for layer in range(spec.num_layers):
+        dt, tokens = run(seqs, layer)
+        total_dt += dt
+        total_tokens += tokens
+        layers_done += 1
+        if total_dt >= target_s:
+            break
+    kv_bytes = total_tokens * 2048
+    return {"value": round(kv_bytes / total_dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(total_dt, 3),
+            "tokens_per_s": round(B * layers_done / spec.num_layers / total_dt, 3),
+            "sample": f"fp64 oracle append + decode of all {B} sequences for {layers_done} of the "
+                      f"{spec.num_layers} layers of the {spec.name} workload ({total_tokens} tokens attended, "
+                      f"{kv_bytes} KV bytes); tokens/s scaled to whole {spec.num_layers}-layer steps"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the decode path shards by sequence or KV head with no exchange, "
+                                   "but no multi-GPU launcher is built)"}))
+        sys.exit(2)
+    import torch
+
+    from paged_kv_gqa_append_amd import binding, build
+
+    if not build.is_built():
+        build.build()
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    device = torch.device("cuda", 0)
+    spec, k_pool, v_pool, layers, lens, rows = build_workload(args.config, device)
+    table = binding.rope_table(2048 + 64, spec.theta, device)
+    ws = binding.decode_workspace(spec.num_seqs, spec.max_blocks, device)
+    stream = torch.cuda.current_stream()
+
+    def step_fused(ev=None):
+        for l, L in enumerate(layers):
+            if ev is not None:
+                ev[l][0].record(stream)
+            binding.append_decode_gqa(L["out"], L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens,
+                                      table, spec.scale, workspace=ws, stream=stream)
+            if ev is not None:
+                ev[l][1].record(stream)
+
+    def step_separate(ev=None):
+        for l, L in enumerate(layers):
+            binding.append_kv_rope(L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens, table,
+                                   stream=stream)
+            binding.decode_gqa(L["out"], L["q"], k_pool, v_pool, L["bt"], lens, spec.scale, workspace=ws,
+                               stream=stream)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    step = step_fused if args.path == "fused" else step_separate
+    ms = timed(step, args.steps, args.warmup)
+    other_ms = timed(step_separate if args.path == "fused" else step_fused, max(3, args.steps // 2), 2)
+
+    # instrumented pass: HIP events around every fused append+decode launch on its stream
+    # (a pass of its own, so the events do not perturb the step time above)
+    dec_ms = []
+    for _ in range(max(3, args.steps // 2)):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+        step_fused(ev)
+        torch.cuda.synchronize()
+        dec_ms += [a.elapsed_time(b) for a, b in ev]
+    dec_ms_mean = float(np.mean(dec_ms))
+
+    kv_step = spec.kv_bytes()
+    kv_launch = kv_step // spec.num_layers
+    gbps = kv_step / (ms * 1e-3) / 1e9
+    dec_gbps = kv_launch / (dec_ms_mean * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": spec.name, "num_seqs": spec.num_seqs, "context_len": int(spec.context_lens.max()),
+                   "mean_context_len": float(spec.context_lens.mean()), "layers": spec.num_layers,
+                   "q_heads": 32, "kv_heads": 8, "head_dim": 64, "page_size": 16, "num_pages": spec.num_pages,
+                   "step": ("per layer: pa_append_decode_gqa (append + RoPE + decode, one launch)"
+                            if args.path == "fused" else "per layer: pa_append_kv_rope then pa_decode_gqa"),
+                   "decode_partition_tokens": binding.decode_partition_tokens()},
+        "tokens_per_s": round(spec.num_seqs / (ms * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "kv_bytes_per_step": kv_step,
+        ("separate_calls_ms_per_step" if args.path == "fused" else "fused_ms_per_step"): round(other_ms, 5),
+        "roofline": {"bound": "hbm", "kernel": "k_decode_paged<8,true> (pa_append_decode_gqa)",
+                     "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": kv_launch, "mean_launch_us": round(dec_ms_mean * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, k_pool, v_pool, rows, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged grouped-query attention for MI355X (gfx950).
+ *
+ * The problem these calls solve is the paged KV cache of a small decoder LLM
+ * engine as the samir-vllm article describes it (section "Gestion de la KV
+ * cache et strategies de batching"): K and V of every layer live in one shared
+ * pool of physical pages of 16 tokens; each (sequence, layer) owns a block table
+ * naming its pages; at decode time each new token is appended at its absolute
+ * RoPE position; paged attention reads only the sequence's own pages, never
+ * concatenates a contiguous prefix and never stores the attention scores.
+ * Geometry is Llama-3.2-1B's (tiny-vllm chapter "Weight Loading and GPU Buffer
+ * Design", section "Preallocating the 16 compute buffers"): 32 query heads,
+ * KV width 512 = 8 KV heads x head dim 64, bf16 storage.  Like that engine the
+ * geometry is fixed at compile time (samir-vllm, section "Limitations").
+ *
+ * ---------------------------------------------------------------- layouts --
+ *   bf16 = IEEE binary32 truncated to its upper 16 bits (1-8-7).
+ *   k_pool, v_pool : [num_pages][8 kv heads][16 slots][64] bf16.  Page p of the
+ *                    K pool and page p of the V pool hold the same 16 tokens.
+ *                    One (page, kv head) is a contiguous 2 KiB tile.
+ *   block_tables   : [num_seqs][max_blocks] int32.  Entry b is the physical page
+ *                    of tokens 16b..16b+15; entries at or past ceil(L/16) are
+ *                    never read and may be -1 (unassigned, as in tiny-vllm's
+ *                    init, section "What else is set up ...").  One layer is
+ *                    selected by passing that layer's table; all layers share
+ *                    the pool.
+ *   context_lens   : [num_seqs] int32, the sequence length INCLUDING the token
+ *                    being appended; that token's position is L-1 (0-based).
+ *   q              : [num_seqs][32][64] bf16; q head h reads KV head h/4.
+ *   k_new, v_new   : [num_seqs][8][64] bf16 (the decode-time K/V batch buffers
+ *                    of tiny-vllm, BATCH_SIZE x KV_DIM).
+ *   rope_cos_sin   : [max_pos][32][2] fp32: (cos, sin) of pos * w_i,
+ *                    w_i = theta^(-2i/64); pair i rotates elements (i, i+32)
+ *                    ("rotate-half").  Build it with pa_rope_table_fill_host.
+ *
+ * ------------------------------------------------------------- conventions --
+ *   Ownership: every array is caller-owned device memory (hipMalloc or any
+ *     allocator); scalars are host values.  The library allocates nothing and
+ *     keeps no mutable global state.
+ *   Streams: each call enqueues its kernels on `stream` and returns without
+ *     synchronising.  Calls that touch the same pool, q or out must be ordered
+ *     by the caller (one stream, or events); concurrent calls on disjoint
+ *     buffers are safe.
+ *   Alignment: every array pointer must be 16-byte aligned.
+ *   Errors: a call returns PA_OK, or an error code *before launching anything*
+ *     when a host-checkable argument is wrong (NULL pointer, non-positive size,
+ *     misalignment, page_size != 16, workspace too small).  Launch failures map
+ *     to PA_ERR_HIP.  Table contents live on the device and cannot be checked
+ *     on the host: a bad length or page id found by a kernel is never
+ *     dereferenced; the kernel skips (append) or zero-fills (decode/prefill)
+ *     the affected sequence and ORs a PA_DEVERR_* bit into *device_flags when
+ *     that pointer is not NULL.
+ */
+#ifndef PAGED_KV_GQA_APPEND_PA_H
+#define PAGED_KV_GQA_APPEND_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_NUM_Q_HEADS 32
+#define PA_NUM_KV_HEADS 8
+#define PA_HEAD_DIM 64
+#define PA_PAGE_SIZE 16
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* NULL, non-positive size, misaligned pointer    */
+    PA_ERR_UNSUPPORTED = 2, /* page_size other than 16, dtype not supported   */
+    PA_ERR_WORKSPACE = 3,   /* decode workspace missing or too small          */
+    PA_ERR_HIP = 4          /* the HIP runtime refused a launch               */
+} pa_status;
+
+typedef enum { PA_OUT_BF16 = 0, PA_OUT_FP32 = 1 } pa_out_dtype;
+
+/* Bits a kernel ORs into *device_flags (caller-owned uint32, may be NULL). */
+#define PA_DEVERR_CONTEXT_LEN 0x1u /* L < 1, or L beyond max_blocks*16 / max_pos */
+#define PA_DEVERR_PAGE_ID 0x2u     /* a used block-table entry outside [0, num_pages) */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *pa_status_string(int status);
+
+/* ABI version of this header (bumped on any signature or layout change). */
+int32_t pa_abi_version(void);
+
+/* Fill a HOST table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),
+ * evaluated in double precision and rounded once to fp32.  The caller copies
+ * it to the device.  Frequencies are unscaled; theta = 500000 for Llama 3.
+ * Returns PA_ERR_INVALID_ARG for a NULL table, max_pos < 1 or theta <= 1.     */
+pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta);
+
+/* Decode-time KV append (samir-vllm, section "Gestion de la KV cache ...": each
+ * new token is written at its absolute RoPE position).  For every sequence s,
+ * pos = context_lens[s]-1, page = block_tables[s][pos/16], slot = pos%16:
+ *   k_pool[page][j][slot][:] = bf16_rne(rope(k_new[s][j][:], pos))   j < 8
+ *   v_pool[page][j][slot][:] = v_new[s][j][:]                           (copy)
+ *   q[s][h][:] = bf16_rne(rope(q[s][h][:], pos)) in place, h < 32 (skipped when
+ *   q is NULL).
+ * Rotation is fp32 (table values, fused multiply-add), stored once, RNE.
+ * Device errors: L < 1 or pos >= min(max_blocks*16, max_pos) -> CONTEXT_LEN,
+ * page id out of range -> PAGE_ID; that sequence is left untouched.           */
+pa_status pa_append_kv_rope(void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                            const int32_t *block_tables, const int32_t *context_lens,
+                            const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                            int32_t num_pages, int32_t page_size, int32_t max_pos,
+                            uint32_t *device_flags, hipStream_t stream);
+
+/* Bytes of device workspace pa_decode_gqa needs for num_seqs sequences whose
+ * block tables have max_blocks entries (0 when one context partition always
+ * suffices).  The workspace holds per-partition softmax partials; it needs no
+ * initialisation and its contents are dead between calls.                    */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks);
+
+/* Tokens per context partition pa_decode_gqa uses (a multiple of 16).  It does
+ * not depend on the batch, so a sequence's result does not either.           */
+int32_t pa_decode_partition_tokens(void);
+
+/* Paged GQA decode (samir-vllm, batched-decode paragraph of "Gestion de la KV
+ * cache ..."; tiny-vllm ch.2, "One buffer, two roles": the attention output is
+ * written over the q buffer).  For each s, h < 32, j = h/4, L = context_lens[s]:
+ *   x_t = scale * <q[s][h], K_t>,  K_t, V_t = pool rows of token t < L, head j
+ *   out[s][h][:] = sum_t exp(x_t - max x) V_t / sum_t exp(x_t - max x)
+ * accumulated in fp32 (online softmax over context partitions, exact merge),
+ * stored as bf16 (RNE) or fp32 per out_dtype.  out MAY ALIAS q exactly
+ * (same pointer); no other overlap is allowed.  q must already be rotated.
+ * Device errors: L < 1 or L > max_blocks*16 -> CONTEXT_LEN and the sequence's
+ * output rows are zero-filled; a used page id out of range -> PAGE_ID and the
+ * same.                                                                       */
+pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void *v_pool,
+                        const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                        int32_t max_blocks, int32_t num_pages, int32_t page_size, float scale,
+                        int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                        uint32_t *device_flags, hipStream_t stream);
+
+/* One decode step of a layer in a single launch: pa_append_kv_rope followed by
+ * pa_decode_gqa, fused (samir-vllm, "Gestion de la KV cache ...": the new
+ * token is appended at its absolute RoPE position, then paged attention reads
+ * the sequence's pages).  Arguments are the union of the two calls; q holds the
+ * UN-rotated query and receives the rotated one in place (unless out == q, in
+ * which case it receives the attention output).  Results are bitwise those of
+ * the two separate calls: the same fp32 rotation and bf16 rounding, and the
+ * appended K/V row is written to its slot exactly as pa_append_kv_rope does.
+ * Device errors: the union of both calls' (L-1 >= max_pos also counts as
+ * CONTEXT_LEN); a failing sequence is neither appended nor attended, its out
+ * rows are zero-filled.                                                        */
+pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                               int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
+                               int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                               uint32_t *device_flags, hipStream_t stream);
+
+/* Chunked prefill (TinyLoop, section "prefill_chunk and scratch residency":
+ * the prompt is processed in row chunks; samir-vllm: the prompt's pages are
+ * filled during prefill).  For each s and chunk token i < chunk_len at
+ * pos = prefix_lens[s] + i: append k_chunk[s][i] / v_chunk[s][i] as
+ * pa_append_kv_rope does and rotate q[s][i] in place; then every chunk query
+ * attends causally (keys 0..pos inclusive) to its sequence's pages:
+ *   out[s][i][h][:] = softmax_t(scale * <q[s][i][h], K_t>) . V_t,  t <= pos
+ * with bf16 MFMA tiles and fp32 accumulation; no score matrix is stored.
+ * q, out: [num_seqs][chunk_len][32][64]; k_chunk, v_chunk: [num_seqs][chunk_len][8][64].
+ * out may alias q exactly.  Device errors as for append (whole sequence
+ * skipped, its out rows zero-filled).                                         */
+pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool,
+                           void *v_pool, const int32_t *block_tables, const int32_t *prefix_lens,
+                           const float *rope_cos_sin, int32_t num_seqs, int32_t chunk_len,
+                           int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
+                           float scale, int32_t out_dtype, uint32_t *device_flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGED_KV_GQA_APPEND_PA_H */

@@ -1,0 +1,256 @@
+"""ctypes binding of libpa.so (include/pa.h) for torch device tensors.
+
+Argument marshalling only: shapes, dtypes and devices are checked, raw device
+pointers and torch's current HIP stream are handed to the C ABI, and a non-zero
+status becomes a :class:`PaError`.  All work runs in the library's HIP kernels;
+if ``libpa.so`` is missing this module raises instead of computing anything
+another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import workloads as _w
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+_lib = None
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OUT_BF16, PA_OUT_FP32 = 0, 1
+PA_DEVERR_CONTEXT_LEN, PA_DEVERR_PAGE_ID = 0x1, 0x2
+
+EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_append_kv_rope",
+           "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode_gqa", "pa_append_decode_gqa",
+           "pa_prefill_chunk")
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def lib():
+    """Load libpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with paged_kv_gqa_append_amd.build.build() "
+                           "(there is no fallback implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_abi_version.restype = i32
+    L.pa_abi_version.argtypes = []
+    L.pa_rope_table_fill_host.restype = ctypes.c_int
+    L.pa_rope_table_fill_host.argtypes = [P, i32, ctypes.c_double]
+    L.pa_append_kv_rope.restype = ctypes.c_int
+    L.pa_append_kv_rope.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P]
+    L.pa_decode_workspace_bytes.restype = u64
+    L.pa_decode_workspace_bytes.argtypes = [i32, i32]
+    L.pa_decode_partition_tokens.restype = i32
+    L.pa_decode_partition_tokens.argtypes = []
+    L.pa_decode_gqa.restype = ctypes.c_int
+    L.pa_decode_gqa.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P]
+    L.pa_append_decode_gqa.restype = ctypes.c_int
+    L.pa_append_decode_gqa.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
+                                       u64, P, P]
+    L.pa_prefill_chunk.restype = ctypes.c_int
+    L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
+                                   P, P]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != PA_OK:
+        raise PaError(rc, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _expect(t: torch.Tensor, name: str, dtype, shape=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def rope_table(max_pos: int, theta: float = _w.ROPE_THETA, device="cuda") -> torch.Tensor:
+    """[max_pos][32][2] fp32 (cos, sin) table, filled by the library on the host, then uploaded."""
+    host = np.empty((max_pos, _w.HEAD_DIM // 2, 2), dtype=np.float32)
+    _check(lib().pa_rope_table_fill_host(host.ctypes.data_as(ctypes.c_void_p), int(max_pos), float(theta)),
+           "pa_rope_table_fill_host")
+    return torch.from_numpy(host).to(device)
+
+
+def decode_workspace_bytes(num_seqs: int, max_blocks: int) -> int:
+    return int(lib().pa_decode_workspace_bytes(int(num_seqs), int(max_blocks)))
+
+
+def decode_partition_tokens() -> int:
+    return int(lib().pa_decode_partition_tokens())
+
+
+def decode_workspace(num_seqs: int, max_blocks: int, device="cuda") -> Optional[torch.Tensor]:
+    n = decode_workspace_bytes(num_seqs, max_blocks)
+    return None if n == 0 else torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def _pool_checks(k_pool, v_pool):
+    _expect(k_pool, "k_pool", torch.bfloat16)
+    _expect(v_pool, "v_pool", torch.bfloat16, shape=k_pool.shape, device=k_pool.device)
+    if k_pool.dim() != 4 or tuple(k_pool.shape[1:]) != (_w.NUM_KV_HEADS, _w.PAGE_SIZE, _w.HEAD_DIM):
+        raise ValueError(f"pools must be [num_pages][8][16][64], got {tuple(k_pool.shape)}")
+    return int(k_pool.shape[0])
+
+
+def append_kv_rope(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+                   v_pool: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   rope_cos_sin: torch.Tensor, device_flags: Optional[torch.Tensor] = None, page_size: int = 16,
+                   stream=None) -> None:
+    """pa_append_kv_rope: write RoPE(k_new), v_new at pos = L-1; rotate q in place (if given)."""
+    num_pages = _pool_checks(k_pool, v_pool)
+    dev = k_pool.device
+    _expect(context_lens, "context_lens", torch.int32, device=dev)
+    B = int(context_lens.shape[0])
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
+    if q is not None:
+        _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_append_kv_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                 _ptr(context_lens), _ptr(rope_cos_sin), B, int(block_tables.shape[1]), num_pages,
+                                 int(page_size), int(rope_cos_sin.shape[0]), _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_append_kv_rope")
+
+
+def decode_gqa(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+               block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float = 0.125,
+               workspace: Optional[torch.Tensor] = None, device_flags: Optional[torch.Tensor] = None,
+               page_size: int = 16, stream=None) -> torch.Tensor:
+    """pa_decode_gqa into ``out`` ([B][32][64] bf16 or fp32; may be ``q`` itself)."""
+    num_pages = _pool_checks(k_pool, v_pool)
+    dev = k_pool.device
+    _expect(context_lens, "context_lens", torch.int32, device=dev)
+    B = int(context_lens.shape[0])
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    if out.dtype == torch.bfloat16:
+        odt = PA_OUT_BF16
+    elif out.dtype == torch.float32:
+        odt = PA_OUT_FP32
+    else:
+        raise TypeError("out must be bfloat16 or float32")
+    _expect(out, "out", out.dtype, (B, 32, 64), dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_decode_gqa(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+                             B, int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
+                             _ptr(workspace), ws_bytes, _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_decode_gqa")
+    return out
+
+
+def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, rope_cos_sin: torch.Tensor, scale: float = 0.125,
+                      workspace: Optional[torch.Tensor] = None, device_flags: Optional[torch.Tensor] = None,
+                      page_size: int = 16, stream=None) -> torch.Tensor:
+    """pa_append_decode_gqa: append (RoPE K, V at pos = L-1), rotate q in place, then decode into ``out``."""
+    num_pages = _pool_checks(k_pool, v_pool)
+    dev = k_pool.device
+    _expect(context_lens, "context_lens", torch.int32, device=dev)
+    B = int(context_lens.shape[0])
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    if out.dtype == torch.bfloat16:
+        odt = PA_OUT_BF16
+    elif out.dtype == torch.float32:
+        odt = PA_OUT_FP32
+    else:
+        raise TypeError("out must be bfloat16 or float32")
+    _expect(out, "out", out.dtype, (B, 32, 64), dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_append_decode_gqa(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                    _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
+                                    int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
+                                    float(scale), odt, _ptr(workspace), ws_bytes, _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_append_decode_gqa")
+    return out
+
+
+def prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                  k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor, prefix_lens: torch.Tensor,
+                  rope_cos_sin: torch.Tensor, scale: float = 0.125, device_flags: Optional[torch.Tensor] = None,
+                  page_size: int = 16, stream=None) -> torch.Tensor:
+    """pa_prefill_chunk: append the chunk (q rotated in place), then causal paged attention into ``out``."""
+    num_pages = _pool_checks(k_pool, v_pool)
+    dev = k_pool.device
+    _expect(prefix_lens, "prefix_lens", torch.int32, device=dev)
+    B = int(prefix_lens.shape[0])
+    if q.dim() != 4:
+        raise ValueError("q must be [num_seqs][chunk_len][32][64]")
+    C = int(q.shape[1])
+    _expect(q, "q", torch.bfloat16, (B, C, 32, 64), dev)
+    _expect(k_chunk, "k_chunk", torch.bfloat16, (B, C, 8, 64), dev)
+    _expect(v_chunk, "v_chunk", torch.bfloat16, (B, C, 8, 64), dev)
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    if out.dtype == torch.bfloat16:
+        odt = PA_OUT_BF16
+    elif out.dtype == torch.float32:
+        odt = PA_OUT_FP32
+    else:
+        raise TypeError("out must be bfloat16 or float32")
+    _expect(out, "out", out.dtype, (B, C, 32, 64), dev)
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_tables), _ptr(prefix_lens), _ptr(rope_cos_sin), B, C,
+                                int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
+                                float(scale), odt, _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_prefill_chunk")
+    return out

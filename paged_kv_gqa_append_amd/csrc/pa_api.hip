@@ -1,0 +1,172 @@
+// pa_api.hip -- the C ABI of libpa.so: argument checks, workspace sizing, launches.
+//
+// Every entry point validates what the host can see (pointers, sizes,
+// alignment, geometry) and returns a status before launching anything; see
+// include/pa.h for the contract.  Nothing here allocates or synchronises.
+#include <math.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t decode_num_parts(int32_t max_blocks) {
+    const int pp = pa::decode_part_pages();
+    return (static_cast<int64_t>(max_blocks) + pp - 1) / pp;
+}
+
+
+// Shared argument checks and launch of the plain and the append-fused decode.
+pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                        const int32_t *block_tables, const int32_t *context_lens, const float *rope,
+                        int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
+                        float scale, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                        uint32_t *device_flags, hipStream_t stream, bool fused) {
+    if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (fused && max_pos < 1) return PA_ERR_INVALID_ARG;
+    if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+    if (out_dtype != PA_OUT_BF16 && out_dtype != PA_OUT_FP32) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(block_tables) ||
+        !aligned16(context_lens))
+        return PA_ERR_INVALID_ARG;
+    if (fused && (!k_new || !v_new || !rope || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rope)))
+        return PA_ERR_INVALID_ARG;
+    const int64_t np = decode_num_parts(max_blocks);
+    const size_t need = pa_decode_workspace_bytes(num_seqs, max_blocks);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PA_ERR_WORKSPACE;
+    float *ws = static_cast<float *>(workspace);
+    const int64_t rows = static_cast<int64_t>(num_seqs) * PA_NUM_Q_HEADS * np;
+    pa::DecodeLaunch d{};
+    d.out = out;
+    d.q = q;
+    d.k_new = k_new;
+    d.v_new = v_new;
+    d.rope = rope;
+    d.max_pos = max_pos;
+    d.fused = fused;
+    d.write_q = fused && out != q;
+    d.k_pool = k_pool;
+    d.v_pool = v_pool;
+    d.block_tables = block_tables;
+    d.context_lens = context_lens;
+    d.num_seqs = num_seqs;
+    d.max_blocks = max_blocks;
+    d.num_pages = num_pages;
+    d.scale = scale;
+    d.out_fp32 = out_dtype == PA_OUT_FP32;
+    d.part_pages = pa::decode_part_pages();
+    d.num_parts = static_cast<int>(np);
+    d.ws_ml = need ? ws : nullptr;
+    d.ws_acc = need ? ws + rows * 2 : nullptr;
+    d.flags = device_flags;
+    return pa::launch_decode(d, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+        default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+int32_t pa_abi_version(void) { return 1; }
+
+pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
+    if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
+    for (int32_t pos = 0; pos < max_pos; ++pos) {
+        for (int i = 0; i < PA_HEAD_DIM / 2; ++i) {
+            const double w = pow(theta, -(2.0 * i) / PA_HEAD_DIM);
+            const double a = static_cast<double>(pos) * w;
+            cos_sin_host[(static_cast<int64_t>(pos) * (PA_HEAD_DIM / 2) + i) * 2] = static_cast<float>(cos(a));
+            cos_sin_host[(static_cast<int64_t>(pos) * (PA_HEAD_DIM / 2) + i) * 2 + 1] = static_cast<float>(sin(a));
+        }
+    }
+    return PA_OK;
+}
+
+pa_status pa_append_kv_rope(void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                            const int32_t *block_tables, const int32_t *context_lens, const float *rope_cos_sin,
+                            int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size,
+                            int32_t max_pos, uint32_t *device_flags, hipStream_t stream) {
+    if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1) return PA_ERR_INVALID_ARG;
+    if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens || !rope_cos_sin)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        !aligned16(block_tables) || !aligned16(context_lens) || !aligned16(rope_cos_sin) || (q && !aligned16(q)))
+        return PA_ERR_INVALID_ARG;
+    pa::AppendLaunch a{q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin,
+                       num_seqs, 1, 0, max_blocks, num_pages, max_pos, device_flags};
+    return pa::launch_append_rope(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks) {
+    if (num_seqs <= 0 || max_blocks <= 0) return 0;
+    const int64_t np = decode_num_parts(max_blocks);
+    if (np <= 1) return 0;
+    const int64_t rows = static_cast<int64_t>(num_seqs) * PA_NUM_Q_HEADS * np;
+    return static_cast<size_t>(rows * (2 + PA_HEAD_DIM) * sizeof(float));
+}
+
+int32_t pa_decode_partition_tokens(void) { return pa::decode_part_pages() * PA_PAGE_SIZE; }
+
+pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void *v_pool,
+                        const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                        int32_t max_blocks, int32_t num_pages, int32_t page_size, float scale, int32_t out_dtype,
+                        void *workspace, size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream) {
+    return decode_common(out, const_cast<void *>(q), nullptr, nullptr, const_cast<void *>(k_pool),
+                         const_cast<void *>(v_pool), block_tables, context_lens, nullptr, num_seqs, max_blocks,
+                         num_pages, page_size, 0, scale, out_dtype, workspace, workspace_bytes, device_flags, stream,
+                         false);
+}
+
+pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
+                               const int32_t *block_tables, const int32_t *context_lens, const float *rope_cos_sin,
+                               int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size,
+                               int32_t max_pos, float scale, int32_t out_dtype, void *workspace,
+                               size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream) {
+    return decode_common(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin, num_seqs,
+                         max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace, workspace_bytes,
+                         device_flags, stream, true);
+}
+
+pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool, void *v_pool,
+                           const int32_t *block_tables, const int32_t *prefix_lens, const float *rope_cos_sin,
+                           int32_t num_seqs, int32_t chunk_len, int32_t max_blocks, int32_t num_pages,
+                           int32_t page_size, int32_t max_pos, float scale, int32_t out_dtype,
+                           uint32_t *device_flags, hipStream_t stream) {
+    if (num_seqs < 0 || chunk_len < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1 || !isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+    if (pa::launch_prefill_attention(pa::PrefillLaunch{}, nullptr) == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+    if (out_dtype != PA_OUT_BF16 && out_dtype != PA_OUT_FP32) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || chunk_len == 0) return PA_OK;
+    if (!out || !q || !k_chunk || !v_chunk || !k_pool || !v_pool || !block_tables || !prefix_lens || !rope_cos_sin)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(k_pool) ||
+        !aligned16(v_pool) || !aligned16(block_tables) || !aligned16(prefix_lens) || !aligned16(rope_cos_sin))
+        return PA_ERR_INVALID_ARG;
+    pa::AppendLaunch a{q, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin,
+                       num_seqs, chunk_len, 1, max_blocks, num_pages, max_pos, device_flags};
+    if (pa::launch_append_rope(a, stream) != hipSuccess) return PA_ERR_HIP;
+    pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, num_seqs, chunk_len, max_blocks,
+                        num_pages, scale, out_dtype == PA_OUT_FP32, device_flags};
+    return pa::launch_prefill_attention(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,546 @@
+// pa_decode.hip -- split-context paged GQA decode attention for gfx950,
+// optionally fused with the KV append + RoPE of the token being decoded.
+//
+// What is computed: for every sequence s and query head h (KV head j = h/4),
+// softmax(scale * q K^T) V over the sequence's L tokens, where K/V rows are
+// found through the sequence's block table (samir-vllm article, section
+// "Gestion de la KV cache ...": attention reads only the sequence's own
+// pages, accumulates weighted V, concatenates nothing and stores no scores).
+// The fused variant first appends the new token at position L-1 exactly as
+// pa_append_kv_rope does (same fp32 rotation, same bf16 rounding) and rotates
+// q in registers, so its results are bitwise those of append-then-decode.
+//
+// Work decomposition
+//   A workgroup of kWaves waves serves one (sequence, KV head, context
+//   partition): the 4 query heads of that KV head share every K/V byte, which
+//   is read from HBM exactly once.  Waves take the partition's pages
+//   round-robin, one 16-token page (a contiguous 2 KiB K tile and 2 KiB V tile
+//   of this KV head) per step, with the next page's loads in flight.
+//
+//   Lanes form 8 groups of 8 (lane = 8g + c).  Every lane holds, for tokens
+//   g and g+8 of the page, the 16-byte chunk c*8..c*8+7 of K and of V.
+//   q.K: each lane forms the partial dot products of its chunk for the 8
+//   (token, head) pairs of its group, then a 3-step reduce-scatter over the 8
+//   lanes (DPP lane permutes) leaves every lane with ONE complete score.  For
+//   that to need no selects, lane c keeps its K tokens and q heads in an
+//   order permuted by its lane bits (tokens by b0^b2, heads by the mask
+//   hm(c)): lane c ends up owning pair (token half b0^b2, head hm(c)).
+//   Softmax: online, in log2 units (scale*log2 e folded in), with a running
+//   max per head that is uniform across the wave and only raised when a score
+//   exceeds it by more than 2^8 (lazy rescale; the final division uses sums
+//   taken with the same max, so the result is exact in exact arithmetic).
+//   Each lane exponentiates only its own score; 9 DPP moves broadcast the 8
+//   weights of the group back to all its lanes, whose V chunk slots and
+//   accumulator head slots are permuted to match (V tokens by b2, heads by 3*b2).
+//   Epilogue: plain sums across the 8 lane groups (one running max per wave),
+//   then an LDS merge of the waves (each with its own max).  A sequence whose
+//   context fits one partition writes its output directly; longer ones leave
+//   (max, sum, acc[64]) per head and partition in the workspace for
+//   k_decode_merge.
+//
+// The partition size depends on nothing but a constant, so a sequence's
+// output is bitwise independent of the batch around it.
+#include <math.h>
+#include <stdlib.h>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+constexpr int kMaxPartPages = 128;
+constexpr float kNegBig = -1.0e30f;   // running-max start (finite, so 2^(x - m) is never NaN)
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold
+
+// quad_perm broadcasts of quad lane a to the whole quad: [a,a,a,a]
+constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRowRor8 = 0x128;
+
+struct KVRegs {
+    u32x4 ka, kb, v0, v1;
+};
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+    const int lane = __lane_id();
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, v)));
+}
+
+// Sum over the 8 lane groups (lanes c, c+8, ..., c+56).
+__device__ __forceinline__ float sum_groups(float v) {
+    v += dpp_f32<kRowRor8>(v);
+    v += shfl_xor_f32(v, 16);
+    v += shfl_xor_f32(v, 32);
+    return v;
+}
+__device__ __forceinline__ float max_groups(float v) {
+    v = fmaxf(v, dpp_f32<kRowRor8>(v));
+    v = fmaxf(v, shfl_xor_f32(v, 16));
+    v = fmaxf(v, shfl_xor_f32(v, 32));
+    return v;
+}
+
+// Score of the lane's own (token, head) pair for one page: partial dots of the
+// lane's 8-element chunk for the 8 pairs of its group (slot i < 4: token half
+// t0, head i^hm; slot i >= 4: token half t0^1), then a reduce-scatter over the
+// 8 lanes with partners c^1, c^2 and c^7.  Returns scale*log2(e)*<q, k>.
+__device__ __forceinline__ float page_score(const u32x4 (&qv)[kGroup], u32x4 ka, u32x4 kb, float scale_log2) {
+    float sa[kGroup], sb[kGroup];
+#pragma unroll
+    for (int m = 0; m < kGroup; ++m) {
+        sa[m] = dot8_bf16(qv[m], ka, 0.0f);
+        sb[m] = dot8_bf16(qv[m], kb, 0.0f);
+    }
+    const float r0 = sa[0] + dpp_f32<kXor1>(sb[0]);
+    const float r1 = sa[1] + dpp_f32<kXor1>(sb[1]);
+    const float r2 = sa[2] + dpp_f32<kXor1>(sb[2]);
+    const float r3 = sa[3] + dpp_f32<kXor1>(sb[3]);
+    const float u0 = r0 + dpp_f32<kXor2>(r2);
+    const float u1 = r1 + dpp_f32<kXor2>(r3);
+    return (u0 + dpp_f32<kHalfMirror>(u1)) * scale_log2;
+}
+
+// Online-softmax step for one page: lazily raise the wave's running max of the
+// lane's head (rescaling the accumulators of all 4 heads when any lane needs
+// it), then return the lane's weight 2^(x - m).
+__device__ __forceinline__ float softmax_step(float x, float &m_run, float &l_run, float (&acc)[kGroup][8]) {
+    const float xm = fmaxf(x, dpp_f32<kXor1>(x));  // this page's max for the head (both tokens)
+    if (__builtin_amdgcn_ballot_w64(xm > m_run + kRescaleLog2)) {
+        const float wm = max_groups(xm);
+        const float mn = wm > m_run + kRescaleLog2 ? wm : m_run;
+        const float f = fast_exp2(m_run - mn);
+        m_run = mn;
+        l_run *= f;
+        // factors per accumulator slot, routed like the weights in accumulate()
+        const float fm = dpp_f32<kHalfMirror>(f);
+        const float F0 = dpp_f32<kBcast0>(f), F2 = dpp_f32<kBcast2>(f);
+        const float G0 = dpp_f32<kBcast0>(fm), G2 = dpp_f32<kBcast2>(fm);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[0][i] *= F0;
+            acc[1][i] *= G0;
+            acc[2][i] *= F2;
+            acc[3][i] *= G2;
+        }
+    }
+    const float pw = fast_exp2(x - m_run);
+    l_run += pw;
+    return pw;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
+    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f[2 * k] = bf16_lo(a[k]);
+        f[2 * k + 1] = bf16_hi(a[k]);
+    }
+}
+
+// acc[e] += sum over the group's 8 (token, head) weights of w * V[token]: P_a is
+// the weight held by quad lane a, Q_a that of its mirror lane; V slot u (va/vb)
+// and accumulator slot e are permuted by the lane bits so that quad lane a's
+// pair always lands in slot e = 2*(a>>1) with V slot a&1 (Q_a: e + 1).
+__device__ __forceinline__ void accumulate(float pw, const float (&va)[8], const float (&vb)[8],
+                                           float (&acc)[kGroup][8]) {
+    const float pm = dpp_f32<kHalfMirror>(pw);
+    const float P0 = dpp_f32<kBcast0>(pw), P1 = dpp_f32<kBcast1>(pw);
+    const float P2 = dpp_f32<kBcast2>(pw), P3 = dpp_f32<kBcast3>(pw);
+    const float Q0 = dpp_f32<kBcast0>(pm), Q1 = dpp_f32<kBcast1>(pm);
+    const float Q2 = dpp_f32<kBcast2>(pm), Q3 = dpp_f32<kBcast3>(pm);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        acc[0][i] = fmaf(P0, va[i], fmaf(P1, vb[i], acc[0][i]));
+        acc[1][i] = fmaf(Q0, va[i], fmaf(Q1, vb[i], acc[1][i]));
+        acc[2][i] = fmaf(P2, va[i], fmaf(P3, vb[i], acc[2][i]));
+        acc[3][i] = fmaf(Q2, va[i], fmaf(Q3, vb[i], acc[3][i]));
+    }
+}
+
+// Rotate-half RoPE of the 8 elements d = c*8 .. c*8+7 of a 64-wide bf16 row,
+// given this chunk (x) and its partner chunk c^4 (xp): for d < 32,
+// y = x*cos - x[d+32]*sin; for d >= 32, y = x*cos + x[d-32]*sin.  The same
+// fp32 operations as k_append_rope, so the rounded results are identical.
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, u32x4 xp, const float *cs /* 8 x (cos, sin) */, bool upper) {
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    const uint32_t pw[4] = {xp.x, xp.y, xp.z, xp.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float y[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float xv = e ? bf16_hi(xw[k]) : bf16_lo(xw[k]);
+            const float pv = e ? bf16_hi(pw[k]) : bf16_lo(pw[k]);
+            const float co = cs[2 * (2 * k + e)], si = cs[2 * (2 * k + e) + 1];
+            y[e] = upper ? fmaf(xv, co, pv * si) : fmaf(xv, co, -(pv * si));
+        }
+        out[k] = pack_bf16x2(y[0], y[1]);
+    }
+    return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+struct DecodeParams {
+    void *out;
+    uint16_t *q;
+    const uint16_t *k_new;
+    const uint16_t *v_new;
+    uint16_t *k_pool;
+    uint16_t *v_pool;
+    const int32_t *bt;
+    const int32_t *lens;
+    const float *rope;
+    int max_blocks;
+    int num_pages;
+    int max_pos;
+    float scale_log2;
+    int out_fp32;
+    int part_pages;
+    int num_parts;
+    int write_q;          // fused only: store the rotated q back (out does not alias q)
+    float *ws_ml;
+    float *ws_acc;
+    uint32_t *flags;
+};
+
+template <int kWaves, bool kFused>
+__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P) {
+    constexpr int kThreads = 64 * kWaves;
+    const int part = blockIdx.x % P.num_parts;
+    const int sj = blockIdx.x / P.num_parts;
+    const int j = sj & (kHKV - 1);
+    const int s = sj >> 3;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+
+    __shared__ int s_pages[kMaxPartPages];
+    __shared__ float s_m[kWaves][kGroup];
+    __shared__ float s_l[kWaves][kGroup];
+    __shared__ float s_acc[kWaves][kGroup][kD];
+    __shared__ u32x4 s_new[2][8];  // appended K and V row, 8 chunks each (fused)
+
+    // ---- page ids of this partition (speculative, independent of L) and L -
+    const int pg0 = part * P.part_pages;
+    const int slice = min(P.part_pages, P.max_blocks - pg0);
+    const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
+    int my_page = 0;
+    if (tid < slice) my_page = bt_row[pg0 + tid];
+    const int L = P.lens[s];
+    bool len_ok = (L >= 1) && (L <= P.max_blocks * kPage);
+    if (kFused) len_ok = len_ok && (L - 1 < P.max_pos);
+    const int n_pages = len_ok ? (L + kPage - 1) / kPage : 0;
+    const int n_parts_s = (n_pages + P.part_pages - 1) / P.part_pages;
+    const int pg1 = min(pg0 + P.part_pages, n_pages);
+    int bad = 0;
+    if (tid < slice) {
+        s_pages[tid] = my_page;
+        bad = (pg0 + tid < n_pages) && (my_page < 0 || my_page >= P.num_pages);
+    }
+    bool ok = len_ok && (__syncthreads_or(bad) == 0);
+    if (ok && n_parts_s > 1) {  // long context: the whole row decides, as in every partition
+        int b2 = 0;
+        for (int b = tid; b < n_pages; b += kThreads) {
+            const int p = bt_row[b];
+            b2 |= (p < 0) | (p >= P.num_pages);
+        }
+        ok = __syncthreads_or(b2) == 0;
+    }
+    if (!ok) {
+        if (part == 0 && tid < kGroup * kD) {  // zero this KV head's 4 output rows, flag once
+            const int64_t o = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD + tid;
+            if (P.out_fp32) static_cast<float *>(P.out)[o] = 0.0f;
+            else static_cast<uint16_t *>(P.out)[o] = 0;
+            if (tid == 0 && P.flags) atomicOr(P.flags, len_ok ? kDevErrPageId : kDevErrContextLen);
+        }
+        return;
+    }
+    if (part >= n_parts_s) return;
+
+    // ---- lane roles --------------------------------------------------------
+    const int g = lane >> 3;
+    const int c = lane & 7;
+    const int b0 = c & 1, b1 = (c >> 1) & 1, b2 = c >> 2;
+    const int t0 = b0 ^ b2;                    // token half of K slot A
+    const int hm = ((b1 ^ b2) << 1) | b2;      // q slot m holds head m ^ hm
+    // element offsets in a tile; bit 9 (8 tokens x 64) selects the token half
+    const uint32_t offA = (g + 8 * t0) * kD + c * 8;
+    const uint32_t offV0 = (g + 8 * b2) * kD + c * 8;  // V slot u holds token half u ^ b2
+
+    // ---- first page's loads go out before anything else -------------------
+    const int64_t tile_j = static_cast<int64_t>(j) * kTile;
+    auto load_page = [&](int p) {
+        // the page id is uniform: keep the tile base in scalar registers
+        const int64_t base = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pages[p - pg0])) * kPageElems + tile_j;
+        const uint16_t *kt = P.k_pool + base;
+        const uint16_t *vt = P.v_pool + base;
+        KVRegs r;
+        r.ka = *reinterpret_cast<const u32x4 *>(kt + offA);
+        r.kb = *reinterpret_cast<const u32x4 *>(kt + (offA ^ 512u));
+        r.v0 = *reinterpret_cast<const u32x4 *>(vt + offV0);
+        r.v1 = *reinterpret_cast<const u32x4 *>(vt + (offV0 ^ 512u));
+        return r;
+    };
+    int p = pg0 + w;
+    KVRegs cur;
+    if (p < pg1) cur = load_page(p);
+
+    // ---- q (rotated in registers when fused) and the appended row ----------
+    const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
+    u32x4 qv[kGroup];
+    const int pos = L - 1;
+    if (kFused) {
+        const float *cs = P.rope + static_cast<int64_t>(pos) * kD + (c & 3) * 16;  // 8 (cos, sin) pairs
+        float csr[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(cs + 4 * k);
+            csr[4 * k] = t.x; csr[4 * k + 1] = t.y; csr[4 * k + 2] = t.z; csr[4 * k + 3] = t.w;
+        }
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m) {
+            const uint16_t *row = P.q + qrow0 + (m ^ hm) * kD;
+            qv[m] = rope_chunk(*reinterpret_cast<const u32x4 *>(row + c * 8),
+                               *reinterpret_cast<const u32x4 *>(row + (c ^ 4) * 8), csr, c >= 4);
+        }
+        // Append (last partition only): lanes 0..7 rotate chunk c of the new K row,
+        // store K and V into the token's slot, and leave both chunks in LDS for the
+        // wave that will meet the token in its page (the slot is never read back).
+        if (part == n_parts_s - 1 && tid < 8) {
+            const int64_t nrow = (static_cast<int64_t>(s) * kHKV + j) * kD;
+            const u32x4 nk = rope_chunk(*reinterpret_cast<const u32x4 *>(P.k_new + nrow + c * 8),
+                                        *reinterpret_cast<const u32x4 *>(P.k_new + nrow + (c ^ 4) * 8), csr, c >= 4);
+            const u32x4 nv = *reinterpret_cast<const u32x4 *>(P.v_new + nrow + c * 8);
+            s_new[0][c] = nk;
+            s_new[1][c] = nv;
+            const int64_t dst = static_cast<int64_t>(s_pages[(pos >> 4) - pg0]) * kPageElems + tile_j +
+                                (pos & (kPage - 1)) * kD + c * 8;
+            *reinterpret_cast<u32x4 *>(P.k_pool + dst) = nk;
+            *reinterpret_cast<u32x4 *>(P.v_pool + dst) = nv;
+        }
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8);
+    }
+
+    // ---- per-lane softmax state ----------------------------------------------
+    float m_run = kNegBig;  // running max (log2 units) of head hm, uniform over the wave
+    float l_run = 0.0f;     // sum of this lane's own weights (pair token t0, head hm)
+    float acc[kGroup][8];   // slot e = head e ^ (3*b2), elements c*8 .. c*8+7
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[e][i] = 0.0f;
+
+    // One page.  process_full: any page but the sequence's last; process_last: the
+    // last page, which may be partly empty and, when fused, holds the appended token
+    // (its dead slots may hold anything, NaN included, so they are selected out).
+    auto process_full = [&](const KVRegs &r) {
+        const float x = page_score(qv, r.ka, r.kb, P.scale_log2);
+        const float pw = softmax_step(x, m_run, l_run, acc);
+        float va[8], vb[8];
+        unpack8(r.v0, va);
+        unpack8(r.v1, vb);
+        accumulate(pw, va, vb, acc);
+    };
+    auto process_last = [&](KVRegs r, int p) {
+        if (kFused && g == (pos & 7)) {  // patch the appended token into the registers
+            const u32x4 nk = s_new[0][c], nv = s_new[1][c];
+            const int half = (pos >> 3) & 1;
+            if (half == t0) r.ka = nk; else r.kb = nk;
+            if (half == b2) r.v0 = nv; else r.v1 = nv;
+        }
+        const int tb = p * kPage;
+        float x = page_score(qv, r.ka, r.kb, P.scale_log2);
+        if (tb + g + 8 * t0 >= L) x = -INFINITY;
+        const float pw = softmax_step(x, m_run, l_run, acc);
+        float va[8], vb[8];
+        unpack8(r.v0, va);
+        unpack8(r.v1, vb);
+        const bool ok0 = tb + g + 8 * b2 < L, ok1 = tb + g + 8 * (b2 ^ 1) < L;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            va[i] = ok0 ? va[i] : 0.0f;
+            vb[i] = ok1 ? vb[i] : 0.0f;
+        }
+        accumulate(pw, va, vb, acc);
+    };
+    // Full pages: two register sets in turn, the next page's loads always in flight.
+    // The sequence's last page is the final page of the wave that owns it; it is
+    // prefetched like any other and handled after the loop.
+    const int p_stop = (pg1 == n_pages) ? n_pages - 1 : pg1;
+    KVRegs alt;
+    bool last_in_alt = false;
+    while (p < p_stop) {
+        if (p + kWaves < pg1) alt = load_page(p + kWaves);
+        process_full(cur);
+        p += kWaves;
+        if (p >= p_stop) { last_in_alt = true; break; }
+        if (p + kWaves < pg1) cur = load_page(p + kWaves);
+        process_full(alt);
+        p += kWaves;
+    }
+    if (pg1 == n_pages && p == n_pages - 1) {  // this wave owns the sequence's last page
+        if (last_in_alt) cur = alt;
+        process_last(cur, p);
+    }
+    // ---- wave epilogue: sums over the 8 lane groups (one max per wave) -----
+    float l_tot = l_run + dpp_f32<kXor1>(l_run);
+    l_tot = sum_groups(l_tot);
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[e][i] = sum_groups(acc[e][i]);
+    if (g == 0) {
+#pragma unroll
+        for (int e = 0; e < kGroup; ++e) {
+            const int h = e ^ (3 * b2);
+            *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8]) = f32x4{acc[e][0], acc[e][1], acc[e][2], acc[e][3]};
+            *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8 + 4]) = f32x4{acc[e][4], acc[e][5], acc[e][6], acc[e][7]};
+        }
+        if (b0 == 0) {
+            s_m[w][hm] = m_run;
+            s_l[w][hm] = l_tot;
+        }
+    }
+    __syncthreads();
+
+    // every wave has read q by now: the rotated q can be stored (fused, single partition)
+    if (kFused && P.write_q && n_parts_s == 1 && w == 0 && g == 0) {
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m)
+            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8) = qv[m];
+    }
+
+    // ---- merge the waves: thread (h, d) --------------------------------------
+    if (tid < kGroup * kD) {
+        const int h = tid >> 6;
+        const int d = tid & 63;
+        float M = kNegBig;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) M = fmaxf(M, s_m[k][h]);
+        float Ls = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            const float wgt = fast_exp2(s_m[k][h] - M);
+            Ls = fmaf(wgt, s_l[k][h], Ls);
+            A = fmaf(wgt, s_acc[k][h][d], A);
+        }
+        const int qh = j * kGroup + h;
+        if (n_parts_s == 1) {
+            const int64_t o = (static_cast<int64_t>(s) * kHQ + qh) * kD + d;
+            const float r = A / Ls;
+            if (P.out_fp32) static_cast<float *>(P.out)[o] = r;
+            else static_cast<uint16_t *>(P.out)[o] = f32_to_bf16(r);
+        } else {
+            const int64_t row = (static_cast<int64_t>(s) * kHQ + qh) * P.num_parts + part;
+            P.ws_acc[row * kD + d] = A;
+            if (d == 0) {
+                P.ws_ml[row * 2] = M;
+                P.ws_ml[row * 2 + 1] = Ls;
+            }
+        }
+    }
+}
+
+// One wave per (sequence, query head): merge that head's partitions.  In the
+// fused variant it also stores the rotated q row (all partitions have read q).
+template <bool kFused>
+__global__ __launch_bounds__(64) void k_decode_merge(DecodeParams P) {
+    const int s = blockIdx.x / kHQ;
+    const int qh = blockIdx.x % kHQ;
+    const int d = threadIdx.x;
+    const int L = P.lens[s];
+    bool len_ok = (L >= 1) && (L <= P.max_blocks * kPage);
+    if (kFused) len_ok = len_ok && (L - 1 < P.max_pos);
+    if (!len_ok) return;  // zero-filled by the partial kernel
+    const int n_pages = (L + kPage - 1) / kPage;
+    const int n_parts_s = (n_pages + P.part_pages - 1) / P.part_pages;
+    if (n_parts_s <= 1) return;  // written directly by the partial kernel
+    const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
+    int bad = 0;
+    for (int b = d; b < n_pages; b += 64) bad |= (bt_row[b] < 0) | (bt_row[b] >= P.num_pages);
+    if (__syncthreads_or(bad)) return;
+    const int64_t row0 = (static_cast<int64_t>(s) * kHQ + qh) * P.num_parts;
+    float M = kNegBig;
+    for (int k = 0; k < n_parts_s; ++k) M = fmaxf(M, P.ws_ml[(row0 + k) * 2]);
+    float Ls = 0.0f, A = 0.0f;
+    for (int k = 0; k < n_parts_s; ++k) {
+        const float wgt = fast_exp2(P.ws_ml[(row0 + k) * 2] - M);
+        Ls = fmaf(wgt, P.ws_ml[(row0 + k) * 2 + 1], Ls);
+        A = fmaf(wgt, P.ws_acc[(row0 + k) * kD + d], A);
+    }
+    const int64_t o = (static_cast<int64_t>(s) * kHQ + qh) * kD + d;
+    if (kFused && P.write_q) {
+        const int pos = L - 1;
+        const int i = d & 31;
+        const float co = P.rope[static_cast<int64_t>(pos) * kD + 2 * i];
+        const float si = P.rope[static_cast<int64_t>(pos) * kD + 2 * i + 1];
+        uint16_t *qr = P.q + o - d;
+        const float xv = bf16_to_f32(qr[d]);
+        const float pv = bf16_to_f32(qr[d ^ 32]);
+        const float y = d >= 32 ? fmaf(xv, co, pv * si) : fmaf(xv, co, -(pv * si));
+        __syncthreads();  // both halves read before either is written
+        qr[d] = f32_to_bf16(y);
+    }
+    const float r = A / Ls;
+    if (P.out_fp32) static_cast<float *>(P.out)[o] = r;
+    else static_cast<uint16_t *>(P.out)[o] = f32_to_bf16(r);
+}
+
+int decode_part_pages() {
+    static int cached = [] {
+        int v = kMaxPartPages;  // 2048 tokens: one partition for every context up to 2048
+        if (const char *e = getenv("PA_DECODE_PART_PAGES")) {
+            const int x = atoi(e);
+            if (x >= 1 && x <= kMaxPartPages) v = x;
+        }
+        return v;
+    }();
+    return cached;
+}
+
+constexpr int kDecodeWaves = 8;
+
+hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream) {
+    if (d.num_seqs == 0) return hipSuccess;
+    DecodeParams P{};
+    P.out = d.out;
+    P.q = static_cast<uint16_t *>(d.q);
+    P.k_new = static_cast<const uint16_t *>(d.k_new);
+    P.v_new = static_cast<const uint16_t *>(d.v_new);
+    P.k_pool = static_cast<uint16_t *>(d.k_pool);
+    P.v_pool = static_cast<uint16_t *>(d.v_pool);
+    P.bt = d.block_tables;
+    P.lens = d.context_lens;
+    P.rope = d.rope;
+    P.max_blocks = d.max_blocks;
+    P.num_pages = d.num_pages;
+    P.max_pos = d.max_pos;
+    P.scale_log2 = d.scale * 1.4426950408889634f;
+    P.out_fp32 = d.out_fp32;
+    P.part_pages = d.part_pages;
+    P.num_parts = d.num_parts;
+    P.write_q = d.write_q;
+    P.ws_ml = d.ws_ml;
+    P.ws_acc = d.ws_acc;
+    P.flags = d.flags;
+    const int64_t blocks = static_cast<int64_t>(d.num_seqs) * kHKV * d.num_parts;
+    if (d.fused)
+        hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(64 * kDecodeWaves), 0, stream, P);
+    else
+        hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(64 * kDecodeWaves), 0, stream, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || d.num_parts == 1) return e;
+    if (d.fused)
+        hipLaunchKernelGGL((k_decode_merge<true>), dim3(static_cast<unsigned>(d.num_seqs * kHQ)), dim3(64), 0, stream,
+                           P);
+    else
+        hipLaunchKernelGGL((k_decode_merge<false>), dim3(static_cast<unsigned>(d.num_seqs * kHQ)), dim3(64), 0, stream,
+                           P);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,72 @@
+// pa_device.h -- small device helpers shared by the libpa kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kHQ = 32;       // query heads
+constexpr int kHKV = 8;       // KV heads
+constexpr int kGroup = 4;     // query heads per KV head
+constexpr int kD = 64;        // head dim
+constexpr int kPage = 16;     // tokens per page
+constexpr int kTile = kPage * kD;          // elements of one (page, kv head) tile
+constexpr int kPageElems = kHKV * kTile;   // elements of one page (all heads)
+
+constexpr uint32_t kDevErrContextLen = 0x1u;
+constexpr uint32_t kDevErrPageId = 0x2u;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// <a, b> over the 8 bf16 elements held in two 16-byte words, fp32 accumulation.
+// The words are reinterpreted whole and split with shufflevector: hipcc 7.2
+// mis-lowers __builtin_bit_cast applied to a single vector element (a.x) into
+// a reload of element 0, which would feed the same pair to all four dot2s.
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, a);
+    const bf16x8 y = __builtin_bit_cast(bf16x8, b);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), __builtin_shufflevector(y, y, 0, 1), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), __builtin_shufflevector(y, y, 2, 3), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), __builtin_shufflevector(y, y, 4, 5), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), __builtin_shufflevector(y, y, 6, 7), acc, false);
+    return acc;
+}
+
+// Data-parallel-primitive lane permutes (DPP).  Control codes (GCN/CDNA):
+//   quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+//   row_half_mirror = 0x141 (lane i <-> 7-i within each 8 lanes),
+//   row_ror:8 = 0x128 (lane i <-> i^8 within each 16 lanes).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over the 8 consecutive lanes of an aligned lane group; every lane gets it.
+__device__ __forceinline__ float sum_lanes8(float v) {
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

@@ -1,0 +1,77 @@
+// pa_internal.h -- launch descriptors passed from the C-ABI layer to the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct AppendLaunch {
+    void *q;              // may be null
+    const void *k_new;
+    const void *v_new;
+    void *k_pool;
+    void *v_pool;
+    const int32_t *block_tables;
+    const int32_t *lens;  // context lengths (decode) or prefix lengths (prefill)
+    const float *rope;
+    int num_seqs;
+    int tokens_per_seq;
+    int prefix_mode;      // 0: pos = lens[s]-1, 1: pos = lens[s]+i
+    int max_blocks;
+    int num_pages;
+    int max_pos;
+    uint32_t *flags;
+};
+
+struct DecodeLaunch {
+    void *out;
+    void *q;              // read-only unless fused (then rotated in place when write_q)
+    const void *k_new;    // fused only
+    const void *v_new;    // fused only
+    const float *rope;    // fused only
+    int max_pos;          // fused only
+    int fused;            // 1: append the token at L-1 and rotate q first
+    int write_q;          // fused only: store the rotated q (out does not alias q)
+    void *k_pool;
+    void *v_pool;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int num_seqs;
+    int max_blocks;
+    int num_pages;
+    float scale;
+    int out_fp32;
+    int part_pages;       // pages per context partition
+    int num_parts;        // ceil(max_blocks / part_pages)
+    float *ws_ml;         // [B][32][num_parts][2]  (max in log2 units, sum of weights)
+    float *ws_acc;        // [B][32][num_parts][64]
+    uint32_t *flags;
+};
+
+struct PrefillLaunch {
+    void *out;
+    const void *q;        // already rotated
+    const void *k_pool;
+    const void *v_pool;
+    const int32_t *block_tables;
+    const int32_t *prefix_lens;
+    int num_seqs;
+    int chunk_len;
+    int max_blocks;
+    int num_pages;
+    float scale;
+    int out_fp32;
+    uint32_t *flags;
+};
+
+// Decode partition size in pages (fixed per process; the default can be
+// overridden with PA_DECODE_PART_PAGES for tuning runs).
+int decode_part_pages();
+
+hipError_t launch_append_rope(const AppendLaunch &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,137 @@
+"""Host-side checks of libpa.so that need no GPU.
+
+* every function include/pa.h declares is exported;
+* host validation returns its status before any launch (so these calls are
+  safe without a device: each one is invalid in some host-visible way);
+* workspace sizing and the fp64 -> fp32 RoPE table builder.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+@pytest.fixture(scope="module")
+def pa():
+    from paged_kv_gqa_append_amd import binding, build
+
+    if not build.is_built():
+        build.build()
+    binding.lib()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(pa):
+    names = declared_functions()
+    assert set(names) >= {"pa_append_kv_rope", "pa_decode_gqa", "pa_prefill_chunk"}
+    lib = pa.lib()
+    for n in names:
+        assert hasattr(lib, n), f"libpa.so does not export {n}"
+    assert set(pa.EXPORTS) == set(names)
+
+
+def test_status_strings(pa):
+    assert pa.status_string(0) == "PA_OK"
+    assert pa.status_string(3) == "PA_ERR_WORKSPACE"
+    assert pa.status_string(99) == "PA_ERR_UNKNOWN"
+    assert pa.lib().pa_abi_version() == 1
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def decode_call(lib, out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, B=4, mb=8, P=64, ps=16, scale=0.125,
+                odt=0, ws=None, wsb=0):
+    v = ctypes.c_void_p
+    return lib.pa_decode_gqa(v(out), v(q), v(kp), v(vp), v(bt), v(cl), B, mb, P, ps, scale, odt, v(ws) if ws else None,
+                             wsb, None, None)
+
+
+def test_decode_validation(pa):
+    lib = pa.lib()
+    assert decode_call(lib, ps=32) == pa.PA_ERR_UNSUPPORTED
+    assert decode_call(lib, odt=7) == pa.PA_ERR_UNSUPPORTED
+    assert decode_call(lib, B=-1) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, mb=0) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, P=0) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, scale=float("nan")) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, q=0) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, out=FAKE + 8) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, kp=FAKE + 2) == pa.PA_ERR_INVALID_ARG
+    # an empty batch is a no-op, whatever the pointers
+    assert decode_call(lib, B=0, q=0, out=0) == pa.PA_OK
+    # long tables need a workspace
+    mb = 128
+    need = lib.pa_decode_workspace_bytes(4, mb)
+    if need:
+        assert decode_call(lib, mb=mb) == pa.PA_ERR_WORKSPACE
+        assert decode_call(lib, mb=mb, ws=FAKE, wsb=need - 4) == pa.PA_ERR_WORKSPACE
+        assert decode_call(lib, mb=mb, ws=FAKE + 4, wsb=need) == pa.PA_ERR_WORKSPACE
+
+
+def test_workspace_arithmetic(pa):
+    lib = pa.lib()
+    pt = lib.pa_decode_partition_tokens()
+    assert pt % 16 == 0 and pt >= 16
+    pp = pt // 16
+    for B, mb in [(1, 1), (3, pp), (3, pp + 1), (64, 128), (256, 128), (7, 1000)]:
+        parts = -(-mb // pp)
+        expect = 0 if parts <= 1 else B * 32 * parts * 66 * 4
+        assert lib.pa_decode_workspace_bytes(B, mb) == expect
+    assert lib.pa_decode_workspace_bytes(0, 128) == 0
+    assert lib.pa_decode_workspace_bytes(5, 0) == 0
+
+
+def test_append_and_prefill_validation(pa):
+    lib = pa.lib()
+    v = ctypes.c_void_p
+    F = v(FAKE)
+
+    def app(q=F, kn=F, vn=F, kp=F, vp=F, bt=F, cl=F, rope=F, B=2, mb=4, P=16, ps=16, mp=64):
+        return lib.pa_append_kv_rope(q, kn, vn, kp, vp, bt, cl, rope, B, mb, P, ps, mp, None, None)
+
+    assert app(ps=8) == pa.PA_ERR_UNSUPPORTED
+    assert app(B=-2) == pa.PA_ERR_INVALID_ARG
+    assert app(mp=0) == pa.PA_ERR_INVALID_ARG
+    assert app(kn=None) == pa.PA_ERR_INVALID_ARG
+    assert app(rope=v(FAKE + 4)) == pa.PA_ERR_INVALID_ARG
+    assert app(q=v(FAKE + 2)) == pa.PA_ERR_INVALID_ARG
+    assert app(B=0) == pa.PA_OK
+
+    def pre(B=2, C=8, ps=16, odt=0, q=F, mp=64):
+        return lib.pa_prefill_chunk(F, q, F, F, F, F, F, F, F, B, C, 4, 16, ps, mp, 0.125, odt, None, None)
+
+    assert pre(ps=32) == pa.PA_ERR_UNSUPPORTED
+    assert pre(C=-1) == pa.PA_ERR_INVALID_ARG
+    assert pre(mp=0) == pa.PA_ERR_INVALID_ARG
+
+
+def test_rope_table_fill(pa):
+    t = np.empty((300, 32, 2), np.float32)
+    assert pa.lib().pa_rope_table_fill_host(t.ctypes.data_as(ctypes.c_void_p), 300, 500000.0) == 0
+    pos = np.arange(300)[:, None].astype(np.float64)
+    w = 500000.0 ** (-2.0 * np.arange(32) / 64.0)
+    assert np.array_equal(t[..., 0], np.cos(pos * w).astype(np.float32))
+    assert np.array_equal(t[..., 1], np.sin(pos * w).astype(np.float32))
+    assert pa.lib().pa_rope_table_fill_host(None, 3, 500000.0) == pa.PA_ERR_INVALID_ARG
+    assert pa.lib().pa_rope_table_fill_host(t.ctypes.data_as(ctypes.c_void_p), 0, 500000.0) == pa.PA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_without_library(tmp_path, monkeypatch):
+    from paged_kv_gqa_append_amd import binding
+
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "libpa.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.lib()
