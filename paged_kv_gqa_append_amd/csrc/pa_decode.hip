@@ -60,23 +60,49 @@ struct KVRegs {
     u32x4 ka, kb, v0, v1;
 };
 
-__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
-    const int lane = __lane_id();
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, v)));
+// Lane pairs (i, i^16) and (i, i^32) through the gfx950 row-swap permutes: with
+// the same value in both operands, the two results hold the lower and the upper
+// partner's value in every lane.  Two hipcc 7.2 pitfalls are avoided: the
+// second operand passes through an empty asm, because a swap of two operands
+// known to be equal is folded into two equal results (wrong for these row-wise
+// exchanges), and each result is copied to a scalar before it is reinterpreted,
+// because __builtin_bit_cast of a vector element is lowered as a load of
+// element 0.
+__device__ __forceinline__ void xor16_pair(float v, float &lo, float &hi) {
+    const unsigned a = __builtin_bit_cast(unsigned, v);
+    unsigned b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    lo = __builtin_bit_cast(float, r0);
+    hi = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void xor32_pair(float v, float &lo, float &hi) {
+    const unsigned a = __builtin_bit_cast(unsigned, v);
+    unsigned b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    lo = __builtin_bit_cast(float, r0);
+    hi = __builtin_bit_cast(float, r1);
 }
 
-// Sum over the 8 lane groups (lanes c, c+8, ..., c+56).
+// Sum over the 8 lane groups (lanes c, c+8, ..., c+56); every lane gets it.
 __device__ __forceinline__ float sum_groups(float v) {
+    float lo, hi;
     v += dpp_f32<kRowRor8>(v);
-    v += shfl_xor_f32(v, 16);
-    v += shfl_xor_f32(v, 32);
-    return v;
+    xor16_pair(v, lo, hi);
+    v = lo + hi;
+    xor32_pair(v, lo, hi);
+    return lo + hi;
 }
 __device__ __forceinline__ float max_groups(float v) {
+    float lo, hi;
     v = fmaxf(v, dpp_f32<kRowRor8>(v));
-    v = fmaxf(v, shfl_xor_f32(v, 16));
-    v = fmaxf(v, shfl_xor_f32(v, 32));
-    return v;
+    xor16_pair(v, lo, hi);
+    v = fmaxf(lo, hi);
+    xor32_pair(v, lo, hi);
+    return fmaxf(lo, hi);
 }
 
 // Score of the lane's own (token, head) pair for one page: partial dots of the
@@ -219,13 +245,84 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     __shared__ float s_acc[kWaves][kGroup][kD];
     __shared__ u32x4 s_new[2][8];  // appended K and V row, 8 chunks each (fused)
 
-    // ---- page ids of this partition (speculative, independent of L) and L -
+    // ---- lane roles --------------------------------------------------------
+    const int g = lane >> 3;
+    const int c = lane & 7;
+    const int b0 = c & 1, b1 = (c >> 1) & 1, b2 = c >> 2;
+    const int t0 = b0 ^ b2;                    // token half of K slot A
+    const int hm = ((b1 ^ b2) << 1) | b2;      // q slot m holds head m ^ hm
+    // element offsets in a tile; bit 9 (8 tokens x 64) selects the token half
+    const uint32_t offA = (g + 8 * t0) * kD + c * 8;
+    const uint32_t offV0 = (g + 8 * b2) * kD + c * 8;  // V slot u holds token half u ^ b2
+
+    // ---- everything that does not depend on L goes out first --------------
     const int pg0 = part * P.part_pages;
     const int slice = min(P.part_pages, P.max_blocks - pg0);
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
     int my_page = 0;
     if (tid < slice) my_page = bt_row[pg0 + tid];
     const int L = P.lens[s];
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    // Wave w takes pages pg0+w, pg0+w+kWaves, ...  Its first page id is read
+    // directly, so that page's loads go out before the table reaches LDS; any id
+    // inside the pool is safe to read, and a page that turns out not to be needed
+    // (or an id that fails validation below) is simply never used.
+    const int first_id = wu < slice ? bt_row[pg0 + wu] : -1;
+    const int64_t tile_j = static_cast<int64_t>(j) * kTile;
+    auto load_tile = [&](int page_id) {
+        // the page id is uniform: keep the tile base in scalar registers
+        const int64_t base = static_cast<int64_t>(page_id) * kPageElems + tile_j;
+        const uint16_t *kt = P.k_pool + base;
+        const uint16_t *vt = P.v_pool + base;
+        KVRegs r;
+        r.ka = *reinterpret_cast<const u32x4 *>(kt + offA);
+        r.kb = *reinterpret_cast<const u32x4 *>(kt + (offA ^ 512u));
+        r.v0 = *reinterpret_cast<const u32x4 *>(vt + offV0);
+        r.v1 = *reinterpret_cast<const u32x4 *>(vt + (offV0 ^ 512u));
+        return r;
+    };
+    KVRegs cur;
+    if (first_id >= 0 && first_id < P.num_pages) cur = load_tile(first_id);
+
+    const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
+    u32x4 qv[kGroup];
+#pragma unroll
+    for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8);
+
+    // ---- fused: rotate q; lanes 0..7 of wave 0 rotate the appended K row ------
+    const int pos = L - 1;
+    u32x4 new_k = {0, 0, 0, 0}, new_v = {0, 0, 0, 0};
+    if (kFused) {
+        u32x4 qp[kGroup];
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m)
+            qp[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + (c ^ 4) * 8);
+        const int64_t nrow = (static_cast<int64_t>(s) * kHKV + j) * kD;
+        u32x4 nk_raw = {0, 0, 0, 0}, nkp_raw = {0, 0, 0, 0};
+        if (tid < 8) {
+            nk_raw = *reinterpret_cast<const u32x4 *>(P.k_new + nrow + c * 8);
+            nkp_raw = *reinterpret_cast<const u32x4 *>(P.k_new + nrow + (c ^ 4) * 8);
+            new_v = *reinterpret_cast<const u32x4 *>(P.v_new + nrow + c * 8);
+        }
+        // the table row is clamped into range: a bad L is rejected below, before any use
+        const int pos_c = min(max(pos, 0), P.max_pos - 1);
+        const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD + (c & 3) * 16;  // 8 (cos, sin) pairs
+        float csr[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(cs + 4 * k);
+            csr[4 * k] = t.x; csr[4 * k + 1] = t.y; csr[4 * k + 2] = t.z; csr[4 * k + 3] = t.w;
+        }
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m) qv[m] = rope_chunk(qv[m], qp[m], csr, c >= 4);
+        if (tid < 8) {
+            new_k = rope_chunk(nk_raw, nkp_raw, csr, c >= 4);
+            s_new[0][c] = new_k;  // read after the barrier below by the wave that owns the token
+            s_new[1][c] = new_v;
+        }
+    }
+
+    // ---- validation of device-resident lengths and page ids ---------------
     bool len_ok = (L >= 1) && (L <= P.max_blocks * kPage);
     if (kFused) len_ok = len_ok && (L - 1 < P.max_pos);
     const int n_pages = len_ok ? (L + kPage - 1) / kPage : 0;
@@ -238,12 +335,12 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     }
     bool ok = len_ok && (__syncthreads_or(bad) == 0);
     if (ok && n_parts_s > 1) {  // long context: the whole row decides, as in every partition
-        int b2 = 0;
+        int bad_row = 0;
         for (int b = tid; b < n_pages; b += kThreads) {
-            const int p = bt_row[b];
-            b2 |= (p < 0) | (p >= P.num_pages);
+            const int pid = bt_row[b];
+            bad_row |= (pid < 0) | (pid >= P.num_pages);
         }
-        ok = __syncthreads_or(b2) == 0;
+        ok = __syncthreads_or(bad_row) == 0;
     }
     if (!ok) {
         if (part == 0 && tid < kGroup * kD) {  // zero this KV head's 4 output rows, flag once
@@ -255,73 +352,16 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         return;
     }
     if (part >= n_parts_s) return;
-
-    // ---- lane roles --------------------------------------------------------
-    const int g = lane >> 3;
-    const int c = lane & 7;
-    const int b0 = c & 1, b1 = (c >> 1) & 1, b2 = c >> 2;
-    const int t0 = b0 ^ b2;                    // token half of K slot A
-    const int hm = ((b1 ^ b2) << 1) | b2;      // q slot m holds head m ^ hm
-    // element offsets in a tile; bit 9 (8 tokens x 64) selects the token half
-    const uint32_t offA = (g + 8 * t0) * kD + c * 8;
-    const uint32_t offV0 = (g + 8 * b2) * kD + c * 8;  // V slot u holds token half u ^ b2
-
-    // ---- first page's loads go out before anything else -------------------
-    const int64_t tile_j = static_cast<int64_t>(j) * kTile;
-    auto load_page = [&](int p) {
-        // the page id is uniform: keep the tile base in scalar registers
-        const int64_t base = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(s_pages[p - pg0])) * kPageElems + tile_j;
-        const uint16_t *kt = P.k_pool + base;
-        const uint16_t *vt = P.v_pool + base;
-        KVRegs r;
-        r.ka = *reinterpret_cast<const u32x4 *>(kt + offA);
-        r.kb = *reinterpret_cast<const u32x4 *>(kt + (offA ^ 512u));
-        r.v0 = *reinterpret_cast<const u32x4 *>(vt + offV0);
-        r.v1 = *reinterpret_cast<const u32x4 *>(vt + (offV0 ^ 512u));
-        return r;
-    };
-    int p = pg0 + w;
-    KVRegs cur;
-    if (p < pg1) cur = load_page(p);
-
-    // ---- q (rotated in registers when fused) and the appended row ----------
-    const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
-    u32x4 qv[kGroup];
-    const int pos = L - 1;
-    if (kFused) {
-        const float *cs = P.rope + static_cast<int64_t>(pos) * kD + (c & 3) * 16;  // 8 (cos, sin) pairs
-        float csr[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(cs + 4 * k);
-            csr[4 * k] = t.x; csr[4 * k + 1] = t.y; csr[4 * k + 2] = t.z; csr[4 * k + 3] = t.w;
-        }
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m) {
-            const uint16_t *row = P.q + qrow0 + (m ^ hm) * kD;
-            qv[m] = rope_chunk(*reinterpret_cast<const u32x4 *>(row + c * 8),
-                               *reinterpret_cast<const u32x4 *>(row + (c ^ 4) * 8), csr, c >= 4);
-        }
-        // Append (last partition only): lanes 0..7 rotate chunk c of the new K row,
-        // store K and V into the token's slot, and leave both chunks in LDS for the
-        // wave that will meet the token in its page (the slot is never read back).
-        if (part == n_parts_s - 1 && tid < 8) {
-            const int64_t nrow = (static_cast<int64_t>(s) * kHKV + j) * kD;
-            const u32x4 nk = rope_chunk(*reinterpret_cast<const u32x4 *>(P.k_new + nrow + c * 8),
-                                        *reinterpret_cast<const u32x4 *>(P.k_new + nrow + (c ^ 4) * 8), csr, c >= 4);
-            const u32x4 nv = *reinterpret_cast<const u32x4 *>(P.v_new + nrow + c * 8);
-            s_new[0][c] = nk;
-            s_new[1][c] = nv;
-            const int64_t dst = static_cast<int64_t>(s_pages[(pos >> 4) - pg0]) * kPageElems + tile_j +
-                                (pos & (kPage - 1)) * kD + c * 8;
-            *reinterpret_cast<u32x4 *>(P.k_pool + dst) = nk;
-            *reinterpret_cast<u32x4 *>(P.v_pool + dst) = nv;
-        }
-        __syncthreads();
-    } else {
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8);
+    // Append: the new row goes into its slot now that the sequence is known good
+    // (last partition only; nothing in this kernel reads the slot back).
+    if (kFused && tid < 8 && pg1 == n_pages) {
+        const int64_t dst = static_cast<int64_t>(s_pages[(pos >> 4) - pg0]) * kPageElems + tile_j +
+                            (pos & (kPage - 1)) * kD + c * 8;
+        *reinterpret_cast<u32x4 *>(P.k_pool + dst) = new_k;
+        *reinterpret_cast<u32x4 *>(P.v_pool + dst) = new_v;
     }
+    auto load_page = [&](int p) { return load_tile(__builtin_amdgcn_readfirstlane(s_pages[p - pg0])); };
+    int p = pg0 + wu;
 
     // ---- per-lane softmax state ----------------------------------------------
     float m_run = kNegBig;  // running max (log2 units) of head hm, uniform over the wave
@@ -365,9 +405,9 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         }
         accumulate(pw, va, vb, acc);
     };
-    // Full pages: two register sets in turn, the next page's loads always in flight.
-    // The sequence's last page is the final page of the wave that owns it; it is
-    // prefetched like any other and handled after the loop.
+    // Full pages: two register sets in turn, the next page's loads always in
+    // flight.  The sequence's last page is the final page of the wave that owns
+    // it; it is prefetched like any other and handled after the loop.
     const int p_stop = (pg1 == n_pages) ? n_pages - 1 : pg1;
     KVRegs alt;
     bool last_in_alt = false;
