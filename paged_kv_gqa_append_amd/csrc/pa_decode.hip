@@ -87,6 +87,23 @@ __device__ __forceinline__ void xor32_pair(float v, float &lo, float &hi) {
     hi = __builtin_bit_cast(float, r1);
 }
 
+// Reduce-scatter step on a pair of values through a row-swap permute: after
+// swap(x, y) the lanes of the lower row (or half) hold their own x and their
+// partner's x, the upper ones their partner's y and their own y, so x' + y' is
+// the pair sum of x in the lower lanes and of y in the upper lanes.
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                    false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                    false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
 // Sum over the 8 lane groups (lanes c, c+8, ..., c+56); every lane gets it.
 __device__ __forceinline__ float sum_groups(float v) {
     float lo, hi;
@@ -182,29 +199,6 @@ __device__ __forceinline__ void accumulate(float pw, const float (&va)[8], const
     }
 }
 
-// Rotate-half RoPE of the 8 elements d = c*8 .. c*8+7 of a 64-wide bf16 row,
-// given this chunk (x) and its partner chunk c^4 (xp): for d < 32,
-// y = x*cos - x[d+32]*sin; for d >= 32, y = x*cos + x[d-32]*sin.  The same
-// fp32 operations as k_append_rope, so the rounded results are identical.
-__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, u32x4 xp, const float *cs /* 8 x (cos, sin) */, bool upper) {
-    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-    const uint32_t pw[4] = {xp.x, xp.y, xp.z, xp.w};
-    uint32_t out[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float y[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float xv = e ? bf16_hi(xw[k]) : bf16_lo(xw[k]);
-            const float pv = e ? bf16_hi(pw[k]) : bf16_lo(pw[k]);
-            const float co = cs[2 * (2 * k + e)], si = cs[2 * (2 * k + e) + 1];
-            y[e] = upper ? fmaf(xv, co, pv * si) : fmaf(xv, co, -(pv * si));
-        }
-        out[k] = pack_bf16x2(y[0], y[1]);
-    }
-    return u32x4{out[0], out[1], out[2], out[3]};
-}
-
 struct DecodeParams {
     void *out;
     uint16_t *q;
@@ -243,7 +237,9 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     __shared__ float s_m[kWaves][kGroup];
     __shared__ float s_l[kWaves][kGroup];
     __shared__ float s_acc[kWaves][kGroup][kD];
-    __shared__ u32x4 s_new[2][8];  // appended K and V row, 8 chunks each (fused)
+    __shared__ __align__(16) uint16_t s_q[kGroup][kD];  // rotated q of the 4 heads (fused)
+    __shared__ __align__(16) uint16_t s_newk[kD];       // appended K row, rotated (fused)
+    __shared__ __align__(16) uint16_t s_newv[kD];       // appended V row (fused)
 
     // ---- lane roles --------------------------------------------------------
     const int g = lane >> 3;
@@ -255,12 +251,13 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     const uint32_t offA = (g + 8 * t0) * kD + c * 8;
     const uint32_t offV0 = (g + 8 * b2) * kD + c * 8;  // V slot u holds token half u ^ b2
 
-    // ---- everything that does not depend on L goes out first --------------
+    // ---- prologue loads, in the order they must complete --------------------
+    // Vector loads complete in issue order (one counter), so the small loads
+    // the prologue waits for go out first and the first page's K/V loads last:
+    // waiting for a small load then never waits for page data.
     const int pg0 = part * P.part_pages;
     const int slice = min(P.part_pages, P.max_blocks - pg0);
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
-    int my_page = 0;
-    if (tid < slice) my_page = bt_row[pg0 + tid];
     const int L = P.lens[s];
     const int wu = __builtin_amdgcn_readfirstlane(w);
     // Wave w takes pages pg0+w, pg0+w+kWaves, ...  Its first page id is read
@@ -268,6 +265,40 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     // inside the pool is safe to read, and a page that turns out not to be needed
     // (or an id that fails validation below) is simply never used.
     const int first_id = wu < slice ? bt_row[pg0 + wu] : -1;
+    const int my_page = bt_row[pg0 + min(tid, slice - 1)];
+    const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
+    const int64_t nrow = (static_cast<int64_t>(s) * kHKV + j) * kD;
+    const int pos = L - 1;
+    const int pr = tid & 31;
+    // fused: raw (i, i+32) pairs of the 4 q heads (threads 0..127), of the
+    // appended K row (128..159), and a word of the appended V row (160..191)
+    // (every load here is unconditional, from an address that is always valid,
+    // so the compiler can count outstanding loads exactly: a load under a branch
+    // makes it wait for all of them, page data included)
+    float x0 = 0.0f, x1 = 0.0f;
+    uint32_t vword = 0;
+    if (kFused) {
+        const uint16_t *src = tid < 128 ? P.q + qrow0 + ((tid >> 5) & 3) * kD : P.k_new + nrow;
+        x0 = bf16_to_f32(src[pr]);
+        x1 = bf16_to_f32(src[pr + 32]);
+        vword = reinterpret_cast<const uint32_t *>(P.v_new + nrow)[pr];
+    }
+    u32x4 qv[kGroup];
+    if (!kFused) {
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // fused: the (cos, sin) of pair pr at position L-1, clamped into the table
+    // (a bad L is rejected below, before anything computed from it is used)
+    float co = 0.0f, si = 0.0f;
+    if (kFused) {
+        const int pos_c = min(max(pos, 0), P.max_pos - 1);
+        const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD + 2 * pr;
+        co = cs[0];
+        si = cs[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t tile_j = static_cast<int64_t>(j) * kTile;
     auto load_tile = [&](int page_id) {
         // the page id is uniform: keep the tile base in scalar registers
@@ -281,44 +312,19 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         r.v1 = *reinterpret_cast<const u32x4 *>(vt + (offV0 ^ 512u));
         return r;
     };
-    KVRegs cur;
-    if (first_id >= 0 && first_id < P.num_pages) cur = load_tile(first_id);
+    // an id outside the pool reads page 0 instead; such a sequence fails validation
+    KVRegs cur = load_tile(first_id >= 0 && first_id < P.num_pages ? first_id : 0);
+    __builtin_amdgcn_sched_barrier(0);
 
-    const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
-    u32x4 qv[kGroup];
-#pragma unroll
-    for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8);
-
-    // ---- fused: rotate q; lanes 0..7 of wave 0 rotate the appended K row ------
-    const int pos = L - 1;
-    u32x4 new_k = {0, 0, 0, 0}, new_v = {0, 0, 0, 0};
-    if (kFused) {
-        u32x4 qp[kGroup];
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m)
-            qp[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + (c ^ 4) * 8);
-        const int64_t nrow = (static_cast<int64_t>(s) * kHKV + j) * kD;
-        u32x4 nk_raw = {0, 0, 0, 0}, nkp_raw = {0, 0, 0, 0};
-        if (tid < 8) {
-            nk_raw = *reinterpret_cast<const u32x4 *>(P.k_new + nrow + c * 8);
-            nkp_raw = *reinterpret_cast<const u32x4 *>(P.k_new + nrow + (c ^ 4) * 8);
-            new_v = *reinterpret_cast<const u32x4 *>(P.v_new + nrow + c * 8);
-        }
-        // the table row is clamped into range: a bad L is rejected below, before any use
-        const int pos_c = min(max(pos, 0), P.max_pos - 1);
-        const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD + (c & 3) * 16;  // 8 (cos, sin) pairs
-        float csr[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(cs + 4 * k);
-            csr[4 * k] = t.x; csr[4 * k + 1] = t.y; csr[4 * k + 2] = t.z; csr[4 * k + 3] = t.w;
-        }
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m) qv[m] = rope_chunk(qv[m], qp[m], csr, c >= 4);
-        if (tid < 8) {
-            new_k = rope_chunk(nk_raw, nkp_raw, csr, c >= 4);
-            s_new[0][c] = new_k;  // read after the barrier below by the wave that owns the token
-            s_new[1][c] = new_v;
+    // fused: rotation once per workgroup, one pair per thread, into LDS (same
+    // fp32 operations as k_append_rope)
+    if (kFused && tid < 192) {
+        if (tid < 160) {
+            uint16_t *dst = tid < 128 ? &s_q[tid >> 5][0] : &s_newk[0];
+            dst[pr] = f32_to_bf16(fmaf(x0, co, -(x1 * si)));
+            dst[pr + 32] = f32_to_bf16(fmaf(x1, co, x0 * si));
+        } else {
+            reinterpret_cast<uint32_t *>(s_newv)[pr] = vword;
         }
     }
 
@@ -352,13 +358,17 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         return;
     }
     if (part >= n_parts_s) return;
-    // Append: the new row goes into its slot now that the sequence is known good
-    // (last partition only; nothing in this kernel reads the slot back).
-    if (kFused && tid < 8 && pg1 == n_pages) {
-        const int64_t dst = static_cast<int64_t>(s_pages[(pos >> 4) - pg0]) * kPageElems + tile_j +
-                            (pos & (kPage - 1)) * kD + c * 8;
-        *reinterpret_cast<u32x4 *>(P.k_pool + dst) = new_k;
-        *reinterpret_cast<u32x4 *>(P.v_pool + dst) = new_v;
+    if (kFused) {
+#pragma unroll
+        for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(&s_q[m ^ hm][c * 8]);
+        // Append: the new row goes into its slot now that the sequence is known
+        // good (last partition only; nothing in this kernel reads the slot back).
+        if (tid < 8 && pg1 == n_pages) {
+            const int64_t dst = static_cast<int64_t>(s_pages[(pos >> 4) - pg0]) * kPageElems + tile_j +
+                                (pos & (kPage - 1)) * kD + c * 8;
+            *reinterpret_cast<u32x4 *>(P.k_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newk[c * 8]);
+            *reinterpret_cast<u32x4 *>(P.v_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newv[c * 8]);
+        }
     }
     auto load_page = [&](int p) { return load_tile(__builtin_amdgcn_readfirstlane(s_pages[p - pg0])); };
     int p = pg0 + wu;
@@ -385,7 +395,8 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     };
     auto process_last = [&](KVRegs r, int p) {
         if (kFused && g == (pos & 7)) {  // patch the appended token into the registers
-            const u32x4 nk = s_new[0][c], nv = s_new[1][c];
+            const u32x4 nk = *reinterpret_cast<const u32x4 *>(&s_newk[c * 8]);
+            const u32x4 nv = *reinterpret_cast<const u32x4 *>(&s_newv[c * 8]);
             const int half = (pos >> 3) & 1;
             if (half == t0) r.ka = nk; else r.kb = nk;
             if (half == b2) r.v0 = nv; else r.v1 = nv;
@@ -425,32 +436,34 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         process_last(cur, p);
     }
     // ---- wave epilogue: sums over the 8 lane groups (one max per wave) -----
+    // acc[e][i] is reduce-scattered over the groups: the xor-32 step leaves slots
+    // e = 0, 1 holding (e, e+2) summed over lane halves, the xor-16 step leaves
+    // slot 0 holding slot (g>>1)&1 of that, the xor-8 step completes the sum.
+    // Group pair g>>1 then owns accumulator slot e = g>>1, fully summed.
     float l_tot = l_run + dpp_f32<kXor1>(l_run);
     l_tot = sum_groups(l_tot);
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[e][i] = sum_groups(acc[e][i]);
-    if (g == 0) {
-#pragma unroll
-        for (int e = 0; e < kGroup; ++e) {
-            const int h = e ^ (3 * b2);
-            *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8]) = f32x4{acc[e][0], acc[e][1], acc[e][2], acc[e][3]};
-            *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8 + 4]) = f32x4{acc[e][4], acc[e][5], acc[e][6], acc[e][7]};
-        }
-        if (b0 == 0) {
-            s_m[w][hm] = m_run;
-            s_l[w][hm] = l_tot;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const float a01 = swap32_sum(acc[0][i], acc[2][i]);
+        const float a11 = swap32_sum(acc[1][i], acc[3][i]);
+        float t = swap16_sum(a01, a11);
+        t += dpp_f32<kRowRor8>(t);
+        acc[0][i] = t;
+    }
+    if ((g & 1) == 0) {
+        const int h = (g >> 1) ^ (3 * b2);
+        *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8]) = f32x4{acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+        *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8 + 4]) = f32x4{acc[0][4], acc[0][5], acc[0][6], acc[0][7]};
+    }
+    if (g == 0 && b0 == 0) {
+        s_m[w][hm] = m_run;
+        s_l[w][hm] = l_tot;
     }
     __syncthreads();
 
     // every wave has read q by now: the rotated q can be stored (fused, single partition)
-    if (kFused && P.write_q && n_parts_s == 1 && w == 0 && g == 0) {
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m)
-            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8) = qv[m];
-    }
+    if (kFused && P.write_q && n_parts_s == 1 && tid < 32)
+        *reinterpret_cast<u32x4 *>(P.q + qrow0 + tid * 8) = *reinterpret_cast<const u32x4 *>(&s_q[0][tid * 8]);
 
     // ---- merge the waves: thread (h, d) --------------------------------------
     if (tid < kGroup * kD) {
