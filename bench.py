@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--config", default="batch64", choices=["batch64", "batch256", "batch8", "tiny"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times): under rocprofv3 --pmc its FETCH_SIZE / "
+                         "WRITE_SIZE give the factor that scales those counters to bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     return ap.parse_args()
 
@@ -76,6 +79,31 @@ def build_workload(name, device):
                            out=torch.empty((spec.num_seqs, 32, 64), dtype=torch.bfloat16, device=device)))
     lens = torch.from_numpy(spec.context_lens).to(device)
     return spec, k_pool, v_pool, layers, lens, rows
+
+
+def measured_traffic():
+    """HBM bytes per fused decode launch from the committed rocprofv3 PMC summary.
+
+    The summary records the sha256 of the decode kernel's source it was taken
+    with; if the source has changed since, the figure no longer applies and
+    None is returned.
+    """
+    import hashlib
+    import re
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(here, "paged_kv_gqa_append_amd", "csrc", "pa_decode.hip")
+    summ = os.path.join(here, "profiles", "decode_batch64_pmc_traffic.md")
+    try:
+        text = open(summ).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    if not m_src or not m_val or m_src.group(1) != digest:
+        return None
+    return int(m_val.group(1))
 
 
 def cpu_baseline(spec, k_pool, v_pool, rows, target_s):
@@ -141,6 +169,15 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     device = torch.device("cuda", 0)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     spec, k_pool, v_pool, layers, lens, rows = build_workload(args.config, device)
     table = binding.rope_table(2048 + 64, spec.theta, device)
     ws = binding.decode_workspace(spec.num_seqs, spec.max_blocks, device)
@@ -179,15 +216,20 @@ def main():
     ms = timed(step, args.steps, args.warmup)
     other_ms = timed(step_separate if args.path == "fused" else step_fused, max(3, args.steps // 2), 2)
 
-    # instrumented pass: HIP events around every fused append+decode launch on its stream
-    # (a pass of its own, so the events do not perturb the step time above)
-    dec_ms = []
+    # Kernel duration for the roofline: HIP events on the launch stream around
+    # each layer sequence of 16 back-to-back fused launches (a pass of its own,
+    # so the events do not perturb the step time above); mean per launch =
+    # elapsed / 16, which includes the gaps between launches.
+    seq_ms = []
     for _ in range(max(3, args.steps // 2)):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
-        step_fused(ev)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step_fused()
+        b.record(stream)
         torch.cuda.synchronize()
-        dec_ms += [a.elapsed_time(b) for a, b in ev]
-    dec_ms_mean = float(np.mean(dec_ms))
+        seq_ms.append(a.elapsed_time(b))
+    dec_ms_mean = float(np.mean(seq_ms)) / spec.num_layers
 
     kv_step = spec.kv_bytes()
     kv_launch = kv_step // spec.num_layers
@@ -209,7 +251,8 @@ def main():
         ("separate_calls_ms_per_step" if args.path == "fused" else "fused_ms_per_step"): round(other_ms, 5),
         "roofline": {"bound": "hbm", "kernel": "k_decode_paged<8,true> (pa_append_decode_gqa)",
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic() if args.config == "batch64" else None,
                      "bytes_per_launch": kv_launch, "mean_launch_us": round(dec_ms_mean * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
