@@ -163,8 +163,13 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
  *   out[s][i][h][:] = softmax_t(scale * <q[s][i][h], K_t>) . V_t,  t <= pos
  * with bf16 MFMA tiles and fp32 accumulation; no score matrix is stored.
  * q, out: [num_seqs][chunk_len][32][64]; k_chunk, v_chunk: [num_seqs][chunk_len][8][64].
- * out may alias q exactly.  Device errors as for append (whole sequence
- * skipped, its out rows zero-filled).                                         */
+ * out may alias q exactly.  max_blocks may be at most 512 (contexts up to
+ * 8192 tokens; larger tables return PA_ERR_UNSUPPORTED).  Device errors: a
+ * chunk token whose position (prefix < 0, or beyond max_blocks*16 or max_pos)
+ * or page id is invalid is not appended (nor is its q row rotated), exactly as
+ * pa_append_kv_rope treats one token; a sequence whose length or any used page
+ * id is invalid has all its out rows zero-filled; the matching PA_DEVERR_* bit
+ * is set.                                                                       */
 pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool,
                            void *v_pool, const int32_t *block_tables, const int32_t *prefix_lens,
                            const float *rope_cos_sin, int32_t num_seqs, int32_t chunk_len,

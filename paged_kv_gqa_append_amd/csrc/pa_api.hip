@@ -153,7 +153,7 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
     if (num_seqs < 0 || chunk_len < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1 || !isfinite(scale))
         return PA_ERR_INVALID_ARG;
     if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
-    if (pa::launch_prefill_attention(pa::PrefillLaunch{}, nullptr) == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+    if (max_blocks > pa::kMaxBlocksPrefill) return PA_ERR_UNSUPPORTED;
     if (out_dtype != PA_OUT_BF16 && out_dtype != PA_OUT_FP32) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || chunk_len == 0) return PA_OK;
     if (!out || !q || !k_chunk || !v_chunk || !k_pool || !v_pool || !block_tables || !prefix_lens || !rope_cos_sin)
@@ -165,7 +165,7 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
                        num_seqs, chunk_len, 1, max_blocks, num_pages, max_pos, device_flags};
     if (pa::launch_append_rope(a, stream) != hipSuccess) return PA_ERR_HIP;
     pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, num_seqs, chunk_len, max_blocks,
-                        num_pages, scale, out_dtype == PA_OUT_FP32, device_flags};
+                        num_pages, max_pos, scale, out_dtype == PA_OUT_FP32, device_flags};
     return pa::launch_prefill_attention(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

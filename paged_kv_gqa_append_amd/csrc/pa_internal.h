@@ -61,10 +61,14 @@ struct PrefillLaunch {
     int chunk_len;
     int max_blocks;
     int num_pages;
+    int max_pos;
     float scale;
     int out_fp32;
     uint32_t *flags;
 };
+
+// Largest block table the prefill kernel stages in LDS (8192 tokens).
+constexpr int kMaxBlocksPrefill = 512;
 
 // Decode partition size in pages (fixed per process; the default can be
 // overridden with PA_DECODE_PART_PAGES for tuning runs).

@@ -41,6 +41,26 @@ def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ordered(a) - ordered(b))
 
 
+def bf16_ulp(bits: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at each (finite) value."""
+    v = np.abs(W.bf16_bits_to_f32(bits).astype(np.float64))
+    _, e = np.frexp(np.where(v > 0, v, 1.0))
+    return np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+
+
+def assert_rope_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, max_abs_input: float, what=""):
+    """Rotated bf16 rows: the device rotates in fp32 with a rounded (cos, sin)
+    table, the oracle in fp64; each result is rounded once to bf16.  They may
+    differ by one bf16 step plus the fp32 evaluation error of x_i cos - x_j sin,
+    at most ~2^-22 (|x_i| + |x_j|) <= 2^-21 max|x|, which spans several steps
+    only when the two terms cancel to a tiny result."""
+    g = W.bf16_bits_to_f32(gpu_bits).astype(np.float64)
+    r = W.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    bound = bf16_ulp(ref_bits) + 2.0 ** -21 * max_abs_input
+    bad = np.abs(g - r) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} rotated elements outside 1 ulp + fp32 bound"
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, tol, what=""):
     atol, rtol = tol
     assert got.shape == ref.shape
