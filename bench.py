@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="batch64", choices=["batch64", "batch256", "batch8", "tiny"])
+    ap.add_argument("--config", default="batch64", choices=["batch64", "batch256", "batch8", "tiny", "prefill"],
+                    help="decode workloads, or 'prefill': 4 x (1536 cached + 512-token chunk) chunked prefill")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -152,6 +153,102 @@ def cpu_baseline(spec, k_pool, v_pool, rows, target_s):
                       f"{kv_bytes} KV bytes); tokens/s scaled to whole {spec.num_layers}-layer steps"}
 
 
+PREFILL_METRIC = "chunked-prefill paged attention: TFLOP/s of the causal QK^T and PV products (1 GPU)"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(prefix_lens, chunk_len):
+    """Algorithmic flops of one chunk: every (query, key) pair a causal row
+    attends (keys 0..pos inclusive) costs 2*64 for q.k and 2*64 for p*v, per
+    query head."""
+    pairs = sum(int(chunk_len) * (int(p) + 1) + chunk_len * (chunk_len - 1) // 2 for p in prefix_lens)
+    return pairs * 32 * 4 * 64, pairs * 32
+
+
+def cpu_baseline_prefill(case, target_s):
+    """Time the fp64 oracle's chunked prefill on whole sequences of the workload."""
+    import oracle
+
+    total, done, flops = 0.0, 0, 0
+    for s in range(case.num_seqs):
+        one = lambda a: np.ascontiguousarray(a[s:s + 1])
+        kp, vp = case.k_pool.copy(), case.v_pool.copy()
+        t0 = time.perf_counter()
+        _, rc = oracle.prefill_chunk(one(case.q).copy(), one(case.k_chunk), one(case.v_chunk), kp, vp,
+                                     one(case.block_tables), one(case.prefix_lens), case.num_pages, case.theta,
+                                     case.scale)
+        total += time.perf_counter() - t0
+        assert rc == oracle.OK
+        done += 1
+        flops += prefill_flops(case.prefix_lens[s:s + 1], case.chunk_len)[0]
+        if total >= target_s:
+            break
+    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(total, 3),
+            "sample": f"fp64 oracle chunked prefill (append + causal attention) of {done} of the {case.num_seqs} "
+                      f"sequences of the workload ({flops} algorithmic flops)"}
+
+
+def main_prefill(args, torch, binding, device):
+    """One step = one pa_prefill_chunk call: append the 4 x 512 chunk rows
+    (K rotated into pages, q rotated in place), then causal MFMA attention of
+    every chunk row over its 1536 + i + 1 keys."""
+    from paged_kv_gqa_append_amd import workloads as W
+
+    c = W.prefill_config()
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+    q, kc, vc, kp, vp = up(c.q), up(c.k_chunk), up(c.v_chunk), up(c.k_pool), up(c.v_pool)
+    bt = torch.from_numpy(c.block_tables).to(device)
+    prefix = torch.from_numpy(c.prefix_lens).to(device)
+    out = torch.empty_like(q)
+    table = binding.rope_table(2048 + 64, c.theta, device)
+    stream = torch.cuda.current_stream()
+
+    # q is rotated in place by every call (a norm-preserving rotation, so its
+    # values stay N(0,1)-like); the chunk rows are re-appended at the same slots.
+    def step():
+        binding.prefill_chunk(out, q, kc, vc, kp, vp, bt, prefix, table, c.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    calls = []
+    for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        calls.append((a, b))
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in calls])
+    ms = float(per_call.mean())
+    flops, n_exp = prefill_flops(c.prefix_lens, c.chunk_len)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "chunked_prefill", "num_seqs": c.num_seqs, "prefix_len": int(c.prefix_lens[0]),
+                   "chunk_len": c.chunk_len, "layers": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
+                   "page_size": 16, "num_pages": c.num_pages, "causal": "inclusive",
+                   "step": "pa_prefill_chunk (chunk append + RoPE, then causal paged attention on MFMA)"},
+        "median_ms_per_step": round(float(np.median(per_call)), 5),
+        "tokens_per_s": round(c.num_seqs * c.chunk_len / (ms * 1e-3), 1),
+        "flops_per_step": flops, "exp_per_step": n_exp,
+        "roofline": {"bound": "mfma", "kernel": "k_append_rope (prefix mode) + k_prefill_attn, one call",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "mean_launch_us": round(ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,6 +274,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.config == "prefill":
+        main_prefill(args, torch, binding, device)
         return
     spec, k_pool, v_pool, layers, lens, rows = build_workload(args.config, device)
     table = binding.rope_table(2048 + 64, spec.theta, device)

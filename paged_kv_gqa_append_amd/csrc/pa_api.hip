@@ -161,11 +161,13 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(k_pool) ||
         !aligned16(v_pool) || !aligned16(block_tables) || !aligned16(prefix_lens) || !aligned16(rope_cos_sin))
         return PA_ERR_INVALID_ARG;
-    pa::AppendLaunch a{q, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin,
+    // K/V rows of the chunk go into their pages first (q is rotated by the
+    // attention kernel itself, which reads it anyway).
+    pa::AppendLaunch a{nullptr, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin,
                        num_seqs, chunk_len, 1, max_blocks, num_pages, max_pos, device_flags};
     if (pa::launch_append_rope(a, stream) != hipSuccess) return PA_ERR_HIP;
-    pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, num_seqs, chunk_len, max_blocks,
-                        num_pages, max_pos, scale, out_dtype == PA_OUT_FP32, device_flags};
+    pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin, num_seqs, chunk_len,
+                        max_blocks, num_pages, max_pos, scale, out_dtype == PA_OUT_FP32, device_flags};
     return pa::launch_prefill_attention(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

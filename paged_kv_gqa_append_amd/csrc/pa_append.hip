@@ -17,8 +17,8 @@ namespace pa {
 __device__ __forceinline__ void rope_pair(const uint16_t *src, uint16_t *dst, int i, float c, float s) {
     const float x0 = bf16_to_f32(src[i]);
     const float x1 = bf16_to_f32(src[i + kD / 2]);
-    dst[i] = f32_to_bf16(fmaf(x0, c, -(x1 * s)));
-    dst[i + kD / 2] = f32_to_bf16(fmaf(x1, c, x0 * s));
+    dst[i] = f32_to_bf16(rope_lo(x0, x1, c, s));
+    dst[i + kD / 2] = f32_to_bf16(rope_hi(x0, x1, c, s));
 }
 
 // token = blockIdx.x = s * tokens_per_seq + i.

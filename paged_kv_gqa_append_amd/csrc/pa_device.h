@@ -69,4 +69,11 @@ __device__ __forceinline__ float sum_lanes8(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotate-half RoPE of the pair (x_i, x_{i+32}) by (c, s) = (cos, sin) of
+// pos * theta^(-2i/64): (x_i c - x_{i+32} s, x_{i+32} c + x_i s), one fused
+// multiply-add each.  Every kernel that rotates uses these two expressions, so
+// a row rotated by any of them has the same bits.
+__device__ __forceinline__ float rope_lo(float x0, float x1, float c, float s) { return fmaf(x0, c, -(x1 * s)); }
+__device__ __forceinline__ float rope_hi(float x0, float x1, float c, float s) { return fmaf(x1, c, x0 * s); }
+
 }  // namespace pa

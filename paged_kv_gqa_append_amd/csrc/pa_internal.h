@@ -52,11 +52,12 @@ struct DecodeLaunch {
 
 struct PrefillLaunch {
     void *out;
-    const void *q;        // already rotated
+    void *q;              // un-rotated; rotated in place unless out == q
     const void *k_pool;
     const void *v_pool;
     const int32_t *block_tables;
     const int32_t *prefix_lens;
+    const float *rope;
     int num_seqs;
     int chunk_len;
     int max_blocks;

@@ -4,29 +4,40 @@
 // What is computed (TinyLoop, section "prefill_chunk and scratch residency":
 // the prompt is processed in row chunks; samir-vllm, "Gestion de la KV cache
 // ...": the prompt's pages are filled during prefill): after the chunk's K/V
-// rows have been appended and its q rows rotated (k_append_rope, prefix mode),
-// every chunk query at absolute position p = prefix + i attends to keys
-// 0..p of its sequence, read through the block table:
-//     out[s][i][h] = sum_t softmax_t(scale <q[s][i][h], K_t>) V_t,  t <= p.
+// rows have been appended (k_append_rope, prefix mode), every chunk query at
+// absolute position p = prefix + i is rotated at p and attends to keys 0..p
+// of its sequence, read through the block table:
+//     out[s][i][h] = sum_t softmax_t(scale <rope(q[s][i][h], p), K_t>) V_t,  t <= p.
 // No score matrix is stored (contrast tiny-vllm's prefill, which keeps a
 // 512 x 512 x 32 score buffer, ch.2 buffer table).
 //
 // Work decomposition
-//   One workgroup per (sequence, KV head j, tile of 32 chunk positions); its 4
-//   waves are the 4 query heads of that KV head, so every K/V block serves 4 x
-//   32 query rows.  Keys are taken 32 at a time (two pages).
-//   Scores are computed transposed, S^T = K Q^T (32 keys x 32 queries per
-//   wave): in the MFMA result layout each lane then holds 16 keys of ONE query
-//   (lane l: query l%32, keys 8i + 4(l/32) + r for register 4i+r), so the
-//   online softmax is lane-local plus one exchange with lane l^32.
-//   The output is accumulated transposed too, O^T = V^T P^T (64 d x 32
-//   queries): same lane-per-query layout, so rescaling is lane-local.  P^T is
-//   the MFMA B operand straight from the score registers; the key slots of
-//   the MFMA are permuted to match, and V^T is staged in LDS in that order.
-//   P is fed as a bf16 hi/lo pair (two MFMAs), so the weights keep ~16
-//   significant bits; V and q, K are bf16 as stored.
-//   Online softmax in log2 units with a lazy running max (rescale only when
-//   a score exceeds it by more than 2^8), as in the decode kernel.
+//   One workgroup per (sequence, KV head j, tile of 64 chunk positions); its 4
+//   waves are the 4 query heads of that KV head, and each wave carries its 64
+//   rows as two 32-row sub-tiles, so every K/V fragment a wave reads from LDS
+//   feeds 2 x 32 query rows.  Keys go 32 at a time (two pages).  Workgroup ids
+//   are mapped so that all tiles of one (sequence, KV head) land on the same
+//   XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
+//   Scores are computed transposed, S^T = K Q^T (32 keys x 32 queries): in the
+//   MFMA result layout a lane holds 16 keys of ONE query (lane l: query l%32,
+//   keys 8i + 4(l/32) + r in register 4i+r), so the online softmax is
+//   lane-local plus one exchange with lane l^32.  The output is accumulated
+//   transposed too, O^T = V^T P^T (64 d x 32 queries): the same lane-per-query
+//   layout, so rescaling is lane-local.  P^T is the MFMA B operand straight
+//   from the score registers; V^T is staged in LDS with its key slots permuted
+//   to match (bits 2 and 3 of the key swapped), so each A fragment is one
+//   16-byte LDS read.
+//   K/V blocks are double-buffered in LDS and prefetched two blocks ahead
+//   through registers; one barrier per block.
+//   Softmax in log2 units with a lazy running max (rescale only when a block
+//   exceeds it by more than 2^8): per score one max, one fused multiply-add,
+//   one exp2, a packed bf16 conversion and half a dot2 for the row sum, which
+//   is taken over the same bf16 weights the P.V product uses.  With fp32
+//   output the weights are fed as a bf16 hi/lo pair (two MFMAs) so they keep
+//   ~16 significant bits.
+//   q is rotated here, from the fp32 cos/sin table, with the same expressions
+//   as the append kernel; the rotated row is written back to q unless out
+//   aliases q.
 #include <math.h>
 
 #include "pa_device.h"
@@ -38,10 +49,11 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kQT = 32;           // chunk positions per workgroup
-constexpr int kKB = 32;           // keys per block
-constexpr int kVtStride = 36;     // bf16 per V^T row in LDS (32 keys + 4 pad: spreads banks)
-constexpr float kNegBig = -1.0e30f;
+constexpr int kRows = 64;                   // chunk positions per workgroup
+constexpr int kKB = 32;                     // keys per block
+constexpr int kKStride = 72;                // bf16 per K row in LDS (64 + 8 pad: conflict-free fragment reads)
+constexpr int kKBuf = kKB * kKStride;       // bf16 per K buffer
+constexpr int kVBuf = kD * kKB / 2;         // 32-bit words per V^T buffer (64 rows x 32 key slots)
 constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -62,199 +74,457 @@ __device__ __forceinline__ float partner32(float v) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// (a, b) -> packed bf16 pair, round to nearest even, one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Slot of key k (0..31) in a V^T row: bits 2 and 3 swapped.  Lane half g of
+// the P.V MFMA over keys 16b..16b+15 holds the weights of keys
+// 16b + 4g + {0..3, 8..11}; with this order they sit in slots 16b + 8g .. +7.
+__device__ __forceinline__ int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// 16-byte unit of V^T row d (0..63) that holds slot chunk ch (slots 8ch..8ch+7),
+// XOR-swizzled by the row so that the 8 rows one LDS phase reads fall in
+// distinct banks.
+__device__ __forceinline__ int vt_unit(int d, int ch) { return d * 4 + (ch ^ (((d >> 1) ^ (d >> 3)) & 3)); }
+
+// acc + the sum of the 8 bf16 weights (dot2 against (1, 1): exact products,
+// fp32 sums), as two independent chains.
+__device__ __forceinline__ float sum8_bf16(bf16x8 v, float acc) {
+    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc, false);
+    float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, 0.0f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, a, false);
+    b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, b, false);
+    return a + b;
+}
+
+// Two 16-byte global loads per thread stage one K/V block (see load_block).
+struct Stage {
+    u32x4 a, b;
+};
+
 }  // namespace
 
 struct PrefillParams {
     void *out;
-    const uint16_t *q;
+    uint16_t *q;
     const uint16_t *k_pool;
     const uint16_t *v_pool;
     const int32_t *bt;
     const int32_t *prefix_lens;
+    const float *rope;
     int chunk_len;
     int max_blocks;
     int num_pages;
     int max_pos;
     int n_tiles;
-    float scale_log2;
+    int write_q;
+    int neg;        // scale < 0: q is negated for the products and c = |scale| log2(e)
+    float c;        // |scale| * log2(e)
+    float thr;      // lazy-rescale threshold in raw score units (2^8 in log2 units)
     int out_fp32;
     uint32_t *flags;
 };
 
-__global__ __launch_bounds__(256) void k_prefill_attn(PrefillParams P) {
-    const int tile = P.n_tiles - 1 - (blockIdx.x % P.n_tiles);  // longest tiles are dispatched first
-    const int sj = blockIdx.x / P.n_tiles;
+namespace {
+
+// Rotated q fragments of one 32-row sub-tile (MFMA B operand): this lane's
+// query row i_c, d = 16kk + 8*half .. +7.  Pairs (d, d+32) are kk and kk+2 of
+// the same lane.
+__device__ __forceinline__ void load_q_rotated(const PrefillParams &P, int s, int h, int i_c, int pos_c, int half,
+                                               u32x4 (&rq)[4]) {
+    const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * P.chunk_len + i_c) * kHQ + h) * kD;
+    u32x4 raw[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) raw[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * half);
+    const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD;  // [32][2]
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int i0 = 16 * kk + 8 * half;  // first pair of this fragment
+        f32x4 t[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = *reinterpret_cast<const f32x4 *>(cs + 2 * i0 + 4 * r);
+        const uint32_t lo[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
+        const uint32_t hi[4] = {raw[kk + 2].x, raw[kk + 2].y, raw[kk + 2].z, raw[kk + 2].w};
+        uint32_t ylo[4], yhi[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            // pairs i0 + 2*e2 (low bf16 of each word) and i0 + 2*e2 + 1 (high bf16)
+            const float c0 = t[e2][0], s0 = t[e2][1], c1 = t[e2][2], s1 = t[e2][3];
+            const float a0 = bf16_lo(lo[e2]), b0 = bf16_lo(hi[e2]);
+            const float a1 = bf16_hi(lo[e2]), b1 = bf16_hi(hi[e2]);
+            ylo[e2] = pack_bf16x2(rope_lo(a0, b0, c0, s0), rope_lo(a1, b1, c1, s1));
+            yhi[e2] = pack_bf16x2(rope_hi(a0, b0, c0, s0), rope_hi(a1, b1, c1, s1));
+        }
+        rq[kk] = u32x4{ylo[0], ylo[1], ylo[2], ylo[3]};
+        rq[kk + 2] = u32x4{yhi[0], yhi[1], yhi[2], yhi[3]};
+    }
+}
+
+// One 32-key block for both sub-tiles of this wave.  sk: K rows [key][72],
+// svt: V^T in swizzled 16-byte units.  pos0: absolute position of this lane's
+// query in sub-tile 0 (sub-tile 1 is +32).  mask: some key of the block may
+// lie past a row's position or past the sequence (wave-uniform); dead keys get
+// score -inf, hence weight exactly 0 (c > 0).
+template <bool kHiLo>
+__device__ __forceinline__ void attend_block(const uint16_t *sk, const uint32_t *svt, int lane, int kb, bool mask,
+                                             const bf16x8 (&qf)[2][4], f32x16 (&o)[2][2], float (&m)[2],
+                                             float (&l)[2], int pos0, int total, float c, float thr) {
+    const int qc = lane & 31, half = lane >> 5;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sk + qc * kKStride + 16 * kk + 8 * half));
+    f32x16 st[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        st[u] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) st[u] = mfma32(kf[kk], qf[u][kk], st[u]);
+    }
+    bf16x8 vf[2][2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+            vf[db][sb] = as_bf16x8(*reinterpret_cast<const u32x4 *>(svt + 4 * vt_unit(32 * db + qc, 2 * sb + half)));
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = st[u][v];
+        if (mask) {
+            // key kb*32 + 8(v/4) + 4*half + v%4 is live iff <= min(pos, total-1)
+            const int lim = min(pos0 + 32 * u, total - 1) - kb * kKB - 4 * half;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3)) > lim ? -INFINITY : x[v];
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, x[v]), x[v + 1]);
+        mx = fmaxf(mx, x[15]);
+        mx = fmaxf(mx, partner32(mx));
+        const bool need = !(mx <= m[u] + thr);  // also true on the first block (m = -inf)
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            // rare after the first block: keep it a branch (the barrier stops
+            // the compiler from multiplying the accumulators unconditionally)
+            asm volatile("" ::: "memory");
+            // lanes that do not need it keep m and factor 1 (their m may be
+            // -inf, and -inf - -inf must not reach the exp); otherwise the
+            // factor is 0 when m was -inf
+            const float f = need ? fast_exp2((m[u] - mx) * c) : 1.0f;
+            m[u] = need ? mx : m[u];
+            l[u] *= f;
+            o[u][0] *= f;
+            o[u][1] *= f;
+        }
+        // m is still -inf only if no key so far is live for this row (a key
+        // half can start past a row's position): every score is -inf then,
+        // and offset 0 keeps their weights at 0 instead of -inf + inf.
+        const float mc = m[u] > -INFINITY ? m[u] * c : 0.0f;
+        bf16x8 pb[2], pl[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[8 * sb + e], c, -mc));
+            uint32_t wh[4], wl[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                wh[e2] = cvt_pk_bf16(p[2 * e2], p[2 * e2 + 1]);
+                if (kHiLo)
+                    wl[e2] = cvt_pk_bf16(p[2 * e2] - bf16_lo(wh[e2]), p[2 * e2 + 1] - bf16_hi(wh[e2]));
+            }
+            pb[sb] = as_bf16x8(u32x4{wh[0], wh[1], wh[2], wh[3]});
+            l[u] = sum8_bf16(pb[sb], l[u]);
+            if (kHiLo) {
+                pl[sb] = as_bf16x8(u32x4{wl[0], wl[1], wl[2], wl[3]});
+                l[u] = sum8_bf16(pl[sb], l[u]);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                o[u][db] = mfma32(vf[db][sb], pb[sb], o[u][db]);
+                if (kHiLo) o[u][db] = mfma32(vf[db][sb], pl[sb], o[u][db]);
+            }
+    }
+}
+
+}  // namespace
+
+// LDS layout of one workgroup: two key halves, each with double-buffered K
+// and V^T blocks; after the block loop the same bytes hold the second half's
+// partial results for the merge.
+constexpr int kKBufBytes = kKBuf * 2;
+constexpr int kVBufBytes = kVBuf * 4;
+constexpr int kHalfBytes = 2 * (kKBufBytes + kVBufBytes);
+constexpr int kStageBytes = 2 * kHalfBytes;
+constexpr int kMergeOBytes = 4 * 2 * 64 * 32 * 4;   // 4 waves x 2 sub-tiles x 64 lanes x 32 floats
+constexpr int kMergeMLBytes = 4 * 2 * 64 * 2 * 4;   // (m, l) per lane and sub-tile
+constexpr int kSmemBytes = kStageBytes > kMergeOBytes + kMergeMLBytes ? kStageBytes : kMergeOBytes + kMergeMLBytes;
+
+template <bool kHiLo>
+__global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
+    // ids -> (sequence, KV head, tile): the 8 low id bits pick the XCD, which
+    // is also the KV head, so every tile of (s, j) runs on XCD j; the longest
+    // tiles (highest positions) go first.
+    const int bid = blockIdx.x;
+    const int mq = bid >> 3;
+    const int sj = (bid & 7) + 8 * (mq / P.n_tiles);
+    const int tile = P.n_tiles - 1 - (mq % P.n_tiles);
     const int j = sj & (kHKV - 1);
     const int s = sj >> 3;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int h = j * kGroup + w;
+    const int kh = w >> 2;            // key half: waves 0-3 take the first half of the blocks, 4-7 the rest
+    const int h = j * kGroup + (w & 3);
     const int C = P.chunk_len;
-    const int i0 = tile * kQT;
+    const int row0 = tile * kRows;
+    const int qc = lane & 31;
+    const int half = lane >> 5;
 
     __shared__ int s_pages[kMaxBlocksPrefill];
-    __shared__ __align__(16) uint16_t s_vt[kD * kVtStride];  // V^T of one key block: [d][key]
+    __shared__ __align__(16) unsigned char s_raw[kSmemBytes];
 
-    // ---- validation: the whole sequence's pages, as the append saw them -----
+    // ---- validation: the whole sequence's pages ------------------------------
     const int prefix = P.prefix_lens[s];
-    const int total = prefix + C;
-    const bool len_ok = prefix >= 0 && total <= P.max_blocks * kPage && total <= P.max_pos &&
-                        P.max_blocks <= kMaxBlocksPrefill;
-    const int n_pages = len_ok ? (total + kPage - 1) / kPage : 0;
+    const int64_t lim = min(static_cast<int64_t>(P.max_blocks) * kPage, static_cast<int64_t>(P.max_pos));
+    const bool len_ok = prefix >= 0 && static_cast<int64_t>(prefix) + C <= lim;
+    const int total = len_ok ? prefix + C : 0;
+    const int n_pages = (total + kPage - 1) / kPage;
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
     int bad = 0;
-    for (int b = tid; b < n_pages; b += 256) {
+    for (int b = tid; b < n_pages; b += 512) {
         const int pid = bt_row[b];
         s_pages[b] = pid;
         bad |= (pid < 0) | (pid >= P.num_pages);
     }
     const bool ok = len_ok && __syncthreads_or(bad) == 0;
-    const int qcol = lane & 31;   // this lane's query within the tile
-    const int half = lane >> 5;   // which 4-key run of every 8 this lane holds
-    const int iq = i0 + qcol;
-    const bool q_valid = iq < C;
-    if (!ok) {  // zero-fill this tile's rows of this head, flag once
-        if (q_valid && half == 0) {
-            const int64_t o = ((static_cast<int64_t>(s) * C + iq) * kHQ + h) * kD;
-            for (int d = 0; d < kD; ++d) {
+
+    if (!ok) {
+        // Rotate q where the append would have (the token's position and page
+        // are valid), then zero-fill this tile's rows of this head.  The first
+        // key half's waves do it.
+        if (kh != 0) return;
+        for (int u = 0; u < 2; ++u) {
+            const int i = row0 + 32 * u + qc;
+            if (i >= C) continue;
+            const int64_t pos = static_cast<int64_t>(prefix) + i;
+            bool tok_ok = prefix >= 0 && pos < lim;
+            if (tok_ok) {
+                const int pid = bt_row[pos >> 4];
+                tok_ok = pid >= 0 && pid < P.num_pages;
+            }
+            if (P.write_q && tok_ok) {
+                u32x4 rq[4];
+                load_q_rotated(P, s, h, i, static_cast<int>(pos), half, rq);
+                uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4 *>(qrow + 16 * kk + 8 * half) = rq[kk];
+            }
+            const int64_t o = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD + 32 * half;
+            for (int d = 0; d < 32; ++d) {
                 if (P.out_fp32) static_cast<float *>(P.out)[o + d] = 0.0f;
                 else static_cast<uint16_t *>(P.out)[o + d] = 0;
             }
         }
-        if (tid == 0 && tile == P.n_tiles - 1 && P.flags) atomicOr(P.flags, len_ok ? kDevErrPageId : kDevErrContextLen);
+        if (tid == 0 && j == 0 && tile == P.n_tiles - 1 && P.flags)
+            atomicOr(P.flags, len_ok ? kDevErrPageId : kDevErrContextLen);
         return;
     }
 
-    // ---- q^T fragments (MFMA B operand): query qcol, d = 16kk + 8*half .. +7 --
-    const int iq_c = min(iq, C - 1);
-    const int pq = prefix + iq_c;  // absolute position of this lane's query
-    const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + iq_c) * kHQ + h) * kD;
-    bf16x8 qf[4];
+    // ---- rotated q fragments of both sub-tiles --------------------------------
+    bf16x8 qf[2][4];
+    int pos0 = 0;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * half));
+    for (int u = 0; u < 2; ++u) {
+        const int i = row0 + 32 * u + qc;
+        const int i_c = min(i, C - 1);  // padding rows compute on the last row, never stored
+        if (u == 0) pos0 = prefix + i_c;
+        u32x4 rq[4];
+        load_q_rotated(P, s, h, i_c, prefix + i_c, half, rq);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[u][kk] = as_bf16x8(P.neg ? (rq[kk] ^ 0x80008000u) : rq[kk]);
+    }
+    // The rotated rows are written back only after the final barrier: both
+    // key halves read the same q rows here.
+    // sub-tile 1 of a partly padded tile: pos0 + 32 overshoots; keys >= total
+    // are masked anyway, and its rows are not stored.
 
-    // keys needed by this tile: 0 .. prefix + last valid query position
-    const int last_key = prefix + min(i0 + kQT, C) - 1;
-    const int n_kb = last_key / kKB + 1;
+    // ---- block ranges -----------------------------------------------------------
+    // keys needed by this tile: 0 .. prefix + last valid row
+    const int last_key = prefix + min(row0 + kRows, C) - 1;
+    const int nb = last_key / kKB + 1;
+    const int nb0 = (nb + 1) / 2;          // blocks of the first key half (the loop trip count)
+    const int kb_begin = kh ? nb0 : 0;
+    const int kb_count = kh ? nb - nb0 : nb0;
+    // first block that needs the causal / length mask for some row of the tile
+    const int first_masked = (prefix + row0) / kKB;
+
+    unsigned char *my_half = s_raw + kh * kHalfBytes;
+    uint16_t *s_k0 = reinterpret_cast<uint16_t *>(my_half);
+    uint16_t *s_k1 = reinterpret_cast<uint16_t *>(my_half + kKBufBytes);
+    uint32_t *s_v0 = reinterpret_cast<uint32_t *>(my_half + 2 * kKBufBytes);
+    uint32_t *s_v1 = reinterpret_cast<uint32_t *>(my_half + 2 * kKBufBytes + kVBufBytes);
+
+    // Staging roles within a key half (256 threads): threads 0..127 move K
+    // (key st&31, d 8p..8p+7 and 32+8p..+7 with p = st>>5), threads 128..255
+    // move V (keys 2kp, 2kp+1 with kp = u&15, d 8c..8c+7 with c = u>>4).  Every
+    // thread issues the same two loads; dead keys (>= total) read a live row so
+    // no NaN reaches the MFMA; blocks past the half's range are clamped.
+    const int st_id = tid & 255;
+    const bool is_k = st_id < 128;
+    const int u_t = st_id & 127;
     const int64_t tile_j = static_cast<int64_t>(j) * kTile;
-
-    float m_run = kNegBig;
-    float l_run = 0.0f;
-    f32x16 o0 = {}, o1 = {};  // O^T for d 0..31 and 32..63 (lane: query qcol)
-
-    for (int kb = 0; kb < n_kb; ++kb) {
-        // -- stage V^T of this block in LDS: thread t moves key t>>3, d 8(t&7)..+7
-        {
-            const int kr = tid >> 3, c8 = tid & 7;
-            const int key = kb * kKB + kr;
-            u32x4 v = {0, 0, 0, 0};
-            if (key < total) {
-                const int64_t row = static_cast<int64_t>(s_pages[key >> 4]) * kPageElems + tile_j + (key & 15) * kD;
-                v = *reinterpret_cast<const u32x4 *>(P.v_pool + row + 8 * c8);
-            }
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s_vt[(8 * c8 + 2 * e) * kVtStride + kr] = static_cast<uint16_t>(wv[e] & 0xFFFFu);
-                s_vt[(8 * c8 + 2 * e + 1) * kVtStride + kr] = static_cast<uint16_t>(wv[e] >> 16);
-            }
+    const uint16_t *pool = is_k ? P.k_pool : P.v_pool;
+    auto load_block = [&](int kbl) -> Stage {
+        const int kb = min(kb_begin + kbl, nb - 1);
+        int key0, key1, d0, d1;
+        if (is_k) {
+            key0 = key1 = kb * kKB + (u_t & 31);
+            d0 = 8 * (u_t >> 5);
+            d1 = d0 + 32;
+        } else {
+            key0 = kb * kKB + 2 * (u_t & 15);
+            key1 = key0 + 1;
+            d0 = d1 = 8 * (u_t >> 4);
         }
-        // -- K fragments (MFMA A operand): key kb*32 + qcol, d = 16kk + 8*half .. +7
-        bf16x8 kf[4];
-        {
-            const int key = kb * kKB + qcol;
-            const int kc = key < total ? key : 0;  // a dead key reads key 0 and is masked below
-            const uint16_t *krow = P.k_pool + static_cast<int64_t>(s_pages[kc >> 4]) * kPageElems + tile_j + (kc & 15) * kD;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(krow + 16 * kk + 8 * half));
-        }
-        // -- S^T = K Q^T (32 keys x 32 queries)
-        f32x16 st = {};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st = mfma32(kf[kk], qf[kk], st);
-        float x[16];
-        const int kbase = kb * kKB + 4 * half;
-        const bool diag = kb * kKB + kKB - 1 > prefix + i0;  // some key of this block may be > some query
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            x[v] = st[v] * P.scale_log2;
-            if (diag) {
-                const int key = kbase + 8 * (v >> 2) + (v & 3);
-                if (key > pq || key >= total) x[v] = -INFINITY;
-            }
-        }
-        // -- online softmax per query (lane-local + partner lane l^32)
-        float mx = x[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
-        mx = fmaxf(mx, partner32(mx));
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2)) {
-            const float mn = mx > m_run + kRescaleLog2 ? mx : m_run;
-            const float f = fast_exp2(m_run - mn);
-            m_run = mn;
-            l_run *= f;
-            o0 *= f;
-            o1 *= f;
-        }
-        float pv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            pv[v] = fast_exp2(x[v] - m_run);
-            l_run += pv[v];
-        }
-        // -- P^T as bf16 hi + lo (B operand), registers 8sb .. 8sb+7 per key half sb
-        bf16x8 phi[2], plo[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        key0 = key0 < total ? key0 : 0;
+        key1 = key1 < total ? key1 : key0;
+        const uint16_t *r0 = pool + static_cast<int64_t>(s_pages[key0 >> 4]) * kPageElems + tile_j + (key0 & 15) * kD;
+        const uint16_t *r1 = pool + static_cast<int64_t>(s_pages[key1 >> 4]) * kPageElems + tile_j + (key1 & 15) * kD;
+        Stage st;
+        st.a = *reinterpret_cast<const u32x4 *>(r0 + d0);
+        st.b = *reinterpret_cast<const u32x4 *>(r1 + d1);
+        return st;
+    };
+    auto store_block = [&](const Stage &st, uint16_t *sk, uint32_t *svt) {
+        if (is_k) {
+            uint16_t *dst = sk + (u_t & 31) * kKStride + 8 * (u_t >> 5);
+            *reinterpret_cast<u32x4 *>(dst) = st.a;
+            *reinterpret_cast<u32x4 *>(dst + 32) = st.b;
+        } else {
+            const int slot = vt_slot(2 * (u_t & 15));
+            const int c8 = u_t >> 4;
+            const uint32_t ra[4] = {st.a.x, st.a.y, st.a.z, st.a.w};
+            const uint32_t rb[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const __bf16 hi = static_cast<__bf16>(pv[8 * sb + e]);
-                phi[sb][e] = hi;
-                plo[sb][e] = static_cast<__bf16>(pv[8 * sb + e] - static_cast<float>(hi));
+                const int d = 8 * c8 + e;
+                // (V[2kp][d], V[2kp+1][d]) as one word: low halves or high halves
+                const uint32_t wv = (e & 1) ? __builtin_amdgcn_perm(rb[e >> 1], ra[e >> 1], 0x07060302u)
+                                            : __builtin_amdgcn_perm(rb[e >> 1], ra[e >> 1], 0x05040100u);
+                svt[4 * vt_unit(d, slot >> 3) + ((slot & 7) >> 1)] = wv;
             }
         }
-        __syncthreads();  // V^T staged
-        // -- O^T += V^T P^T: A = V^T rows d, key slots (16sb + 4*half + 0..3, +8 + 0..3)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                const int d = 32 * db + qcol;
-                const uint16_t *r = &s_vt[d * kVtStride + 16 * sb + 4 * half];
-                const uint2 lo4 = *reinterpret_cast<const uint2 *>(r);
-                const uint2 hi4 = *reinterpret_cast<const uint2 *>(r + 8);
-                const bf16x8 va = as_bf16x8(u32x4{lo4.x, lo4.y, hi4.x, hi4.y});
-                if (db == 0) {
-                    o0 = mfma32(va, phi[sb], o0);
-                    o0 = mfma32(va, plo[sb], o0);
-                } else {
-                    o1 = mfma32(va, phi[sb], o1);
-                    o1 = mfma32(va, plo[sb], o1);
-                }
-            }
-        }
-        __syncthreads();  // V^T consumed before the next block overwrites it
+    };
+
+    f32x16 o[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+    float m[2] = {-INFINITY, -INFINITY};
+    float l[2] = {0.0f, 0.0f};
+    auto attend = [&](int kbl, const uint16_t *sk, const uint32_t *svt) {
+        if (kbl >= kb_count) return;  // the second half may run out first
+        const int kb = kb_begin + kbl;
+        attend_block<kHiLo>(sk, svt, lane, kb, kb >= first_masked, qf, o, m, l, pos0, total, P.c, P.thr);
+    };
+
+    // Two register stages in flight: while block kb is consumed from LDS,
+    // block kb+1 waits in registers and block kb+2 is being loaded.  Both key
+    // halves run the same trip count (nb0) so that their barriers pair up.
+    Stage sa = load_block(0);
+    Stage sb = load_block(1);
+    store_block(sa, s_k0, s_v0);
+    __syncthreads();
+    sa = load_block(2);
+    for (int kbl = 0;; kbl += 2) {
+        attend(kbl, s_k0, s_v0);
+        store_block(sb, s_k1, s_v1);
+        __syncthreads();
+        if (kbl + 1 >= nb0) break;
+        sb = load_block(kbl + 3);
+        attend(kbl + 1, s_k1, s_v1);
+        store_block(sa, s_k0, s_v0);
+        __syncthreads();
+        if (kbl + 2 >= nb0) break;
+        sa = load_block(kbl + 4);
     }
 
-    // ---- out[s][iq][h][d] = O^T[d][query] / l, d = 32db + 8i + 4*half + r ------
-    const float l_tot = l_run + partner32(l_run);
-    if (!q_valid) return;
-    const float inv = 1.0f / l_tot;
-    const int64_t orow = ((static_cast<int64_t>(s) * C + iq) * kHQ + h) * kD;
+    // ---- merge the two key halves through LDS ---------------------------------
+    // slot of this lane's results: (head-in-group, sub-tile, lane); lane-major
+    float *mo = reinterpret_cast<float *>(s_raw);
+    float *mml = reinterpret_cast<float *>(s_raw + kMergeOBytes);
+    const int wq = w & 3;
+    if (kh == 1) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+        for (int u = 0; u < 2; ++u) {
+            float *dst = mo + ((wq * 2 + u) * 64 + lane) * 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = 32 * db + 8 * i + 4 * half;
-            float r4[4];
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) r4[r] = (db == 0 ? o0[4 * i + r] : o1[4 * i + r]) * inv;
-            if (P.out_fp32) {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{r4[0], r4[1], r4[2], r4[3]};
-            } else {
-                const uint2 pk = {pack_bf16x2(r4[0], r4[1]), pack_bf16x2(r4[2], r4[3])};
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<f32x4 *>(dst + 16 * db + 4 * r4) =
+                        f32x4{o[u][db][4 * r4], o[u][db][4 * r4 + 1], o[u][db][4 * r4 + 2], o[u][db][4 * r4 + 3]};
+            mml[((wq * 2 + u) * 64 + lane) * 2] = m[u];
+            mml[((wq * 2 + u) * 64 + lane) * 2 + 1] = l[u];
+        }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+
+    // ---- rotated q back in place (unless out aliases q) -------------------------
+    if (P.write_q) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = row0 + 32 * u + qc;
+            if (i >= C) continue;
+            uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x4 v = __builtin_bit_cast(u32x4, qf[u][kk]);
+                *reinterpret_cast<u32x4 *>(qrow + 16 * kk + 8 * half) = P.neg ? (v ^ 0x80008000u) : v;
+            }
+        }
+    }
+
+    // ---- out[s][i][h][d] = O^T[d][query] / l, d = 32db + 8r4 + 4*half + r ------
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float *src = mo + ((wq * 2 + u) * 64 + lane) * 32;
+        const float mB = mml[((wq * 2 + u) * 64 + lane) * 2];
+        const float lB = mml[((wq * 2 + u) * 64 + lane) * 2 + 1];
+        const float mt = fmaxf(m[u], mB);  // finite: the first half always holds key 0
+        const float fA = fast_exp2((m[u] - mt) * P.c);
+        const float fB = fast_exp2((mB - mt) * P.c);  // 0 when the second half had no block
+        const float lh = l[u] * fA + lB * fB;
+        const float l_tot = lh + partner32(lh);
+        const int i = row0 + 32 * u + qc;
+        if (i >= C) continue;
+        const float inv = 1.0f / l_tot;
+        const int64_t orow = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 16 * db + 4 * r4);
+                const int d = 32 * db + 8 * r4 + 4 * half;
+                const float y0 = (o[u][db][4 * r4] * fA + ob[0] * fB) * inv;
+                const float y1 = (o[u][db][4 * r4 + 1] * fA + ob[1] * fB) * inv;
+                const float y2 = (o[u][db][4 * r4 + 2] * fA + ob[2] * fB) * inv;
+                const float y3 = (o[u][db][4 * r4 + 3] * fA + ob[3] * fB) * inv;
+                if (P.out_fp32) {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
+                } else {
+                    const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
+                }
             }
         }
     }
@@ -265,21 +535,33 @@ hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream) 
     if (p.max_blocks > kMaxBlocksPrefill) return hipErrorInvalidValue;
     PrefillParams P{};
     P.out = p.out;
-    P.q = static_cast<const uint16_t *>(p.q);
+    P.q = static_cast<uint16_t *>(p.q);
     P.k_pool = static_cast<const uint16_t *>(p.k_pool);
     P.v_pool = static_cast<const uint16_t *>(p.v_pool);
     P.bt = p.block_tables;
     P.prefix_lens = p.prefix_lens;
+    P.rope = p.rope;
     P.chunk_len = p.chunk_len;
     P.max_blocks = p.max_blocks;
     P.num_pages = p.num_pages;
     P.max_pos = p.max_pos;
-    P.n_tiles = (p.chunk_len + kQT - 1) / kQT;
-    P.scale_log2 = p.scale * 1.4426950408889634f;
+    P.n_tiles = (p.chunk_len + kRows - 1) / kRows;
+    P.write_q = p.out != p.q;
+    // Scores are taken in units of c = |scale| log2(e) (q is negated when
+    // scale < 0).  c is kept >= 1e-30 so that a masked score of -inf always
+    // maps to weight 0; for scale == 0 the weights are then exp2(~0) = 1, the
+    // uniform average the definition gives.
+    const float c = p.scale * 1.4426950408889634f;
+    P.neg = c < 0.0f;
+    P.c = fmaxf(fabsf(c), 1e-30f);
+    P.thr = kRescaleLog2 / P.c;
     P.out_fp32 = p.out_fp32;
     P.flags = p.flags;
     const int64_t blocks = static_cast<int64_t>(p.num_seqs) * kHKV * P.n_tiles;
-    hipLaunchKernelGGL(k_prefill_attn, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, P);
+    if (p.out_fp32)
+        hipLaunchKernelGGL(k_prefill_attn<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, P);
+    else
+        hipLaunchKernelGGL(k_prefill_attn<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, P);
     return hipGetLastError();
 }
 
