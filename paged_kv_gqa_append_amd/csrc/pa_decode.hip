@@ -232,6 +232,11 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
+    // Issue priority starts high and steps down as the wave's pages run out
+    // (see the main loop): two workgroups share each CU, and age-ordered
+    // arbitration alone lets the older one finish far ahead of the younger,
+    // which then streams alone with half the loads in flight.
+    __builtin_amdgcn_s_setprio(3);
 
     __shared__ int s_pages[kMaxPartPages];
     __shared__ float s_m[kWaves][kGroup];
@@ -422,14 +427,26 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     const int p_stop = (pg1 == n_pages) ? n_pages - 1 : pg1;
     KVRegs alt;
     bool last_in_alt = false;
+    // Priority levels by progress through the partition (10/16, 13/16, 15/16):
+    // a workgroup that has fallen behind its CU neighbour keeps the higher
+    // level and catches up, so both end close together.
+    const int span = pg1 - pg0;
+    auto level = [&]() {
+        const int done16 = 16 * (p - pg0);
+        if (done16 >= 15 * span) __builtin_amdgcn_s_setprio(0);
+        else if (done16 >= 13 * span) __builtin_amdgcn_s_setprio(1);
+        else if (done16 >= 10 * span) __builtin_amdgcn_s_setprio(2);
+    };
     while (p < p_stop) {
         if (p + kWaves < pg1) alt = load_page(p + kWaves);
         process_full(cur);
         p += kWaves;
+        level();
         if (p >= p_stop) { last_in_alt = true; break; }
         if (p + kWaves < pg1) cur = load_page(p + kWaves);
         process_full(alt);
         p += kWaves;
+        level();
     }
     if (pg1 == n_pages && p == n_pages - 1) {  // this wave owns the sequence's last page
         if (last_in_alt) cur = alt;
