@@ -225,6 +225,7 @@ struct DecodeParams {
 template <int kWaves, bool kFused>
 __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P) {
     constexpr int kThreads = 64 * kWaves;
+    static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
     const int part = blockIdx.x % P.num_parts;
     const int sj = blockIdx.x / P.num_parts;
     const int j = sj & (kHKV - 1);
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     // which then streams alone with half the loads in flight.
     __builtin_amdgcn_s_setprio(3);
 
-    __shared__ int s_pages[kMaxPartPages];
+    __shared__ int s_app_page;  // fused: page of the appended token (last partition)
     __shared__ float s_m[kWaves][kGroup];
     __shared__ float s_l[kWaves][kGroup];
     __shared__ float s_acc[kWaves][kGroup][kD];
@@ -265,12 +266,15 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
     const int L = P.lens[s];
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    // Wave w takes pages pg0+w, pg0+w+kWaves, ...  Its first page id is read
-    // directly, so that page's loads go out before the table reaches LDS; any id
-    // inside the pool is safe to read, and a page that turns out not to be needed
-    // (or an id that fails validation below) is simply never used.
+    // Wave w takes pages pg0+w, pg0+w+kWaves, ...; lane i of the wave holds the
+    // id of its i-th page (at most 16 per wave), read back with readlane in the
+    // loop, so no page id goes through LDS.  The first id is also read by a
+    // scalar load, so that page's loads go out as early as possible; any id
+    // inside the pool is safe to read, and a page that turns out not to be
+    // needed (or an id that fails validation below) is simply never used.
     const int first_id = wu < slice ? bt_row[pg0 + wu] : -1;
-    const int my_page = bt_row[pg0 + min(tid, slice - 1)];
+    const int my_idx = wu + kWaves * lane;  // partition-relative page of this lane's id
+    const int my_id = bt_row[pg0 + min(my_idx, slice - 1)];
     const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
     const int64_t nrow = (static_cast<int64_t>(s) * kHKV + j) * kD;
     const int pos = L - 1;
@@ -339,10 +343,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     const int n_pages = len_ok ? (L + kPage - 1) / kPage : 0;
     const int n_parts_s = (n_pages + P.part_pages - 1) / P.part_pages;
     const int pg1 = min(pg0 + P.part_pages, n_pages);
-    int bad = 0;
-    if (tid < slice) {
-        s_pages[tid] = my_page;
-        bad = (pg0 + tid < n_pages) && (my_page < 0 || my_page >= P.num_pages);
+    const int bad = (my_idx < slice) && (pg0 + my_idx < n_pages) && (my_id < 0 || my_id >= P.num_pages);
+    if (kFused) {  // the lane holding the appended token's page publishes it
+        const int rel = (pos >> 4) - pg0;
+        if (len_ok && rel >= 0 && rel == my_idx && rel < slice) s_app_page = my_id;
     }
     bool ok = len_ok && (__syncthreads_or(bad) == 0);
     if (ok && n_parts_s > 1) {  // long context: the whole row decides, as in every partition
@@ -369,13 +373,21 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         // Append: the new row goes into its slot now that the sequence is known
         // good (last partition only; nothing in this kernel reads the slot back).
         if (tid < 8 && pg1 == n_pages) {
-            const int64_t dst = static_cast<int64_t>(s_pages[(pos >> 4) - pg0]) * kPageElems + tile_j +
+            const int64_t dst = static_cast<int64_t>(s_app_page) * kPageElems + tile_j +
                                 (pos & (kPage - 1)) * kD + c * 8;
             *reinterpret_cast<u32x4 *>(P.k_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newk[c * 8]);
             *reinterpret_cast<u32x4 *>(P.v_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newv[c * 8]);
         }
+        // The rotated q can be stored now: this workgroup's raw q loads completed
+        // before the rotation, and with one partition no other workgroup reads
+        // these rows (longer contexts leave it to k_decode_merge).
+        if (P.write_q && n_parts_s == 1 && tid >= 64 && tid < 96)
+            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 64) * 8) =
+                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 64) * 8]);
     }
-    auto load_page = [&](int p) { return load_tile(__builtin_amdgcn_readfirstlane(s_pages[p - pg0])); };
+    auto load_page = [&](int p) {
+        return load_tile(__builtin_amdgcn_readlane(my_id, (p - pg0 - wu) / kWaves));
+    };
     int p = pg0 + wu;
 
     // ---- per-lane softmax state ----------------------------------------------
@@ -477,10 +489,6 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         s_l[w][hm] = l_tot;
     }
     __syncthreads();
-
-    // every wave has read q by now: the rotated q can be stored (fused, single partition)
-    if (kFused && P.write_q && n_parts_s == 1 && tid < 32)
-        *reinterpret_cast<u32x4 *>(P.q + qrow0 + tid * 8) = *reinterpret_cast<const u32x4 *>(&s_q[0][tid * 8]);
 
     // ---- merge the waves: thread (h, d) --------------------------------------
     if (tid < kGroup * kD) {
