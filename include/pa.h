@@ -72,7 +72,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1, /* NULL, non-positive size, misaligned pointer    */
     PA_ERR_UNSUPPORTED = 2, /* page_size other than 16, dtype not supported   */
     PA_ERR_WORKSPACE = 3,   /* decode workspace missing or too small          */
-    PA_ERR_HIP = 4          /* the HIP runtime refused a launch               */
+    PA_ERR_HIP = 4,         /* the HIP runtime refused a launch               */
+    PA_ERR_REJECTED = 5     /* request budget exceeds the whole pool (pa_kvm) */
 } pa_status;
 
 typedef enum { PA_OUT_BF16 = 0, PA_OUT_FP32 = 1 } pa_out_dtype;
@@ -175,6 +176,74 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
                            const float *rope_cos_sin, int32_t num_seqs, int32_t chunk_len,
                            int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                            float scale, int32_t out_dtype, uint32_t *device_flags, hipStream_t stream);
+
+/* ------------------------------------------------ host KV page manager --
+ * Host-side bookkeeping that produces the block tables and lengths the calls
+ * above consume (samir-vllm, section "Gestion de la KV cache et strategies de
+ * batching": one shared pool of 16-token pages, a block table per sequence and
+ * per layer, admission once a request's page budget is available, the budget
+ * being prompt_tokens + allowed_new_tokens - 1 tokens rounded up to 16-token
+ * pages for every layer, continuous or static batching, explicit refusal of a
+ * request larger than the pool).  Initial state as tiny-vllm ch.2 "What else is
+ * set up ...": all pages free, all block-table entries -1, all slots free.
+ *
+ * Ownership: the manager is a host object created by pa_kvm_create and owned by
+ * the caller until pa_kvm_destroy; it allocates host memory only, never device
+ * memory, and the caller uploads the tables it exposes.  Not thread-safe: one
+ * thread (or external locking) per manager.
+ * Policies: budgets are reserved at admission and pages are taken from the free
+ * list as a slot grows (so growth within the budget cannot fail); the free list
+ * is a stack (page 0 first on a fresh pool, the page freed last is reused
+ * first); admission is first-come first-served with no overtaking.          */
+typedef struct pa_kv_manager pa_kv_manager;
+typedef enum { PA_BATCH_CONTINUOUS = 0, PA_BATCH_STATIC = 1 } pa_batching;
+
+/* Pages a request reserves: ceil((prompt + max_new - 1) / 16) * num_layers; the
+ * last generated token is never appended, hence the -1.  -1 for a non-positive
+ * argument.                                                                  */
+int64_t pa_admission_credit_pages(int32_t prompt_tokens, int32_t max_new_tokens, int32_t num_layers);
+
+/* Create a manager for a pool of num_pages pages shared by num_layers layers,
+ * max_slots batch slots and block tables of max_blocks entries.  batching is a
+ * pa_batching value.  *out receives the handle (NULL on error).              */
+pa_status pa_kvm_create(int32_t num_pages, int32_t num_layers, int32_t max_slots, int32_t max_blocks,
+                        int32_t batching, pa_kv_manager **out);
+void pa_kvm_destroy(pa_kv_manager *m);
+
+/* Queue a request.  PA_ERR_REJECTED when its budget exceeds the pool or its
+ * token budget exceeds max_blocks*16 (it could never run); PA_ERR_INVALID_ARG
+ * for prompt_tokens < 1 or max_new_tokens < 1.  *request_id gets a
+ * non-negative id, or -1 on error.                                           */
+pa_status pa_kvm_submit(pa_kv_manager *m, int32_t prompt_tokens, int32_t max_new_tokens, int32_t *request_id);
+
+/* Admit queued requests in arrival order while the head's budget fits in the
+ * unreserved pages and a slot is free (static batching: only when no slot is
+ * active).  Writes the admitted slots to admitted_slots[0..n) and returns n
+ * (at most max_out), or -1 for bad arguments.  An admitted slot starts at
+ * length 0 with its budget reserved.                                         */
+int32_t pa_kvm_schedule(pa_kv_manager *m, int32_t *admitted_slots, int32_t max_out);
+
+/* Grow an active slot to len tokens (its context_lens value): blocks
+ * ceil(old/16) .. ceil(len/16)-1 get pages from the free list in every layer.
+ * PA_ERR_INVALID_ARG for a free slot, a shrinking len or len beyond the slot's
+ * budget of prompt + max_new - 1 tokens.                                     */
+pa_status pa_kvm_set_length(pa_kv_manager *m, int32_t slot, int32_t len);
+
+/* Finish a slot: its pages return to the free list (all layers), its budget is
+ * released, its table rows become -1 and its length 0.                       */
+pa_status pa_kvm_release(pa_kv_manager *m, int32_t slot);
+
+/* Read-only views, valid until the next call that modifies the manager:
+ * block tables [num_layers][max_slots][max_blocks] int32 (-1 unassigned; the
+ * table of layer l is the slice at l*max_slots*max_blocks) and lengths
+ * [max_slots] int32 (0 for a free slot).                                     */
+const int32_t *pa_kvm_block_tables(const pa_kv_manager *m);
+const int32_t *pa_kvm_lengths(const pa_kv_manager *m);
+int32_t pa_kvm_slot_request(const pa_kv_manager *m, int32_t slot);  /* request id, -1 if free */
+int32_t pa_kvm_slot_budget(const pa_kv_manager *m, int32_t slot);   /* token budget, -1 if bad */
+int32_t pa_kvm_free_pages(const pa_kv_manager *m);                  /* pages on the free list   */
+int64_t pa_kvm_reserved_pages(const pa_kv_manager *m);              /* budgets of active slots   */
+int32_t pa_kvm_queued(const pa_kv_manager *m);                      /* requests not yet admitted */
 
 #ifdef __cplusplus
 }

@@ -20,13 +20,17 @@ from . import workloads as _w
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 _lib = None
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_REJECTED = range(6)
+PA_BATCH_CONTINUOUS, PA_BATCH_STATIC = 0, 1
 PA_OUT_BF16, PA_OUT_FP32 = 0, 1
 PA_DEVERR_CONTEXT_LEN, PA_DEVERR_PAGE_ID = 0x1, 0x2
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_append_kv_rope",
            "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode_gqa", "pa_append_decode_gqa",
-           "pa_prefill_chunk")
+           "pa_prefill_chunk", "pa_admission_credit_pages", "pa_kvm_create", "pa_kvm_destroy", "pa_kvm_submit",
+           "pa_kvm_schedule", "pa_kvm_set_length", "pa_kvm_release", "pa_kvm_block_tables", "pa_kvm_lengths",
+           "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
+           "pa_kvm_queued")
 
 
 class PaError(RuntimeError):
@@ -65,6 +69,30 @@ def lib():
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
                                    P, P]
+    i64 = ctypes.c_int64
+    L.pa_admission_credit_pages.restype = i64
+    L.pa_admission_credit_pages.argtypes = [i32, i32, i32]
+    L.pa_kvm_create.restype = ctypes.c_int
+    L.pa_kvm_create.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(P)]
+    L.pa_kvm_destroy.restype = None
+    L.pa_kvm_destroy.argtypes = [P]
+    L.pa_kvm_submit.restype = ctypes.c_int
+    L.pa_kvm_submit.argtypes = [P, i32, i32, ctypes.POINTER(i32)]
+    L.pa_kvm_schedule.restype = i32
+    L.pa_kvm_schedule.argtypes = [P, P, i32]
+    L.pa_kvm_set_length.restype = ctypes.c_int
+    L.pa_kvm_set_length.argtypes = [P, i32, i32]
+    L.pa_kvm_release.restype = ctypes.c_int
+    L.pa_kvm_release.argtypes = [P, i32]
+    for name in ("pa_kvm_block_tables", "pa_kvm_lengths"):
+        getattr(L, name).restype = ctypes.POINTER(i32)
+        getattr(L, name).argtypes = [P]
+    for name in ("pa_kvm_slot_request", "pa_kvm_slot_budget"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [P, i32]
+    for name, rt in (("pa_kvm_free_pages", i32), ("pa_kvm_reserved_pages", i64), ("pa_kvm_queued", i32)):
+        getattr(L, name).restype = rt
+        getattr(L, name).argtypes = [P]
     _lib = L
     return L
 
@@ -254,3 +282,82 @@ def prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_chunk: torch.Tensor, v_c
                                 float(scale), odt, _ptr(device_flags), _stream(stream))
     _check(rc, "pa_prefill_chunk")
     return out
+
+
+def admission_credit_pages(prompt_tokens: int, max_new_tokens: int, num_layers: int) -> int:
+    return int(lib().pa_admission_credit_pages(int(prompt_tokens), int(max_new_tokens), int(num_layers)))
+
+
+class KVManager:
+    """Host page manager of libpa (pa_kvm_*): free list, per-(slot, layer) block
+    tables, admission credit and batching policy.  Thin wrapper: every decision
+    is made by the library; this class only copies its tables into numpy."""
+
+    def __init__(self, num_pages: int, num_layers: int, max_slots: int, max_blocks: int,
+                 batching: int = PA_BATCH_CONTINUOUS):
+        self.num_pages, self.num_layers = int(num_pages), int(num_layers)
+        self.max_slots, self.max_blocks = int(max_slots), int(max_blocks)
+        h = ctypes.c_void_p()
+        _check(lib().pa_kvm_create(self.num_pages, self.num_layers, self.max_slots, self.max_blocks, int(batching),
+                                   ctypes.byref(h)), "pa_kvm_create")
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().pa_kvm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, prompt_tokens: int, max_new_tokens: int) -> int:
+        rid = ctypes.c_int32(-1)
+        _check(lib().pa_kvm_submit(self._h, int(prompt_tokens), int(max_new_tokens), ctypes.byref(rid)),
+               "pa_kvm_submit")
+        return int(rid.value)
+
+    def schedule(self, max_out: Optional[int] = None) -> list:
+        n_max = self.max_slots if max_out is None else int(max_out)
+        buf = (ctypes.c_int32 * max(n_max, 1))()
+        n = int(lib().pa_kvm_schedule(self._h, buf, n_max))
+        if n < 0:
+            raise PaError(PA_ERR_INVALID_ARG, "pa_kvm_schedule")
+        return [int(buf[i]) for i in range(n)]
+
+    def set_length(self, slot: int, length: int) -> None:
+        _check(lib().pa_kvm_set_length(self._h, int(slot), int(length)), "pa_kvm_set_length")
+
+    def release(self, slot: int) -> None:
+        _check(lib().pa_kvm_release(self._h, int(slot)), "pa_kvm_release")
+
+    def block_tables(self) -> np.ndarray:
+        """Copy of the tables, [num_layers][max_slots][max_blocks] int32."""
+        n = self.num_layers * self.max_slots * self.max_blocks
+        p = lib().pa_kvm_block_tables(self._h)
+        return np.ctypeslib.as_array(p, shape=(n,)).reshape(self.num_layers, self.max_slots,
+                                                             self.max_blocks).copy()
+
+    def lengths(self) -> np.ndarray:
+        p = lib().pa_kvm_lengths(self._h)
+        return np.ctypeslib.as_array(p, shape=(self.max_slots,)).copy()
+
+    def slot_request(self, slot: int) -> int:
+        return int(lib().pa_kvm_slot_request(self._h, int(slot)))
+
+    def slot_budget(self, slot: int) -> int:
+        return int(lib().pa_kvm_slot_budget(self._h, int(slot)))
+
+    @property
+    def free_pages(self) -> int:
+        return int(lib().pa_kvm_free_pages(self._h))
+
+    @property
+    def reserved_pages(self) -> int:
+        return int(lib().pa_kvm_reserved_pages(self._h))
+
+    @property
+    def queued(self) -> int:
+        return int(lib().pa_kvm_queued(self._h))

@@ -79,11 +79,12 @@ const char *pa_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
         case PA_ERR_HIP: return "PA_ERR_HIP";
+        case PA_ERR_REJECTED: return "PA_ERR_REJECTED";
         default: return "PA_ERR_UNKNOWN";
     }
 }
 
-int32_t pa_abi_version(void) { return 1; }
+int32_t pa_abi_version(void) { return 2; }
 
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;

@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == 1
+    assert pa.lib().pa_abi_version() == 2
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
