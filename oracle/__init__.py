@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-               "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -149,4 +149,58 @@ def prefill_chunk(q, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens
     out = np.zeros((B, C, 32, 64), dtype=np.float64)
     rc = lib.oracle_prefill_chunk(_ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(k_pool), _ptr(v_pool), _ptr(bt),
                                   _ptr(pl), B, C, int(bt.shape[-1]), int(num_pages), float(theta), float(scale))
+    return out, int(rc)
+
+
+# ------------------------------------------------------------------ INT8 pages --
+I8_TILE_BYTES = 2176
+
+
+def _i8_setup(lib):
+    P, i32, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double
+    lib.oracle_quantize_row_i8.restype = None
+    lib.oracle_quantize_row_i8.argtypes = [P, P, P]
+    lib.oracle_append_kv_rope_i8.restype = ctypes.c_int
+    lib.oracle_append_kv_rope_i8.argtypes = [P, P, P, P, P, P, i32, i32, i32, dbl]
+    lib.oracle_decode_gqa_i8.restype = ctypes.c_int
+    lib.oracle_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, dbl]
+
+
+def quantize_row_i8(x_bits):
+    """One 64-value row (bf16 patterns) -> (int8 codes [64], fp32 scale)."""
+    lib = _load()
+    _i8_setup(lib)
+    x = _u16(x_bits)
+    assert x.shape == (64,)
+    codes = np.zeros(64, dtype=np.int8)
+    sc = np.zeros(1, dtype=np.float32)
+    lib.oracle_quantize_row_i8(_ptr(x), _ptr(codes), _ptr(sc))
+    return codes, np.float32(sc[0])
+
+
+def append_kv_rope_i8(q, k_new, v_new, pool, block_tables, context_lens, num_pages: int, theta: float) -> int:
+    """In place on ``q`` (may be None) and ``pool`` (uint8 [P][8][2176]); returns a status code."""
+    lib = _load()
+    _i8_setup(lib)
+    if not (pool.flags.c_contiguous and pool.dtype == np.uint8):
+        raise TypeError("pool must be C-contiguous uint8")
+    if q is not None and not (q.flags.c_contiguous and q.dtype == np.uint16):
+        raise TypeError("q must be C-contiguous uint16")
+    kn, vn = _u16(k_new), _u16(v_new)
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    return int(lib.oracle_append_kv_rope_i8(_ptr(q), _ptr(kn), _ptr(vn), _ptr(pool), _ptr(bt), _ptr(cl),
+                                            int(cl.shape[0]), int(bt.shape[-1]), int(num_pages), float(theta)))
+
+
+def decode_gqa_i8(q, pool, block_tables, context_lens, num_pages: int, scale: float):
+    """Returns (out fp64 [B][32][64], status)."""
+    lib = _load()
+    _i8_setup(lib)
+    qq = _u16(q)
+    pl = np.ascontiguousarray(pool, dtype=np.uint8)
+    bt, cl = _i32(block_tables), _i32(context_lens)
+    B = int(cl.shape[0])
+    out = np.zeros((B, 32, 64), dtype=np.float64)
+    rc = lib.oracle_decode_gqa_i8(_ptr(out), _ptr(qq), _ptr(pl), _ptr(bt), _ptr(cl), B, int(bt.shape[-1]),
+                                  int(num_pages), float(scale))
     return out, int(rc)

@@ -275,6 +275,171 @@ int oracle_prefill_chunk(double *out, uint16_t *q, const uint16_t *k_chunk, cons
     return rc;
 }
 
+/* ----------------------------------------------------------- INT8 pages --
+ * A KV cache stored as INT8 K/V (TinyLoop, "Lifecycle and Memory Model",
+ * RuntimeKVCache INT8 K/V mode).  The pages give no quantisation rule; the
+ * reading taken (and the library's documented format) is one symmetric scale
+ * per (token, KV head) row of 64 values:
+ *     scale = max|x| / 127,   code = round-half-even(x / scale) in [-127, 127],
+ * taken in IEEE binary32 (the precision the decision is made in on the device;
+ * x86-64 SSE float arithmetic is exactly that), a zero row giving scale 0 and
+ * codes 0.  The value a code stands for is code * scale, exact in double.
+ * K rows are quantised after RoPE from their bf16-rounded values, V rows from
+ * their bf16 input.
+ * Tile of (page, head): 2176 bytes = K codes [0,1024) + V codes [1024,2048) +
+ * per token t the K scale (float) at 2048+8t and the V scale at 2052+8t; code
+ * of element d of token t at byte ((t&7)*8 + d/8)*16 + (t/8)*8 + d%8 of its
+ * block.                                                                   */
+#define O_I8_TILE 2176
+
+static size_t i8_tile(int64_t page, int head) { return ((size_t)page * O_HKV + (size_t)head) * O_I8_TILE; }
+static size_t i8_pos(int t, int d) { return (size_t)((((t & 7) * 8 + d / 8) * 16) + (t / 8) * 8 + d % 8); }
+
+/* One row: x given as 64 bf16 patterns. */
+void oracle_quantize_row_i8(const uint16_t *x, int8_t *codes, float *scale_out)
+{
+    float v[O_D];
+    float amax = 0.0f;
+    for (int d = 0; d < O_D; ++d) {
+        v[d] = (float)oracle_bf16_to_f64(x[d]); /* exact */
+        if (fabsf(v[d]) > amax) amax = fabsf(v[d]);
+    }
+    float scale = amax / 127.0f;
+    for (int d = 0; d < O_D; ++d) {
+        float c = 0.0f;
+        if (scale > 0.0f) {
+            c = rintf(v[d] / scale);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+        }
+        codes[d] = (int8_t)c;
+    }
+    *scale_out = scale;
+}
+
+static void store_row_i8(uint8_t *tile, int block_off, int scale_off, int slot, const uint16_t *row)
+{
+    int8_t codes[O_D];
+    float sc;
+    oracle_quantize_row_i8(row, codes, &sc);
+    for (int d = 0; d < O_D; ++d) tile[block_off + i8_pos(slot, d)] = (uint8_t)codes[d];
+    memcpy(tile + 2048 + 8 * slot + scale_off, &sc, 4);
+}
+
+static int append_token_i8(uint16_t *q_tok, const uint16_t *k_tok, const uint16_t *v_tok, uint8_t *pool,
+                           const int32_t *bt_row, int32_t max_blocks, int32_t num_pages, int64_t pos, double theta)
+{
+    int64_t blk = pos / O_PS;
+    int slot = (int)(pos % O_PS);
+    if (blk >= max_blocks) return ORACLE_BAD_LEN;
+    int64_t page = bt_row[blk];
+    if (page < 0 || page >= num_pages) return ORACLE_BAD_PAGE;
+    double y[O_D];
+    uint16_t kb[O_D];
+    for (int j = 0; j < O_HKV; ++j) {
+        uint8_t *tile = pool + i8_tile(page, j);
+        oracle_rope_head(k_tok + (size_t)j * O_D, pos, theta, y);
+        for (int d = 0; d < O_D; ++d) kb[d] = oracle_f64_to_bf16(y[d]);
+        store_row_i8(tile, 0, 0, slot, kb);
+        store_row_i8(tile, 1024, 4, slot, v_tok + (size_t)j * O_D);
+    }
+    if (q_tok) {
+        for (int h = 0; h < O_HQ; ++h) {
+            oracle_rope_head(q_tok + (size_t)h * O_D, pos, theta, y);
+            for (int d = 0; d < O_D; ++d) q_tok[(size_t)h * O_D + d] = oracle_f64_to_bf16(y[d]);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Decode-time append into an INT8 pool (pool: num_pages * 8 * 2176 bytes). */
+int oracle_append_kv_rope_i8(uint16_t *q, const uint16_t *k_new, const uint16_t *v_new, uint8_t *pool,
+                             const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                             int32_t max_blocks, int32_t num_pages, double theta)
+{
+    if (num_seqs < 0 || max_blocks <= 0 || num_pages <= 0) return ORACLE_BAD_ARG;
+    int rc = ORACLE_OK;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int64_t L = context_lens[s];
+        if (L < 1) { rc = ORACLE_BAD_LEN; continue; }
+        int r = append_token_i8(q ? q + (size_t)s * O_HQ * O_D : NULL, k_new + (size_t)s * O_HKV * O_D,
+                                v_new + (size_t)s * O_HKV * O_D, pool, block_tables + (size_t)s * max_blocks,
+                                max_blocks, num_pages, L - 1, theta);
+        if (r != ORACLE_OK) rc = r;
+    }
+    return rc;
+}
+
+/* Value of element d of token t of a block (0: K, 1024: V) of a tile.      */
+static double i8_value(const uint8_t *tile, int block_off, int scale_off, int t, int d)
+{
+    float sc;
+    memcpy(&sc, tile + 2048 + 8 * t + scale_off, 4);
+    return (double)(int8_t)tile[block_off + i8_pos(t, d)] * (double)sc;
+}
+
+static int attend_i8(double *out, const uint16_t *q_head, const uint8_t *pool, const int32_t *bt_row,
+                     int32_t max_blocks, int32_t num_pages, int kv_head, int64_t n, double scale, double *score_buf)
+{
+    double qd[O_D];
+    for (int d = 0; d < O_D; ++d) qd[d] = oracle_bf16_to_f64(q_head[d]);
+    if ((n + O_PS - 1) / O_PS > max_blocks) return ORACLE_BAD_LEN;
+    double m = -INFINITY;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t page = bt_row[t / O_PS];
+        if (page < 0 || page >= num_pages) return ORACLE_BAD_PAGE;
+        const uint8_t *tile = pool + i8_tile(page, kv_head);
+        double acc = 0.0;
+        for (int d = 0; d < O_D; ++d) acc += qd[d] * i8_value(tile, 0, 0, (int)(t % O_PS), d);
+        score_buf[t] = scale * acc;
+        if (score_buf[t] > m) m = score_buf[t];
+    }
+    double z = 0.0, o[O_D];
+    for (int d = 0; d < O_D; ++d) o[d] = 0.0;
+    for (int64_t t = 0; t < n; ++t) {
+        const uint8_t *tile = pool + i8_tile(bt_row[t / O_PS], kv_head);
+        double w = exp(score_buf[t] - m);
+        z += w;
+        for (int d = 0; d < O_D; ++d) o[d] += w * i8_value(tile, 1024, 4, (int)(t % O_PS), d);
+    }
+    for (int d = 0; d < O_D; ++d) out[d] = o[d] / z;
+    return ORACLE_OK;
+}
+
+/* Decode over an INT8 pool: the decode definition with K_t, V_t the values
+ * the codes stand for.  out: [B][32][64] fp64.                             */
+int oracle_decode_gqa_i8(double *out, const uint16_t *q, const uint8_t *pool, const int32_t *block_tables,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
+                         double scale)
+{
+    if (num_seqs < 0 || max_blocks <= 0 || num_pages <= 0) return ORACLE_BAD_ARG;
+    int rc = ORACLE_OK;
+    int64_t maxn = 0;
+    for (int32_t s = 0; s < num_seqs; ++s)
+        if (context_lens[s] > maxn) maxn = context_lens[s];
+    #pragma omp parallel for schedule(dynamic) collapse(2) reduction(max : rc)
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        for (int h = 0; h < O_HQ; ++h) {
+            double *o = out + ((size_t)s * O_HQ + h) * O_D;
+            int64_t L = context_lens[s];
+            int r;
+            if (L < 1) {
+                r = ORACLE_BAD_LEN;
+            } else {
+                double *buf = (double *)malloc(sizeof(double) * (size_t)(maxn > 0 ? maxn : 1));
+                r = attend_i8(o, q + ((size_t)s * O_HQ + h) * O_D, pool, block_tables + (size_t)s * max_blocks,
+                              max_blocks, num_pages, h / (O_HQ / O_HKV), L, scale, buf);
+                free(buf);
+            }
+            if (r != ORACLE_OK) {
+                for (int d = 0; d < O_D; ++d) o[d] = NAN;
+                if (r > rc) rc = r;
+            }
+        }
+    }
+    return rc;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
