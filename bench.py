@@ -29,6 +29,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+# sources the fused decode kernel is compiled from (its traffic figure is tied to them)
+DECODE_SOURCES = ("pa_decode.hip", "pa_decode_core.h", "pa_device.h")
 METRIC = "paged GQA decode: KV-read GB/s and % of HBM peak; decode tokens/s (1 GPU)"
 
 
@@ -85,19 +87,22 @@ def build_workload(name, device):
 def measured_traffic():
     """HBM bytes per fused decode launch from the committed rocprofv3 PMC summary.
 
-    The summary records the sha256 of the decode kernel's source it was taken
-    with; if the source has changed since, the figure no longer applies and
-    None is returned.
+    The summary records the sha256 of the decode kernel's sources (the files
+    of DECODE_SOURCES, concatenated in that order) it was taken with; if they
+    have changed since, the figure no longer applies and None is returned.
     """
     import hashlib
     import re
 
     here = os.path.dirname(os.path.abspath(__file__))
-    src = os.path.join(here, "paged_kv_gqa_append_amd", "csrc", "pa_decode.hip")
+    csrc = os.path.join(here, "paged_kv_gqa_append_amd", "csrc")
     summ = os.path.join(here, "profiles", "decode_batch64_pmc_traffic.md")
     try:
         text = open(summ).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for name in DECODE_SOURCES:
+            h.update(open(os.path.join(csrc, name), "rb").read())
+        digest = h.hexdigest()
     except OSError:
         return None
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)

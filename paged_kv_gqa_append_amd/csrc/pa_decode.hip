@@ -43,184 +43,9 @@
 #include <math.h>
 #include <stdlib.h>
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_decode_core.h"
 
 namespace pa {
-
-constexpr int kMaxPartPages = 128;
-constexpr float kNegBig = -1.0e30f;   // running-max start (finite, so 2^(x - m) is never NaN)
-constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold
-
-// quad_perm broadcasts of quad lane a to the whole quad: [a,a,a,a]
-constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;
-constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRowRor8 = 0x128;
-
-struct KVRegs {
-    u32x4 ka, kb, v0, v1;
-};
-
-// Lane pairs (i, i^16) and (i, i^32) through the gfx950 row-swap permutes: with
-// the same value in both operands, the two results hold the lower and the upper
-// partner's value in every lane.  Two hipcc 7.2 pitfalls are avoided: the
-// second operand passes through an empty asm, because a swap of two operands
-// known to be equal is folded into two equal results (wrong for these row-wise
-// exchanges), and each result is copied to a scalar before it is reinterpreted,
-// because __builtin_bit_cast of a vector element is lowered as a load of
-// element 0.
-__device__ __forceinline__ void xor16_pair(float v, float &lo, float &hi) {
-    const unsigned a = __builtin_bit_cast(unsigned, v);
-    unsigned b = a;
-    asm volatile("" : "+v"(b));
-    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-    const unsigned r0 = r[0], r1 = r[1];
-    lo = __builtin_bit_cast(float, r0);
-    hi = __builtin_bit_cast(float, r1);
-}
-__device__ __forceinline__ void xor32_pair(float v, float &lo, float &hi) {
-    const unsigned a = __builtin_bit_cast(unsigned, v);
-    unsigned b = a;
-    asm volatile("" : "+v"(b));
-    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-    const unsigned r0 = r[0], r1 = r[1];
-    lo = __builtin_bit_cast(float, r0);
-    hi = __builtin_bit_cast(float, r1);
-}
-
-// Reduce-scatter step on a pair of values through a row-swap permute: after
-// swap(x, y) the lanes of the lower row (or half) hold their own x and their
-// partner's x, the upper ones their partner's y and their own y, so x' + y' is
-// the pair sum of x in the lower lanes and of y in the upper lanes.
-__device__ __forceinline__ float swap16_sum(float x, float y) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
-                                                    false, false);
-    const unsigned r0 = r[0], r1 = r[1];
-    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
-}
-__device__ __forceinline__ float swap32_sum(float x, float y) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
-                                                    false, false);
-    const unsigned r0 = r[0], r1 = r[1];
-    return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
-}
-
-// Sum over the 8 lane groups (lanes c, c+8, ..., c+56); every lane gets it.
-__device__ __forceinline__ float sum_groups(float v) {
-    float lo, hi;
-    v += dpp_f32<kRowRor8>(v);
-    xor16_pair(v, lo, hi);
-    v = lo + hi;
-    xor32_pair(v, lo, hi);
-    return lo + hi;
-}
-__device__ __forceinline__ float max_groups(float v) {
-    float lo, hi;
-    v = fmaxf(v, dpp_f32<kRowRor8>(v));
-    xor16_pair(v, lo, hi);
-    v = fmaxf(lo, hi);
-    xor32_pair(v, lo, hi);
-    return fmaxf(lo, hi);
-}
-
-// Score of the lane's own (token, head) pair for one page: partial dots of the
-// lane's 8-element chunk for the 8 pairs of its group (slot i < 4: token half
-// t0, head i^hm; slot i >= 4: token half t0^1), then a reduce-scatter over the
-// 8 lanes with partners c^1, c^2 and c^7.  Returns scale*log2(e)*<q, k>.
-__device__ __forceinline__ float page_score(const u32x4 (&qv)[kGroup], u32x4 ka, u32x4 kb, float scale_log2) {
-    float sa[kGroup], sb[kGroup];
-#pragma unroll
-    for (int m = 0; m < kGroup; ++m) {
-        sa[m] = dot8_bf16(qv[m], ka, 0.0f);
-        sb[m] = dot8_bf16(qv[m], kb, 0.0f);
-    }
-    const float r0 = sa[0] + dpp_f32<kXor1>(sb[0]);
-    const float r1 = sa[1] + dpp_f32<kXor1>(sb[1]);
-    const float r2 = sa[2] + dpp_f32<kXor1>(sb[2]);
-    const float r3 = sa[3] + dpp_f32<kXor1>(sb[3]);
-    const float u0 = r0 + dpp_f32<kXor2>(r2);
-    const float u1 = r1 + dpp_f32<kXor2>(r3);
-    return (u0 + dpp_f32<kHalfMirror>(u1)) * scale_log2;
-}
-
-// Online-softmax step for one page: lazily raise the wave's running max of the
-// lane's head (rescaling the accumulators of all 4 heads when any lane needs
-// it), then return the lane's weight 2^(x - m).
-__device__ __forceinline__ float softmax_step(float x, float &m_run, float &l_run, float (&acc)[kGroup][8]) {
-    const float xm = fmaxf(x, dpp_f32<kXor1>(x));  // this page's max for the head (both tokens)
-    if (__builtin_amdgcn_ballot_w64(xm > m_run + kRescaleLog2)) {
-        const float wm = max_groups(xm);
-        const float mn = wm > m_run + kRescaleLog2 ? wm : m_run;
-        const float f = fast_exp2(m_run - mn);
-        m_run = mn;
-        l_run *= f;
-        // factors per accumulator slot, routed like the weights in accumulate()
-        const float fm = dpp_f32<kHalfMirror>(f);
-        const float F0 = dpp_f32<kBcast0>(f), F2 = dpp_f32<kBcast2>(f);
-        const float G0 = dpp_f32<kBcast0>(fm), G2 = dpp_f32<kBcast2>(fm);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            acc[0][i] *= F0;
-            acc[1][i] *= G0;
-            acc[2][i] *= F2;
-            acc[3][i] *= G2;
-        }
-    }
-    const float pw = fast_exp2(x - m_run);
-    l_run += pw;
-    return pw;
-}
-
-__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
-    const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        f[2 * k] = bf16_lo(a[k]);
-        f[2 * k + 1] = bf16_hi(a[k]);
-    }
-}
-
-// acc[e] += sum over the group's 8 (token, head) weights of w * V[token]: P_a is
-// the weight held by quad lane a, Q_a that of its mirror lane; V slot u (va/vb)
-// and accumulator slot e are permuted by the lane bits so that quad lane a's
-// pair always lands in slot e = 2*(a>>1) with V slot a&1 (Q_a: e + 1).
-__device__ __forceinline__ void accumulate(float pw, const float (&va)[8], const float (&vb)[8],
-                                           float (&acc)[kGroup][8]) {
-    const float pm = dpp_f32<kHalfMirror>(pw);
-    const float P0 = dpp_f32<kBcast0>(pw), P1 = dpp_f32<kBcast1>(pw);
-    const float P2 = dpp_f32<kBcast2>(pw), P3 = dpp_f32<kBcast3>(pw);
-    const float Q0 = dpp_f32<kBcast0>(pm), Q1 = dpp_f32<kBcast1>(pm);
-    const float Q2 = dpp_f32<kBcast2>(pm), Q3 = dpp_f32<kBcast3>(pm);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        acc[0][i] = fmaf(P0, va[i], fmaf(P1, vb[i], acc[0][i]));
-        acc[1][i] = fmaf(Q0, va[i], fmaf(Q1, vb[i], acc[1][i]));
-        acc[2][i] = fmaf(P2, va[i], fmaf(P3, vb[i], acc[2][i]));
-        acc[3][i] = fmaf(Q2, va[i], fmaf(Q3, vb[i], acc[3][i]));
-    }
-}
-
-struct DecodeParams {
-    void *out;
-    uint16_t *q;
-    const uint16_t *k_new;
-    const uint16_t *v_new;
-    uint16_t *k_pool;
-    uint16_t *v_pool;
-    const int32_t *bt;
-    const int32_t *lens;
-    const float *rope;
-    int max_blocks;
-    int num_pages;
-    int max_pos;
-    float scale_log2;
-    int out_fp32;
-    int part_pages;
-    int num_parts;
-    int write_q;          // fused only: store the rotated q back (out does not alias q)
-    float *ws_ml;
-    float *ws_acc;
-    uint32_t *flags;
-};
 
 template <int kWaves, bool kFused>
 __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P) {
@@ -521,50 +346,6 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     }
 }
 
-// One wave per (sequence, query head): merge that head's partitions.  In the
-// fused variant it also stores the rotated q row (all partitions have read q).
-template <bool kFused>
-__global__ __launch_bounds__(64) void k_decode_merge(DecodeParams P) {
-    const int s = blockIdx.x / kHQ;
-    const int qh = blockIdx.x % kHQ;
-    const int d = threadIdx.x;
-    const int L = P.lens[s];
-    bool len_ok = (L >= 1) && (L <= P.max_blocks * kPage);
-    if (kFused) len_ok = len_ok && (L - 1 < P.max_pos);
-    if (!len_ok) return;  // zero-filled by the partial kernel
-    const int n_pages = (L + kPage - 1) / kPage;
-    const int n_parts_s = (n_pages + P.part_pages - 1) / P.part_pages;
-    if (n_parts_s <= 1) return;  // written directly by the partial kernel
-    const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
-    int bad = 0;
-    for (int b = d; b < n_pages; b += 64) bad |= (bt_row[b] < 0) | (bt_row[b] >= P.num_pages);
-    if (__syncthreads_or(bad)) return;
-    const int64_t row0 = (static_cast<int64_t>(s) * kHQ + qh) * P.num_parts;
-    float M = kNegBig;
-    for (int k = 0; k < n_parts_s; ++k) M = fmaxf(M, P.ws_ml[(row0 + k) * 2]);
-    float Ls = 0.0f, A = 0.0f;
-    for (int k = 0; k < n_parts_s; ++k) {
-        const float wgt = fast_exp2(P.ws_ml[(row0 + k) * 2] - M);
-        Ls = fmaf(wgt, P.ws_ml[(row0 + k) * 2 + 1], Ls);
-        A = fmaf(wgt, P.ws_acc[(row0 + k) * kD + d], A);
-    }
-    const int64_t o = (static_cast<int64_t>(s) * kHQ + qh) * kD + d;
-    if (kFused && P.write_q) {
-        const int pos = L - 1;
-        const int i = d & 31;
-        const float co = P.rope[static_cast<int64_t>(pos) * kD + 2 * i];
-        const float si = P.rope[static_cast<int64_t>(pos) * kD + 2 * i + 1];
-        uint16_t *qr = P.q + o - d;
-        const float xv = bf16_to_f32(qr[d]);
-        const float pv = bf16_to_f32(qr[d ^ 32]);
-        const float y = d >= 32 ? fmaf(xv, co, pv * si) : fmaf(xv, co, -(pv * si));
-        __syncthreads();  // both halves read before either is written
-        qr[d] = f32_to_bf16(y);
-    }
-    const float r = A / Ls;
-    if (P.out_fp32) static_cast<float *>(P.out)[o] = r;
-    else static_cast<uint16_t *>(P.out)[o] = f32_to_bf16(r);
-}
 
 int decode_part_pages() {
     static int cached = [] {
