@@ -29,8 +29,14 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
-# sources the fused decode kernel is compiled from (its traffic figure is tied to them)
-DECODE_SOURCES = ("pa_decode.hip", "pa_decode_core.h", "pa_device.h")
+# sources each fused decode kernel is compiled from (its traffic figure is tied to them),
+# and the committed rocprofv3 summary that holds that figure
+TRAFFIC = {
+    "bf16": (("pa_decode.hip", "pa_decode_core.h", "pa_device.h"), "decode_batch64_pmc_traffic.md"),
+    "int8": (("pa_i8.hip", "pa_decode_core.h", "pa_device.h"), "decode_batch64_i8_pmc_traffic.md"),
+}
+# K+V bytes per (token, layer): 8 heads x 2 x 64 x 2 B in bf16; 8 tiles' share (2176 B / 16 slots) in INT8
+KV_TOKEN_BYTES = {"bf16": 2048, "int8": 8 * 2176 // 16}
 METRIC = "paged GQA decode: KV-read GB/s and % of HBM peak; decode tokens/s (1 GPU)"
 
 
@@ -42,6 +48,9 @@ def parse():
     ap.add_argument("--config", default="batch64", choices=["batch64", "batch256", "batch8", "tiny", "prefill"],
                     help="decode workloads, or 'prefill': 4 x (1536 cached + 512-token chunk) chunked prefill")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"])
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
+                    help="K/V page format: bf16 pools, or INT8 tiles (codes + one fp32 scale per token and head), "
+                         "quantised on the device from the same bf16 pages before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times): under rocprofv3 --pmc its FETCH_SIZE / "
@@ -84,11 +93,11 @@ def build_workload(name, device):
     return spec, k_pool, v_pool, layers, lens, rows
 
 
-def measured_traffic():
+def measured_traffic(kv="bf16"):
     """HBM bytes per fused decode launch from the committed rocprofv3 PMC summary.
 
     The summary records the sha256 of the decode kernel's sources (the files
-    of DECODE_SOURCES, concatenated in that order) it was taken with; if they
+    of TRAFFIC[kv], concatenated in that order) it was taken with; if they
     have changed since, the figure no longer applies and None is returned.
     """
     import hashlib
@@ -96,11 +105,12 @@ def measured_traffic():
 
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "paged_kv_gqa_append_amd", "csrc")
-    summ = os.path.join(here, "profiles", "decode_batch64_pmc_traffic.md")
+    sources, summary = TRAFFIC[kv]
+    summ = os.path.join(here, "profiles", summary)
     try:
         text = open(summ).read()
         h = hashlib.sha256()
-        for name in DECODE_SOURCES:
+        for name in sources:
             h.update(open(os.path.join(csrc, name), "rb").read())
         digest = h.hexdigest()
     except OSError:
@@ -112,8 +122,11 @@ def measured_traffic():
     return int(m_val.group(1))
 
 
-def cpu_baseline(spec, k_pool, v_pool, rows, target_s):
-    """Time the fp64 oracle's append + decode on whole layers of the workload (host cores)."""
+def cpu_baseline(spec, k_pool, v_pool, rows, target_s, kv="bf16"):
+    """Time the fp64 oracle's append + decode on whole layers of the workload (host cores).
+
+    For INT8 pages the oracle quantises the layer's bf16 pages itself (untimed)
+    and its INT8 append + decode are timed."""
     import oracle
     import torch
 
@@ -132,9 +145,15 @@ def cpu_baseline(spec, k_pool, v_pool, rows, target_s):
 
     def run(seqs, layer):
         kp, vp, bt, q, kn, vn, lens, npg = host_case(layer, seqs)
-        t0 = time.perf_counter()
-        rc = oracle.append_kv_rope(q, kn, vn, kp, vp, bt, lens, npg, spec.theta)
-        out, rc2 = oracle.decode_gqa(q, kp, vp, bt, lens, npg, spec.scale)
+        if kv == "int8":
+            pool = oracle.quantize_pages_i8(kp, vp)
+            t0 = time.perf_counter()
+            rc = oracle.append_kv_rope_i8(q, kn, vn, pool, bt, lens, npg, spec.theta)
+            out, rc2 = oracle.decode_gqa_i8(q, pool, bt, lens, npg, spec.scale)
+        else:
+            t0 = time.perf_counter()
+            rc = oracle.append_kv_rope(q, kn, vn, kp, vp, bt, lens, npg, spec.theta)
+            out, rc2 = oracle.decode_gqa(q, kp, vp, bt, lens, npg, spec.scale)
         dt = time.perf_counter() - t0
         assert rc == oracle.OK and rc2 == oracle.OK
         return dt, int(lens.astype(np.int64).sum())
@@ -149,11 +168,12 @@ def cpu_baseline(spec, k_pool, v_pool, rows, target_s):
         layers_done += 1
         if total_dt >= target_s:
             break
-    kv_bytes = total_tokens * 2048
+    kv_bytes = total_tokens * KV_TOKEN_BYTES[kv]
     return {"value": round(kv_bytes / total_dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(total_dt, 3),
             "tokens_per_s": round(B * layers_done / spec.num_layers / total_dt, 3),
-            "sample": f"fp64 oracle append + decode of all {B} sequences for {layers_done} of the "
+            "sample": f"fp64 oracle {'INT8 ' if kv == 'int8' else ''}append + decode of all {B} sequences for "
+                      f"{layers_done} of the "
                       f"{spec.num_layers} layers of the {spec.name} workload ({total_tokens} tokens attended, "
                       f"{kv_bytes} KV bytes); tokens/s scaled to whole {spec.num_layers}-layer steps"}
 
@@ -236,7 +256,8 @@ def main_prefill(args, torch, binding, device):
     res = {
         "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16" if not i8 else "int8 K/V, bf16 q/out, fp32 accumulation",
+        "data": "synthetic",
         "config": {"workload": "chunked_prefill", "num_seqs": c.num_seqs, "prefix_len": int(c.prefix_lens[0]),
                    "chunk_len": c.chunk_len, "layers": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
                    "page_size": 16, "num_pages": c.num_pages, "causal": "inclusive",
@@ -287,22 +308,32 @@ def main():
     table = binding.rope_table(2048 + 64, spec.theta, device)
     ws = binding.decode_workspace(spec.num_seqs, spec.max_blocks, device)
     stream = torch.cuda.current_stream()
+    i8 = args.kv == "int8"
+    if i8:
+        pool = binding.i8_pool(spec.num_pages, device)
+        binding.quantize_pages_i8(pool, k_pool, v_pool)
+        torch.cuda.synchronize()
 
-    def step_fused(ev=None):
-        for l, L in enumerate(layers):
-            if ev is not None:
-                ev[l][0].record(stream)
-            binding.append_decode_gqa(L["out"], L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens,
-                                      table, spec.scale, workspace=ws, stream=stream)
-            if ev is not None:
-                ev[l][1].record(stream)
+    def step_fused():
+        for L in layers:
+            if i8:
+                binding.append_decode_gqa_i8(L["out"], L["q"], L["k_new"], L["v_new"], pool, L["bt"], lens, table,
+                                             spec.scale, workspace=ws, stream=stream)
+            else:
+                binding.append_decode_gqa(L["out"], L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens,
+                                          table, spec.scale, workspace=ws, stream=stream)
 
-    def step_separate(ev=None):
-        for l, L in enumerate(layers):
-            binding.append_kv_rope(L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens, table,
+    def step_separate():
+        for L in layers:
+            if i8:
+                binding.append_kv_rope_i8(L["q"], L["k_new"], L["v_new"], pool, L["bt"], lens, table, stream=stream)
+                binding.decode_gqa_i8(L["out"], L["q"], pool, L["bt"], lens, spec.scale, workspace=ws,
+                                      stream=stream)
+            else:
+                binding.append_kv_rope(L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens, table,
+                                       stream=stream)
+                binding.decode_gqa(L["out"], L["q"], k_pool, v_pool, L["bt"], lens, spec.scale, workspace=ws,
                                    stream=stream)
-            binding.decode_gqa(L["out"], L["q"], k_pool, v_pool, L["bt"], lens, spec.scale, workspace=ws,
-                               stream=stream)
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -336,32 +367,38 @@ def main():
         seq_ms.append(a.elapsed_time(b))
     dec_ms_mean = float(np.mean(seq_ms)) / spec.num_layers
 
-    kv_step = spec.kv_bytes()
+    kv_step = spec.kv_bytes() // 2048 * KV_TOKEN_BYTES[args.kv]
     kv_launch = kv_step // spec.num_layers
     gbps = kv_step / (ms * 1e-3) / 1e9
     dec_gbps = kv_launch / (dec_ms_mean * 1e-3) / 1e9
+    sfx = "_i8" if i8 else ""
     res = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16" if not i8 else "int8 K/V, bf16 q/out, fp32 accumulation",
+        "data": "synthetic",
         "config": {"workload": spec.name, "num_seqs": spec.num_seqs, "context_len": int(spec.context_lens.max()),
                    "mean_context_len": float(spec.context_lens.mean()), "layers": spec.num_layers,
                    "q_heads": 32, "kv_heads": 8, "head_dim": 64, "page_size": 16, "num_pages": spec.num_pages,
-                   "step": ("per layer: pa_append_decode_gqa (append + RoPE + decode, one launch)"
-                            if args.path == "fused" else "per layer: pa_append_kv_rope then pa_decode_gqa"),
+                   "kv_format": args.kv, "kv_bytes_per_token_layer": KV_TOKEN_BYTES[args.kv],
+                   "step": ("per layer: pa_append_decode_gqa%s (append + RoPE + decode, one launch)" % sfx
+                            if args.path == "fused" else
+                            "per layer: pa_append_kv_rope%s then pa_decode_gqa%s" % (sfx, sfx)),
                    "decode_partition_tokens": binding.decode_partition_tokens()},
         "tokens_per_s": round(spec.num_seqs / (ms * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "kv_bytes_per_step": kv_step,
         ("separate_calls_ms_per_step" if args.path == "fused" else "fused_ms_per_step"): round(other_ms, 5),
-        "roofline": {"bound": "hbm", "kernel": "k_decode_paged<8,true> (pa_append_decode_gqa)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("k_decode_paged_i8<8,true> (pa_append_decode_gqa_i8)" if i8 else
+                                "k_decode_paged<8,true> (pa_append_decode_gqa)"),
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic() if args.config == "batch64" else None,
+                     "traffic": measured_traffic(args.kv) if args.config == "batch64" else None,
                      "bytes_per_launch": kv_launch, "mean_launch_us": round(dec_ms_mean * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(spec, k_pool, v_pool, rows, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(spec, k_pool, v_pool, rows, args.cpu_seconds, args.kv)
     print(json.dumps(res), flush=True)
 
 

@@ -177,6 +177,67 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
                            int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                            float scale, int32_t out_dtype, uint32_t *device_flags, hipStream_t stream);
 
+/* ------------------------------------------------------ INT8 K/V pages --
+ * An INT8 KV cache (TinyLoop, "Lifecycle and Memory Model", section
+ * "Per-request / handle-owned memory": the runtime KV cache holds K/V as FP16
+ * or INT8).  The pages give no quantisation rule; this library's format is one
+ * symmetric fp32 scale per (token, KV head) row of 64 values:
+ *   scale = max|x| / 127,  code = round-half-even(x / scale) in [-127, 127],
+ * both in IEEE binary32, scale 0 and codes 0 for an all-zero row (rows must be
+ * finite).  The value a code stands for is code * scale.  K rows are quantised
+ * after RoPE from the bf16-rounded rotated row (the row pa_append_kv_rope would
+ * store), V rows from their bf16 input.
+ *
+ *   kv_pool_i8 : [num_pages][8 kv heads] tiles of PA_I8_TILE_BYTES = 2176 bytes,
+ *                K and V together (there is no separate V pool):
+ *                  bytes [0, 1024)    K codes (int8), [1024, 2048) V codes,
+ *                  2048 + 8t          K scale (fp32) of slot t, 2052 + 8t its V scale,
+ *                code of element d of slot t at byte ((t%8)*8 + d/8)*16 + (t/8)*8 + d%8
+ *                of its 1 KiB block.  A token costs 8 x 136 = 1088 bytes per layer,
+ *                against 2048 in bf16.
+ * Block tables, lengths, q, k_new, v_new, the RoPE table, out, workspace and
+ * device_flags mean exactly what they mean for the bf16 calls above; the decode
+ * workspace is sized by pa_decode_workspace_bytes.                           */
+#define PA_I8_TILE_BYTES 2176
+
+/* Bytes of an INT8 pool of num_pages pages (0 for num_pages < 1). */
+size_t pa_i8_pool_bytes(int32_t num_pages);
+
+/* Quantise whole pages of a bf16 pool pair into the INT8 pool: for each listed
+ * page id p (page_ids: device int32[count]; NULL means pages 0..count-1), all
+ * 16 slots of all 8 heads of k_pool/v_pool page p go to INT8 page p.  Slots
+ * that hold no token are quantised too (their codes are never read by decode).
+ * Device errors: an id outside [0, num_pages) -> PAGE_ID, that page skipped.  */
+pa_status pa_quantize_pages_i8(void *kv_pool_i8, const void *k_pool, const void *v_pool, const int32_t *page_ids,
+                               int32_t count, int32_t num_pages, uint32_t *device_flags, hipStream_t stream);
+
+/* pa_append_kv_rope into an INT8 pool: the rotated K row (bf16-rounded) and the
+ * V row of every KV head are quantised into slot pos%16 of page
+ * block_tables[s][pos/16], pos = context_lens[s]-1; q rotated in place as by
+ * pa_append_kv_rope (skipped when q is NULL).  Device errors as there.        */
+pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                               int32_t num_pages, int32_t page_size, int32_t max_pos,
+                               uint32_t *device_flags, hipStream_t stream);
+
+/* pa_decode_gqa over an INT8 pool: K_t, V_t are the values the codes stand for
+ * (code * scale); everything else as pa_decode_gqa, out may alias q.        */
+pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, const int32_t *block_tables,
+                           const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
+                           int32_t page_size, float scale, int32_t out_dtype, void *workspace,
+                           size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream);
+
+/* pa_append_kv_rope_i8 followed by pa_decode_gqa_i8 in one launch, bitwise equal
+ * to the two calls (same rotation, rounding and quantisation); q as in
+ * pa_append_decode_gqa.                                                       */
+pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                  int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
+                                  int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                  uint32_t *device_flags, hipStream_t stream);
+
 /* ------------------------------------------------ host KV page manager --
  * Host-side bookkeeping that produces the block tables and lengths the calls
  * above consume (samir-vllm, section "Gestion de la KV cache et strategies de

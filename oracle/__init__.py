@@ -164,6 +164,8 @@ def _i8_setup(lib):
     lib.oracle_append_kv_rope_i8.argtypes = [P, P, P, P, P, P, i32, i32, i32, dbl]
     lib.oracle_decode_gqa_i8.restype = ctypes.c_int
     lib.oracle_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, dbl]
+    lib.oracle_quantize_pages_i8.restype = None
+    lib.oracle_quantize_pages_i8.argtypes = [P, P, P, i32]
 
 
 def quantize_row_i8(x_bits):
@@ -176,6 +178,22 @@ def quantize_row_i8(x_bits):
     sc = np.zeros(1, dtype=np.float32)
     lib.oracle_quantize_row_i8(_ptr(x), _ptr(codes), _ptr(sc))
     return codes, np.float32(sc[0])
+
+
+def quantize_pages_i8(k_pool, v_pool, pool=None):
+    """bf16 pools [P][8][16][64] -> INT8 pool uint8 [P][8][2176] (rows with a
+    non-finite value keep the bytes ``pool`` had; a fresh pool starts zeroed)."""
+    lib = _load()
+    _i8_setup(lib)
+    kp, vp = _u16(k_pool), _u16(v_pool)
+    assert kp.shape == vp.shape and kp.shape[1:] == (8, 16, 64)
+    P = int(kp.shape[0])
+    if pool is None:
+        pool = np.zeros((P, 8, 2176), dtype=np.uint8)
+    if not (pool.flags.c_contiguous and pool.dtype == np.uint8 and pool.shape == (P, 8, 2176)):
+        raise TypeError("pool must be C-contiguous uint8 [P][8][2176]")
+    lib.oracle_quantize_pages_i8(_ptr(pool), _ptr(kp), _ptr(vp), P)
+    return pool
 
 
 def append_kv_rope_i8(q, k_new, v_new, pool, block_tables, context_lens, num_pages: int, theta: float) -> int:

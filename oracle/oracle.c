@@ -370,6 +370,29 @@ int oracle_append_kv_rope_i8(uint16_t *q, const uint16_t *k_new, const uint16_t 
     return rc;
 }
 
+/* Quantise whole pages of a bf16 pool pair (K, V: [P][8][16][64]) into an
+ * INT8 pool of the same page count, every (page, head, slot) row through
+ * oracle_quantize_row_i8.  A row holding a non-finite value is not a value
+ * the format can represent: its bytes are left as they are.                */
+static int row_finite(const uint16_t *row)
+{
+    for (int d = 0; d < O_D; ++d)
+        if (!isfinite(oracle_bf16_to_f64(row[d]))) return 0;
+    return 1;
+}
+
+void oracle_quantize_pages_i8(uint8_t *pool, const uint16_t *k_pool, const uint16_t *v_pool, int32_t num_pages)
+{
+    for (int64_t p = 0; p < num_pages; ++p)
+        for (int j = 0; j < O_HKV; ++j)
+            for (int t = 0; t < O_PS; ++t) {
+                size_t src = pool_index(p, j, t);
+                uint8_t *tile = pool + i8_tile(p, j);
+                if (row_finite(k_pool + src)) store_row_i8(tile, 0, 0, t, k_pool + src);
+                if (row_finite(v_pool + src)) store_row_i8(tile, 1024, 4, t, v_pool + src);
+            }
+}
+
 /* Value of element d of token t of a block (0: K, 1024: V) of a tile.      */
 static double i8_value(const uint8_t *tile, int block_off, int scale_off, int t, int d)
 {

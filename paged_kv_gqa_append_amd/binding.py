@@ -30,7 +30,9 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_prefill_chunk", "pa_admission_credit_pages", "pa_kvm_create", "pa_kvm_destroy", "pa_kvm_submit",
            "pa_kvm_schedule", "pa_kvm_set_length", "pa_kvm_release", "pa_kvm_block_tables", "pa_kvm_lengths",
            "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
-           "pa_kvm_queued")
+           "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
+           "pa_append_decode_gqa_i8")
+PA_I8_TILE_BYTES = 2176
 
 
 class PaError(RuntimeError):
@@ -69,6 +71,17 @@ def lib():
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
                                    P, P]
+    L.pa_i8_pool_bytes.restype = u64
+    L.pa_i8_pool_bytes.argtypes = [i32]
+    L.pa_quantize_pages_i8.restype = ctypes.c_int
+    L.pa_quantize_pages_i8.argtypes = [P, P, P, P, i32, i32, P, P]
+    L.pa_append_kv_rope_i8.restype = ctypes.c_int
+    L.pa_append_kv_rope_i8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P]
+    L.pa_decode_gqa_i8.restype = ctypes.c_int
+    L.pa_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P]
+    L.pa_append_decode_gqa_i8.restype = ctypes.c_int
+    L.pa_append_decode_gqa_i8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
+                                          u64, P, P]
     i64 = ctypes.c_int64
     L.pa_admission_credit_pages.restype = i64
     L.pa_admission_credit_pages.argtypes = [i32, i32, i32]
@@ -281,6 +294,126 @@ def prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_chunk: torch.Tensor, v_c
                                 int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
                                 float(scale), odt, _ptr(device_flags), _stream(stream))
     _check(rc, "pa_prefill_chunk")
+    return out
+
+
+# ------------------------------------------------------------ INT8 pages --
+
+def i8_pool(num_pages: int, device="cuda") -> torch.Tensor:
+    """An (uninitialised) INT8 pool: uint8 [num_pages][8][2176] (pa_i8_pool_bytes bytes)."""
+    n = int(lib().pa_i8_pool_bytes(int(num_pages)))
+    if n == 0:
+        raise ValueError("num_pages must be positive")
+    return torch.empty((int(num_pages), _w.NUM_KV_HEADS, PA_I8_TILE_BYTES), dtype=torch.uint8, device=device)
+
+
+def _i8_pool_checks(pool):
+    _expect(pool, "kv_pool_i8", torch.uint8)
+    if pool.dim() != 3 or tuple(pool.shape[1:]) != (_w.NUM_KV_HEADS, PA_I8_TILE_BYTES):
+        raise ValueError(f"INT8 pool must be [num_pages][8][2176] uint8, got {tuple(pool.shape)}")
+    return int(pool.shape[0])
+
+
+def _tables(block_tables, context_lens, dev):
+    _expect(context_lens, "context_lens", torch.int32, device=dev)
+    B = int(context_lens.shape[0])
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    return B
+
+
+def _out_dtype(out):
+    if out.dtype == torch.bfloat16:
+        return PA_OUT_BF16
+    if out.dtype == torch.float32:
+        return PA_OUT_FP32
+    raise TypeError("out must be bfloat16 or float32")
+
+
+def quantize_pages_i8(kv_pool_i8: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      page_ids: Optional[torch.Tensor] = None, device_flags: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """pa_quantize_pages_i8: quantise the listed bf16 pages (all when page_ids is None) into the INT8 pool."""
+    num_pages = _i8_pool_checks(kv_pool_i8)
+    if _pool_checks(k_pool, v_pool) != num_pages:
+        raise ValueError("bf16 pools and the INT8 pool must have the same number of pages")
+    dev = kv_pool_i8.device
+    if page_ids is not None:
+        _expect(page_ids, "page_ids", torch.int32, device=dev)
+        count = int(page_ids.numel())
+    else:
+        count = num_pages
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    _check(lib().pa_quantize_pages_i8(_ptr(kv_pool_i8), _ptr(k_pool), _ptr(v_pool), _ptr(page_ids), count, num_pages,
+                                      _ptr(device_flags), _stream(stream)), "pa_quantize_pages_i8")
+
+
+def append_kv_rope_i8(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.Tensor, kv_pool_i8: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor, rope_cos_sin: torch.Tensor,
+                      device_flags: Optional[torch.Tensor] = None, page_size: int = 16, stream=None) -> None:
+    """pa_append_kv_rope_i8: quantise RoPE(k_new) and v_new into slot pos = L-1; rotate q in place (if given)."""
+    num_pages = _i8_pool_checks(kv_pool_i8)
+    dev = kv_pool_i8.device
+    B = _tables(block_tables, context_lens, dev)
+    _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
+    if q is not None:
+        _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_append_kv_rope_i8(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_pool_i8), _ptr(block_tables),
+                                    _ptr(context_lens), _ptr(rope_cos_sin), B, int(block_tables.shape[1]), num_pages,
+                                    int(page_size), int(rope_cos_sin.shape[0]), _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_append_kv_rope_i8")
+
+
+def decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, kv_pool_i8: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float = 0.125, workspace: Optional[torch.Tensor] = None,
+                  device_flags: Optional[torch.Tensor] = None, page_size: int = 16, stream=None) -> torch.Tensor:
+    """pa_decode_gqa_i8 into ``out`` ([B][32][64] bf16 or fp32; may be ``q`` itself)."""
+    num_pages = _i8_pool_checks(kv_pool_i8)
+    dev = kv_pool_i8.device
+    B = _tables(block_tables, context_lens, dev)
+    _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    odt = _out_dtype(out)
+    _expect(out, "out", out.dtype, (B, 32, 64), dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(kv_pool_i8), _ptr(block_tables), _ptr(context_lens), B,
+                                int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
+                                _ptr(workspace), ws_bytes, _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_decode_gqa_i8")
+    return out
+
+
+def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                         kv_pool_i8: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                         rope_cos_sin: torch.Tensor, scale: float = 0.125, workspace: Optional[torch.Tensor] = None,
+                         device_flags: Optional[torch.Tensor] = None, page_size: int = 16,
+                         stream=None) -> torch.Tensor:
+    """pa_append_decode_gqa_i8: quantised append at pos = L-1, q rotated in place, then decode into ``out``."""
+    num_pages = _i8_pool_checks(kv_pool_i8)
+    dev = kv_pool_i8.device
+    B = _tables(block_tables, context_lens, dev)
+    _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    odt = _out_dtype(out)
+    _expect(out, "out", out.dtype, (B, 32, 64), dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_append_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_pool_i8),
+                                       _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
+                                       int(block_tables.shape[1]), num_pages, int(page_size),
+                                       int(rope_cos_sin.shape[0]), float(scale), odt, _ptr(workspace), ws_bytes,
+                                       _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_append_decode_gqa_i8")
     return out
 
 

@@ -20,12 +20,14 @@ int64_t decode_num_parts(int32_t max_blocks) {
 }
 
 
-// Shared argument checks and launch of the plain and the append-fused decode.
+// Shared argument checks and launch of the plain and the append-fused decode,
+// over bf16 pools (k_pool, v_pool) or an INT8 tile pool (k_pool; v_pool unused).
 pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
                         const int32_t *block_tables, const int32_t *context_lens, const float *rope,
                         int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                         float scale, int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                        uint32_t *device_flags, hipStream_t stream, bool fused) {
+                        uint32_t *device_flags, hipStream_t stream, bool fused, bool i8 = false) {
+    if (i8) v_pool = k_pool;
     if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
     if (fused && max_pos < 1) return PA_ERR_INVALID_ARG;
     if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
@@ -65,7 +67,7 @@ pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new
     d.ws_ml = need ? ws : nullptr;
     d.ws_acc = need ? ws + rows * 2 : nullptr;
     d.flags = device_flags;
-    return pa::launch_decode(d, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+    return (i8 ? pa::launch_decode_i8(d, stream) : pa::launch_decode(d, stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
@@ -84,7 +86,7 @@ const char *pa_status_string(int status) {
     }
 }
 
-int32_t pa_abi_version(void) { return 2; }
+int32_t pa_abi_version(void) { return 3; }
 
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
@@ -170,6 +172,59 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
     pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin, num_seqs, chunk_len,
                         max_blocks, num_pages, max_pos, scale, out_dtype == PA_OUT_FP32, device_flags};
     return pa::launch_prefill_attention(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+size_t pa_i8_pool_bytes(int32_t num_pages) {
+    return num_pages < 1 ? 0 : static_cast<size_t>(num_pages) * PA_NUM_KV_HEADS * PA_I8_TILE_BYTES;
+}
+
+pa_status pa_quantize_pages_i8(void *kv_pool_i8, const void *k_pool, const void *v_pool, const int32_t *page_ids,
+                               int32_t count, int32_t num_pages, uint32_t *device_flags, hipStream_t stream) {
+    if (count < 0 || num_pages < 1) return PA_ERR_INVALID_ARG;
+    if (!page_ids && count > num_pages) return PA_ERR_INVALID_ARG;
+    if (count == 0) return PA_OK;
+    if (!kv_pool_i8 || !k_pool || !v_pool) return PA_ERR_INVALID_ARG;
+    if (!aligned16(kv_pool_i8) || !aligned16(k_pool) || !aligned16(v_pool) || (page_ids && !aligned16(page_ids)))
+        return PA_ERR_INVALID_ARG;
+    return pa::launch_quantize_pages_i8(kv_pool_i8, k_pool, v_pool, page_ids, count, num_pages, device_flags,
+                                        stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                               int32_t num_pages, int32_t page_size, int32_t max_pos,
+                               uint32_t *device_flags, hipStream_t stream) {
+    if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1) return PA_ERR_INVALID_ARG;
+    if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_new || !v_new || !kv_pool_i8 || !block_tables || !context_lens || !rope_cos_sin) return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_pool_i8) || !aligned16(block_tables) ||
+        !aligned16(context_lens) || !aligned16(rope_cos_sin) || (q && !aligned16(q)))
+        return PA_ERR_INVALID_ARG;
+    pa::AppendLaunch a{q, k_new, v_new, kv_pool_i8, nullptr, block_tables, context_lens, rope_cos_sin,
+                       num_seqs, 1, 0, max_blocks, num_pages, max_pos, device_flags};
+    return pa::launch_append_rope_i8(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, const int32_t *block_tables,
+                           const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
+                           int32_t page_size, float scale, int32_t out_dtype, void *workspace,
+                           size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream) {
+    return decode_common(out, const_cast<void *>(q), nullptr, nullptr, const_cast<void *>(kv_pool_i8), nullptr,
+                         block_tables, context_lens, nullptr, num_seqs, max_blocks, num_pages, page_size, 0, scale,
+                         out_dtype, workspace, workspace_bytes, device_flags, stream, false, true);
+}
+
+pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                  int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
+                                  int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                  uint32_t *device_flags, hipStream_t stream) {
+    return decode_common(out, q, k_new, v_new, kv_pool_i8, nullptr, block_tables, context_lens, rope_cos_sin,
+                         num_seqs, max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace,
+                         workspace_bytes, device_flags, stream, true, true);
 }
 
 }  // extern "C"

@@ -112,8 +112,11 @@ __device__ __forceinline__ float page_score(const u32x4 (&qv)[kGroup], u32x4 ka,
 
 // Online-softmax step for one page: lazily raise the wave's running max of the
 // lane's head (rescaling the accumulators of all 4 heads when any lane needs
-// it), then return the lane's weight 2^(x - m).
-__device__ __forceinline__ float softmax_step(float x, float &m_run, float &l_run, float (&acc)[kGroup][8]) {
+// it), then return the lane's weight 2^(x - m).  With kSecondSum a second
+// per-lane running sum of the lane's head (l2_run) is rescaled with l_run.
+template <bool kSecondSum>
+__device__ __forceinline__ float softmax_step_t(float x, float &m_run, float &l_run, float &l2_run,
+                                                float (&acc)[kGroup][8]) {
     const float xm = fmaxf(x, dpp_f32<kXor1>(x));  // this page's max for the head (both tokens)
     if (__builtin_amdgcn_ballot_w64(xm > m_run + kRescaleLog2)) {
         const float wm = max_groups(xm);
@@ -121,6 +124,7 @@ __device__ __forceinline__ float softmax_step(float x, float &m_run, float &l_ru
         const float f = fast_exp2(m_run - mn);
         m_run = mn;
         l_run *= f;
+        if (kSecondSum) l2_run *= f;
         // factors per accumulator slot, routed like the weights in accumulate()
         const float fm = dpp_f32<kHalfMirror>(f);
         const float F0 = dpp_f32<kBcast0>(f), F2 = dpp_f32<kBcast2>(f);
@@ -136,6 +140,10 @@ __device__ __forceinline__ float softmax_step(float x, float &m_run, float &l_ru
     const float pw = fast_exp2(x - m_run);
     l_run += pw;
     return pw;
+}
+__device__ __forceinline__ float softmax_step(float x, float &m_run, float &l_run, float (&acc)[kGroup][8]) {
+    float unused = 0.0f;
+    return softmax_step_t<false>(x, m_run, l_run, unused, acc);
 }
 
 __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {

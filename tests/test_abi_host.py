@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == 2
+    assert pa.lib().pa_abi_version() == 3
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -115,6 +115,52 @@ def test_append_and_prefill_validation(pa):
     assert pre(ps=32) == pa.PA_ERR_UNSUPPORTED
     assert pre(C=-1) == pa.PA_ERR_INVALID_ARG
     assert pre(mp=0) == pa.PA_ERR_INVALID_ARG
+
+
+def test_i8_validation(pa):
+    lib = pa.lib()
+    v = ctypes.c_void_p
+    F = v(FAKE)
+    assert lib.pa_i8_pool_bytes(10) == 10 * 8 * 2176
+    assert lib.pa_i8_pool_bytes(0) == 0
+
+    def quant(pool=F, kp=F, vp=F, ids=F, n=4, P=16):
+        return lib.pa_quantize_pages_i8(pool, kp, vp, ids, n, P, None, None)
+
+    assert quant(n=-1) == pa.PA_ERR_INVALID_ARG
+    assert quant(P=0) == pa.PA_ERR_INVALID_ARG
+    assert quant(ids=None, n=17) == pa.PA_ERR_INVALID_ARG   # more pages than the pool holds
+    assert quant(pool=None) == pa.PA_ERR_INVALID_ARG
+    assert quant(kp=v(FAKE + 8)) == pa.PA_ERR_INVALID_ARG
+    assert quant(n=0, pool=None) == pa.PA_OK
+
+    def app(q=F, pool=F, B=2, ps=16, mp=64, kn=F):
+        return lib.pa_append_kv_rope_i8(q, kn, F, pool, F, F, F, B, 4, 16, ps, mp, None, None)
+
+    assert app(ps=8) == pa.PA_ERR_UNSUPPORTED
+    assert app(mp=0) == pa.PA_ERR_INVALID_ARG
+    assert app(pool=None) == pa.PA_ERR_INVALID_ARG
+    assert app(kn=v(FAKE + 2)) == pa.PA_ERR_INVALID_ARG
+    assert app(B=0) == pa.PA_OK
+
+    def dec(out=F, pool=F, B=4, mb=8, ps=16, odt=0, scale=0.125, ws=None, wsb=0):
+        return lib.pa_decode_gqa_i8(out, F, pool, F, F, B, mb, 64, ps, scale, odt, ws, wsb, None, None)
+
+    assert dec(ps=32) == pa.PA_ERR_UNSUPPORTED
+    assert dec(odt=3) == pa.PA_ERR_UNSUPPORTED
+    assert dec(pool=None) == pa.PA_ERR_INVALID_ARG
+    assert dec(out=v(FAKE + 4)) == pa.PA_ERR_INVALID_ARG
+    assert dec(scale=float("inf")) == pa.PA_ERR_INVALID_ARG
+    assert dec(B=0, out=None) == pa.PA_OK
+    need = lib.pa_decode_workspace_bytes(4, 1000)
+    assert need > 0 and dec(mb=1000) == pa.PA_ERR_WORKSPACE
+
+    def fused(rope=F, mp=64):
+        return lib.pa_append_decode_gqa_i8(F, F, F, F, F, F, F, rope, 4, 8, 64, 16, mp, 0.125, 0, None, 0, None,
+                                           None)
+
+    assert fused(rope=None) == pa.PA_ERR_INVALID_ARG
+    assert fused(mp=0) == pa.PA_ERR_INVALID_ARG
 
 
 def test_rope_table_fill(pa):

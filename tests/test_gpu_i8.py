@@ -1,0 +1,363 @@
+"""GPU parity of the INT8 K/V page calls against the fp64 oracle.
+
+* pa_quantize_pages_i8: every byte of the INT8 pool equals the oracle's
+  quantisation of the same bf16 pages (codes and scales are integer/binary32
+  decisions taken in binary32 on both sides), unlisted pages untouched.
+* pa_append_kv_rope_i8: the only bytes that change are the appended slots' K/V
+  codes and scales; V rows are bit-exact; K rows are bit-exact wherever the
+  oracle's fp64 rotation is farther from a bf16 rounding midpoint than the
+  fp32 evaluation error (the rotated bf16 row is then the same on both sides),
+  and elsewhere within half a quantisation step of the oracle's rotated row;
+  q is rotated within 1 bf16 step + the fp32 bound, as for bf16 pools.
+* pa_decode_gqa_i8 / pa_append_decode_gqa_i8: outputs within the stated
+  tolerance of the oracle's decode over the same INT8 pool (bf16 out
+  1e-2 + 1e-2|ref|, fp32 out 2e-3 + 2e-3|ref|); the fused call is bitwise the
+  two separate calls; contexts past one partition; unused slots hold NaN scales
+  and random codes.
+* Full size: the batch-64 x 2048 workload's pool quantised on the device is
+  bit-identical, on sampled sequences' pages, to the oracle's quantisation of
+  the same bf16 pages (copied to the host before any of our kernels ran), and
+  the fused decode matches the oracle on those sequences.
+The INT8 pools the oracle reads are built on the host by the oracle itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu_helpers import (TOL_BF16, TOL_FP32, assert_close, assert_rope_close, dev, rope, to_dev_bf16, to_dev_i32,
+                          to_host_bits, to_host_f64)
+from paged_kv_gqa_append_amd import binding
+from paged_kv_gqa_append_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TILE = 2176
+NAN32 = np.array([0x7FC00000], np.uint32).view(np.uint8)
+
+
+def code_pos(t, d):
+    """Byte of element d of slot t inside a 1024-byte code block (include/pa.h)."""
+    return ((t & 7) * 8 + (d >> 3)) * 16 + (t >> 3) * 8 + (d & 7)
+
+
+SLOT_BYTES = np.array([[code_pos(t, d) for d in range(64)] for t in range(16)])  # [16][64]
+
+
+def poison_i8(pool, block_tables, lens, seed):
+    """Every slot no sequence uses (any layer): NaN scales and random codes."""
+    rng = np.random.default_rng(seed)
+    used = np.zeros((pool.shape[0], 16), bool)
+    for layer in range(block_tables.shape[0]):
+        p, t = W.used_slots(block_tables[layer], lens)
+        used[p, t] = True
+    for p, t in np.argwhere(~used):
+        page = pool[p]  # [8][2176] view
+        for base in (0, 1024):
+            page[:, base + SLOT_BYTES[t]] = rng.integers(0, 256, (8, 64), dtype=np.uint8)
+        page[:, 2048 + 8 * t:2048 + 8 * t + 4] = NAN32
+        page[:, 2052 + 8 * t:2052 + 8 * t + 4] = NAN32
+
+
+def host_i8(case, poison=True):
+    pool = oracle.quantize_pages_i8(case.k_pool, case.v_pool)
+    if poison:
+        poison_i8(pool, case.block_tables, case.context_lens, case.seed + 1000)
+    return pool
+
+
+def to_dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def oracle_decode_i8(case, pool, q_bits=None):
+    out, rc = oracle.decode_gqa_i8(case.q[0] if q_bits is None else q_bits, pool, case.block_tables[0],
+                                   case.context_lens, case.num_pages, case.scale)
+    assert rc == oracle.OK
+    return out
+
+
+EDGE = [1, 2, 15, 16, 17, 31, 33, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047, 2048]
+CASES = {
+    "tiny": lambda: W.tiny_decode(),
+    "batch8": lambda: W.batch8_decode(),
+    "edges": lambda: W.make_decode_case("edges", 71, EDGE, dist="normal", max_blocks=130),
+    "ragged_outliers": lambda: W.make_decode_case("ragged", 72, W.ragged_lengths(72, 24), dist="normal",
+                                                  layout="fragmented", outlier_frac=0.01, max_blocks=128),
+    "long": lambda: W.make_decode_case("long", 73, [1, 17, 2048, 2049, 3000, 4113], dist="normal", max_blocks=260),
+}
+
+
+def test_quantize_pages_bitexact():
+    case = W.make_decode_case("quant", 74, [700, 1, 33, 2048], dist="normal", poison=False, outlier_frac=0.02)
+    kp, vp = case.k_pool.copy(), case.v_pool.copy()
+    kp[0, 2, 5, :] = 0                                                  # an all-zero row: scale 0, codes 0
+    vp[1, 0, 3, :] = W.f32_to_bf16_bits(np.full(64, 1e-30, np.float32))  # tiny values
+    P = case.num_pages
+    rng = np.random.default_rng(75)
+    start = rng.integers(0, 256, (P, 8, TILE), dtype=np.uint8)
+    ids = np.sort(rng.choice(P, size=P // 2, replace=False)).astype(np.int32)
+    full = oracle.quantize_pages_i8(kp, vp)
+    print(f"quantize pages P={P} listed={len(ids)}", flush=True)
+    # listed pages only
+    pool = to_dev_u8(start)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    binding.quantize_pages_i8(pool, to_dev_bf16(kp), to_dev_bf16(vp), to_dev_i32(ids), device_flags=flags)
+    torch.cuda.synchronize()
+    want = start.copy()
+    want[ids] = full[ids]
+    assert np.array_equal(pool.cpu().numpy(), want)
+    assert int(flags.item()) == 0
+    # all pages
+    pool = to_dev_u8(start)
+    binding.quantize_pages_i8(pool, to_dev_bf16(kp), to_dev_bf16(vp))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), full)
+    # an id outside the pool is skipped and flagged
+    bad = np.array([0, P, 3, -1], np.int32)
+    pool = to_dev_u8(start)
+    binding.quantize_pages_i8(pool, to_dev_bf16(kp), to_dev_bf16(vp), to_dev_i32(bad), device_flags=flags)
+    torch.cuda.synchronize()
+    want = start.copy()
+    want[[0, 3]] = full[[0, 3]]
+    assert np.array_equal(pool.cpu().numpy(), want)
+    assert int(flags.item()) & binding.PA_DEVERR_PAGE_ID
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_i8_parity(name, out_dtype):
+    case = CASES[name]()
+    print(f"i8 decode parity case={name} B={case.num_seqs} out={out_dtype}", flush=True)
+    pool = host_i8(case)
+    out = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(case.block_tables[0]),
+                          to_dev_i32(case.context_lens), case.scale,
+                          workspace=binding.decode_workspace(case.num_seqs, case.max_blocks, dev()),
+                          device_flags=flags)
+    torch.cuda.synchronize()
+    got = to_host_f64(out)
+    assert_close(got, oracle_decode_i8(case, pool), TOL_BF16 if out_dtype == torch.bfloat16 else TOL_FP32, name)
+    assert int(flags.item()) == 0
+
+
+def rotation_is_unambiguous(x_bits, pos, theta):
+    """True when every element of the oracle's fp64 rotation of this row lies
+    farther from a bf16 rounding midpoint than the device's fp32 evaluation
+    error: the (cos, sin) table entries, the product and the fused
+    multiply-add each round once, relative 2^-24, so the device's value of an
+    element of pair (x_i, x_{i+32}) is within 3 * 2^-24 (|x_i| + |x_{i+32}|)
+    < 2^-22 (|x_i| + |x_{i+32}|) of the exact rotation.  Then both sides store
+    the same bf16 row."""
+    y = oracle.rope_head(x_bits, pos, theta)
+    x = np.abs(W.bf16_bits_to_f32(x_bits).astype(np.float64))
+    pair = x[:32] + x[32:]
+    bound = 2.0 ** -22 * np.concatenate([pair, pair])
+    a = np.abs(y)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    for spacing in (np.ldexp(1.0, np.maximum(e - 1, -126) - 7), np.ldexp(1.0, np.maximum(e - 2, -126) - 7)):
+        frac = a / spacing - np.floor(a / spacing)
+        if np.any(np.abs(frac - 0.5) * spacing <= bound):
+            return False
+    return True
+
+
+def read_row(pool, page, head, t, which):
+    base = 0 if which == "k" else 1024
+    codes = pool[page, head, base + SLOT_BYTES[t]].view(np.int8)
+    sc = pool[page, head, 2048 + 8 * t + (0 if which == "k" else 4):][:4].view(np.float32)[0]
+    return codes, sc
+
+
+def test_append_i8_against_oracle():
+    case = W.batch8_decode()
+    pool = host_i8(case)
+    table = rope()
+    q = to_dev_bf16(case.q[0])
+    dpool = to_dev_u8(pool)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    binding.append_kv_rope_i8(q, to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0]), dpool,
+                              to_dev_i32(case.block_tables[0]), to_dev_i32(case.context_lens), table,
+                              device_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    got = dpool.cpu().numpy()
+    ref = pool.copy()
+    oq = case.q[0].copy()
+    assert oracle.append_kv_rope_i8(oq, case.k_new[0], case.v_new[0], ref, case.block_tables[0], case.context_lens,
+                                    case.num_pages, case.theta) == oracle.OK
+    # only the appended slots' K codes and K scales may differ from the oracle
+    allowed = np.zeros(got.shape, bool)
+    n_exact = n_bound = 0
+    for s, L in enumerate(case.context_lens):
+        pos = int(L) - 1
+        pg, t = case.block_tables[0][s, pos // 16], pos % 16
+        for j in range(8):
+            kx = case.k_new[0][s, j]
+            if rotation_is_unambiguous(kx, pos, case.theta):
+                n_exact += 1
+                continue
+            n_bound += 1
+            allowed[pg, j, SLOT_BYTES[t]] = True
+            allowed[pg, j, 2048 + 8 * t:2052 + 8 * t] = True
+            gc, gs = read_row(got, pg, j, t, "k")
+            rc_, rs = read_row(ref, pg, j, t, "k")
+            y = oracle.rope_head(kx, pos, case.theta)
+            xmax = float(np.abs(W.bf16_bits_to_f32(kx)).max())
+            assert abs(float(gs) - float(rs)) <= float(rs) * 2.0 ** -7
+            err = np.abs(gc.astype(np.float64) * float(gs) - y)
+            assert np.all(err <= float(gs) * (0.5 + 2.0 ** -16) + 2.0 ** -7 * np.abs(y) + 2.0 ** -21 * xmax)
+    diff = got != ref
+    assert not (diff & ~allowed).any(), f"{int((diff & ~allowed).sum())} bytes differ outside the allowed K rows"
+    print(f"appended K rows: {n_exact} bit-exact by construction, {n_bound} checked by bound", flush=True)
+    xmax = float(np.abs(W.bf16_bits_to_f32(case.q[0])).max())
+    assert_rope_close(to_host_bits(q), oq, xmax, "rotated q")
+
+
+@pytest.mark.parametrize("name", ["tiny", "edges", "long"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_fused_i8_equals_separate(name, out_dtype):
+    case = CASES[name]()
+    if name == "tiny":
+        case.context_lens[:] = 64
+    print(f"i8 fused vs separate case={name} out={out_dtype}", flush=True)
+    pool = host_i8(case)
+    table = rope(4200)
+    bt, lens = to_dev_i32(case.block_tables[0]), to_dev_i32(case.context_lens)
+    kn, vn = to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0])
+    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+    # separate
+    q1, p1 = to_dev_bf16(case.q[0]), to_dev_u8(pool)
+    o1 = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    binding.append_kv_rope_i8(q1, kn, vn, p1, bt, lens, table)
+    binding.decode_gqa_i8(o1, q1, p1, bt, lens, case.scale, workspace=ws)
+    # fused
+    q2, p2 = to_dev_bf16(case.q[0]), to_dev_u8(pool)
+    o2 = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    binding.append_decode_gqa_i8(o2, q2, kn, vn, p2, bt, lens, table, case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                       o2.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
+    assert torch.equal(q1.view(torch.int16), q2.view(torch.int16))
+    assert torch.equal(p1, p2)
+    # and against the oracle's append + decode
+    ref_pool, oq = pool.copy(), case.q[0].copy()
+    assert oracle.append_kv_rope_i8(oq, case.k_new[0], case.v_new[0], ref_pool, case.block_tables[0],
+                                    case.context_lens, case.num_pages, case.theta) == oracle.OK
+    ref, rc = oracle.decode_gqa_i8(oq, ref_pool, case.block_tables[0], case.context_lens, case.num_pages, case.scale)
+    assert rc == oracle.OK
+    assert_close(to_host_f64(o2), ref, TOL_BF16 if out_dtype == torch.bfloat16 else TOL_FP32, name)
+    # out may alias q
+    q3, p3 = to_dev_bf16(case.q[0]), to_dev_u8(pool)
+    binding.append_decode_gqa_i8(q3, q3, kn, vn, p3, bt, lens, table, case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    if out_dtype == torch.bfloat16:
+        assert torch.equal(q3.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(p3, p1)
+
+
+def test_single_token_returns_its_v():
+    """L = 1: the weight is exactly 1, so out = V scale x code up to the one
+    fp32 rounding of scale x (code + 128)."""
+    case = W.make_decode_case("one", 76, [1] * 5, dist="normal")
+    pool = host_i8(case)
+    out = torch.empty((5, 32, 64), dtype=torch.float32, device=dev())
+    binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(case.block_tables[0]),
+                          to_dev_i32(case.context_lens), case.scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for s in range(5):
+        pg = case.block_tables[0][s, 0]
+        for h in range(32):
+            codes, sc = read_row(pool, pg, h // 4, 0, "v")
+            want = codes.astype(np.float64) * float(sc)
+            assert np.all(np.abs(got[s, h] - want) <= 256 * float(sc) * 2.0 ** -23)
+
+
+def test_i8_device_errors():
+    case = W.make_decode_case("err", 77, [40, 40, 40], dist="normal", max_blocks=4)
+    pool = host_i8(case)
+    bt = case.block_tables[0].copy()
+    lens = case.context_lens.copy()
+    lens[0] = 0                 # bad length
+    bt[1, 1] = case.num_pages   # bad page id in the used range
+    out = torch.full((3, 32, 64), 7.0, dtype=torch.float32, device=dev())
+    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(bt), to_dev_i32(lens),
+                          case.scale, device_flags=flags)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[0] == 0) and np.all(got[1] == 0)
+    assert int(flags.item()) == binding.PA_DEVERR_CONTEXT_LEN | binding.PA_DEVERR_PAGE_ID
+    ok = case.context_lens[2:]
+    ref, rc = oracle.decode_gqa_i8(case.q[0][2:], pool, case.block_tables[0][2:], ok, case.num_pages, case.scale)
+    assert rc == oracle.OK
+    assert_close(got[2:].astype(np.float64), ref, TOL_FP32, "good sequence beside bad ones")
+    # append: the bad sequences are left untouched, the good one appended
+    dpool = to_dev_u8(pool)
+    flags.zero_()
+    bt_app = case.block_tables[0].copy()
+    bt_app[1, 39 // 16] = case.num_pages   # the page the appended token of sequence 1 would go to
+    binding.append_kv_rope_i8(None, to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0]), dpool,
+                              to_dev_i32(bt_app), to_dev_i32(lens), rope(), device_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == binding.PA_DEVERR_CONTEXT_LEN | binding.PA_DEVERR_PAGE_ID
+    got_pool = dpool.cpu().numpy()
+    ref_pool = pool.copy()
+    sel = [2]
+    assert oracle.append_kv_rope_i8(None, case.k_new[0][sel], case.v_new[0][sel], ref_pool,
+                                    case.block_tables[0][sel], case.context_lens[sel], case.num_pages,
+                                    case.theta) == oracle.OK
+    pos = int(case.context_lens[2]) - 1
+    pg, t = case.block_tables[0][2, pos // 16], pos % 16
+    diff = got_pool != ref_pool
+    allowed = np.zeros_like(diff)
+    allowed[pg, :, SLOT_BYTES[t]] = True
+    allowed[pg, :, 2048 + 8 * t:2052 + 8 * t] = True
+    assert not (diff & ~allowed).any()
+
+
+def test_batch64_i8_full_size_sampled():
+    """The benchmark's INT8 step on one layer of the batch-64 x 2048 workload."""
+    spec = W.batch64_spec()
+    layer, seqs = 9, np.array([0, 5, 31, 62])
+    print(f"i8 full-size layer={layer} sampled={list(seqs)}", flush=True)
+    k_pool = W.fill_pool_device(spec, dev(), "k")
+    v_pool = W.fill_pool_device(spec, dev(), "v")
+    bt = spec.block_tables[layer][seqs]
+    used = np.unique(bt[bt >= 0])
+    idx = torch.from_numpy(used).to(dev())
+    kp = to_host_bits(k_pool.index_select(0, idx)).copy()   # bf16 pages, before any of our kernels
+    vp = to_host_bits(v_pool.index_select(0, idx)).copy()
+    remap = np.full(spec.num_pages, -1, np.int64)
+    remap[used] = np.arange(len(used))
+    bt_small = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    pool = binding.i8_pool(spec.num_pages, dev())
+    binding.quantize_pages_i8(pool, k_pool, v_pool)
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    ref_pool = oracle.quantize_pages_i8(kp, vp)
+    assert np.array_equal(pool.index_select(0, idx).cpu().numpy(), ref_pool)
+    q, kn, vn = spec.host_rows(layer)
+    dq = to_dev_bf16(q)
+    out = torch.empty((spec.num_seqs, 32, 64), dtype=torch.bfloat16, device=dev())
+    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    binding.append_decode_gqa_i8(out, dq, to_dev_bf16(kn), to_dev_bf16(vn), pool,
+                                 to_dev_i32(spec.block_tables[layer]), to_dev_i32(spec.context_lens),
+                                 binding.rope_table(2048 + 64, spec.theta, dev()), spec.scale,
+                                 workspace=binding.decode_workspace(spec.num_seqs, spec.max_blocks, dev()),
+                                 device_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    lens = spec.context_lens[seqs].copy()
+    oq = q[seqs].copy()
+    assert oracle.append_kv_rope_i8(oq, kn[seqs].copy(), vn[seqs].copy(), ref_pool, bt_small, lens, len(used),
+                                    spec.theta) == oracle.OK
+    ref, rc = oracle.decode_gqa_i8(oq, ref_pool, bt_small, lens, len(used), spec.scale)
+    assert rc == oracle.OK
+    assert_close(to_host_f64(out)[seqs], ref, TOL_BF16, "batch64 i8")
+    xmax = float(np.abs(W.bf16_bits_to_f32(q)).max())
+    assert_rope_close(to_host_bits(dq)[seqs], oq, xmax, "rotated q")
+    del pool
+    torch.cuda.empty_cache()

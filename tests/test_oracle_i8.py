@@ -225,3 +225,29 @@ def test_decode_closed_forms():
     assert rc == oracle.OK
     for h in range(32):
         np.testing.assert_allclose(out[0, h], read_row(pool, 2, h // 4, 0, "v")[0], rtol=1e-14, atol=1e-15)
+
+
+def test_quantize_pages_places_every_row():
+    """The oracle's whole-page quantiser: every (page, head, slot) row of a bf16
+    pool pair lands where the header formula says, as the exact-rational
+    quantisation of that row; rows holding a NaN keep the bytes they had."""
+    rng = np.random.default_rng(31)
+    P = 3
+    kp = W.f32_to_bf16_bits((rng.standard_normal((P, 8, 16, 64)) * rng.uniform(0.1, 5)).astype(np.float32))
+    vp = W.f32_to_bf16_bits(rng.standard_normal((P, 8, 16, 64)).astype(np.float32))
+    vp[1, 3, 7, 5] = W.BF16_NAN
+    kp[2, 0, 15, :] = 0
+    start = rng.integers(0, 256, (P, 8, TILE), dtype=np.uint8)
+    pool = oracle.quantize_pages_i8(kp, vp, start.copy())
+    for p in range(P):
+        for j in range(8):
+            for t in range(16):
+                for which, src in (("k", kp), ("v", vp)):
+                    _, codes, sc = read_row(pool, p, j, t, which)
+                    if which == "v" and (p, j, t) == (1, 3, 7):
+                        _, codes0, sc0 = read_row(start, p, j, t, which)
+                        assert np.array_equal(codes, codes0) and sc.tobytes() == sc0.tobytes()
+                        continue
+                    want_codes, want_sc = exact_quantise(W.bf16_bits_to_f32(src[p, j, t]))
+                    assert np.array_equal(codes.astype(np.int64), want_codes), (p, j, t, which)
+                    assert float(sc) == want_sc
