@@ -222,3 +222,19 @@ def decode_gqa_i8(q, pool, block_tables, context_lens, num_pages: int, scale: fl
     rc = lib.oracle_decode_gqa_i8(_ptr(out), _ptr(qq), _ptr(pl), _ptr(bt), _ptr(cl), B, int(bt.shape[-1]),
                                   int(num_pages), float(scale))
     return out, int(rc)
+
+
+def argmax(logits) -> np.ndarray:
+    """Lowest index of the row maximum over non-NaN entries (0 for an all-NaN
+    row).  ``logits``: [rows][vocab] as uint16 bf16 patterns or float32."""
+    lib = _load()
+    lib.oracle_argmax.restype = ctypes.c_int
+    lib.oracle_argmax.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+    x = np.ascontiguousarray(logits)
+    if x.ndim != 2 or x.dtype not in (np.uint16, np.float32):
+        raise TypeError("logits must be 2-D uint16 (bf16 patterns) or float32")
+    out = np.zeros(x.shape[0], dtype=np.int32)
+    rc = lib.oracle_argmax(_ptr(out), _ptr(x), int(x.shape[0]), int(x.shape[1]), int(x.dtype == np.uint16))
+    if rc != OK:
+        raise ValueError(f"oracle_argmax: status {rc}")
+    return out

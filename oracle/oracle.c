@@ -463,6 +463,40 @@ int oracle_decode_gqa_i8(double *out, const uint16_t *q, const uint8_t *pool, co
     return rc;
 }
 
+/* ------------------------------------------------------------- argmax --
+ * Greedy next-token choice over a row of logits (samir-vllm article, section
+ * "Architecture et flux d'inference": the argmax runs on the GPU; tiny-vllm
+ * ch.2, section "Preallocating the 16 compute buffers": a CPU argmax over the
+ * logits row, scanning with a strict greater-than, so the first maximum wins).
+ * Reading where the pages are silent: NaN entries are never chosen; the
+ * result is the lowest index holding the maximum of the non-NaN entries
+ * (-0.0 and +0.0 are equal), and 0 for a row that holds only NaN.
+ * logits: [rows][vocab], bf16 patterns (is_bf16) or fp32; out: [rows] int32. */
+int oracle_argmax(int32_t *out, const void *logits, int32_t rows, int32_t vocab, int is_bf16)
+{
+    if (rows < 0 || vocab < 1) return ORACLE_BAD_ARG;
+    for (int32_t r = 0; r < rows; ++r) {
+        int64_t best = -1;
+        double bv = 0.0;
+        for (int64_t i = 0; i < vocab; ++i) {
+            size_t k = (size_t)r * (size_t)vocab + (size_t)i;
+            double v;
+            if (is_bf16) {
+                v = oracle_bf16_to_f64(((const uint16_t *)logits)[k]);
+            } else {
+                v = (double)((const float *)logits)[k];
+            }
+            if (isnan(v)) continue;
+            if (best < 0 || v > bv) {
+                best = i;
+                bv = v;
+            }
+        }
+        out[r] = best < 0 ? 0 : (int32_t)best;
+    }
+    return ORACLE_OK;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
