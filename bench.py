@@ -45,8 +45,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="batch64", choices=["batch64", "batch256", "batch8", "tiny", "prefill"],
-                    help="decode workloads, or 'prefill': 4 x (1536 cached + 512-token chunk) chunked prefill")
+    ap.add_argument("--config", default="batch64",
+                    choices=["batch64", "batch256", "batch8", "tiny", "prefill", "argmax"],
+                    help="decode workloads, 'prefill': 4 x (1536 cached + 512-token chunk) chunked prefill, or "
+                         "'argmax': greedy choice over 64 x 128,256 bf16 logits")
     ap.add_argument("--path", default="fused", choices=["fused", "separate"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "int8"],
                     help="K/V page format: bf16 pools, or INT8 tiles (codes + one fp32 scale per token and head), "
@@ -256,7 +258,7 @@ def main_prefill(args, torch, binding, device):
     res = {
         "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if not i8 else "int8 K/V, bf16 q/out, fp32 accumulation",
+        "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "chunked_prefill", "num_seqs": c.num_seqs, "prefix_len": int(c.prefix_lens[0]),
                    "chunk_len": c.chunk_len, "layers": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
@@ -272,6 +274,66 @@ def main_prefill(args, torch, binding, device):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(c, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+ARGMAX_METRIC = "greedy argmax over logit rows: logits GB/s and % of HBM peak (1 GPU)"
+
+
+def main_argmax(args, torch, binding, device):
+    """One step = one pa_argmax call over 64 rows of the 128,256-entry Llama 3.2
+    vocabulary (bf16 logits ~N(0,1)): the greedy choice of a batch-64 decode step."""
+    import oracle
+    from paged_kv_gqa_append_amd import workloads as W
+
+    rows, vocab = 64, W.VOCAB_SIZE
+    host = W.f32_to_bf16_bits(W.argmax_logits(5, rows, vocab, specials=False))
+    logits = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).to(device)
+    out = torch.empty(rows, dtype=torch.int32, device=device)
+    ws = binding.argmax_workspace(rows, vocab, torch.bfloat16, device)
+    stream = torch.cuda.current_stream()
+    calls_per_step = 16
+
+    def step():
+        for _ in range(calls_per_step):
+            binding.argmax(out, logits, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (args.steps * calls_per_step)
+    assert np.array_equal(out.cpu().numpy(), oracle.argmax(host)), "argmax differs from the oracle"
+    nbytes = rows * vocab * 2
+    gbps = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "metric": ARGMAX_METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us * calls_per_step * 1e-3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "argmax_batch64", "rows": rows, "vocab": vocab,
+                   "step": f"{calls_per_step} x pa_argmax (k_argmax_chunk + k_argmax_final)"},
+        "us_per_call": round(us, 3),
+        "roofline": {"bound": "hbm", "kernel": "k_argmax_chunk<bf16,vec> + k_argmax_final, one call",
+                     "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                     "mean_launch_us": round(us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.argmax(host)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "seconds": round(dt * reps, 3),
+                               "sample": f"fp64-compare oracle argmax over the same {rows} x {vocab} bf16 rows, "
+                                         f"{reps} repetitions, one thread"}
     print(json.dumps(res), flush=True)
 
 
@@ -303,6 +365,9 @@ def main():
         return
     if args.config == "prefill":
         main_prefill(args, torch, binding, device)
+        return
+    if args.config == "argmax":
+        main_argmax(args, torch, binding, device)
         return
     spec, k_pool, v_pool, layers, lens, rows = build_workload(args.config, device)
     table = binding.rope_table(2048 + 64, spec.theta, device)

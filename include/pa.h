@@ -238,6 +238,29 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
                                   uint32_t *device_flags, hipStream_t stream);
 
+/* --------------------------------------------------------------- argmax --
+ * Greedy next-token choice on the GPU (samir-vllm, section "Architecture et
+ * flux d'inference": the argmax runs on the GPU; tiny-vllm ch.2, section
+ * "Preallocating the 16 compute buffers": the CPU argmax it replaces scans the
+ * logits row with a strict greater-than, so the first maximum wins).
+ *   out_index[r] = lowest i with logits[r][i] = max over the row's non-NaN
+ *                  entries (-0.0 == +0.0); 0 for a row holding only NaN.
+ *   logits : [num_rows][vocab] bf16 or fp32 (logits_dtype), caller-owned device
+ *            memory, 2-byte (bf16) or 4-byte (fp32) aligned; rows that start on
+ *            16-byte boundaries with a 16-byte multiple of bytes take the
+ *            vector path, any other layout a scalar one (same results).
+ *   out_index : [num_rows] int32, device.
+ *   workspace : pa_argmax_workspace_bytes(num_rows, vocab, logits_dtype) bytes,
+ *            8-byte aligned (may be NULL when that is 0); contents dead between
+ *            calls.  Stream-ordered, no synchronisation, nothing allocated.
+ *   Errors: PA_ERR_UNSUPPORTED for another dtype or more than 65535 rows.     */
+typedef enum { PA_LOGITS_BF16 = 0, PA_LOGITS_FP32 = 1 } pa_logits_dtype;
+
+size_t pa_argmax_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t logits_dtype);
+
+pa_status pa_argmax(int32_t *out_index, const void *logits, int32_t num_rows, int32_t vocab, int32_t logits_dtype,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------ host KV page manager --
  * Host-side bookkeeping that produces the block tables and lengths the calls
  * above consume (samir-vllm, section "Gestion de la KV cache et strategies de

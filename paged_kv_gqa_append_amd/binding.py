@@ -31,7 +31,8 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_schedule", "pa_kvm_set_length", "pa_kvm_release", "pa_kvm_block_tables", "pa_kvm_lengths",
            "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
-           "pa_append_decode_gqa_i8")
+           "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax")
+PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 
 
@@ -82,6 +83,10 @@ def lib():
     L.pa_append_decode_gqa_i8.restype = ctypes.c_int
     L.pa_append_decode_gqa_i8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
                                           u64, P, P]
+    L.pa_argmax_workspace_bytes.restype = u64
+    L.pa_argmax_workspace_bytes.argtypes = [i32, i32, i32]
+    L.pa_argmax.restype = ctypes.c_int
+    L.pa_argmax.argtypes = [P, P, i32, i32, i32, P, u64, P]
     i64 = ctypes.c_int64
     L.pa_admission_credit_pages.restype = i64
     L.pa_admission_credit_pages.argtypes = [i32, i32, i32]
@@ -415,6 +420,34 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
                                        _ptr(device_flags), _stream(stream))
     _check(rc, "pa_append_decode_gqa_i8")
     return out
+
+
+# ----------------------------------------------------------------- argmax --
+
+def argmax_workspace(num_rows: int, vocab: int, dtype: torch.dtype, device="cuda") -> Optional[torch.Tensor]:
+    code = PA_LOGITS_BF16 if dtype == torch.bfloat16 else PA_LOGITS_FP32
+    n = int(lib().pa_argmax_workspace_bytes(int(num_rows), int(vocab), code))
+    return None if n == 0 else torch.empty(n // 8, dtype=torch.int64, device=device)
+
+
+def argmax(out_index: torch.Tensor, logits: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """pa_argmax: out_index[r] = lowest index of the row's non-NaN maximum (0 for an all-NaN row)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [num_rows][vocab]")
+    if logits.dtype == torch.bfloat16:
+        code = PA_LOGITS_BF16
+    elif logits.dtype == torch.float32:
+        code = PA_LOGITS_FP32
+    else:
+        raise TypeError("logits must be bfloat16 or float32")
+    _expect(logits, "logits", logits.dtype)
+    rows, vocab = int(logits.shape[0]), int(logits.shape[1])
+    _expect(out_index, "out_index", torch.int32, (rows,), logits.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_argmax(_ptr(out_index), _ptr(logits), rows, vocab, code, _ptr(workspace), ws_bytes,
+                           _stream(stream)), "pa_argmax")
+    return out_index
 
 
 def admission_credit_pages(prompt_tokens: int, max_new_tokens: int, num_layers: int) -> int:

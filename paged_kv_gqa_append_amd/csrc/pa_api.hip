@@ -86,7 +86,7 @@ const char *pa_status_string(int status) {
     }
 }
 
-int32_t pa_abi_version(void) { return 3; }
+int32_t pa_abi_version(void) { return 4; }
 
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
@@ -225,6 +225,32 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
     return decode_common(out, q, k_new, v_new, kv_pool_i8, nullptr, block_tables, context_lens, rope_cos_sin,
                          num_seqs, max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace,
                          workspace_bytes, device_flags, stream, true, true);
+}
+
+size_t pa_argmax_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t logits_dtype) {
+    if (num_rows < 1 || vocab < 1 || (logits_dtype != PA_LOGITS_BF16 && logits_dtype != PA_LOGITS_FP32)) return 0;
+    const int64_t chunk = pa::argmax_chunk_elems(logits_dtype == PA_LOGITS_BF16);
+    const int64_t splits = (static_cast<int64_t>(vocab) + chunk - 1) / chunk;
+    return splits <= 1 ? 0 : static_cast<size_t>(num_rows) * static_cast<size_t>(splits) * sizeof(uint64_t);
+}
+
+pa_status pa_argmax(int32_t *out_index, const void *logits, int32_t num_rows, int32_t vocab, int32_t logits_dtype,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_rows < 0 || vocab < 1) return PA_ERR_INVALID_ARG;
+    if (logits_dtype != PA_LOGITS_BF16 && logits_dtype != PA_LOGITS_FP32) return PA_ERR_UNSUPPORTED;
+    if (num_rows > 65535) return PA_ERR_UNSUPPORTED;  // rows are the grid's second dimension
+    if (num_rows == 0) return PA_OK;
+    const bool bf16 = logits_dtype == PA_LOGITS_BF16;
+    const size_t esz = bf16 ? 2 : 4;
+    if (!out_index || !logits) return PA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(out_index) & 3u) || (reinterpret_cast<uintptr_t>(logits) & (esz - 1)))
+        return PA_ERR_INVALID_ARG;
+    const size_t need = pa_argmax_workspace_bytes(num_rows, vocab, logits_dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7u)))
+        return PA_ERR_WORKSPACE;
+    const bool vec = aligned16(logits) && (static_cast<size_t>(vocab) * esz) % 16 == 0;
+    return pa::launch_argmax(out_index, logits, num_rows, vocab, bf16, vec, workspace, stream) == hipSuccess
+               ? PA_OK : PA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -82,6 +82,10 @@ hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream);
 // INT8 K/V pages (pa_i8.hip).  The tile pool travels in k_pool; v_pool is unused.
 hipError_t launch_append_rope_i8(const AppendLaunch &a, hipStream_t stream);
 hipError_t launch_decode_i8(const DecodeLaunch &d, hipStream_t stream);
+// argmax over logit rows (pa_argmax.hip)
+int argmax_chunk_elems(bool bf16);
+hipError_t launch_argmax(int32_t *out, const void *logits, int rows, int vocab, bool bf16, bool vec, void *workspace,
+                         hipStream_t stream);
 hipError_t launch_quantize_pages_i8(void *pool, const void *k_pool, const void *v_pool, const int32_t *page_ids,
                                     int count, int num_pages, uint32_t *flags, hipStream_t stream);
 

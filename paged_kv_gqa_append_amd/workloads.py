@@ -402,3 +402,32 @@ def prefill_config(seed: int = 4) -> PrefillCase:
     """4 sequences, 1536 cached prefix tokens + a 512-token chunk, 4096-page pool."""
     return make_prefill_case("chunked_prefill", seed, [1536] * 4, 512, num_pages=4096,
                              max_blocks=MAX_CONTEXT // PAGE_SIZE)
+
+
+# ---------------------------------------------------------------------------
+# greedy-decoding logits (argmax)
+# ---------------------------------------------------------------------------
+
+VOCAB_SIZE = 128256  # Llama 3.2 vocabulary (tiny-vllm ch.2, "Preallocating the 16 compute buffers")
+_T_LOGITS = 20
+
+
+def argmax_logits(seed: int, rows: int, vocab: int = VOCAB_SIZE, specials: bool = True) -> np.ndarray:
+    """Seeded N(0,1) logit rows as float32 [rows][vocab].  With ``specials``, a
+    few rows carry the cases a greedy choice must get right: the maximum
+    repeated at several places, NaN entries, a -inf row, an all-NaN row and
+    signed zeros.  Callers round to bf16 themselves when they need it."""
+    rng = _rng(seed, 0, _T_LOGITS)
+    x = rng.standard_normal((rows, vocab), dtype=np.float32)
+    if specials and rows >= 6 and vocab >= 8:
+        x[0, rng.choice(vocab, 4, replace=False)] = 12.0                     # tied maxima
+        x[1, rng.choice(vocab, max(1, vocab // 100), replace=False)] = np.nan  # scattered NaN
+        x[1, 0] = np.nan
+        x[2, :] = -np.inf                                                   # all -inf
+        x[2, rng.integers(vocab)] = np.nan
+        x[3, :] = np.nan                                                    # only NaN
+        x[4, :] = -1.0                                                      # signed zeros tie
+        x[4, vocab // 2] = -0.0
+        x[4, vocab - 1] = 0.0
+        x[5, vocab - 1] = 50.0                                              # maximum at the very end
+    return x

@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == 3
+    assert pa.lib().pa_abi_version() == 4
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -161,6 +161,32 @@ def test_i8_validation(pa):
 
     assert fused(rope=None) == pa.PA_ERR_INVALID_ARG
     assert fused(mp=0) == pa.PA_ERR_INVALID_ARG
+
+
+def test_argmax_validation(pa):
+    lib = pa.lib()
+    v = ctypes.c_void_p
+    F = v(FAKE)
+    chunk_bf16, chunk_fp32 = 256 * 8 * 8, 256 * 8 * 4
+    assert lib.pa_argmax_workspace_bytes(64, 128256, 0) == 64 * (-(-128256 // chunk_bf16)) * 8
+    assert lib.pa_argmax_workspace_bytes(64, 128256, 1) == 64 * (-(-128256 // chunk_fp32)) * 8
+    assert lib.pa_argmax_workspace_bytes(5, chunk_bf16, 0) == 0          # one chunk per row: no workspace
+    assert lib.pa_argmax_workspace_bytes(5, 100, 2) == 0
+
+    def am(out=F, lg=F, rows=4, vocab=128256, dt=0, ws=None, wsb=0):
+        return lib.pa_argmax(out, lg, rows, vocab, dt, ws, wsb, None)
+
+    assert am(dt=2) == pa.PA_ERR_UNSUPPORTED
+    assert am(vocab=0) == pa.PA_ERR_INVALID_ARG
+    assert am(rows=-1) == pa.PA_ERR_INVALID_ARG
+    assert am(out=None) == pa.PA_ERR_INVALID_ARG
+    assert am(lg=v(FAKE + 1)) == pa.PA_ERR_INVALID_ARG
+    assert am(dt=1, lg=v(FAKE + 2)) == pa.PA_ERR_INVALID_ARG
+    assert am() == pa.PA_ERR_WORKSPACE
+    need = lib.pa_argmax_workspace_bytes(4, 128256, 0)
+    assert am(ws=F, wsb=need - 8) == pa.PA_ERR_WORKSPACE
+    assert am(ws=v(FAKE + 4), wsb=need) == pa.PA_ERR_WORKSPACE
+    assert am(rows=0, out=None) == pa.PA_OK
 
 
 def test_rope_table_fill(pa):
