@@ -287,13 +287,18 @@ int oracle_prefill_chunk(double *out, uint16_t *q, const uint16_t *k_chunk, cons
  * K rows are quantised after RoPE from their bf16-rounded values, V rows from
  * their bf16 input.
  * Tile of (page, head): 2176 bytes = K codes [0,1024) + V codes [1024,2048) +
- * per token t the K scale (float) at 2048+8t and the V scale at 2052+8t; code
- * of element d of token t at byte ((t&7)*8 + d/8)*16 + (t/8)*8 + d%8 of its
- * block.                                                                   */
+ * the 16 K scales (float) at 2048+4t + the 16 V scales at 2112+4t.  Code of
+ * element d of token t:
+ *   K: 16-byte unit ((d mod 32) div 8)*16 + t, byte (d div 32)*8 + d mod 8 in it;
+ *   V: 16-byte unit (t div 4)*16 + d mod 16, byte (d div 16)*4 + t mod 4 in it.
+ * (A storage layout of this library's own choosing; the pages give none.)  */
 #define O_I8_TILE 2176
 
 static size_t i8_tile(int64_t page, int head) { return ((size_t)page * O_HKV + (size_t)head) * O_I8_TILE; }
-static size_t i8_pos(int t, int d) { return (size_t)((((t & 7) * 8 + d / 8) * 16) + (t / 8) * 8 + d % 8); }
+static size_t i8_kpos(int t, int d) { return (size_t)((((d % 32) / 8) * 16 + t) * 16 + (d / 32) * 8 + d % 8); }
+static size_t i8_vpos(int t, int d) { return (size_t)(1024 + ((t / 4) * 16 + d % 16) * 16 + (d / 16) * 4 + t % 4); }
+static size_t i8_kscale(int t) { return (size_t)(2048 + 4 * t); }
+static size_t i8_vscale(int t) { return (size_t)(2112 + 4 * t); }
 
 /* One row: x given as 64 bf16 patterns. */
 void oracle_quantize_row_i8(const uint16_t *x, int8_t *codes, float *scale_out)
@@ -317,13 +322,14 @@ void oracle_quantize_row_i8(const uint16_t *x, int8_t *codes, float *scale_out)
     *scale_out = scale;
 }
 
-static void store_row_i8(uint8_t *tile, int block_off, int scale_off, int slot, const uint16_t *row)
+/* Quantise one row into slot `slot` of a tile: is_v selects the V block. */
+static void store_row_i8(uint8_t *tile, int is_v, int slot, const uint16_t *row)
 {
     int8_t codes[O_D];
     float sc;
     oracle_quantize_row_i8(row, codes, &sc);
-    for (int d = 0; d < O_D; ++d) tile[block_off + i8_pos(slot, d)] = (uint8_t)codes[d];
-    memcpy(tile + 2048 + 8 * slot + scale_off, &sc, 4);
+    for (int d = 0; d < O_D; ++d) tile[is_v ? i8_vpos(slot, d) : i8_kpos(slot, d)] = (uint8_t)codes[d];
+    memcpy(tile + (is_v ? i8_vscale(slot) : i8_kscale(slot)), &sc, 4);
 }
 
 static int append_token_i8(uint16_t *q_tok, const uint16_t *k_tok, const uint16_t *v_tok, uint8_t *pool,
@@ -340,8 +346,8 @@ static int append_token_i8(uint16_t *q_tok, const uint16_t *k_tok, const uint16_
         uint8_t *tile = pool + i8_tile(page, j);
         oracle_rope_head(k_tok + (size_t)j * O_D, pos, theta, y);
         for (int d = 0; d < O_D; ++d) kb[d] = oracle_f64_to_bf16(y[d]);
-        store_row_i8(tile, 0, 0, slot, kb);
-        store_row_i8(tile, 1024, 4, slot, v_tok + (size_t)j * O_D);
+        store_row_i8(tile, 0, slot, kb);
+        store_row_i8(tile, 1, slot, v_tok + (size_t)j * O_D);
     }
     if (q_tok) {
         for (int h = 0; h < O_HQ; ++h) {
@@ -388,17 +394,17 @@ void oracle_quantize_pages_i8(uint8_t *pool, const uint16_t *k_pool, const uint1
             for (int t = 0; t < O_PS; ++t) {
                 size_t src = pool_index(p, j, t);
                 uint8_t *tile = pool + i8_tile(p, j);
-                if (row_finite(k_pool + src)) store_row_i8(tile, 0, 0, t, k_pool + src);
-                if (row_finite(v_pool + src)) store_row_i8(tile, 1024, 4, t, v_pool + src);
+                if (row_finite(k_pool + src)) store_row_i8(tile, 0, t, k_pool + src);
+                if (row_finite(v_pool + src)) store_row_i8(tile, 1, t, v_pool + src);
             }
 }
 
-/* Value of element d of token t of a block (0: K, 1024: V) of a tile.      */
-static double i8_value(const uint8_t *tile, int block_off, int scale_off, int t, int d)
+/* Value of element d of token t of a tile's K (is_v 0) or V (is_v 1) row.  */
+static double i8_value(const uint8_t *tile, int is_v, int t, int d)
 {
     float sc;
-    memcpy(&sc, tile + 2048 + 8 * t + scale_off, 4);
-    return (double)(int8_t)tile[block_off + i8_pos(t, d)] * (double)sc;
+    memcpy(&sc, tile + (is_v ? i8_vscale(t) : i8_kscale(t)), 4);
+    return (double)(int8_t)tile[is_v ? i8_vpos(t, d) : i8_kpos(t, d)] * (double)sc;
 }
 
 static int attend_i8(double *out, const uint16_t *q_head, const uint8_t *pool, const int32_t *bt_row,
@@ -413,7 +419,7 @@ static int attend_i8(double *out, const uint16_t *q_head, const uint8_t *pool, c
         if (page < 0 || page >= num_pages) return ORACLE_BAD_PAGE;
         const uint8_t *tile = pool + i8_tile(page, kv_head);
         double acc = 0.0;
-        for (int d = 0; d < O_D; ++d) acc += qd[d] * i8_value(tile, 0, 0, (int)(t % O_PS), d);
+        for (int d = 0; d < O_D; ++d) acc += qd[d] * i8_value(tile, 0, (int)(t % O_PS), d);
         score_buf[t] = scale * acc;
         if (score_buf[t] > m) m = score_buf[t];
     }
@@ -423,7 +429,7 @@ static int attend_i8(double *out, const uint16_t *q_head, const uint8_t *pool, c
         const uint8_t *tile = pool + i8_tile(bt_row[t / O_PS], kv_head);
         double w = exp(score_buf[t] - m);
         z += w;
-        for (int d = 0; d < O_D; ++d) o[d] += w * i8_value(tile, 1024, 4, (int)(t % O_PS), d);
+        for (int d = 0; d < O_D; ++d) o[d] += w * i8_value(tile, 1, (int)(t % O_PS), d);
     }
     for (int d = 0; d < O_D; ++d) out[d] = o[d] / z;
     return ORACLE_OK;

@@ -36,12 +36,20 @@ TILE = 2176
 NAN32 = np.array([0x7FC00000], np.uint32).view(np.uint8)
 
 
-def code_pos(t, d):
-    """Byte of element d of slot t inside a 1024-byte code block (include/pa.h)."""
-    return ((t & 7) * 8 + (d >> 3)) * 16 + (t >> 3) * 8 + (d & 7)
+def k_pos(t, d):
+    """Byte of K element d of slot t in a 2176-byte tile (include/pa.h)."""
+    return (((d % 32) // 8) * 16 + t) * 16 + (d // 32) * 8 + d % 8
 
 
-SLOT_BYTES = np.array([[code_pos(t, d) for d in range(64)] for t in range(16)])  # [16][64]
+def v_pos(t, d):
+    """Byte of V element d of slot t in a tile (include/pa.h)."""
+    return 1024 + ((t // 4) * 16 + d % 16) * 16 + (d // 16) * 4 + t % 4
+
+
+K_BYTES = np.array([[k_pos(t, d) for d in range(64)] for t in range(16)])  # [16][64]
+V_BYTES = np.array([[v_pos(t, d) for d in range(64)] for t in range(16)])
+K_SCALE = [2048 + 4 * t for t in range(16)]
+V_SCALE = [2112 + 4 * t for t in range(16)]
 
 
 def poison_i8(pool, block_tables, lens, seed):
@@ -53,10 +61,10 @@ def poison_i8(pool, block_tables, lens, seed):
         used[p, t] = True
     for p, t in np.argwhere(~used):
         page = pool[p]  # [8][2176] view
-        for base in (0, 1024):
-            page[:, base + SLOT_BYTES[t]] = rng.integers(0, 256, (8, 64), dtype=np.uint8)
-        page[:, 2048 + 8 * t:2048 + 8 * t + 4] = NAN32
-        page[:, 2052 + 8 * t:2052 + 8 * t + 4] = NAN32
+        for idx in (K_BYTES[t], V_BYTES[t]):
+            page[:, idx] = rng.integers(0, 256, (8, 64), dtype=np.uint8)
+        page[:, K_SCALE[t]:K_SCALE[t] + 4] = NAN32
+        page[:, V_SCALE[t]:V_SCALE[t] + 4] = NAN32
 
 
 def host_i8(case, poison=True):
@@ -164,9 +172,9 @@ def rotation_is_unambiguous(x_bits, pos, theta):
 
 
 def read_row(pool, page, head, t, which):
-    base = 0 if which == "k" else 1024
-    codes = pool[page, head, base + SLOT_BYTES[t]].view(np.int8)
-    sc = pool[page, head, 2048 + 8 * t + (0 if which == "k" else 4):][:4].view(np.float32)[0]
+    codes = pool[page, head, (K_BYTES if which == "k" else V_BYTES)[t]].view(np.int8)
+    s = (K_SCALE if which == "k" else V_SCALE)[t]
+    sc = pool[page, head, s:s + 4].view(np.float32)[0]
     return codes, sc
 
 
@@ -199,8 +207,8 @@ def test_append_i8_against_oracle():
                 n_exact += 1
                 continue
             n_bound += 1
-            allowed[pg, j, SLOT_BYTES[t]] = True
-            allowed[pg, j, 2048 + 8 * t:2052 + 8 * t] = True
+            allowed[pg, j, K_BYTES[t]] = True
+            allowed[pg, j, K_SCALE[t]:K_SCALE[t] + 4] = True
             gc, gs = read_row(got, pg, j, t, "k")
             rc_, rs = read_row(ref, pg, j, t, "k")
             y = oracle.rope_head(kx, pos, case.theta)
@@ -313,8 +321,8 @@ def test_i8_device_errors():
     pg, t = case.block_tables[0][2, pos // 16], pos % 16
     diff = got_pool != ref_pool
     allowed = np.zeros_like(diff)
-    allowed[pg, :, SLOT_BYTES[t]] = True
-    allowed[pg, :, 2048 + 8 * t:2052 + 8 * t] = True
+    allowed[pg, :, K_BYTES[t]] = True
+    allowed[pg, :, K_SCALE[t]:K_SCALE[t] + 4] = True
     assert not (diff & ~allowed).any()
 
 

@@ -10,8 +10,9 @@ scale = max|x| / 127, code = round-half-even(x / scale), decided in binary32.
   random rows, outliers and tiny values: every code and scale must agree;
 * the dequantisation error bound |code*scale - x| <= scale/2 (plus the binary32
   rounding of x/scale) and max |code| = 127;
-* the tile layout: rows appended by the oracle read back at the byte positions
-  the header formula gives, nothing else in the pool changes;
+* the tile layout: the header's byte formula is a bijection onto the 2176
+  bytes; rows appended by the oracle read back at those positions, nothing
+  else in the pool changes;
 * decode: torch's fp64 SDPA on the dequantised, gathered K/V; closed forms
   (one token -> its V, identical V rows -> that V).
 """
@@ -114,17 +115,42 @@ def test_error_bound_and_range():
         assert err.max() <= float(sc) * (0.5 + 128 * 2.0 ** -24)
 
 
-def code_pos(t, d):
-    """Byte of element d of token t inside a 1024-byte code block (include/pa.h)."""
-    return ((t & 7) * 8 + (d >> 3)) * 16 + (t >> 3) * 8 + (d & 7)
+def k_pos(t, d):
+    """Byte of K element d of token t in a 2176-byte tile (include/pa.h)."""
+    return (((d % 32) // 8) * 16 + t) * 16 + (d // 32) * 8 + d % 8
+
+
+def v_pos(t, d):
+    """Byte of V element d of token t in a tile (include/pa.h)."""
+    return 1024 + ((t // 4) * 16 + d % 16) * 16 + (d // 16) * 4 + t % 4
+
+
+def scale_pos(t, which):
+    return (2048 if which == "k" else 2112) + 4 * t
 
 
 def read_row(pool, page, head, t, which):
     tile = pool[page, head]
-    base = 0 if which == "k" else 1024
-    codes = np.array([tile[base + code_pos(t, d)] for d in range(64)], np.uint8).view(np.int8)
-    sc = tile[2048 + 8 * t + (0 if which == "k" else 4):][:4].view(np.float32)[0]
+    pos = k_pos if which == "k" else v_pos
+    codes = np.array([tile[pos(t, d)] for d in range(64)], np.uint8).view(np.int8)
+    sc = tile[scale_pos(t, which):][:4].view(np.float32)[0]
     return codes.astype(np.float64) * float(sc), codes, sc
+
+
+def test_layout_is_a_bijection():
+    """Every code byte and scale slot of a tile belongs to exactly one (row, element)."""
+    seen = {}
+    for t in range(16):
+        for d in range(64):
+            for which, pos in (("k", k_pos), ("v", v_pos)):
+                b = pos(t, d)
+                assert b not in seen, (which, t, d, seen.get(b))
+                seen[b] = (which, t, d)
+        for which in ("k", "v"):
+            for b in range(scale_pos(t, which), scale_pos(t, which) + 4):
+                assert b not in seen
+                seen[b] = (which, t, "scale")
+    assert sorted(seen) == list(range(TILE))
 
 
 def test_layout_and_append_touch_only_the_row():
@@ -147,10 +173,11 @@ def test_layout_and_append_touch_only_the_row():
         allowed = set()
         for j in range(8):
             for d in range(64):
-                allowed.add((page, j, code_pos(t, d)))
-                allowed.add((page, j, 1024 + code_pos(t, d)))
-            for b in range(8):
-                allowed.add((page, j, 2048 + 8 * t + b))
+                allowed.add((page, j, k_pos(t, d)))
+                allowed.add((page, j, v_pos(t, d)))
+            for which in ("k", "v"):
+                for b in range(4):
+                    allowed.add((page, j, scale_pos(t, which) + b))
         assert all(tuple(c) in allowed for c in changed)
         for j in range(8):
             _, vcodes, vsc = read_row(pool, page, j, t, "v")
@@ -166,7 +193,7 @@ def random_i8_pool(rng, P):
     """A valid INT8 pool: random codes, positive scales."""
     pool = rng.integers(0, 256, (P, 8, TILE), dtype=np.uint8)
     sc = (np.abs(rng.standard_normal((P, 8, 16, 2))) * 3 / 127 + 1e-3).astype(np.float32)
-    pool[:, :, 2048:] = sc.view(np.uint8).reshape(P, 8, 128)
+    pool[:, :, 2048:] = sc.transpose(0, 1, 3, 2).copy().view(np.uint8).reshape(P, 8, 128)  # 16 K, then 16 V scales
     return pool
 
 
@@ -210,17 +237,18 @@ def test_decode_closed_forms():
         assert np.array_equal(out[0, h], read_row(pool, 2, h // 4, 0, "v")[0])
     # identical V rows (same codes and scale for all 40 tokens): output is that row
     vt = pool[2, :, 1024:2048].copy()
+    s0 = pool[2, :, scale_pos(0, "v"):scale_pos(0, "v") + 4].copy()
     for p in range(P):
         pool[p, :, 1024:2048] = vt
         for t in range(16):
-            pool[p, :, 2048 + 8 * t + 4:2048 + 8 * t + 8] = pool[2, :, 2048 + 4:2048 + 8]
-    # the code block holds tokens 0 and 8 interleaved; make every token equal to token 0
+            pool[p, :, scale_pos(t, "v"):scale_pos(t, "v") + 4] = s0
+    # the V block interleaves the tokens; make every token equal to token 0
     for p in range(P):
         for j in range(8):
-            row0 = np.array([pool[p, j, 1024 + code_pos(0, d)] for d in range(64)], np.uint8)
+            row0 = np.array([pool[p, j, v_pos(0, d)] for d in range(64)], np.uint8)
             for t in range(16):
                 for d in range(64):
-                    pool[p, j, 1024 + code_pos(t, d)] = row0[d]
+                    pool[p, j, v_pos(t, d)] = row0[d]
     out, rc = oracle.decode_gqa_i8(q, pool, bt, np.array([40], np.int32), P, 0.125)
     assert rc == oracle.OK
     for h in range(32):
