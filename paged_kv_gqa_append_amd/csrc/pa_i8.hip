@@ -1,5 +1,5 @@
 // pa_i8.hip -- INT8 K/V pages: quantising append, bulk quantiser, and paged
-// GQA decode over INT8 tiles (optionally fused with the append).
+// GQA decode over INT8 tiles on f16 MFMAs (optionally fused with the append).
 //
 // TinyLoop ("Lifecycle and Memory Model", section "Per-request / handle-owned
 // memory") names an INT8 K/V cache mode beside FP16 and gives no rule.  The
@@ -11,21 +11,36 @@
 // V rows from their bf16 input.
 //
 // Tile of (page, KV head), PA_I8_TILE_BYTES = 2176 bytes:
-//   [0, 1024)     K codes, [1024, 2048) V codes,
-//   2048 + 8t     K scale (fp32) of token t, 2052 + 8t its V scale.
-//   Code of element d of token t at byte ((t & 7) * 8 + d / 8) * 16 + (t / 8) * 8 + d % 8
-//   of its 1 KiB block, so 16-byte unit u = 8g + c holds the chunk c*8..c*8+7
-//   of tokens g (bytes 0-7) and g+8 (bytes 8-15): exactly what lane u of the
-//   bf16 decode kernel holds, read here with ONE 16-byte load per block.
+//   [0, 1024)     K codes: 16-byte unit 16*((d%32)/8) + t holds dims
+//                 8*((d%32)/8) .. +7 (bytes 0-7) and 32 + the same (bytes 8-15)
+//                 of token t;
+//   [1024, 2048)  V codes: 16-byte unit 16*(t/4) + d%16 holds tokens
+//                 4*(t/4) .. +3 of dims d%16 + 16n at bytes 4n .. 4n+3;
+//   2048 + 4t     K scale (fp32) of token t;  2112 + 4t  V scale of token t.
+// One 16-byte K unit and one V unit are exactly the operands lane u of a wave
+// feeds to the MFMAs below, so a page costs each lane two 16-byte loads (plus
+// two 16-byte scale loads shared by 16 lanes).
 //
-// Decode arithmetic: codes enter as u = code + 128 (an XOR of the sign bit)
-// converted exactly to fp32 and, for K, to bf16 pairs, so the bf16 kernel's
-// dot-product and reduction machinery applies unchanged:
-//   <q, code> = <q, u> - 128 * sum(q)            (per query head, fp32)
-//   x_t = scale * K_scale_t * <q, code_t>
-//   acc = sum_t w_t V_scale_t (u_t - 128) = sum_t (w_t V_scale_t) u_t - 128 * sum_t w_t V_scale_t
-// Everything else (online softmax, lazy max, wave and partition merges) is the
-// bf16 kernel's, from pa_decode_core.h.
+// Decode per page and wave (16 tokens of one KV head, its 4 query heads):
+//   S^T[16 tokens][16] = K[16 x 64] . Q^T[64 x 16]   two v_mfma_f32_16x16x32_f16,
+//       columns 0-3 the 4 query heads, 4-15 zero (lane l holds tokens
+//       4(l/16)..+3 of column l%16);
+//   O[16][64] += P'[16][16 tokens] . V[16 tokens][64] four v_mfma_f32_16x16x16_f16,
+//       whose A operand is exactly the lane's 4 weights from S^T (rows 0-3
+//       are the 4 heads; rows 4-15 are never read).
+// Codes enter the MFMAs as f16 values 1152 + code: the byte code ^ 0x80 (= code
+// + 128) under an f16 exponent pattern 0x64 is 1024 + code + 128, built with
+// one v_perm per pair, exactly.  The offsets come out again exactly where they
+// went in: the score subtracts 1152 * <q, 1> (an MFMA over a key row of 1152s),
+// and the output subtracts 1152 * the sum of the fed weights, taken by the
+// same MFMA against a ones column.  q enters as f16 after a power-of-two
+// scaling (exact) that puts its largest element in [2^14, 2^15).  Weights
+// P' = 2^(x - m) * V scale are fed as an f16 pair hi + lo (two MFMA passes,
+// about 22 significant bits, so the weights' rounding stays ~2^-22 of |V|);
+// the running sum uses the fp32 2^(x - m).  P' stays below 2^8 * V scale, so
+// V rows must hold |values| < 65504 * 127 / 2^8 (about 32000) for hi to fit f16.
+// Online softmax (log2 units, lazy max), wave and partition merges follow the
+// bf16 kernel's.
 #include <math.h>
 
 #include "pa_decode_core.h"
@@ -34,10 +49,21 @@ namespace pa {
 
 constexpr int kI8Tile = 2176;     // bytes per (page, KV head) tile
 constexpr int kI8VOff = 1024;     // V block offset
-constexpr int kI8ScOff = 2048;    // scales offset
+constexpr int kI8KScOff = 2048;   // K scales
+constexpr int kI8VScOff = 2112;   // V scales
 constexpr int kPageBytesI8 = kHKV * kI8Tile;
+constexpr float kOffsetF16 = 1152.0f;  // value of the f16 an INT8 code c becomes, minus c
 
-__device__ __forceinline__ int i8_pos(int t, int d) { return (((t & 7) * 8 + (d >> 3)) * 16) + (t >> 3) * 8 + (d & 7); }
+__device__ __forceinline__ int i8_kpos(int t, int d) { return (((d & 31) >> 3) * 16 + t) * 16 + (d >> 5) * 8 + (d & 7); }
+__device__ __forceinline__ int i8_vpos(int t, int d) {
+    return kI8VOff + ((t >> 2) * 16 + (d & 15)) * 16 + (d >> 4) * 4 + (t & 3);
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Quantise one value against a row scale (binary32 throughout, the decision
 // the format defines): round-half-even(x / scale), clamped to [-127, 127].
@@ -62,37 +88,28 @@ __device__ __forceinline__ float max_lanes8(float v) {
     return v;
 }
 
-// 4 codes (two's complement bytes) -> u = code + 128 as two bf16 pairs (exact:
-// every integer up to 256 is a bf16 value, whose fp32 pattern has a zero low half).
-__device__ __forceinline__ void codes_to_bf16x4(uint32_t w, uint32_t &p01, uint32_t &p23) {
+// 4 codes (two's complement bytes of w) -> the f16 values 1152 + code, as two
+// packed pairs (bytes 0,1 and 2,3): code ^ 0x80 = code + 128 under the f16
+// exponent byte 0x64 is 1024 + code + 128, exactly.
+__device__ __forceinline__ void codes_to_f16x4(uint32_t w, uint32_t &p01, uint32_t &p23) {
     const uint32_t u = w ^ 0x80808080u;
-    const uint32_t f0 = __builtin_bit_cast(uint32_t, static_cast<float>(u & 0xFFu));
-    const uint32_t f1 = __builtin_bit_cast(uint32_t, static_cast<float>((u >> 8) & 0xFFu));
-    const uint32_t f2 = __builtin_bit_cast(uint32_t, static_cast<float>((u >> 16) & 0xFFu));
-    const uint32_t f3 = __builtin_bit_cast(uint32_t, static_cast<float>(u >> 24));
-    p01 = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-    p23 = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    p01 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    p23 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
 }
-// 8 codes (two words) -> 8 bf16 values of u = code + 128, in element order.
-__device__ __forceinline__ u32x4 codes8_to_bf16(uint32_t w0, uint32_t w1) {
-    u32x4 r;
+__device__ __forceinline__ half8 codes8_to_f16(uint32_t w0, uint32_t w1) {
     uint32_t a, b, c, d;
-    codes_to_bf16x4(w0, a, b);
-    codes_to_bf16x4(w1, c, d);
-    r.x = a;
-    r.y = b;
-    r.z = c;
-    r.w = d;
-    return r;
+    codes_to_f16x4(w0, a, b);
+    codes_to_f16x4(w1, c, d);
+    return __builtin_bit_cast(half8, u32x4{a, b, c, d});
 }
-// 8 codes (two words) -> 8 fp32 values of u = code + 128, in element order.
-__device__ __forceinline__ void codes8_to_f32(uint32_t w0, uint32_t w1, float (&f)[8]) {
-    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        f[k] = static_cast<float>((u0 >> (8 * k)) & 0xFFu);
-        f[4 + k] = static_cast<float>((u1 >> (8 * k)) & 0xFFu);
-    }
+__device__ __forceinline__ half4 codes4_to_f16(uint32_t w) {
+    uint32_t a, b;
+    codes_to_f16x4(w, a, b);
+    return __builtin_bit_cast(half4, u32x2{a, b});
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, half2v));
 }
 
 // ------------------------------------------------------------- append ------
@@ -128,19 +145,18 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
         const float y0 = bf16_to_f32(f32_to_bf16(rope_lo(x0, x1, c, sn)));
         const float y1 = bf16_to_f32(f32_to_bf16(rope_hi(x0, x1, c, sn)));
         const float sc = max_lanes32(fmaxf(fabsf(y0), fabsf(y1))) / 127.0f;
-        tile[i8_pos(slot, p)] = static_cast<uint8_t>(quant_code(y0, sc));
-        tile[i8_pos(slot, p + 32)] = static_cast<uint8_t>(quant_code(y1, sc));
-        if (p == 0) *reinterpret_cast<float *>(tile + kI8ScOff + 8 * slot) = sc;
+        tile[i8_kpos(slot, p)] = static_cast<uint8_t>(quant_code(y0, sc));
+        tile[i8_kpos(slot, p + 32)] = static_cast<uint8_t>(quant_code(y1, sc));
+        if (p == 0) *reinterpret_cast<float *>(tile + kI8KScOff + 4 * slot) = sc;
     }
     {
         // V: elements 2p, 2p+1 verbatim from bf16, quantised with the row's scale
         const uint32_t wv = reinterpret_cast<const uint32_t *>(v_new + (static_cast<int64_t>(s) * kHKV + j) * kD)[p];
         const float v0 = bf16_lo(wv), v1 = bf16_hi(wv);
         const float sc = max_lanes32(fmaxf(fabsf(v0), fabsf(v1))) / 127.0f;
-        const uint32_t pair = (static_cast<uint32_t>(quant_code(v0, sc)) & 0xFFu) |
-                              ((static_cast<uint32_t>(quant_code(v1, sc)) & 0xFFu) << 8);
-        *reinterpret_cast<uint16_t *>(tile + kI8VOff + i8_pos(slot, 2 * p)) = static_cast<uint16_t>(pair);
-        if (p == 0) *reinterpret_cast<float *>(tile + kI8ScOff + 8 * slot + 4) = sc;
+        tile[i8_vpos(slot, 2 * p)] = static_cast<uint8_t>(quant_code(v0, sc));
+        tile[i8_vpos(slot, 2 * p + 1)] = static_cast<uint8_t>(quant_code(v1, sc));
+        if (p == 0) *reinterpret_cast<float *>(tile + kI8VScOff + 4 * slot) = sc;
     }
     if (q) {
 #pragma unroll
@@ -158,7 +174,7 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
 
 // --------------------------------------------------------- bulk quantiser --
 // One workgroup (256 threads) per (listed page, KV head): thread t quantises
-// chunk c = t%8 of row r = t/8 (rows 0-15: K slots, 16-31: V slots).
+// chunk c = t%8 (dims 8c..8c+7) of row r = t/8 (rows 0-15: K slots, 16-31: V slots).
 __global__ __launch_bounds__(256) void k_quantize_pages_i8(uint8_t *__restrict__ pool, const uint16_t *__restrict__ k_pool,
                                                            const uint16_t *__restrict__ v_pool,
                                                            const int32_t *__restrict__ page_ids, int num_pages,
@@ -186,25 +202,54 @@ __global__ __launch_bounds__(256) void k_quantize_pages_i8(uint8_t *__restrict__
 #pragma unroll
     for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
     const float sc = max_lanes8(a) / 127.0f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        lo |= (static_cast<uint32_t>(quant_code(x[k], sc)) & 0xFFu) << (8 * k);
-        hi |= (static_cast<uint32_t>(quant_code(x[4 + k], sc)) & 0xFFu) << (8 * k);
-    }
     uint8_t *tile = pool + (static_cast<int64_t>(page) * kHKV + j) * kI8Tile;
-    *reinterpret_cast<uint2 *>(tile + is_v * kI8VOff + i8_pos(slot, c * 8)) = make_uint2(lo, hi);
-    if (c == 0) *reinterpret_cast<float *>(tile + kI8ScOff + 8 * slot + 4 * is_v) = sc;
+    if (is_v) {
+        // V: the 8 dims of this chunk lie in 8 different 16-byte units
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tile[i8_vpos(slot, c * 8 + k)] = static_cast<uint8_t>(quant_code(x[k], sc));
+    } else {
+        // K: dims 8c..8c+7 are 8 consecutive bytes of one unit
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            lo |= (static_cast<uint32_t>(quant_code(x[k], sc)) & 0xFFu) << (8 * k);
+            hi |= (static_cast<uint32_t>(quant_code(x[4 + k], sc)) & 0xFFu) << (8 * k);
+        }
+        *reinterpret_cast<uint2 *>(tile + i8_kpos(slot, c * 8)) = make_uint2(lo, hi);
+    }
+    if (c == 0) *reinterpret_cast<float *>(tile + (is_v ? kI8VScOff : kI8KScOff) + 4 * slot) = sc;
 }
 
 // ------------------------------------------------------------- decode ------
-// The bf16 kernel's structure (see pa_decode.hip) over INT8 tiles.  The pool
-// travels in DecodeParams::k_pool (v_pool is unused): K, V and scales of a
-// (page, head) are one tile.
-struct I8Regs {
-    u32x4 k, v;   // K / V codes of tokens g (words 0,1) and g+8 (words 2,3), chunk c
-    float2 sc;    // (K scale, V scale) of the lane's score token g + 8*t0
+// Workgroups and page ids as in the bf16 kernel (pa_decode.hip): one
+// workgroup of kWaves waves per (sequence, KV head, context partition), pages
+// dealt round-robin to the waves, the next page's loads always in flight.
+// The pool travels in DecodeParams::k_pool (v_pool is unused).
+struct I8Page {
+    u32x4 k, v;   // the lane's K unit and V unit
+    f32x4 ks, vs; // K and V scales of tokens 4(l/16) .. +3
 };
+
+// The value lane src (wave-uniform) holds, as a scalar.
+__device__ __forceinline__ float lane_value(float v, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
+// Sum (or max) over the four lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float sum_quarters(float v) {
+    float lo, hi;
+    xor16_pair(v, lo, hi);
+    v = lo + hi;
+    xor32_pair(v, lo, hi);
+    return lo + hi;
+}
+__device__ __forceinline__ float max_quarters(float v) {
+    float lo, hi;
+    xor16_pair(v, lo, hi);
+    v = fmaxf(lo, hi);
+    xor32_pair(v, lo, hi);
+    return fmaxf(lo, hi);
+}
 
 template <int kWaves, bool kFused>
 __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P) {
@@ -223,19 +268,17 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     __shared__ int s_app_page;
     __shared__ float s_m[kWaves][kGroup];
     __shared__ float s_l[kWaves][kGroup];
-    __shared__ float s_l2[kWaves][kGroup];   // sum of w * V scale (the 128-offset correction)
     __shared__ float s_acc[kWaves][kGroup][kD];
     __shared__ __align__(16) uint16_t s_q[kGroup][kD];  // rotated q (fused)
     __shared__ __align__(16) int8_t s_nk[kD];           // appended K row codes (fused)
     __shared__ __align__(16) int8_t s_nv[kD];           // appended V row codes (fused)
     __shared__ float s_nsc[2];                          // appended row scales (K, V)
 
-    const int g = lane >> 3;
-    const int c = lane & 7;
-    const int b0 = c & 1, b1 = (c >> 1) & 1, b2 = c >> 2;
-    const int t0 = b0 ^ b2;
-    const int hm = ((b1 ^ b2) << 1) | b2;
-    const int tok_s = g + 8 * t0;  // the lane's score token in a page
+    // ---- lane roles: column hh of the MFMAs (query head hh < 4, K token hh),
+    // quarter qd (K dims 8qd..+7 and 32+8qd..+7; V tokens and scales 4qd..+3)
+    const int hh = lane & 15;
+    const int qd = lane >> 4;
+    const bool head_lane = hh < kGroup;
 
     const int pg0 = part * P.part_pages;
     const int slice = min(P.part_pages, P.max_blocks - pg0);
@@ -257,10 +300,15 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         x1 = bf16_to_f32(src[pr + 32]);
         vword = reinterpret_cast<const uint32_t *>(P.v_new + nrow)[pr];
     }
-    u32x4 qv[kGroup];
+    // q chunks of this lane (non-fused: straight from q; head lanes only, the
+    // other columns are zero): dims 8qd..8qd+7 and 32+8qd..+7 of head hh
+    u32x4 qraw0 = {0u, 0u, 0u, 0u}, qraw1 = {0u, 0u, 0u, 0u};
     if (!kFused) {
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(P.q + qrow0 + (m ^ hm) * kD + c * 8);
+        const uint16_t *qh = P.q + qrow0 + min(hh, kGroup - 1) * kD;
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(qh + 8 * qd);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(qh + 32 + 8 * qd);
+        qraw0 = head_lane ? a : qraw0;
+        qraw1 = head_lane ? b : qraw1;
     }
     __builtin_amdgcn_sched_barrier(0);
     float co = 0.0f, si = 0.0f;
@@ -274,13 +322,14 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     const int64_t tile_j = static_cast<int64_t>(j) * kI8Tile;
     auto load_tile = [&](int page_id) {
         const uint8_t *t = pool + static_cast<int64_t>(page_id) * kPageBytesI8 + tile_j;
-        I8Regs r;
+        I8Page r;
         r.k = *reinterpret_cast<const u32x4 *>(t + lane * 16);
         r.v = *reinterpret_cast<const u32x4 *>(t + kI8VOff + lane * 16);
-        r.sc = *reinterpret_cast<const float2 *>(t + kI8ScOff + 8 * tok_s);
+        r.ks = *reinterpret_cast<const f32x4 *>(t + kI8KScOff + qd * 16);
+        r.vs = *reinterpret_cast<const f32x4 *>(t + kI8VScOff + qd * 16);
         return r;
     };
-    I8Regs cur = load_tile(first_id >= 0 && first_id < P.num_pages ? first_id : 0);
+    I8Page cur = load_tile(first_id >= 0 && first_id < P.num_pages ? first_id : 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // fused: rotate q into LDS (threads 0..127); wave 2 rotates the new K row
@@ -336,89 +385,166 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         return;
     }
     if (part >= n_parts_s) return;
+    const int sl = pos & (kPage - 1);  // slot of the appended token (fused)
     if (kFused) {
-#pragma unroll
-        for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(&s_q[m ^ hm][c * 8]);
-        if (tid < 9 && pg1 == n_pages) {  // append the quantised row (last partition only)
-            const int sl = pos & (kPage - 1);
+        if (head_lane) {
+            qraw0 = *reinterpret_cast<const u32x4 *>(&s_q[hh][8 * qd]);
+            qraw1 = *reinterpret_cast<const u32x4 *>(&s_q[hh][32 + 8 * qd]);
+        }
+        if (pg1 == n_pages) {  // append the quantised row (last partition only)
             uint8_t *tw = const_cast<uint8_t *>(pool) + static_cast<int64_t>(s_app_page) * kPageBytesI8 + tile_j;
-            if (tid < 8) {
-                *reinterpret_cast<uint2 *>(tw + i8_pos(sl, tid * 8)) = *reinterpret_cast<const uint2 *>(&s_nk[tid * 8]);
-                *reinterpret_cast<uint2 *>(tw + kI8VOff + i8_pos(sl, tid * 8)) =
-                    *reinterpret_cast<const uint2 *>(&s_nv[tid * 8]);
-            } else {
-                *reinterpret_cast<float2 *>(tw + kI8ScOff + 8 * sl) = make_float2(s_nsc[0], s_nsc[1]);
+            if (tid < 4) {  // K unit 16*tid + sl: dims 8tid..+7 and 32+8tid..+7
+                const uint2 a = *reinterpret_cast<const uint2 *>(&s_nk[8 * tid]);
+                const uint2 b = *reinterpret_cast<const uint2 *>(&s_nk[32 + 8 * tid]);
+                *reinterpret_cast<u32x4 *>(tw + (16 * tid + sl) * 16) = u32x4{a.x, a.y, b.x, b.y};
+            } else if (tid >= 64 && tid < 128) {
+                const int d = tid - 64;
+                tw[i8_vpos(sl, d)] = static_cast<uint8_t>(s_nv[d]);
+            } else if (tid == 4) {
+                *reinterpret_cast<float *>(tw + kI8KScOff + 4 * sl) = s_nsc[0];
+                *reinterpret_cast<float *>(tw + kI8VScOff + 4 * sl) = s_nsc[1];
             }
         }
-        if (P.write_q && n_parts_s == 1 && tid >= 64 && tid < 96)
-            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 64) * 8) =
-                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 64) * 8]);
+        if (P.write_q && n_parts_s == 1 && tid >= 192 && tid < 224)
+            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 192) * 8) =
+                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 192) * 8]);
     }
-    // scale * log2(e) * <q, 128> of the lane's own score head: the offset the
-    // u = code + 128 encoding adds to every K score.  It goes through the same
-    // lane-permuted reduction as the scores (a key row of bf16 128.0s), so it
-    // lands on the lane that owns that head's score.
-    const u32x4 k128 = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
-    const float corr_k = page_score(qv, k128, k128, P.scale_log2);
 
-    auto load_page = [&](int p) {
-        return load_tile(__builtin_amdgcn_readlane(my_id, (p - pg0 - wu) / kWaves));
-    };
+    // ---- q as the f16 B operand of Q.K^T, scaled by 2^(15 - e) so that its
+    // largest element (over the 4 heads: every wave finds the same e) lies in
+    // [2^14, 2^15); the score then carries 2^(e - 15), folded into the scale.
+    float qf[16];
+    {
+        const uint32_t a[8] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w, qraw1.x, qraw1.y, qraw1.z, qraw1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            qf[2 * k] = bf16_lo(a[k]);
+            qf[2 * k + 1] = bf16_hi(a[k]);
+        }
+    }
+    float qmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qmax = fmaxf(qmax, fabsf(qf[k]));
+    qmax = max_groups(max_lanes8(qmax));
+    int qe = 0;
+    if (qmax > 0.0f) (void)frexpf(qmax, &qe);  // qmax in [2^(qe-1), 2^qe)
+    const int qshift = min(15 - qe, 126);       // (kept a finite fp32 power of two)
+    const float qscale = ldexpf(1.0f, qshift);
+    half8 qb0, qb1;
+    {
+        uint32_t h[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = pack_f16x2(qf[2 * k] * qscale, qf[2 * k + 1] * qscale);
+        qb0 = __builtin_bit_cast(half8, u32x4{h[0], h[1], h[2], h[3]});
+        qb1 = __builtin_bit_cast(half8, u32x4{h[4], h[5], h[6], h[7]});
+    }
+    // 1152 * <q', 1> for column hh: the offset the code encoding adds to a score
+    float corr;
+    {
+        const uint32_t c1152 = 0x64806480u;  // f16 1152.0 twice
+        const half8 k1152 = __builtin_bit_cast(half8, u32x4{c1152, c1152, c1152, c1152});
+        f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qb0, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qb1, z, 0, 0, 0);
+        corr = z[0];
+    }
+    const float sc_log2 = P.scale_log2 * ldexpf(1.0f, -qshift);
+
     int p = pg0 + wu;
 
-    float m_run = kNegBig;
-    float l_run = 0.0f;   // sum of the lane's own weights
-    float l2_run = 0.0f;  // sum of the lane's own weights times their V scales
-    float acc[kGroup][8];
+    float m_run = kNegBig;  // running max (log2 units) of head hh
+    float l_run = 0.0f;     // sum of 2^(x - m) over the lane's tokens
+    // acc[n]: O[head 4qd + r][dim 16n + hh] (rows 0-3, lanes 0-15, are the
+    // heads); acc[4]: the fed weights' sum of head 4qd + r (the 1152 offset)
+    f32x4 acc[5];
 #pragma unroll
-    for (int e = 0; e < kGroup; ++e)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[e][i] = 0.0f;
+    for (int n = 0; n < 5; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t one2 = 0x3C003C00u;  // f16 1.0 twice
+    const half4 ones = __builtin_bit_cast(half4, u32x2{one2, one2});
 
-    // One page; `last` pages may be partly empty (dead slots hold anything:
-    // their weight is forced to 0 before it meets a scale).
-    auto process = [&](const I8Regs &r, bool last, int p) {
-        const uint32_t kw0 = t0 ? r.k.z : r.k.x, kw1 = t0 ? r.k.w : r.k.y;
-        const uint32_t kw2 = t0 ? r.k.x : r.k.z, kw3 = t0 ? r.k.y : r.k.w;
-        const u32x4 ka = codes8_to_bf16(kw0, kw1);
-        const u32x4 kb = codes8_to_bf16(kw2, kw3);
-        float x = (page_score(qv, ka, kb, P.scale_log2) - corr_k) * r.sc.x;
-        bool dead = false;
+    auto process = [&](const I8Page &r, bool last, int p) {
+        // scores of tokens 4qd + i (i < 4) for column hh
+        f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(r.k.x, r.k.y), qb0, st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(r.k.z, r.k.w), qb1, st, 0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (st[i] - corr) * (r.ks[i] * sc_log2);
+        bool dead[4] = {false, false, false, false};
         if (last) {
-            dead = p * kPage + tok_s >= L;
-            if (dead) x = -INFINITY;
-        }
-        const float pw = softmax_step_t<true>(x, m_run, l_run, l2_run, acc);
-        float pv = pw * r.sc.y;
-        if (last && dead) pv = 0.0f;
-        l2_run += pv;
-        float va[8], vb[8];
-        const uint32_t vw0 = b2 ? r.v.z : r.v.x, vw1 = b2 ? r.v.w : r.v.y;
-        const uint32_t vw2 = b2 ? r.v.x : r.v.z, vw3 = b2 ? r.v.y : r.v.w;
-        codes8_to_f32(vw0, vw1, va);
-        codes8_to_f32(vw2, vw3, vb);
-        accumulate(pv, va, vb, acc);
-    };
-    auto process_last = [&](I8Regs r, int p) {
-        if (kFused) {  // patch the appended token's codes and scales into the registers
-            const int sl = pos & (kPage - 1);
-            if (g == (sl & 7)) {
-                const uint2 nk = *reinterpret_cast<const uint2 *>(&s_nk[c * 8]);
-                const uint2 nv = *reinterpret_cast<const uint2 *>(&s_nv[c * 8]);
-                if (sl >> 3) {
-                    r.k.z = nk.x; r.k.w = nk.y;
-                    r.v.z = nv.x; r.v.w = nv.y;
-                } else {
-                    r.k.x = nk.x; r.k.y = nk.y;
-                    r.v.x = nv.x; r.v.y = nv.y;
-                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dead[i] = p * kPage + 4 * qd + i >= L;
+                if (dead[i]) x[i] = -INFINITY;
             }
-            if (tok_s == sl) r.sc = make_float2(s_nsc[0], s_nsc[1]);
+        }
+        // lazy running max of head hh (uniform over the 4 lanes of column hh)
+        const float xm = max_quarters(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const bool need = xm > m_run + kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(need && head_lane)) {
+            const float mn = need ? xm : m_run;
+            const float f = fast_exp2(m_run - mn);
+            m_run = mn;
+            l_run *= f;
+            // accumulator row i of lanes 0-15 is head i: its factor is lane i's
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float fi = lane_value(f, i);
+#pragma unroll
+                for (int n = 0; n < 5; ++n) acc[n][i] *= fi;
+            }
+        }
+        float pw[4], pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pw[i] = fast_exp2(x[i] - m_run);
+            pv[i] = pw[i] * r.vs[i];
+            if (last && dead[i]) pv[i] = 0.0f;  // a dead slot's scale may be anything
+        }
+        l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+        // weights as an f16 pair hi + lo (lo = the rounding remainder of hi)
+        const uint32_t h01 = pack_f16x2(pv[0], pv[1]);
+        const uint32_t h23 = pack_f16x2(pv[2], pv[3]);
+        const half2v e01 = __builtin_bit_cast(half2v, h01), e23 = __builtin_bit_cast(half2v, h23);
+        const uint32_t l01 = pack_f16x2(pv[0] - static_cast<float>(e01[0]), pv[1] - static_cast<float>(e01[1]));
+        const uint32_t l23 = pack_f16x2(pv[2] - static_cast<float>(e23[0]), pv[3] - static_cast<float>(e23[1]));
+        const half4 ph = __builtin_bit_cast(half4, u32x2{h01, h23});
+        const half4 pl = __builtin_bit_cast(half4, u32x2{l01, l23});
+        const half4 vb[4] = {codes4_to_f16(r.v.x), codes4_to_f16(r.v.y), codes4_to_f16(r.v.z),
+                             codes4_to_f16(r.v.w)};
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb[n], acc[n], 0, 0, 0);
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb[n], acc[n], 0, 0, 0);
+        }
+        acc[4] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, ones, acc[4], 0, 0, 0);
+        acc[4] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, ones, acc[4], 0, 0, 0);
+    };
+    auto process_last = [&](I8Page r, int p) {
+        if (kFused) {  // patch the appended token's codes and scales into the registers
+            if (hh == sl) {
+                const uint2 a = *reinterpret_cast<const uint2 *>(&s_nk[8 * qd]);
+                const uint2 b = *reinterpret_cast<const uint2 *>(&s_nk[32 + 8 * qd]);
+                r.k = u32x4{a.x, a.y, b.x, b.y};
+            }
+            if ((sl >> 2) == qd) {
+                const int sh = 8 * (sl & 3);
+                const uint32_t keep = ~(0xFFu << sh);
+                r.v.x = (r.v.x & keep) | (static_cast<uint32_t>(static_cast<uint8_t>(s_nv[hh])) << sh);
+                r.v.y = (r.v.y & keep) | (static_cast<uint32_t>(static_cast<uint8_t>(s_nv[16 + hh])) << sh);
+                r.v.z = (r.v.z & keep) | (static_cast<uint32_t>(static_cast<uint8_t>(s_nv[32 + hh])) << sh);
+                r.v.w = (r.v.w & keep) | (static_cast<uint32_t>(static_cast<uint8_t>(s_nv[48 + hh])) << sh);
+                r.ks[sl & 3] = s_nsc[0];
+                r.vs[sl & 3] = s_nsc[1];
+            }
         }
         process(r, true, p);
     };
+    auto load_page = [&](int p) {
+        return load_tile(__builtin_amdgcn_readlane(my_id, (p - pg0 - wu) / kWaves));
+    };
     const int p_stop = (pg1 == n_pages) ? n_pages - 1 : pg1;
-    I8Regs alt;
+    I8Page alt;
     bool last_in_alt = false;
     const int span = pg1 - pg0;
     auto level = [&]() {
@@ -442,28 +568,17 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         if (last_in_alt) cur = alt;
         process_last(cur, p);
     }
-    // ---- wave epilogue (as the bf16 kernel, plus the V offset sum) ---------
-    float l_tot = l_run + dpp_f32<kXor1>(l_run);
-    l_tot = sum_groups(l_tot);
-    float l2_tot = l2_run + dpp_f32<kXor1>(l2_run);
-    l2_tot = sum_groups(l2_tot);
+    // ---- wave epilogue ---------------------------------------------------------
+    const float l_tot = sum_quarters(l_run);
+    if (lane < 16) {  // O minus 1152 x (sum of the fed weights), per head
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float a01 = swap32_sum(acc[0][i], acc[2][i]);
-        const float a11 = swap32_sum(acc[1][i], acc[3][i]);
-        float t = swap16_sum(a01, a11);
-        t += dpp_f32<kRowRor8>(t);
-        acc[0][i] = t;
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_acc[w][i][16 * n + hh] = fmaf(-kOffsetF16, acc[4][i], acc[n][i]);
     }
-    if ((g & 1) == 0) {
-        const int h = (g >> 1) ^ (3 * b2);
-        *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8]) = f32x4{acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
-        *reinterpret_cast<f32x4 *>(&s_acc[w][h][c * 8 + 4]) = f32x4{acc[0][4], acc[0][5], acc[0][6], acc[0][7]};
-    }
-    if (g == 0 && b0 == 0) {
-        s_m[w][hm] = m_run;
-        s_l[w][hm] = l_tot;
-        s_l2[w][hm] = l2_tot;
+    if (lane < kGroup) {
+        s_m[w][lane] = m_run;
+        s_l[w][lane] = l_tot;
     }
     __syncthreads();
 
@@ -478,7 +593,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         for (int k = 0; k < kWaves; ++k) {
             const float wgt = fast_exp2(s_m[k][h] - M);
             Ls = fmaf(wgt, s_l[k][h], Ls);
-            A = fmaf(wgt, fmaf(-128.0f, s_l2[k][h], s_acc[k][h][d]), A);
+            A = fmaf(wgt, s_acc[k][h][d], A);
         }
         const int qh = j * kGroup + h;
         if (n_parts_s == 1) {
