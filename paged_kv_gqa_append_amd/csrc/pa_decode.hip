@@ -195,20 +195,6 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     if (kFused) {
 #pragma unroll
         for (int m = 0; m < kGroup; ++m) qv[m] = *reinterpret_cast<const u32x4 *>(&s_q[m ^ hm][c * 8]);
-        // Append: the new row goes into its slot now that the sequence is known
-        // good (last partition only; nothing in this kernel reads the slot back).
-        if (tid < 8 && pg1 == n_pages) {
-            const int64_t dst = static_cast<int64_t>(s_app_page) * kPageElems + tile_j +
-                                (pos & (kPage - 1)) * kD + c * 8;
-            *reinterpret_cast<u32x4 *>(P.k_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newk[c * 8]);
-            *reinterpret_cast<u32x4 *>(P.v_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newv[c * 8]);
-        }
-        // The rotated q can be stored now: this workgroup's raw q loads completed
-        // before the rotation, and with one partition no other workgroup reads
-        // these rows (longer contexts leave it to k_decode_merge).
-        if (P.write_q && n_parts_s == 1 && tid >= 64 && tid < 96)
-            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 64) * 8) =
-                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 64) * 8]);
     }
     auto load_page = [&](int p) {
         return load_tile(__builtin_amdgcn_readlane(my_id, (p - pg0 - wu) / kWaves));
@@ -343,6 +329,24 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
                 P.ws_ml[row * 2 + 1] = Ls;
             }
         }
+    }
+    if (kFused) {
+        // The appended row and the rotated q are stored last.  Nothing in this
+        // kernel reads them back (the loop took the new token from LDS), and a
+        // store issued ahead of the page loads would hold up the wave's first
+        // wait for page data, since vector memory operations complete in order.
+        // Append: last partition only (the sequence is known good here).
+        if (tid < 8 && pg1 == n_pages) {
+            const int64_t dst = static_cast<int64_t>(s_app_page) * kPageElems + tile_j +
+                                (pos & (kPage - 1)) * kD + c * 8;
+            *reinterpret_cast<u32x4 *>(P.k_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newk[c * 8]);
+            *reinterpret_cast<u32x4 *>(P.v_pool + dst) = *reinterpret_cast<const u32x4 *>(&s_newv[c * 8]);
+        }
+        // With one partition no other workgroup reads these q rows (longer
+        // contexts leave the rotated q to k_decode_merge).
+        if (P.write_q && n_parts_s == 1 && tid >= 64 && tid < 96)
+            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 64) * 8) =
+                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 64) * 8]);
     }
 }
 

@@ -391,23 +391,6 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
             qraw0 = *reinterpret_cast<const u32x4 *>(&s_q[hh][8 * qd]);
             qraw1 = *reinterpret_cast<const u32x4 *>(&s_q[hh][32 + 8 * qd]);
         }
-        if (pg1 == n_pages) {  // append the quantised row (last partition only)
-            uint8_t *tw = const_cast<uint8_t *>(pool) + static_cast<int64_t>(s_app_page) * kPageBytesI8 + tile_j;
-            if (tid < 4) {  // K unit 16*tid + sl: dims 8tid..+7 and 32+8tid..+7
-                const uint2 a = *reinterpret_cast<const uint2 *>(&s_nk[8 * tid]);
-                const uint2 b = *reinterpret_cast<const uint2 *>(&s_nk[32 + 8 * tid]);
-                *reinterpret_cast<u32x4 *>(tw + (16 * tid + sl) * 16) = u32x4{a.x, a.y, b.x, b.y};
-            } else if (tid >= 64 && tid < 128) {
-                const int d = tid - 64;
-                tw[i8_vpos(sl, d)] = static_cast<uint8_t>(s_nv[d]);
-            } else if (tid == 4) {
-                *reinterpret_cast<float *>(tw + kI8KScOff + 4 * sl) = s_nsc[0];
-                *reinterpret_cast<float *>(tw + kI8VScOff + 4 * sl) = s_nsc[1];
-            }
-        }
-        if (P.write_q && n_parts_s == 1 && tid >= 192 && tid < 224)
-            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 192) * 8) =
-                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 192) * 8]);
     }
 
     // ---- q as the f16 B operand of Q.K^T, scaled by 2^(15 - e) so that its
@@ -609,6 +592,29 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
                 P.ws_ml[row * 2 + 1] = Ls;
             }
         }
+    }
+    if (kFused) {
+        // The appended row and the rotated q are stored last: nothing in this
+        // kernel reads them back (the last page's registers were patched from
+        // LDS), and stores issued ahead of the page loads would hold up the
+        // wave's first wait for page data (vector memory completes in order).
+        if (pg1 == n_pages) {  // append the quantised row (last partition only)
+            uint8_t *tw = const_cast<uint8_t *>(pool) + static_cast<int64_t>(s_app_page) * kPageBytesI8 + tile_j;
+            if (tid < 4) {  // K unit 16*tid + sl: dims 8tid..+7 and 32+8tid..+7
+                const uint2 a = *reinterpret_cast<const uint2 *>(&s_nk[8 * tid]);
+                const uint2 b = *reinterpret_cast<const uint2 *>(&s_nk[32 + 8 * tid]);
+                *reinterpret_cast<u32x4 *>(tw + (16 * tid + sl) * 16) = u32x4{a.x, a.y, b.x, b.y};
+            } else if (tid >= 64 && tid < 128) {
+                const int d = tid - 64;
+                tw[i8_vpos(sl, d)] = static_cast<uint8_t>(s_nv[d]);
+            } else if (tid == 4) {
+                *reinterpret_cast<float *>(tw + kI8KScOff + 4 * sl) = s_nsc[0];
+                *reinterpret_cast<float *>(tw + kI8VScOff + 4 * sl) = s_nsc[1];
+            }
+        }
+        if (P.write_q && n_parts_s == 1 && tid >= 192 && tid < 224)
+            *reinterpret_cast<u32x4 *>(P.q + qrow0 + (tid - 192) * 8) =
+                *reinterpret_cast<const u32x4 *>(&s_q[0][(tid - 192) * 8]);
     }
 }
 
