@@ -189,12 +189,15 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
  * store), V rows from their bf16 input.
  *
  *   kv_pool_i8 : [num_pages][8 kv heads] tiles of PA_I8_TILE_BYTES = 2176 bytes,
- *                K and V together (there is no separate V pool):
- *                  bytes [0, 1024)    K codes (int8), [1024, 2048) V codes,
- *                  2048 + 8t          K scale (fp32) of slot t, 2052 + 8t its V scale,
- *                code of element d of slot t at byte ((t%8)*8 + d/8)*16 + (t/8)*8 + d%8
- *                of its 1 KiB block.  A token costs 8 x 136 = 1088 bytes per layer,
- *                against 2048 in bf16.
+ *                K and V together (there is no separate V pool); for slot t
+ *                (0..15) and element d (0..63) of the row:
+ *                  K code at byte ((d%32)/8*16 + t)*16 + (d/32)*8 + d%8
+ *                    (sixteen-byte units ordered by dim quarter, then token),
+ *                  V code at byte 1024 + ((t/4)*16 + d%16)*16 + (d/16)*4 + t%4
+ *                    (units ordered by token quad, then dim mod 16),
+ *                  K scale (fp32) at byte 2048 + 4t, V scale at 2112 + 4t.
+ *                A token costs 8 x 136 = 1088 bytes per layer, against 2048 in
+ *                bf16.
  * Block tables, lengths, q, k_new, v_new, the RoPE table, out, workspace and
  * device_flags mean exactly what they mean for the bf16 calls above; the decode
  * workspace is sized by pa_decode_workspace_bytes.                           */
