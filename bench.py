@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC = {
     "bf16": (("pa_decode.hip", "pa_decode_core.h", "pa_device.h"), "decode_batch64_pmc_traffic.md"),
     "int8": (("pa_i8.hip", "pa_decode_core.h", "pa_device.h"), "decode_batch64_i8_pmc_traffic.md"),
+    "argmax": (("pa_argmax.hip", "pa_device.h"), "argmax_batch64_pmc_traffic.md"),
 }
 # K+V bytes per (token, layer): 8 heads x 2 x 64 x 2 B in bf16; 8 tiles' share (2176 B / 16 slots) in INT8
 KV_TOKEN_BYTES = {"bf16": 2048, "int8": 8 * 2176 // 16}
@@ -317,11 +318,12 @@ def main_argmax(args, torch, binding, device):
         "warmup": args.warmup, "ms_per_step": round(us * calls_per_step * 1e-3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "argmax_batch64", "rows": rows, "vocab": vocab,
-                   "step": f"{calls_per_step} x pa_argmax (k_argmax_chunk + k_argmax_final)"},
+                   "step": f"{calls_per_step} x pa_argmax (k_argmax, one launch per call)"},
         "us_per_call": round(us, 3),
-        "roofline": {"bound": "hbm", "kernel": "k_argmax_chunk<bf16,vec> + k_argmax_final, one call",
+        "roofline": {"bound": "hbm", "kernel": "k_argmax<bf16,vec>, one launch per call",
                      "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("argmax"),
+                     "bytes_per_launch": nbytes,
                      "mean_launch_us": round(us, 3)},
     }
     if not args.no_cpu_baseline:

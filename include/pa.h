@@ -253,9 +253,15 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
  *            16-byte boundaries with a 16-byte multiple of bytes take the
  *            vector path, any other layout a scalar one (same results).
  *   out_index : [num_rows] int32, device.
- *   workspace : pa_argmax_workspace_bytes(num_rows, vocab, logits_dtype) bytes,
- *            8-byte aligned (may be NULL when that is 0); contents dead between
- *            calls.  Stream-ordered, no synchronisation, nothing allocated.
+ *   workspace : pa_argmax_workspace_bytes(num_rows, vocab, logits_dtype) bytes
+ *            (16 per row when a row spans more than one chunk, else 0),
+ *            8-byte aligned, may be NULL when that is 0.  It must be all zero
+ *            before its first use; every call that returns PA_OK leaves it all
+ *            zero again once its kernel has finished (the last chunk of each
+ *            row resets the row's words), so a workspace is zeroed once, at
+ *            allocation.  Calls sharing one workspace must not overlap in time
+ *            (same stream, or ordered by the caller).  Stream-ordered, one
+ *            launch, no synchronisation, nothing allocated.
  *   Errors: PA_ERR_UNSUPPORTED for another dtype or more than 65535 rows.     */
 typedef enum { PA_LOGITS_BF16 = 0, PA_LOGITS_FP32 = 1 } pa_logits_dtype;
 

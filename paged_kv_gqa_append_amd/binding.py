@@ -427,7 +427,8 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
 def argmax_workspace(num_rows: int, vocab: int, dtype: torch.dtype, device="cuda") -> Optional[torch.Tensor]:
     code = PA_LOGITS_BF16 if dtype == torch.bfloat16 else PA_LOGITS_FP32
     n = int(lib().pa_argmax_workspace_bytes(int(num_rows), int(vocab), code))
-    return None if n == 0 else torch.empty(n // 8, dtype=torch.int64, device=device)
+    # zeroed once here; every pa_argmax call leaves it zeroed again
+    return None if n == 0 else torch.zeros(n // 8, dtype=torch.int64, device=device)
 
 
 def argmax(out_index: torch.Tensor, logits: torch.Tensor, workspace: Optional[torch.Tensor] = None,

@@ -86,7 +86,7 @@ const char *pa_status_string(int status) {
     }
 }
 
-int32_t pa_abi_version(void) { return 4; }
+int32_t pa_abi_version(void) { return 5; }
 
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
@@ -231,7 +231,8 @@ size_t pa_argmax_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t logits
     if (num_rows < 1 || vocab < 1 || (logits_dtype != PA_LOGITS_BF16 && logits_dtype != PA_LOGITS_FP32)) return 0;
     const int64_t chunk = pa::argmax_chunk_elems(logits_dtype == PA_LOGITS_BF16);
     const int64_t splits = (static_cast<int64_t>(vocab) + chunk - 1) / chunk;
-    return splits <= 1 ? 0 : static_cast<size_t>(num_rows) * static_cast<size_t>(splits) * sizeof(uint64_t);
+    // Per row: the running key and the arrival count, one 64-bit word each.
+    return splits <= 1 ? 0 : static_cast<size_t>(num_rows) * 2 * sizeof(uint64_t);
 }
 
 pa_status pa_argmax(int32_t *out_index, const void *logits, int32_t num_rows, int32_t vocab, int32_t logits_dtype,

@@ -14,7 +14,10 @@
 // a thread indices only grow, so a strict > keeps the first maximum.  Threads,
 // waves and chunks then combine (value, index) pairs through a 64-bit key
 // that orders by value first and by lower index second.  Rows longer than
-// one chunk leave one key per chunk in the workspace for k_argmax_final.
+// one chunk fold each chunk's key into the row's word of the workspace with an
+// atomic max; the chunk that arrives last (an arrival count beside the key)
+// writes the index and sets both words back to zero, so one launch does the
+// whole call and the workspace is left as it was found.
 #include <math.h>
 
 #include "pa_device.h"
@@ -72,10 +75,12 @@ __device__ __forceinline__ float load_scalar(const void *p, int64_t k) {
 
 // grid (splits, rows).  kVec: every row starts 16-byte aligned and holds a
 // whole number of 16-byte vectors, and chunk is a multiple of 256 vectors.
+// ws (splits > 1): per row a running key and an arrival count, both zero on
+// entry and zero again once the row's last chunk has finished.
 template <bool kBF16, bool kVec>
-__global__ __launch_bounds__(kArgThreads) void k_argmax_chunk(const void *__restrict__ logits, int vocab, int chunk,
-                                                             int splits, uint64_t *__restrict__ partials,
-                                                             int32_t *__restrict__ out) {
+__global__ __launch_bounds__(kArgThreads) void k_argmax(const void *__restrict__ logits, int vocab, int chunk,
+                                                       int splits, uint64_t *__restrict__ ws,
+                                                       int32_t *__restrict__ out) {
     constexpr int E = kBF16 ? 8 : 4;  // elements per 16-byte vector
     const int split = blockIdx.x;
     const int row = blockIdx.y;
@@ -119,22 +124,32 @@ __global__ __launch_bounds__(kArgThreads) void k_argmax_chunk(const void *__rest
     __shared__ uint64_t s_key[kArgThreads / 64];
     if ((tid & 63) == 0) s_key[tid >> 6] = key;
     __syncthreads();
-    if (tid == 0) {
+    if (tid != 0) return;
 #pragma unroll
-        for (int w = 1; w < kArgThreads / 64; ++w) key = max_u64(key, s_key[w]);
-        if (splits == 1) out[row] = unpack_index(key);
-        else partials[static_cast<int64_t>(row) * splits + split] = key;
+    for (int w = 1; w < kArgThreads / 64; ++w) key = max_u64(key, s_key[w]);
+    if (splits == 1) {
+        out[row] = unpack_index(key);
+        return;
     }
-}
-
-// One wave per row: combine the row's chunk keys.
-__global__ __launch_bounds__(64) void k_argmax_final(const uint64_t *__restrict__ partials, int splits,
-                                                     int32_t *__restrict__ out) {
-    const int row = blockIdx.x;
-    uint64_t key = 0;
-    for (int k = threadIdx.x; k < splits; k += 64) key = max_u64(key, partials[static_cast<int64_t>(row) * splits + k]);
-    key = wave_max_u64(key);
-    if (threadIdx.x == 0) out[row] = unpack_index(key);
+    uint64_t *row_key = ws + 2 * static_cast<int64_t>(row);
+    uint64_t *row_count = row_key + 1;
+    // Ordering without cache maintenance.  Every access to the row's two
+    // words is an agent-scope atomic read-modify-write, so each is performed at
+    // the one point where that address is kept coherent for all XCDs.  The
+    // arrival is not issued until the max has returned its old value (the
+    // increment is computed from it; no key is all ones), so the max has been
+    // performed first.  The last arrival sees every other arrival performed,
+    // hence every maximum, before it reads and clears the key.  An agent-scope
+    // release/acquire pair would say the same to the compiler, but it writes
+    // back and invalidates the whole L2 in every workgroup (a third slower).
+    const uint64_t prev = __hip_atomic_fetch_max(row_key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t before =
+        __hip_atomic_fetch_add(row_count, prev == ~0ull ? 2ull : 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == static_cast<uint64_t>(splits - 1)) {
+        const uint64_t row_best = __hip_atomic_exchange(row_key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_exchange(row_count, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        out[row] = unpack_index(row_best);
+    }
 }
 
 int argmax_chunk_elems(bool bf16) { return kArgThreads * kArgLoads * (bf16 ? 8 : 4); }
@@ -144,18 +159,15 @@ hipError_t launch_argmax(int32_t *out, const void *logits, int rows, int vocab, 
     if (rows == 0) return hipSuccess;
     const int chunk = argmax_chunk_elems(bf16);
     const int splits = (vocab + chunk - 1) / chunk;
-    uint64_t *partials = static_cast<uint64_t *>(workspace);
+    uint64_t *ws = static_cast<uint64_t *>(workspace);
     const dim3 grid(static_cast<unsigned>(splits), static_cast<unsigned>(rows));
     if (bf16) {
-        if (vec) hipLaunchKernelGGL((k_argmax_chunk<true, true>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, partials, out);
-        else hipLaunchKernelGGL((k_argmax_chunk<true, false>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, partials, out);
+        if (vec) hipLaunchKernelGGL((k_argmax<true, true>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, ws, out);
+        else hipLaunchKernelGGL((k_argmax<true, false>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, ws, out);
     } else {
-        if (vec) hipLaunchKernelGGL((k_argmax_chunk<false, true>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, partials, out);
-        else hipLaunchKernelGGL((k_argmax_chunk<false, false>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, partials, out);
+        if (vec) hipLaunchKernelGGL((k_argmax<false, true>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, ws, out);
+        else hipLaunchKernelGGL((k_argmax<false, false>), grid, dim3(kArgThreads), 0, stream, logits, vocab, chunk, splits, ws, out);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    hipLaunchKernelGGL(k_argmax_final, dim3(static_cast<unsigned>(rows)), dim3(64), 0, stream, partials, splits, out);
     return hipGetLastError();
 }
 

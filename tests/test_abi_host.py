@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == 4
+    assert pa.lib().pa_abi_version() == 5
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -168,8 +168,9 @@ def test_argmax_validation(pa):
     v = ctypes.c_void_p
     F = v(FAKE)
     chunk_bf16, chunk_fp32 = 256 * 8 * 8, 256 * 8 * 4
-    assert lib.pa_argmax_workspace_bytes(64, 128256, 0) == 64 * (-(-128256 // chunk_bf16)) * 8
-    assert lib.pa_argmax_workspace_bytes(64, 128256, 1) == 64 * (-(-128256 // chunk_fp32)) * 8
+    assert -(-128256 // chunk_bf16) > 1 and -(-128256 // chunk_fp32) > 1
+    assert lib.pa_argmax_workspace_bytes(64, 128256, 0) == 64 * 16      # per row: running key + arrival count
+    assert lib.pa_argmax_workspace_bytes(64, 128256, 1) == 64 * 16
     assert lib.pa_argmax_workspace_bytes(5, chunk_bf16, 0) == 0          # one chunk per row: no workspace
     assert lib.pa_argmax_workspace_bytes(5, 100, 2) == 0
 

@@ -62,3 +62,28 @@ def test_argmax_bf16_ties_from_rounding():
         x[r, pos] = 9.0 + rng.uniform(0, 0.01, 5).astype(np.float32)   # one bf16 value after rounding
     got, ref = run(x, torch.bfloat16)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_argmax_workspace_reused_and_left_zero(dtype):
+    """One workspace, zeroed once, serves calls of shrinking size back to back on
+    one stream: every call matches the oracle and the workspace ends all zero
+    (the last chunk of each row resets the row's key and arrival count)."""
+    rows0, vocab0 = 40, W.VOCAB_SIZE
+    ws = binding.argmax_workspace(rows0, vocab0, dtype, dev())
+    assert ws is not None and ws.numel() == 2 * rows0
+    for k, (rows, vocab) in enumerate([(40, W.VOCAB_SIZE), (40, W.VOCAB_SIZE), (17, 70001), (3, 16385)]):
+        print(f"argmax reuse call {k}: rows={rows} vocab={vocab} dtype={dtype}", flush=True)
+        x = W.argmax_logits(93 + k, rows, vocab)
+        if dtype == torch.bfloat16:
+            host = W.f32_to_bf16_bits(x)
+            logits = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).to(dev())
+            ref = oracle.argmax(host)
+        else:
+            logits = torch.from_numpy(x).to(dev())
+            ref = oracle.argmax(x)
+        out = torch.full((rows,), -7, dtype=torch.int32, device=dev())
+        binding.argmax(out, logits, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), f"call {k}"
+        assert int(torch.count_nonzero(ws)) == 0, f"workspace not reset after call {k}"
