@@ -251,7 +251,7 @@ __device__ __forceinline__ float max_quarters(float v) {
     return fmaxf(lo, hi);
 }
 
-template <int kWaves, bool kFused>
+template <int kWaves, bool kFused, bool kNt>
 __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
@@ -323,8 +323,15 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     auto load_tile = [&](int page_id) {
         const uint8_t *t = pool + static_cast<int64_t>(page_id) * kPageBytesI8 + tile_j;
         I8Page r;
-        r.k = *reinterpret_cast<const u32x4 *>(t + lane * 16);
-        r.v = *reinterpret_cast<const u32x4 *>(t + kI8VOff + lane * 16);
+        // kNt: the 2 KiB of codes are read with the non-temporal hint, the
+        // scales without (the host picks it by grid size; see launch_decode_i8).
+        if (kNt) {
+            r.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(t + lane * 16));
+            r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(t + kI8VOff + lane * 16));
+        } else {
+            r.k = *reinterpret_cast<const u32x4 *>(t + lane * 16);
+            r.v = *reinterpret_cast<const u32x4 *>(t + kI8VOff + lane * 16);
+        }
         r.ks = *reinterpret_cast<const f32x4 *>(t + kI8KScOff + qd * 16);
         r.vs = *reinterpret_cast<const f32x4 *>(t + kI8VScOff + qd * 16);
         return r;
@@ -662,12 +669,20 @@ hipError_t launch_decode_i8(const DecodeLaunch &d, hipStream_t stream) {
     P.ws_acc = d.ws_acc;
     P.flags = d.flags;
     const int64_t blocks = static_cast<int64_t>(d.num_seqs) * kHKV * d.num_parts;
-    if (d.fused)
-        hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(64 * kDecodeWavesI8), 0, stream, P);
-    else
-        hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(64 * kDecodeWavesI8), 0, stream, P);
+    // The non-temporal hint on the codes, by grid size, as measured on MI355X
+    // (fused step): from 128 workgroups up (uniform 2048-token batches of 16 to
+    // 128 sequences, 256 x 512 tokens, the ragged 256-sequence batch) it is
+    // 0-10 % faster, never slower; with 64 workgroups (few long, latency-bound
+    // streams) it is 14 % slower.  Hinting the scales as well gains nothing.
+    const bool nt = blocks >= kNtMinBlocks;
+    const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWavesI8);
+    if (d.fused) {
+        if (nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, true>), grid, wg, 0, stream, P);
+        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, false>), grid, wg, 0, stream, P);
+    } else {
+        if (nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, true>), grid, wg, 0, stream, P);
+        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, false>), grid, wg, 0, stream, P);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.num_parts == 1) return e;
     if (d.fused)
