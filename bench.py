@@ -457,8 +457,8 @@ def main():
         "kv_bytes_per_step": kv_step,
         ("separate_calls_ms_per_step" if args.path == "fused" else "fused_ms_per_step"): round(other_ms, 5),
         "roofline": {"bound": "hbm",
-                     "kernel": ("k_decode_paged_i8<8,true> (pa_append_decode_gqa_i8)" if i8 else
-                                "k_decode_paged<8,true> (pa_append_decode_gqa)"),
+                     "kernel": ("k_decode_paged_i8<8,true,nt> (pa_append_decode_gqa_i8)" if i8 else
+                                "k_decode_paged<8,true,nt> (pa_append_decode_gqa)"),
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.kv) if args.config == "batch64" else None,
