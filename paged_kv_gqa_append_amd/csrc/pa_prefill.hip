@@ -53,7 +53,7 @@ constexpr int kRows = 64;                   // chunk positions per workgroup
 constexpr int kKB = 32;                     // keys per block
 constexpr int kKStride = 72;                // bf16 per K row in LDS (64 + 8 pad: conflict-free fragment reads)
 constexpr int kKBuf = kKB * kKStride;       // bf16 per K buffer
-constexpr int kVBuf = kD * kKB / 2;         // 32-bit words per V^T buffer (64 rows x 32 key slots)
+constexpr int kVBuf = kD * 20;              // 32-bit words per V^T buffer (64 rows of 5 units)
 constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -86,10 +86,12 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // 16b + 4g + {0..3, 8..11}; with this order they sit in slots 16b + 8g .. +7.
 __device__ __forceinline__ int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-// 16-byte unit of V^T row d (0..63) that holds slot chunk ch (slots 8ch..8ch+7),
-// XOR-swizzled by the row so that the 8 rows one LDS phase reads fall in
-// distinct banks.
-__device__ __forceinline__ int vt_unit(int d, int ch) { return d * 4 + (ch ^ (((d >> 1) ^ (d >> 3)) & 3)); }
+// 16-byte unit of V^T row d (0..63) that holds slot chunk ch (slots 8ch..8ch+7).
+// Rows are 5 units apart (one unit of padding): the MFMA fragment reads (16
+// consecutive rows, one unit each) then fall in distinct banks, and the
+// transposing stores (4 rows 8 apart, 16 words each, per instruction) meet at
+// most two to a bank instead of four.
+__device__ __forceinline__ int vt_unit(int d, int ch) { return d * 5 + ch; }
 
 // acc + the sum of the 8 bf16 weights (dot2 against (1, 1): exact products,
 // fp32 sums), as two independent chains.
@@ -444,14 +446,29 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
     store_block(sa, s_k0, s_v0);
     __syncthreads();
     sa = load_block(2);
+    // Within one barrier interval the staging of the next block and the use of
+    // the current one are independent, so the two key halves take them in
+    // opposite orders: the second half's MFMAs then start while the first
+    // half's waves (which share its SIMDs) are in their softmax, instead of
+    // both halves contending for the MFMA unit and then for the VALU.
     for (int kbl = 0;; kbl += 2) {
-        attend(kbl, s_k0, s_v0);
-        store_block(sb, s_k1, s_v1);
+        if (kh == 0) {
+            attend(kbl, s_k0, s_v0);
+            store_block(sb, s_k1, s_v1);
+        } else {
+            store_block(sb, s_k1, s_v1);
+            attend(kbl, s_k0, s_v0);
+        }
         __syncthreads();
         if (kbl + 1 >= nb0) break;
         sb = load_block(kbl + 3);
-        attend(kbl + 1, s_k1, s_v1);
-        store_block(sa, s_k0, s_v0);
+        if (kh == 0) {
+            attend(kbl + 1, s_k1, s_v1);
+            store_block(sa, s_k0, s_v0);
+        } else {
+            store_block(sa, s_k0, s_v0);
+            attend(kbl + 1, s_k1, s_v1);
+        }
         __syncthreads();
         if (kbl + 2 >= nb0) break;
         sa = load_block(kbl + 4);
