@@ -14,9 +14,11 @@ HBM before timing starts.
 Prints ONE JSON line.  value = algorithmic KV bytes read per step (tokens
 attended x 2048 B x layers) / step time, in GB/s; tokens/s = sequences /
 step time.  The roofline object reports the decode kernel alone: its
-algorithmic bytes per launch over its mean duration from HIP events recorded
-around each launch, on the stream it runs on.  cpu_baseline times the fp64
-CPU oracle (append + decode) on a bounded sample of the same workload.
+algorithmic bytes per launch over its mean duration, from the HIP events that
+bracket the timed steps on the stream it runs on (the fused step is nothing
+but that kernel, once per layer).  Warmup runs until the GPU's clocks have
+settled (100 ms of work unless --warmup is given).  cpu_baseline times the
+fp64 CPU oracle (append + decode) on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -45,7 +47,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps; by default, steps until 100 ms of work have run (at least 5), "
+                         "since the GPU's clocks take about 10-20 ms of sustained load to settle")
     ap.add_argument("--config", default="batch64",
                     choices=["batch64", "batch256", "batch8", "tiny", "prefill", "argmax"],
                     help="decode workloads, 'prefill': 4 x (1536 cached + 512-token chunk) chunked prefill, or "
@@ -94,6 +98,35 @@ def build_workload(name, device):
                            out=torch.empty((spec.num_seqs, 32, 64), dtype=torch.bfloat16, device=device)))
     lens = torch.from_numpy(spec.context_lens).to(device)
     return spec, k_pool, v_pool, layers, lens, rows
+
+
+def warm_up(fn, torch, n):
+    """Run fn untimed n times, or (n None) in rounds of 5 until 100 ms have passed; the count run."""
+    if n is not None:
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return n
+    t0, k = time.perf_counter(), 0
+    while True:
+        for _ in range(5):
+            fn()
+        k += 5
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= 0.1:
+            return k
+
+
+def host_cpu_model():
+    """The host CPU's model name, as /proc/cpuinfo gives it (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def measured_traffic(kv="bf16"):
@@ -173,7 +206,7 @@ def cpu_baseline(spec, k_pool, v_pool, rows, target_s, kv="bf16"):
             break
     kv_bytes = total_tokens * KV_TOKEN_BYTES[kv]
     return {"value": round(kv_bytes / total_dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(total_dt, 3),
+            "cpu_model": host_cpu_model(), "kind": "oracle", "seconds": round(total_dt, 3),
             "tokens_per_s": round(B * layers_done / spec.num_layers / total_dt, 3),
             "sample": f"fp64 oracle {'INT8 ' if kv == 'int8' else ''}append + decode of all {B} sequences for "
                       f"{layers_done} of the "
@@ -212,7 +245,7 @@ def cpu_baseline_prefill(case, target_s):
         if total >= target_s:
             break
     return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(total, 3),
+            "cpu_model": host_cpu_model(), "kind": "oracle", "seconds": round(total, 3),
             "sample": f"fp64 oracle chunked prefill (append + causal attention) of {done} of the {case.num_seqs} "
                       f"sequences of the workload ({flops} algorithmic flops)"}
 
@@ -240,9 +273,7 @@ def main_prefill(args, torch, binding, device):
     def step():
         binding.prefill_chunk(out, q, kc, vc, kp, vp, bt, prefix, table, c.scale, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(step, torch, args.warmup)
     calls = []
     for _ in range(args.steps):
         a = torch.cuda.Event(enable_timing=True)
@@ -258,7 +289,7 @@ def main_prefill(args, torch, binding, device):
     tflops = flops / (ms * 1e-3) / 1e12
     res = {
         "metric": PREFILL_METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": warm, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "chunked_prefill", "num_seqs": c.num_seqs, "prefix_len": int(c.prefix_lens[0]),
@@ -299,9 +330,7 @@ def main_argmax(args, torch, binding, device):
         for _ in range(calls_per_step):
             binding.argmax(out, logits, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(step, torch, args.warmup)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record(stream)
@@ -315,7 +344,7 @@ def main_argmax(args, torch, binding, device):
     gbps = nbytes / (us * 1e-6) / 1e9
     res = {
         "metric": ARGMAX_METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(us * calls_per_step * 1e-3, 5), "higher_is_better": True,
+        "warmup": warm, "ms_per_step": round(us * calls_per_step * 1e-3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "argmax_batch64", "rows": rows, "vocab": vocab,
                    "step": f"{calls_per_step} x pa_argmax (k_argmax, one launch per call)"},
@@ -332,7 +361,8 @@ def main_argmax(args, torch, binding, device):
             oracle.argmax(host)
             reps += 1
         dt = (time.perf_counter() - t0) / reps
-        res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        res["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "cpu_model": host_cpu_model(), "kind": "oracle",
                                "seconds": round(dt * reps, 3),
                                "sample": f"fp64-compare oracle argmax over the same {rows} x {vocab} bf16 rows, "
                                          f"{reps} repetitions, one thread"}
@@ -403,9 +433,7 @@ def main():
                                    stream=stream)
 
     def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm = warm_up(fn, torch, warmup)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
@@ -413,35 +441,62 @@ def main():
             fn()
         t1.record(stream)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        return t0.elapsed_time(t1) / steps, warm
 
     step = step_fused if args.path == "fused" else step_separate
-    ms = timed(step, args.steps, args.warmup)
-    other_ms = timed(step_separate if args.path == "fused" else step_fused, max(3, args.steps // 2), 2)
+    ms, warm = timed(step, args.steps, args.warmup)
+    other_ms = timed(step_separate if args.path == "fused" else step_fused, max(3, args.steps // 2), 2)[0]
 
-    # Kernel duration for the roofline: HIP events on the launch stream around
-    # each layer sequence of 16 back-to-back fused launches (a pass of its own,
-    # so the events do not perturb the step time above); mean per launch =
-    # elapsed / 16, which includes the gaps between launches.
+    # Kernel duration for the roofline.  With the fused path the timed region above is
+    # nothing but the fused kernel, num_layers launches per step back to back on the
+    # launch stream, so its mean per launch (gaps included) is ms / num_layers.  With the
+    # separate path the fused kernel is timed the same way in a pass of its own.
+    n_pass = max(3, args.steps // 2)
+    if args.path == "fused":
+        dec_ms_mean = ms / spec.num_layers
+    else:
+        dec_ms_mean = timed(step_fused, n_pass, 1)[0] / spec.num_layers
+    # Median per launch: one event pair per step of a further pass (steps of many launches
+    # only, where the events' own cost is small against the step).
     seq_ms = []
-    for _ in range(max(3, args.steps // 2)):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        step_fused()
-        b.record(stream)
-        torch.cuda.synchronize()
-        seq_ms.append(a.elapsed_time(b))
-    dec_ms_mean = float(np.mean(seq_ms)) / spec.num_layers
+    if spec.num_layers > 1:
+        for _ in range(n_pass):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step_fused()
+            b.record(stream)
+            torch.cuda.synchronize()
+            seq_ms.append(a.elapsed_time(b))
 
-    kv_step = spec.kv_bytes() // 2048 * KV_TOKEN_BYTES[args.kv]
+    # Cold runs for workloads whose K/V fit in the 256 MB MALL (Infinity Cache): before each
+    # timed step, outside its events, 512 MiB are written so the step starts from HBM.
+    kv_step_bytes = spec.kv_bytes() // 2048 * KV_TOKEN_BYTES[args.kv]
+    cold_ms = None
+    if kv_step_bytes < (512 << 20):
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=device)
+        cold = []
+        for i in range(max(5, args.steps // 2)):
+            flush.fill_(i & 0xFF)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        cold_ms = float(np.median(cold))
+        del flush
+
+    kv_step = kv_step_bytes
     kv_launch = kv_step // spec.num_layers
     gbps = kv_step / (ms * 1e-3) / 1e9
     dec_gbps = kv_launch / (dec_ms_mean * 1e-3) / 1e9
     sfx = "_i8" if i8 else ""
     res = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": warm, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if not i8 else "int8 K/V, bf16 q/out, fp32 accumulation",
         "data": "synthetic",
         "config": {"workload": spec.name, "num_seqs": spec.num_seqs, "context_len": int(spec.context_lens.max()),
@@ -462,8 +517,15 @@ def main():
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.kv) if args.config == "batch64" else None,
-                     "bytes_per_launch": kv_launch, "mean_launch_us": round(dec_ms_mean * 1e3, 2)},
+                     "bytes_per_launch": kv_launch, "mean_launch_us": round(dec_ms_mean * 1e3, 2),
+                     "median_launch_us": (round(float(np.median(seq_ms)) / spec.num_layers * 1e3, 2)
+                                          if seq_ms else None)},
     }
+    if cold_ms is not None:
+        res["cold"] = {"ms_per_step": round(cold_ms, 5), "value": round(kv_step / (cold_ms * 1e-3) / 1e9, 2),
+                       "unit": "GB/s", "pct_hbm_peak": round(100.0 * kv_step / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                       "note": "median of steps each preceded (outside its events) by a 512 MiB write that evicts "
+                               "the MALL; the main figures are warm"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, k_pool, v_pool, rows, args.cpu_seconds, args.kv)
     print(json.dumps(res), flush=True)
