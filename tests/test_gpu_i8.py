@@ -328,11 +328,10 @@ def test_i8_device_errors():
     assert not (diff & ~allowed).any()
 
 
-def test_batch64_i8_full_size_sampled():
-    """The benchmark's INT8 step on one layer of the batch-64 x 2048 workload."""
-    spec = W.batch64_spec()
-    layer, seqs = 9, np.array([0, 5, 31, 62])
-    print(f"i8 full-size layer={layer} sampled={list(seqs)}", flush=True)
+def _full_size_i8(spec, layer, seqs, what):
+    """The benchmark's INT8 step on one layer of a full-size workload, sampled sequences checked
+    against the oracle on bf16 pages copied to the host before any of our kernels ran."""
+    print(f"i8 full-size {what} layer={layer} sampled={list(seqs)}", flush=True)
     k_pool = W.fill_pool_device(spec, dev(), "k")
     v_pool = W.fill_pool_device(spec, dev(), "v")
     bt = spec.block_tables[layer][seqs]
@@ -366,8 +365,21 @@ def test_batch64_i8_full_size_sampled():
                                     spec.theta) == oracle.OK
     ref, rc = oracle.decode_gqa_i8(oq, ref_pool, bt_small, lens, len(used), spec.scale)
     assert rc == oracle.OK
-    assert_close(to_host_f64(out)[seqs], ref, TOL_BF16, "batch64 i8")
+    assert_close(to_host_f64(out)[seqs], ref, TOL_BF16, what)
     xmax = float(np.abs(W.bf16_bits_to_f32(q)).max())
     assert_rope_close(to_host_bits(dq)[seqs], oq, xmax, "rotated q")
     del pool
     torch.cuda.empty_cache()
+
+
+def test_batch64_i8_full_size_sampled():
+    """64 x 2048 tokens: the launch reads its codes with the non-temporal hint (512 workgroups)."""
+    _full_size_i8(W.batch64_spec(), 9, np.array([0, 5, 31, 62]), "batch64 i8")
+
+
+def test_batch256_i8_full_size_sampled():
+    """The ragged, fragmented 256-sequence workload with 1 % outlier rows (2048 workgroups)."""
+    spec = W.batch256_spec()
+    lens = spec.context_lens
+    seqs = np.unique(np.array([0, int(np.argmax(lens)), int(np.argmin(lens)), 100, 255]))
+    _full_size_i8(spec, 11, seqs, "batch256 i8")
