@@ -21,6 +21,8 @@ constexpr int kMaxPartPages = 128;
 // hint: bf16 from kNtMinBlocks to kNtMaxBlocksBf16, INT8 from kNtMinBlocks up.
 constexpr int64_t kNtMinBlocks = 128;
 constexpr int64_t kNtMaxBlocksBf16 = 1024;
+// Grid sizes up to which the INT8 kernel levels its wave priorities.
+constexpr int64_t kPrioMaxBlocksI8 = 1024;
 constexpr float kNegBig = -1.0e30f;   // running-max start (finite, so 2^(x - m) is never NaN)
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold
 

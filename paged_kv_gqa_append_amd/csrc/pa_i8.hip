@@ -251,7 +251,11 @@ __device__ __forceinline__ float max_quarters(float v) {
     return fmaxf(lo, hi);
 }
 
-template <int kWaves, bool kFused, bool kNt>
+// kLevel: the wave priority starts high and steps down as the wave's pages run
+// out (as in the bf16 kernel).  The s_setprio instructions also constrain how
+// the compiler schedules the page loop, so the form without them is kept for
+// grids where levelling does not pay (see launch_decode_i8).
+template <int kWaves, bool kFused, bool kNt, bool kLevel>
 __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    __builtin_amdgcn_s_setprio(3);
+    if (kLevel) __builtin_amdgcn_s_setprio(3);
     const uint8_t *pool = reinterpret_cast<const uint8_t *>(P.k_pool);
 
     __shared__ int s_app_page;
@@ -538,6 +542,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     bool last_in_alt = false;
     const int span = pg1 - pg0;
     auto level = [&]() {
+        if (!kLevel) return;
         const int done16 = 16 * (p - pg0);
         if (done16 >= 15 * span) __builtin_amdgcn_s_setprio(0);
         else if (done16 >= 13 * span) __builtin_amdgcn_s_setprio(1);
@@ -674,14 +679,19 @@ hipError_t launch_decode_i8(const DecodeLaunch &d, hipStream_t stream) {
     // 128 sequences, 256 x 512 tokens, the ragged 256-sequence batch) it is
     // 0-10 % faster, never slower; with 64 workgroups (few long, latency-bound
     // streams) it is 14 % slower.  Hinting the scales as well gains nothing.
+    // Priority levelling pays up to 1024 workgroups (0.5 % at 512); above that
+    // the form without it ran the ragged 256-sequence batch 4.5 % faster.
     const bool nt = blocks >= kNtMinBlocks;
+    const bool level = blocks <= kPrioMaxBlocksI8;
     const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWavesI8);
     if (d.fused) {
-        if (nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, true>), grid, wg, 0, stream, P);
-        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, false>), grid, wg, 0, stream, P);
+        if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, false, true>), grid, wg, 0, stream, P);
+        else if (level) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, true, true>), grid, wg, 0, stream, P);
+        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, true, false>), grid, wg, 0, stream, P);
     } else {
-        if (nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, true>), grid, wg, 0, stream, P);
-        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, false>), grid, wg, 0, stream, P);
+        if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, false, true>), grid, wg, 0, stream, P);
+        else if (level) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, true, true>), grid, wg, 0, stream, P);
+        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, true, false>), grid, wg, 0, stream, P);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.num_parts == 1) return e;

@@ -1,6 +1,7 @@
 """The decode kernels read their pages with a non-temporal cache hint for some
 grid sizes (bf16: 128 to 1024 workgroups, one per sequence and KV head here;
-INT8: from 128 up) and without it otherwise.  The hint changes no arithmetic:
+INT8: from 128 up) and without it otherwise, and the INT8 kernel levels its
+wave priorities only up to 1024 workgroups.  Neither changes any arithmetic:
 a batch that takes one form and the same sequences split into batches that
 take the other give the same bits (decode, and append + decode: out, the
 rotated q and the pool), and the hinted batch matches the oracle."""
@@ -57,7 +58,8 @@ def device_pools(case, kv, host_i8):
 # opposite sides of a hint threshold.
 SPLITS = [("bf16", 16, 8),      # 128 workgroups (hinted) vs 2 x 64 (plain)
           ("bf16", 130, 65),    # 1040 (plain) vs 2 x 520 (hinted)
-          ("int8", 16, 8)]      # 128 (hinted) vs 2 x 64 (plain)
+          ("int8", 16, 8),      # 128 (hinted) vs 2 x 64 (plain)
+          ("int8", 130, 65)]    # 1040 (hinted, no priority levelling) vs 2 x 520 (hinted, levelled)
 
 
 @pytest.mark.parametrize("kv,n,cut", SPLITS)
