@@ -129,7 +129,7 @@ def host_cpu_model():
     return None
 
 
-def measured_traffic(kv="bf16"):
+def measured_traffic(kv="bf16", profiles_dir=None):
     """HBM bytes per fused decode launch from the committed rocprofv3 PMC summary.
 
     The summary records the sha256 of the decode kernel's sources (the files
@@ -142,7 +142,7 @@ def measured_traffic(kv="bf16"):
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "paged_kv_gqa_append_amd", "csrc")
     sources, summary = TRAFFIC[kv]
-    summ = os.path.join(here, "profiles", summary)
+    summ = os.path.join(profiles_dir or os.path.join(here, "profiles"), summary)
     try:
         text = open(summ).read()
         h = hashlib.sha256()
