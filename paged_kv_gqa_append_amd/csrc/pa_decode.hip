@@ -267,6 +267,21 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         else if (done16 >= 13 * span) __builtin_amdgcn_s_setprio(1);
         else if (done16 >= 10 * span) __builtin_amdgcn_s_setprio(2);
     };
+    // Steady state: both loads of a double step are known to be needed, so they
+    // are issued unconditionally.  A load under a branch leaves the compiler's
+    // wait counting unsure how many loads are outstanding after the join, and
+    // it then waits for all of them (the next page's included) every step.
+    while (p + kWaves < p_stop && p + 2 * kWaves < pg1) {
+        alt = load_page(p + kWaves);
+        process_full(cur);
+        p += kWaves;
+        level();
+        cur = load_page(p + kWaves);
+        process_full(alt);
+        p += kWaves;
+        level();
+    }
+    // The last page or two of the wave.
     while (p < p_stop) {
         if (p + kWaves < pg1) alt = load_page(p + kWaves);
         process_full(cur);

@@ -548,6 +548,20 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         else if (done16 >= 13 * span) __builtin_amdgcn_s_setprio(1);
         else if (done16 >= 10 * span) __builtin_amdgcn_s_setprio(2);
     };
+    // Steady state: both loads of a double step are known to be needed, so they
+    // are issued unconditionally (a load under a branch makes the compiler's
+    // wait counting drain every outstanding load each step).
+    while (p + kWaves < p_stop && p + 2 * kWaves < pg1) {
+        alt = load_page(p + kWaves);
+        process(cur, false, p);
+        p += kWaves;
+        level();
+        cur = load_page(p + kWaves);
+        process(alt, false, p);
+        p += kWaves;
+        level();
+    }
+    // The last page or two of the wave.
     while (p < p_stop) {
         if (p + kWaves < pg1) alt = load_page(p + kWaves);
         process(cur, false, p);
