@@ -39,7 +39,9 @@
 //   k_decode_merge.
 //
 // The partition size depends on nothing but a constant, so a sequence's
-// output is bitwise independent of the batch around it.
+// output is bitwise independent of the batch around it.  The one thing the
+// grid size does choose, the cache hint on the K tile loads, changes no
+// arithmetic.
 #include <math.h>
 #include <stdlib.h>
 

@@ -40,7 +40,8 @@
 // the running sum uses the fp32 2^(x - m).  P' stays below 2^8 * V scale, so
 // V rows must hold |values| < 65504 * 127 / 2^8 (about 32000) for hi to fit f16.
 // Online softmax (log2 units, lazy max), wave and partition merges follow the
-// bf16 kernel's.
+// bf16 kernel's.  The grid size chooses the cache hint on the code loads and
+// whether wave priorities are levelled; neither changes the arithmetic.
 #include <math.h>
 
 #include "pa_decode_core.h"
