@@ -158,6 +158,35 @@ def measured_traffic(kv="bf16", profiles_dir=None):
     return int(m_val.group(1))
 
 
+def stream_read_ceiling(buffers, chunk_bytes, per_step, steps, torch, binding, device, stream):
+    """Read bandwidth of the plain contiguous-read probe (pa_probe_stream_read) over chunks of
+    chunk_bytes, per_step launches back to back per step, each on a different chunk of the given
+    device buffers (as a decode step reads different pages in every layer, so no launch finds the
+    previous one's bytes in cache).  Returns (GB/s, mean us per launch)."""
+    chunk = chunk_bytes // 16 * 16
+    flat = [b.view(torch.uint8).reshape(-1) for b in buffers]
+    chunks = [f[o:o + chunk] for f in flat for o in range(0, f.numel() - chunk + 1, chunk)]
+    if not chunks or chunk == 0:
+        return None, None
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    seq = [chunks[i % len(chunks)] for i in range(per_step)]
+
+    def step():
+        for c in seq:
+            binding.probe_stream_read(c, sink, stream=stream)
+
+    warm_up(step, torch, None)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (steps * per_step)
+    return chunk / (us * 1e-6) / 1e9, us
+
+
 def cpu_baseline(spec, k_pool, v_pool, rows, target_s, kv="bf16"):
     """Time the fp64 oracle's append + decode on whole layers of the workload (host cores).
 
@@ -491,6 +520,10 @@ def main():
 
     kv_step = kv_step_bytes
     kv_launch = kv_step // spec.num_layers
+    # The same bytes per launch read as one contiguous stream by the plain read probe, from the
+    # same pools, a different chunk per launch: the read bandwidth this GPU reaches at this size.
+    ceil_gbps, ceil_us = stream_read_ceiling([pool] if i8 else [k_pool, v_pool], kv_launch, spec.num_layers,
+                                             n_pass, torch, binding, device, stream)
     gbps = kv_step / (ms * 1e-3) / 1e9
     dec_gbps = kv_launch / (dec_ms_mean * 1e-3) / 1e9
     sfx = "_i8" if i8 else ""
@@ -513,13 +546,19 @@ def main():
         ("separate_calls_ms_per_step" if args.path == "fused" else "fused_ms_per_step"): round(other_ms, 5),
         "roofline": {"bound": "hbm",
                      "kernel": ("k_decode_paged_i8<8,true,nt> (pa_append_decode_gqa_i8)" if i8 else
-                                "k_decode_paged<8,true,nt> (pa_append_decode_gqa)"),
+                                "k_decode_paged<8,true,rows> (pa_append_decode_gqa)"),
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.kv) if args.config == "batch64" else None,
                      "bytes_per_launch": kv_launch, "mean_launch_us": round(dec_ms_mean * 1e3, 2),
                      "median_launch_us": (round(float(np.median(seq_ms)) / spec.num_layers * 1e3, 2)
-                                          if seq_ms else None)},
+                                          if seq_ms else None),
+                     "stream_read": (None if ceil_gbps is None else
+                                     {"kernel": "k_stream_read (pa_probe_stream_read), same bytes per launch",
+                                      "achieved": round(ceil_gbps, 2), "unit": "GB/s",
+                                      "mean_launch_us": round(ceil_us, 2),
+                                      "frac_of_peak": round(ceil_gbps / HBM_PEAK_GBPS, 4),
+                                      "decode_frac_of_stream_read": round(dec_gbps / ceil_gbps, 4)})},
     }
     if cold_ms is not None:
         res["cold"] = {"ms_per_step": round(cold_ms, 5), "value": round(kv_step / (cold_ms * 1e-3) / 1e9, 2),

@@ -338,6 +338,17 @@ int32_t pa_kvm_free_pages(const pa_kv_manager *m);                  /* pages on 
 int64_t pa_kvm_reserved_pages(const pa_kv_manager *m);              /* budgets of active slots   */
 int32_t pa_kvm_queued(const pa_kv_manager *m);                      /* requests not yet admitted */
 
+/* ------------------------------------------------------------ diagnostics --
+ * Contiguous-read probe, for measurement: reads bytes from buf (device,
+ * 16-byte aligned, bytes a multiple of 16) once, with 16-byte loads and no
+ * other memory traffic, so its time gives the read bandwidth a plain stream
+ * reaches on this GPU, the ceiling the decode kernels' figures are set
+ * against.  sink (device uint32, 4-byte aligned) is written only if a 32-bit
+ * XOR of all the data equals a fixed constant; it exists so the loads are kept.
+ * PA_ERR_INVALID_ARG for a NULL or misaligned pointer or a bad size; 0 bytes
+ * is a no-op.  Stream-ordered, nothing allocated.                            */
+pa_status pa_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_schedule", "pa_kvm_set_length", "pa_kvm_release", "pa_kvm_block_tables", "pa_kvm_lengths",
            "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
-           "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax")
+           "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 
@@ -87,6 +87,8 @@ def lib():
     L.pa_argmax_workspace_bytes.argtypes = [i32, i32, i32]
     L.pa_argmax.restype = ctypes.c_int
     L.pa_argmax.argtypes = [P, P, i32, i32, i32, P, u64, P]
+    L.pa_probe_stream_read.restype = ctypes.c_int
+    L.pa_probe_stream_read.argtypes = [P, u64, P, P]
     i64 = ctypes.c_int64
     L.pa_admission_credit_pages.restype = i64
     L.pa_admission_credit_pages.argtypes = [i32, i32, i32]
@@ -449,6 +451,15 @@ def argmax(out_index: torch.Tensor, logits: torch.Tensor, workspace: Optional[to
     _check(lib().pa_argmax(_ptr(out_index), _ptr(logits), rows, vocab, code, _ptr(workspace), ws_bytes,
                            _stream(stream)), "pa_argmax")
     return out_index
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """pa_probe_stream_read: read all of buf's bytes once (a contiguous-read bandwidth probe)."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous tensor")
+    _expect(sink, "sink", torch.int32, (1,), buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().pa_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "pa_probe_stream_read")
 
 
 def admission_credit_pages(prompt_tokens: int, max_new_tokens: int, num_layers: int) -> int:

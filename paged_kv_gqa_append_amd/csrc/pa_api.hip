@@ -86,7 +86,7 @@ const char *pa_status_string(int status) {
     }
 }
 
-int32_t pa_abi_version(void) { return 5; }
+int32_t pa_abi_version(void) { return 6; }
 
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
@@ -252,6 +252,13 @@ pa_status pa_argmax(int32_t *out_index, const void *logits, int32_t num_rows, in
     const bool vec = aligned16(logits) && (static_cast<size_t>(vocab) * esz) % 16 == 0;
     return pa::launch_argmax(out_index, logits, num_rows, vocab, bf16, vec, workspace, stream) == hipSuccess
                ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    if (bytes == 0) return PA_OK;
+    if (!buf || !sink || !aligned16(buf) || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return PA_ERR_INVALID_ARG;
+    return pa::launch_stream_read(buf, bytes, sink, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // extern "C"

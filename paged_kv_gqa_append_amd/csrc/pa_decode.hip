@@ -38,10 +38,17 @@
 //   (max, sum, acc[64]) per head and partition in the workspace for
 //   k_decode_merge.
 //
+// Page loads come in two forms, chosen by grid size (see launch_decode).
+// Whole rows: each lane loads its chunk of token g, then of token g + 8, so one
+// load instruction reads 8 whole 128-byte token rows; both tiles carry the
+// non-temporal hint, and the lane's slot order above is made with per-lane
+// selects where the page is consumed.  Slot order: each lane loads straight
+// into its slots, so a load instruction reads half of each of the tile's 16
+// rows; no hint, no selects.  The slots hold the same values either way.
+//
 // The partition size depends on nothing but a constant, so a sequence's
 // output is bitwise independent of the batch around it.  The one thing the
-// grid size does choose, the cache hint on the K tile loads, changes no
-// arithmetic.
+// grid size does choose, the load form, changes no arithmetic.
 #include <math.h>
 #include <stdlib.h>
 
@@ -49,7 +56,7 @@
 
 namespace pa {
 
-template <int kWaves, bool kFused, bool kNtK>
+template <int kWaves, bool kFused, bool kRows>
 __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
@@ -80,9 +87,14 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     const int b0 = c & 1, b1 = (c >> 1) & 1, b2 = c >> 2;
     const int t0 = b0 ^ b2;                    // token half of K slot A
     const int hm = ((b1 ^ b2) << 1) | b2;      // q slot m holds head m ^ hm
-    // element offsets in a tile; bit 9 (8 tokens x 64) selects the token half
-    const uint32_t offA = (g + 8 * t0) * kD + c * 8;
-    const uint32_t offV0 = (g + 8 * b2) * kD + c * 8;  // V slot u holds token half u ^ b2
+    // Element offsets in a tile of the lane's first K and V load; bit 9 (8
+    // tokens x 64) selects the token half, flipped for the second load.  Whole
+    // rows: token g (offset 8 * lane) for both.  Slot order: K slot A holds
+    // token half t0, V slot u token half u ^ b2.
+    const uint32_t offK = (g + (kRows ? 0 : 8 * t0)) * kD + c * 8;
+    const uint32_t offV = (g + (kRows ? 0 : 8 * b2)) * kD + c * 8;
+    // whole rows: the loads hold the halves in order and the slots swap them
+    const bool swapK = kRows && t0, swapV = kRows && b2;
 
     // ---- prologue loads, in the order they must complete --------------------
     // Vector loads complete in issue order (one counter), so the small loads
@@ -142,17 +154,17 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
         const uint16_t *kt = P.k_pool + base;
         const uint16_t *vt = P.v_pool + base;
         KVRegs r;
-        // kNtK: the K tile is read with the non-temporal hint and the V tile
-        // without (the host picks it by grid size; see launch_decode).
-        if (kNtK) {
-            r.ka = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kt + offA));
-            r.kb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kt + (offA ^ 512u)));
+        if (kRows) {
+            r.k0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kt + offK));
+            r.k1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kt + (offK ^ 512u)));
+            r.v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vt + offV));
+            r.v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vt + (offV ^ 512u)));
         } else {
-            r.ka = *reinterpret_cast<const u32x4 *>(kt + offA);
-            r.kb = *reinterpret_cast<const u32x4 *>(kt + (offA ^ 512u));
+            r.k0 = *reinterpret_cast<const u32x4 *>(kt + offK);
+            r.k1 = *reinterpret_cast<const u32x4 *>(kt + (offK ^ 512u));
+            r.v0 = *reinterpret_cast<const u32x4 *>(vt + offV);
+            r.v1 = *reinterpret_cast<const u32x4 *>(vt + (offV ^ 512u));
         }
-        r.v0 = *reinterpret_cast<const u32x4 *>(vt + offV0);
-        r.v1 = *reinterpret_cast<const u32x4 *>(vt + (offV0 ^ 512u));
         return r;
     };
     // an id outside the pool reads page 0 instead; such a sequence fails validation
@@ -222,29 +234,32 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P)
     // One page.  process_full: any page but the sequence's last; process_last: the
     // last page, which may be partly empty and, when fused, holds the appended token
     // (its dead slots may hold anything, NaN included, so they are selected out).
+    // The slot selects of the whole-row form sit here, where the page is
+    // consumed: placed after the loads they would wait for them.
     auto process_full = [&](const KVRegs &r) {
-        const float x = page_score(qv, r.ka, r.kb, P.scale_log2);
+        const float x = page_score(qv, swapK ? r.k1 : r.k0, swapK ? r.k0 : r.k1, P.scale_log2);
         const float pw = softmax_step(x, m_run, l_run, acc);
         float va[8], vb[8];
-        unpack8(r.v0, va);
-        unpack8(r.v1, vb);
+        unpack8(swapV ? r.v1 : r.v0, va);
+        unpack8(swapV ? r.v0 : r.v1, vb);
         accumulate(pw, va, vb, acc);
     };
     auto process_last = [&](KVRegs r, int p) {
         if (kFused && g == (pos & 7)) {  // patch the appended token into the registers
             const u32x4 nk = *reinterpret_cast<const u32x4 *>(&s_newk[c * 8]);
             const u32x4 nv = *reinterpret_cast<const u32x4 *>(&s_newv[c * 8]);
+            // register of token half `half`: load order (whole rows) or slot order
             const int half = (pos >> 3) & 1;
-            if (half == t0) r.ka = nk; else r.kb = nk;
-            if (half == b2) r.v0 = nv; else r.v1 = nv;
+            if (kRows ? half : half ^ t0) r.k1 = nk; else r.k0 = nk;
+            if (kRows ? half : half ^ b2) r.v1 = nv; else r.v0 = nv;
         }
         const int tb = p * kPage;
-        float x = page_score(qv, r.ka, r.kb, P.scale_log2);
+        float x = page_score(qv, swapK ? r.k1 : r.k0, swapK ? r.k0 : r.k1, P.scale_log2);
         if (tb + g + 8 * t0 >= L) x = -INFINITY;
         const float pw = softmax_step(x, m_run, l_run, acc);
         float va[8], vb[8];
-        unpack8(r.v0, va);
-        unpack8(r.v1, vb);
+        unpack8(swapV ? r.v1 : r.v0, va);
+        unpack8(swapV ? r.v0 : r.v1, vb);
         const bool ok0 = tb + g + 8 * b2 < L, ok1 = tb + g + 8 * (b2 ^ 1) < L;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -413,19 +428,23 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream) {
     P.ws_acc = d.ws_acc;
     P.flags = d.flags;
     const int64_t blocks = static_cast<int64_t>(d.num_seqs) * kHKV * d.num_parts;
-    // The non-temporal hint on the K tiles, by grid size, as measured on MI355X
-    // (fused step, uniform 2048-token batches and the ragged 256-sequence one):
-    // with 128 to 1024 workgroups the hinted stream is 2-7 % faster; with 64
-    // (few long, latency-bound streams) it is 15 % slower, and with 2048
-    // (several dispatch rounds) 2-8 % slower.  Hinting both tiles, or half of
-    // each, was no faster than hinting none at any size.
-    const bool nt = blocks >= kNtMinBlocks && blocks <= kNtMaxBlocksBf16;
+    // The load form by grid size, as measured on MI355X (fused step, 16 layers):
+    // from 128 workgroups, whole rows with the non-temporal hint on both tiles
+    // (64 x 2048 tokens, 512 workgroups: 44.3 us per launch against 46.3 for
+    // the best slot-order form, which hinted K alone; 256 ragged sequences,
+    // 2048 workgroups: 61.6 against 69.0 unhinted).  The hint pays only on
+    // whole-row loads: a read-only kernel over the same page pattern takes
+    // 42.9 us with whole rows and 45.2 us with half rows when K is hinted, and
+    // hinting V as well takes the half-row form to 49.4 us.  Below 128
+    // workgroups (a few long, latency-bound streams: 8 sequences, 64
+    // workgroups) the slot-order form is ahead, 11.9 against 12.9 us.
+    const bool rows = blocks >= kNtMinBlocks;
     const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWaves);
     if (d.fused) {
-        if (nt) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, true>), grid, wg, 0, stream, P);
+        if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, true>), grid, wg, 0, stream, P);
         else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, false>), grid, wg, 0, stream, P);
     } else {
-        if (nt) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, true>), grid, wg, 0, stream, P);
+        if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, true>), grid, wg, 0, stream, P);
         else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, false>), grid, wg, 0, stream, P);
     }
     hipError_t e = hipGetLastError();

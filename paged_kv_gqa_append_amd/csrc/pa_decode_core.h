@@ -17,10 +17,9 @@
 namespace pa {
 
 constexpr int kMaxPartPages = 128;
-// Grid sizes (workgroups per launch) whose page loads carry the non-temporal
-// hint: bf16 from kNtMinBlocks to kNtMaxBlocksBf16, INT8 from kNtMinBlocks up.
+// Grid sizes (workgroups per launch) from which the page loads carry the
+// non-temporal hint (bf16: with whole-row loads; INT8: on the code loads).
 constexpr int64_t kNtMinBlocks = 128;
-constexpr int64_t kNtMaxBlocksBf16 = 1024;
 // Grid sizes up to which the INT8 kernel levels its wave priorities.
 constexpr int64_t kPrioMaxBlocksI8 = 1024;
 constexpr float kNegBig = -1.0e30f;   // running-max start (finite, so 2^(x - m) is never NaN)
@@ -30,8 +29,9 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold
 constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;
 constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRowRor8 = 0x128;
 
+// a page's K and V chunks of one lane, in load order (two loads of each tile)
 struct KVRegs {
-    u32x4 ka, kb, v0, v1;
+    u32x4 k0, k1, v0, v1;
 };
 
 // Lane pairs (i, i^16) and (i, i^32) through the gfx950 row-swap permutes: with

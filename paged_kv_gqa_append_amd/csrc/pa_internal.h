@@ -86,6 +86,9 @@ hipError_t launch_decode_i8(const DecodeLaunch &d, hipStream_t stream);
 int argmax_chunk_elems(bool bf16);
 hipError_t launch_argmax(int32_t *out, const void *logits, int rows, int vocab, bool bf16, bool vec, void *workspace,
                          hipStream_t stream);
+
+// Contiguous-read probe over [buf, buf + bytes), bytes a multiple of 16.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 hipError_t launch_quantize_pages_i8(void *pool, const void *k_pool, const void *v_pool, const int32_t *page_ids,
                                     int count, int num_pages, uint32_t *flags, hipStream_t stream);
 

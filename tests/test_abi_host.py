@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == 5
+    assert pa.lib().pa_abi_version() == 6
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -188,6 +188,18 @@ def test_argmax_validation(pa):
     assert am(ws=F, wsb=need - 8) == pa.PA_ERR_WORKSPACE
     assert am(ws=v(FAKE + 4), wsb=need) == pa.PA_ERR_WORKSPACE
     assert am(rows=0, out=None) == pa.PA_OK
+
+
+def test_stream_read_probe_validation(pa):
+    lib = pa.lib()
+    v = ctypes.c_void_p
+    F = v(FAKE)
+    assert lib.pa_probe_stream_read(F, 1 << 20, None, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_stream_read(None, 1 << 20, F, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_stream_read(v(FAKE + 8), 1 << 20, F, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_stream_read(F, (1 << 20) + 8, F, None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_stream_read(F, 1 << 20, v(FAKE + 2), None) == pa.PA_ERR_INVALID_ARG
+    assert lib.pa_probe_stream_read(None, 0, None, None) == pa.PA_OK
 
 
 def test_rope_table_fill(pa):

@@ -1,10 +1,12 @@
-"""The decode kernels read their pages with a non-temporal cache hint for some
-grid sizes (bf16: 128 to 1024 workgroups, one per sequence and KV head here;
-INT8: from 128 up) and without it otherwise, and the INT8 kernel levels its
-wave priorities only up to 1024 workgroups.  Neither changes any arithmetic:
-a batch that takes one form and the same sequences split into batches that
-take the other give the same bits (decode, and append + decode: out, the
-rotated q and the pool), and the hinted batch matches the oracle."""
+"""The decode kernels choose their page-load form by grid size (one workgroup
+per sequence and KV head here).  bf16: from 128 workgroups, whole-row loads
+with the non-temporal hint, whose registers are put in the lane's slot order
+by selects; below, plain loads straight into slot order.  INT8: the hint on
+the code loads from 128 workgroups, and wave priorities levelled only up to
+1024.  None of this changes any arithmetic: a batch that takes one form and
+the same sequences split into batches that take the other give the same bits
+(decode, and append + decode: out, the rotated q and the pool), and the
+larger batch matches the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -56,8 +58,8 @@ def device_pools(case, kv, host_i8):
 
 # (kv, number of sequences of the whole batch, split point): the whole batch and its parts fall on
 # opposite sides of a hint threshold.
-SPLITS = [("bf16", 16, 8),      # 128 workgroups (hinted) vs 2 x 64 (plain)
-          ("bf16", 130, 65),    # 1040 (plain) vs 2 x 520 (hinted)
+SPLITS = [("bf16", 16, 8),      # 128 workgroups (whole rows) vs 2 x 64 (slot order)
+          ("bf16", 20, 15),     # 160 (whole rows) vs 120 + 40 (slot order)
           ("int8", 16, 8),      # 128 (hinted) vs 2 x 64 (plain)
           ("int8", 130, 65)]    # 1040 (hinted, no priority levelling) vs 2 x 520 (hinted, levelled)
 
