@@ -290,7 +290,13 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
     const int L = P.lens[s];
     const int wu = __builtin_amdgcn_readfirstlane(w);
+    // The wave's first two pages are issued in the prologue: the prologue's
+    // arithmetic (q rotation and scaling, quantising the appended rows, a
+    // barrier) then runs under two pages of loads per wave instead of one.
+    // An id past the table or outside the pool reads page 0 instead; such a
+    // page is never used.
     const int first_id = wu < slice ? bt_row[pg0 + wu] : -1;
+    const int second_id = wu + kWaves < slice ? bt_row[pg0 + wu + kWaves] : -1;
     const int my_idx = wu + kWaves * lane;
     const int my_id = bt_row[pg0 + min(my_idx, slice - 1)];
     const int64_t qrow0 = (static_cast<int64_t>(s) * kHQ + j * kGroup) * kD;
@@ -342,6 +348,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         return r;
     };
     I8Page cur = load_tile(first_id >= 0 && first_id < P.num_pages ? first_id : 0);
+    I8Page alt = load_tile(second_id >= 0 && second_id < P.num_pages ? second_id : 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // fused: rotate q into LDS (threads 0..127); wave 2 rotates the new K row
@@ -539,8 +546,6 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         return load_tile(__builtin_amdgcn_readlane(my_id, (p - pg0 - wu) / kWaves));
     };
     const int p_stop = (pg1 == n_pages) ? n_pages - 1 : pg1;
-    I8Page alt;
-    bool last_in_alt = false;
     const int span = pg1 - pg0;
     auto level = [&]() {
         if (!kLevel) return;
@@ -549,11 +554,13 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         else if (done16 >= 13 * span) __builtin_amdgcn_s_setprio(1);
         else if (done16 >= 10 * span) __builtin_amdgcn_s_setprio(2);
     };
+    // At the top of each step cur holds page p and alt page p + kWaves, both
+    // issued; a page is consumed before the one after next is issued, so one
+    // page is in flight while another is processed, as in the bf16 kernel.
     // Steady state: both loads of a double step are known to be needed, so they
     // are issued unconditionally (a load under a branch makes the compiler's
     // wait counting drain every outstanding load each step).
-    while (p + kWaves < p_stop && p + 2 * kWaves < pg1) {
-        alt = load_page(p + kWaves);
+    while (p + kWaves < p_stop && p + 3 * kWaves < pg1) {
         process(cur, false, p);
         p += kWaves;
         level();
@@ -561,23 +568,17 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         process(alt, false, p);
         p += kWaves;
         level();
+        alt = load_page(p + kWaves);
     }
-    // The last page or two of the wave.
+    // The wave's last full pages, one per step.
     while (p < p_stop) {
-        if (p + kWaves < pg1) alt = load_page(p + kWaves);
         process(cur, false, p);
         p += kWaves;
         level();
-        if (p >= p_stop) { last_in_alt = true; break; }
-        if (p + kWaves < pg1) cur = load_page(p + kWaves);
-        process(alt, false, p);
-        p += kWaves;
-        level();
+        cur = alt;
+        if (p + kWaves < pg1) alt = load_page(p + kWaves);
     }
-    if (pg1 == n_pages && p == n_pages - 1) {
-        if (last_in_alt) cur = alt;
-        process_last(cur, p);
-    }
+    if (pg1 == n_pages && p == n_pages - 1) process_last(cur, p);  // the sequence's last page
     // ---- wave epilogue ---------------------------------------------------------
     const float l_tot = sum_quarters(l_run);
     if (lane < 16) {  // O minus 1152 x (sum of the fed weights), per head
