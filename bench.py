@@ -17,8 +17,11 @@ step time.  The roofline object reports the decode kernel alone: its
 algorithmic bytes per launch over its mean duration, from the HIP events that
 bracket the timed steps on the stream it runs on (the fused step is nothing
 but that kernel, once per layer).  Warmup runs until the GPU's clocks have
-settled (100 ms of work unless --warmup is given).  cpu_baseline times the
-fp64 CPU oracle (append + decode) on a bounded sample of the same workload.
+settled (100 ms of work unless --warmup is given).  roofline.stream_read is the
+read ceiling at the same size: pa_probe_stream_read reads the same bytes per
+launch as one contiguous stream, one launch per layer over different chunks of
+the same pools, timed the same way.  cpu_baseline times the fp64 CPU oracle
+(append + decode) on a bounded sample of the same workload.
 """
 from __future__ import annotations
 

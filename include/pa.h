@@ -343,8 +343,9 @@ int32_t pa_kvm_queued(const pa_kv_manager *m);                      /* requests 
  * 16-byte aligned, bytes a multiple of 16) once, with 16-byte loads and no
  * other memory traffic, so its time gives the read bandwidth a plain stream
  * reaches on this GPU, the ceiling the decode kernels' figures are set
- * against.  sink (device uint32, 4-byte aligned) is written only if a 32-bit
- * XOR of all the data equals a fixed constant; it exists so the loads are kept.
+ * against.  sink (device uint32, 4-byte aligned) receives a fixed constant
+ * (0x9E3779B9) only if the 32-bit XOR of the words one lane read equals that
+ * constant, never for all-zero data; it exists so the loads are kept.
  * PA_ERR_INVALID_ARG for a NULL or misaligned pointer or a bad size; 0 bytes
  * is a no-op.  Stream-ordered, nothing allocated.                            */
 pa_status pa_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
