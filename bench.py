@@ -165,12 +165,14 @@ def stream_read_ceiling(buffers, chunk_bytes, per_step, steps, torch, binding, d
     """Read bandwidth of the plain contiguous-read probe (pa_probe_stream_read) over chunks of
     chunk_bytes, per_step launches back to back per step, each on a different chunk of the given
     device buffers (as a decode step reads different pages in every layer, so no launch finds the
-    previous one's bytes in cache).  Returns (GB/s, mean us per launch)."""
+    previous one's bytes in cache).  Returns (GB/s, mean us per launch, distinct chunks); with
+    fewer distinct chunks than launches per step (small pools) the chunks repeat and may be read
+    from the 256 MB MALL, as the decode's own pages are then."""
     chunk = chunk_bytes // 16 * 16
     flat = [b.view(torch.uint8).reshape(-1) for b in buffers]
     chunks = [f[o:o + chunk] for f in flat for o in range(0, f.numel() - chunk + 1, chunk)]
     if not chunks or chunk == 0:
-        return None, None
+        return None, None, 0
     sink = torch.zeros(1, dtype=torch.int32, device=device)
     seq = [chunks[i % len(chunks)] for i in range(per_step)]
 
@@ -187,7 +189,7 @@ def stream_read_ceiling(buffers, chunk_bytes, per_step, steps, torch, binding, d
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / (steps * per_step)
-    return chunk / (us * 1e-6) / 1e9, us
+    return chunk / (us * 1e-6) / 1e9, us, min(len(chunks), per_step)
 
 
 def cpu_baseline(spec, k_pool, v_pool, rows, target_s, kv="bf16"):
@@ -525,7 +527,7 @@ def main():
     kv_launch = kv_step // spec.num_layers
     # The same bytes per launch read as one contiguous stream by the plain read probe, from the
     # same pools, a different chunk per launch: the read bandwidth this GPU reaches at this size.
-    ceil_gbps, ceil_us = stream_read_ceiling([pool] if i8 else [k_pool, v_pool], kv_launch, spec.num_layers,
+    ceil_gbps, ceil_us, ceil_chunks = stream_read_ceiling([pool] if i8 else [k_pool, v_pool], kv_launch, spec.num_layers,
                                              n_pass, torch, binding, device, stream)
     gbps = kv_step / (ms * 1e-3) / 1e9
     dec_gbps = kv_launch / (dec_ms_mean * 1e-3) / 1e9
@@ -560,6 +562,7 @@ def main():
                                      {"kernel": "k_stream_read (pa_probe_stream_read), same bytes per launch",
                                       "achieved": round(ceil_gbps, 2), "unit": "GB/s",
                                       "mean_launch_us": round(ceil_us, 2),
+                                      "distinct_chunks_per_step": ceil_chunks,
                                       "frac_of_peak": round(ceil_gbps / HBM_PEAK_GBPS, 4),
                                       "decode_frac_of_stream_read": round(dec_gbps / ceil_gbps, 4)})},
     }
