@@ -85,7 +85,10 @@ typedef enum { PA_OUT_BF16 = 0, PA_OUT_FP32 = 1 } pa_out_dtype;
 /* Human-readable name of a status code (static string, never NULL). */
 const char *pa_status_string(int status);
 
-/* ABI version of this header (bumped on any signature or layout change). */
+/* ABI version of this header, bumped on any signature or layout change;
+ * pa_abi_version() returns the value of the header the library was built
+ * from, so a caller can refuse a library built from another header.        */
+#define PA_ABI_VERSION 6
 int32_t pa_abi_version(void);
 
 /* Fill a HOST table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),

@@ -34,6 +34,8 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
+# PA_ABI_VERSION of the header whose signatures this module declares
+ABI_VERSION = 6
 
 
 class PaError(RuntimeError):
@@ -42,8 +44,15 @@ class PaError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)} ({status})")
 
 
+def _require_abi(found: int) -> None:
+    """A library built from another header would be called with the wrong argument lists."""
+    if found != ABI_VERSION:
+        raise RuntimeError(f"{_LIB_PATH} has ABI version {found}, this binding expects {ABI_VERSION}: "
+                           "rebuild it with paged_kv_gqa_append_amd.build.build()")
+
+
 def lib():
-    """Load libpa.so (raises if it has not been built)."""
+    """Load libpa.so (raises if it has not been built, or was built from another header)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -51,6 +60,9 @@ def lib():
         raise RuntimeError(f"{_LIB_PATH} is missing: build it with paged_kv_gqa_append_amd.build.build() "
                            "(there is no fallback implementation)")
     L = ctypes.CDLL(_LIB_PATH)
+    L.pa_abi_version.restype = ctypes.c_int32
+    L.pa_abi_version.argtypes = []
+    _require_abi(int(L.pa_abi_version()))
     P, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_status_string.argtypes = [ctypes.c_int]

@@ -86,7 +86,7 @@ const char *pa_status_string(int status) {
     }
 }
 
-int32_t pa_abi_version(void) { return 6; }
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;

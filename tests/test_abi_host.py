@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == 6
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 6
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -211,6 +211,16 @@ def test_rope_table_fill(pa):
     assert np.array_equal(t[..., 1], np.sin(pos * w).astype(np.float32))
     assert pa.lib().pa_rope_table_fill_host(None, 3, 500000.0) == pa.PA_ERR_INVALID_ARG
     assert pa.lib().pa_rope_table_fill_host(t.ctypes.data_as(ctypes.c_void_p), 0, 500000.0) == pa.PA_ERR_INVALID_ARG
+
+
+def test_abi_version_matches_header():
+    from paged_kv_gqa_append_amd import binding
+
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")).read()
+    assert int(re.search(r"#define PA_ABI_VERSION (\d+)", hdr).group(1)) == binding.ABI_VERSION
+    binding._require_abi(binding.ABI_VERSION)
+    with pytest.raises(RuntimeError, match="rebuild"):
+        binding._require_abi(binding.ABI_VERSION - 1)
 
 
 def test_binding_refuses_without_library(tmp_path, monkeypatch):
