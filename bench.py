@@ -445,14 +445,14 @@ def main():
         binding.quantize_pages_i8(pool, k_pool, v_pool)
         torch.cuda.synchronize()
 
-    def step_fused():
+    def step_fused(order=None):
         for L in layers:
             if i8:
                 binding.append_decode_gqa_i8(L["out"], L["q"], L["k_new"], L["v_new"], pool, L["bt"], lens, table,
-                                             spec.scale, workspace=ws, stream=stream)
+                                             spec.scale, workspace=ws, dispatch_order=order, stream=stream)
             else:
                 binding.append_decode_gqa(L["out"], L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens,
-                                          table, spec.scale, workspace=ws, stream=stream)
+                                          table, spec.scale, workspace=ws, dispatch_order=order, stream=stream)
 
     def step_separate():
         for L in layers:
@@ -525,6 +525,16 @@ def main():
 
     kv_step = kv_step_bytes
     kv_launch = kv_step // spec.num_layers
+    # Ragged batches: the same fused step with the sequences dispatched longest first (the
+    # dispatch_order argument; same results bit for bit), reported beside the slot-order figures.
+    longest = None
+    if len(set(spec.context_lens.tolist())) > 1 and spec.num_seqs <= 1024:
+        order = np.ascontiguousarray(np.argsort(-spec.context_lens, kind="stable"), dtype=np.int32)
+        lf_ms = timed(lambda: step_fused(order), n_pass, 2)[0]
+        longest = {"ms_per_step": round(lf_ms, 5), "value": round(kv_step / (lf_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                   "tokens_per_s": round(spec.num_seqs / (lf_ms * 1e-3), 1),
+                   "mean_launch_us": round(lf_ms / spec.num_layers * 1e3, 2),
+                   "note": "fused step with dispatch_order = sequences by length, longest first"}
     # The same bytes per launch read as one contiguous stream by the plain read probe, from the
     # same pools, a different chunk per launch: the read bandwidth this GPU reaches at this size.
     ceil_gbps, ceil_us, ceil_chunks = stream_read_ceiling([pool] if i8 else [k_pool, v_pool], kv_launch, spec.num_layers,
@@ -566,6 +576,8 @@ def main():
                                       "frac_of_peak": round(ceil_gbps / HBM_PEAK_GBPS, 4),
                                       "decode_frac_of_stream_read": round(dec_gbps / ceil_gbps, 4)})},
     }
+    if longest is not None:
+        res["longest_first"] = longest
     if cold_ms is not None:
         res["cold"] = {"ms_per_step": round(cold_ms, 5), "value": round(kv_step / (cold_ms * 1e-3) / 1e9, 2),
                        "unit": "GB/s", "pct_hbm_peak": round(100.0 * kv_step / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),

@@ -88,7 +88,7 @@ const char *pa_status_string(int status);
 /* ABI version of this header, bumped on any signature or layout change;
  * pa_abi_version() returns the value of the header the library was built
  * from, so a caller can refuse a library built from another header.        */
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 int32_t pa_abi_version(void);
 
 /* Fill a HOST table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),
@@ -123,6 +123,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks);
  * not depend on the batch, so a sequence's result does not either.           */
 int32_t pa_decode_partition_tokens(void);
 
+/* dispatch_order (every decode entry point; HOST int32[num_seqs], may be NULL):
+ * the order in which the sequences' workgroups are dispatched, a permutation
+ * of 0 .. num_seqs-1 (entry 0 first).  NULL dispatches in slot order.  It
+ * changes no result: each sequence is computed the same way wherever it is
+ * dispatched.  A caller that knows its lengths on the host can pass them
+ * longest first, so that long sequences do not start last and form the
+ * launch's tail (ragged batches).  The order is copied into the launch's
+ * arguments, so the array may be reused when the call returns.  With
+ * P = ceil(max_blocks * 16 / pa_decode_partition_tokens()) partitions per
+ * sequence, PA_ERR_INVALID_ARG when it is not a permutation, when
+ * num_seqs * P exceeds PA_MAX_DISPATCH_ORDER, or when P exceeds 64.          */
+#define PA_MAX_DISPATCH_ORDER 1024
+
 /* Paged GQA decode (samir-vllm, batched-decode paragraph of "Gestion de la KV
  * cache ..."; tiny-vllm ch.2, "One buffer, two roles": the attention output is
  * written over the q buffer).  For each s, h < 32, j = h/4, L = context_lens[s]:
@@ -138,7 +151,7 @@ pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void
                         const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
                         int32_t max_blocks, int32_t num_pages, int32_t page_size, float scale,
                         int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                        uint32_t *device_flags, hipStream_t stream);
+                        uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
 
 /* One decode step of a layer in a single launch: pa_append_kv_rope followed by
  * pa_decode_gqa, fused (samir-vllm, "Gestion de la KV cache ...": the new
@@ -156,7 +169,7 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
                                const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                               uint32_t *device_flags, hipStream_t stream);
+                               uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
 
 /* Chunked prefill (TinyLoop, section "prefill_chunk and scratch residency":
  * the prompt is processed in row chunks; samir-vllm: the prompt's pages are
@@ -232,7 +245,7 @@ pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, vo
 pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, const int32_t *block_tables,
                            const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
                            int32_t page_size, float scale, int32_t out_dtype, void *workspace,
-                           size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream);
+                           size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
 
 /* pa_append_kv_rope_i8 followed by pa_decode_gqa_i8 in one launch, bitwise equal
  * to the two calls (same rotation, rounding and quantisation); q as in
@@ -242,7 +255,7 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
                                   const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                   int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                                  uint32_t *device_flags, hipStream_t stream);
+                                  uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
 
 /* --------------------------------------------------------------- argmax --
  * Greedy next-token choice on the GPU (samir-vllm, section "Architecture et

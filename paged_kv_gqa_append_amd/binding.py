@@ -35,7 +35,7 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class PaError(RuntimeError):
@@ -77,10 +77,10 @@ def lib():
     L.pa_decode_partition_tokens.restype = i32
     L.pa_decode_partition_tokens.argtypes = []
     L.pa_decode_gqa.restype = ctypes.c_int
-    L.pa_decode_gqa.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P]
+    L.pa_decode_gqa.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P, P]
     L.pa_append_decode_gqa.restype = ctypes.c_int
     L.pa_append_decode_gqa.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
-                                       u64, P, P]
+                                       u64, P, P, P]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
                                    P, P]
@@ -91,10 +91,10 @@ def lib():
     L.pa_append_kv_rope_i8.restype = ctypes.c_int
     L.pa_append_kv_rope_i8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P]
     L.pa_decode_gqa_i8.restype = ctypes.c_int
-    L.pa_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P]
+    L.pa_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P, P]
     L.pa_append_decode_gqa_i8.restype = ctypes.c_int
     L.pa_append_decode_gqa_i8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
-                                          u64, P, P]
+                                          u64, P, P, P]
     L.pa_argmax_workspace_bytes.restype = u64
     L.pa_argmax_workspace_bytes.argtypes = [i32, i32, i32]
     L.pa_argmax.restype = ctypes.c_int
@@ -140,6 +140,16 @@ def _check(rc: int, where: str) -> None:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _order(dispatch_order):
+    """Host int32 copy of an optional dispatch order (kept alive by the caller for the call)."""
+    if dispatch_order is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(dispatch_order, dtype=np.int32))
+    if arr.ndim != 1:
+        raise ValueError("dispatch_order must be a 1-D sequence of sequence indices")
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -218,7 +228,7 @@ def append_kv_rope(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.
 def decode_gqa(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float = 0.125,
                workspace: Optional[torch.Tensor] = None, device_flags: Optional[torch.Tensor] = None,
-               page_size: int = 16, stream=None) -> torch.Tensor:
+               page_size: int = 16, dispatch_order=None, stream=None) -> torch.Tensor:
     """pa_decode_gqa into ``out`` ([B][32][64] bf16 or fp32; may be ``q`` itself)."""
     num_pages = _pool_checks(k_pool, v_pool)
     dev = k_pool.device
@@ -238,9 +248,10 @@ def decode_gqa(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    order_arr, order_ptr = _order(dispatch_order)
     rc = lib().pa_decode_gqa(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
                              B, int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
-                             _ptr(workspace), ws_bytes, _ptr(device_flags), _stream(stream))
+                             _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, _stream(stream))
     _check(rc, "pa_decode_gqa")
     return out
 
@@ -249,7 +260,7 @@ def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
                       k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
                       context_lens: torch.Tensor, rope_cos_sin: torch.Tensor, scale: float = 0.125,
                       workspace: Optional[torch.Tensor] = None, device_flags: Optional[torch.Tensor] = None,
-                      page_size: int = 16, stream=None) -> torch.Tensor:
+                      page_size: int = 16, dispatch_order=None, stream=None) -> torch.Tensor:
     """pa_append_decode_gqa: append (RoPE K, V at pos = L-1), rotate q in place, then decode into ``out``."""
     num_pages = _pool_checks(k_pool, v_pool)
     dev = k_pool.device
@@ -272,10 +283,12 @@ def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    order_arr, order_ptr = _order(dispatch_order)
     rc = lib().pa_append_decode_gqa(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                     _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
                                     int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
-                                    float(scale), odt, _ptr(workspace), ws_bytes, _ptr(device_flags), _stream(stream))
+                                    float(scale), odt, _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr,
+                                    _stream(stream))
     _check(rc, "pa_append_decode_gqa")
     return out
 
@@ -391,7 +404,8 @@ def append_kv_rope_i8(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: tor
 
 def decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, kv_pool_i8: torch.Tensor, block_tables: torch.Tensor,
                   context_lens: torch.Tensor, scale: float = 0.125, workspace: Optional[torch.Tensor] = None,
-                  device_flags: Optional[torch.Tensor] = None, page_size: int = 16, stream=None) -> torch.Tensor:
+                  device_flags: Optional[torch.Tensor] = None, page_size: int = 16, dispatch_order=None,
+                  stream=None) -> torch.Tensor:
     """pa_decode_gqa_i8 into ``out`` ([B][32][64] bf16 or fp32; may be ``q`` itself)."""
     num_pages = _i8_pool_checks(kv_pool_i8)
     dev = kv_pool_i8.device
@@ -402,9 +416,10 @@ def decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, kv_pool_i8: torch.Tensor, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    order_arr, order_ptr = _order(dispatch_order)
     rc = lib().pa_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(kv_pool_i8), _ptr(block_tables), _ptr(context_lens), B,
                                 int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
-                                _ptr(workspace), ws_bytes, _ptr(device_flags), _stream(stream))
+                                _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, _stream(stream))
     _check(rc, "pa_decode_gqa_i8")
     return out
 
@@ -413,7 +428,7 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
                          kv_pool_i8: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                          rope_cos_sin: torch.Tensor, scale: float = 0.125, workspace: Optional[torch.Tensor] = None,
                          device_flags: Optional[torch.Tensor] = None, page_size: int = 16,
-                         stream=None) -> torch.Tensor:
+                         dispatch_order=None, stream=None) -> torch.Tensor:
     """pa_append_decode_gqa_i8: quantised append at pos = L-1, q rotated in place, then decode into ``out``."""
     num_pages = _i8_pool_checks(kv_pool_i8)
     dev = kv_pool_i8.device
@@ -427,11 +442,12 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    order_arr, order_ptr = _order(dispatch_order)
     rc = lib().pa_append_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_pool_i8),
                                        _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
                                        int(block_tables.shape[1]), num_pages, int(page_size),
                                        int(rope_cos_sin.shape[0]), float(scale), odt, _ptr(workspace), ws_bytes,
-                                       _ptr(device_flags), _stream(stream))
+                                       _ptr(device_flags), order_ptr, _stream(stream))
     _check(rc, "pa_append_decode_gqa_i8")
     return out
 

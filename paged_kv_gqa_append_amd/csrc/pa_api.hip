@@ -20,15 +20,33 @@ int64_t decode_num_parts(int32_t max_blocks) {
 }
 
 
+static_assert(PA_MAX_DISPATCH_ORDER == pa::kMaxDispatchOrder, "dispatch order bound");
+
+// A dispatch order: at most PA_MAX_DISPATCH_ORDER entries, each of 0 .. n-1 once.
+bool is_permutation(const int32_t *order, int32_t n) {
+    if (n > PA_MAX_DISPATCH_ORDER) return false;
+    bool seen[PA_MAX_DISPATCH_ORDER] = {};
+    for (int32_t i = 0; i < n; ++i) {
+        const int32_t s = order[i];
+        if (s < 0 || s >= n || seen[s]) return false;
+        seen[s] = true;
+    }
+    return true;
+}
+
 // Shared argument checks and launch of the plain and the append-fused decode,
 // over bf16 pools (k_pool, v_pool) or an INT8 tile pool (k_pool; v_pool unused).
 pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
                         const int32_t *block_tables, const int32_t *context_lens, const float *rope,
                         int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                         float scale, int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                        uint32_t *device_flags, hipStream_t stream, bool fused, bool i8 = false) {
+                        uint32_t *device_flags, const int32_t *order, hipStream_t stream, bool fused,
+                        bool i8 = false) {
     if (i8) v_pool = k_pool;
     if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (order && (!is_permutation(order, num_seqs) || decode_num_parts(max_blocks) > pa::kMaxOrderParts ||
+                  static_cast<int64_t>(num_seqs) * decode_num_parts(max_blocks) > PA_MAX_DISPATCH_ORDER))
+        return PA_ERR_INVALID_ARG;
     if (fused && max_pos < 1) return PA_ERR_INVALID_ARG;
     if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
     if (out_dtype != PA_OUT_BF16 && out_dtype != PA_OUT_FP32) return PA_ERR_UNSUPPORTED;
@@ -67,6 +85,7 @@ pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new
     d.ws_ml = need ? ws : nullptr;
     d.ws_acc = need ? ws + rows * 2 : nullptr;
     d.flags = device_flags;
+    d.order = order;
     return (i8 ? pa::launch_decode_i8(d, stream) : pa::launch_decode(d, stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -131,21 +150,23 @@ int32_t pa_decode_partition_tokens(void) { return pa::decode_part_pages() * PA_P
 pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void *v_pool,
                         const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
                         int32_t max_blocks, int32_t num_pages, int32_t page_size, float scale, int32_t out_dtype,
-                        void *workspace, size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream) {
+                        void *workspace, size_t workspace_bytes, uint32_t *device_flags,
+                        const int32_t *dispatch_order, hipStream_t stream) {
     return decode_common(out, const_cast<void *>(q), nullptr, nullptr, const_cast<void *>(k_pool),
                          const_cast<void *>(v_pool), block_tables, context_lens, nullptr, num_seqs, max_blocks,
-                         num_pages, page_size, 0, scale, out_dtype, workspace, workspace_bytes, device_flags, stream,
-                         false);
+                         num_pages, page_size, 0, scale, out_dtype, workspace, workspace_bytes, device_flags,
+                         dispatch_order, stream, false);
 }
 
 pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
                                const int32_t *block_tables, const int32_t *context_lens, const float *rope_cos_sin,
                                int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size,
                                int32_t max_pos, float scale, int32_t out_dtype, void *workspace,
-                               size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream) {
+                               size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
+                               hipStream_t stream) {
     return decode_common(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin, num_seqs,
                          max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace, workspace_bytes,
-                         device_flags, stream, true);
+                         device_flags, dispatch_order, stream, true);
 }
 
 pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool, void *v_pool,
@@ -210,10 +231,11 @@ pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, vo
 pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, const int32_t *block_tables,
                            const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
                            int32_t page_size, float scale, int32_t out_dtype, void *workspace,
-                           size_t workspace_bytes, uint32_t *device_flags, hipStream_t stream) {
+                           size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
+                           hipStream_t stream) {
     return decode_common(out, const_cast<void *>(q), nullptr, nullptr, const_cast<void *>(kv_pool_i8), nullptr,
                          block_tables, context_lens, nullptr, num_seqs, max_blocks, num_pages, page_size, 0, scale,
-                         out_dtype, workspace, workspace_bytes, device_flags, stream, false, true);
+                         out_dtype, workspace, workspace_bytes, device_flags, dispatch_order, stream, false, true);
 }
 
 pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
@@ -221,10 +243,10 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
                                   const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                   int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                                  uint32_t *device_flags, hipStream_t stream) {
+                                  uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream) {
     return decode_common(out, q, k_new, v_new, kv_pool_i8, nullptr, block_tables, context_lens, rope_cos_sin,
                          num_seqs, max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace,
-                         workspace_bytes, device_flags, stream, true, true);
+                         workspace_bytes, device_flags, dispatch_order, stream, true, true);
 }
 
 size_t pa_argmax_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t logits_dtype) {

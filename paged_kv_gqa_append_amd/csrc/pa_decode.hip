@@ -56,14 +56,14 @@
 
 namespace pa {
 
-template <int kWaves, bool kFused, bool kRows>
-__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P) {
+template <int kWaves, bool kFused, bool kRows, bool kOrd>
+__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P, DispatchOrder<kOrd> order) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
-    const int part = blockIdx.x % P.num_parts;
-    const int sj = blockIdx.x / P.num_parts;
-    const int j = sj & (kHKV - 1);
-    const int s = sj >> 3;
+    const WgCoords wc = wg_coords(order, P.num_parts);
+    const int part = wc.part;
+    const int j = wc.j;
+    const int s = wc.s;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -440,13 +440,18 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream) {
     // workgroups) the slot-order form is ahead, 11.9 against 12.9 us.
     const bool rows = blocks >= kNtMinBlocks;
     const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWaves);
-    if (d.fused) {
-        if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, true>), grid, wg, 0, stream, P);
-        else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, false>), grid, wg, 0, stream, P);
-    } else {
-        if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, true>), grid, wg, 0, stream, P);
-        else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, false>), grid, wg, 0, stream, P);
-    }
+    auto go = [&](auto order) {
+        constexpr bool kOrd = !std::is_empty_v<decltype(order)>;
+        if (d.fused) {
+            if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, true, kOrd>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, false, kOrd>), grid, wg, 0, stream, P, order);
+        } else {
+            if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, true, kOrd>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, false, kOrd>), grid, wg, 0, stream, P, order);
+        }
+    };
+    if (d.order) go(make_dispatch_order(d.order, d.num_seqs, d.num_parts));
+    else go(DispatchOrder<false>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.num_parts == 1) return e;
     if (d.fused)

@@ -11,6 +11,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -28,6 +30,48 @@ constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold
 // quad_perm broadcasts of quad lane a to the whole quad: [a,a,a,a]
 constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;
 constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRowRor8 = 0x128;
+
+// Dispatch order, passed by value in the launch arguments.  Workgroups
+// 8i .. 8i+7 (the 8 KV heads) serve item[i] = (sequence << 6) | partition;
+// the item depends on the workgroup id alone, so its load from the launch
+// arguments goes out with the parameters' and adds no step to a workgroup's
+// start.  The unordered form is empty: workgroup b serves (sequence, KV head)
+// b / num_parts and partition b % num_parts.
+constexpr int kOrderPartBits = 6;
+static_assert((1 << kOrderPartBits) == kMaxOrderParts, "partition field of a dispatch item");
+template <bool kOrd>
+struct DispatchOrder {};
+template <>
+struct DispatchOrder<true> {
+    uint16_t item[kMaxDispatchOrder];
+};
+
+struct WgCoords {
+    int s, j, part;
+};
+
+template <bool kOrd>
+__device__ __forceinline__ WgCoords wg_coords(const DispatchOrder<kOrd> &o, int num_parts) {
+    const int b = blockIdx.x;
+    if constexpr (kOrd) {
+        const int item = o.item[b >> 3];
+        return {item >> kOrderPartBits, b & (kHKV - 1), item & (kMaxOrderParts - 1)};
+    } else {
+        const int sj = b / num_parts;
+        return {sj >> 3, sj & (kHKV - 1), b % num_parts};
+    }
+}
+
+// The ordered form for a host-checked permutation of the n sequences, with
+// n * num_parts <= kMaxDispatchOrder and num_parts <= kMaxOrderParts: each
+// sequence's partitions follow one another, in the given sequence order.
+inline DispatchOrder<true> make_dispatch_order(const int32_t *order, int n, int num_parts) {
+    DispatchOrder<true> o{};
+    int k = 0;
+    for (int i = 0; i < n; ++i)
+        for (int p = 0; p < num_parts; ++p) o.item[k++] = static_cast<uint16_t>((order[i] << kOrderPartBits) | p);
+    return o;
+}
 
 // a page's K and V chunks of one lane, in load order (two loads of each tile)
 struct KVRegs {

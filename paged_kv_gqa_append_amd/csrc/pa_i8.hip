@@ -256,14 +256,14 @@ __device__ __forceinline__ float max_quarters(float v) {
 // out (as in the bf16 kernel).  The s_setprio instructions also constrain how
 // the compiler schedules the page loop, so the form without them is kept for
 // grids where levelling does not pay (see launch_decode_i8).
-template <int kWaves, bool kFused, bool kNt, bool kLevel>
-__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P) {
+template <int kWaves, bool kFused, bool kNt, bool kLevel, bool kOrd>
+__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P, DispatchOrder<kOrd> order) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
-    const int part = blockIdx.x % P.num_parts;
-    const int sj = blockIdx.x / P.num_parts;
-    const int j = sj & (kHKV - 1);
-    const int s = sj >> 3;
+    const WgCoords wc = wg_coords(order, P.num_parts);
+    const int part = wc.part;
+    const int j = wc.j;
+    const int s = wc.s;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -700,15 +700,21 @@ hipError_t launch_decode_i8(const DecodeLaunch &d, hipStream_t stream) {
     const bool nt = blocks >= kNtMinBlocks;
     const bool level = blocks <= kPrioMaxBlocksI8;
     const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWavesI8);
-    if (d.fused) {
-        if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, false, true>), grid, wg, 0, stream, P);
-        else if (level) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, true, true>), grid, wg, 0, stream, P);
-        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, true, true, false>), grid, wg, 0, stream, P);
-    } else {
-        if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, false, true>), grid, wg, 0, stream, P);
-        else if (level) hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, true, true>), grid, wg, 0, stream, P);
-        else hipLaunchKernelGGL((k_decode_paged_i8<kDecodeWavesI8, false, true, false>), grid, wg, 0, stream, P);
-    }
+    auto go = [&](auto order) {
+        constexpr bool kOrd = !std::is_empty_v<decltype(order)>;
+        constexpr int W = kDecodeWavesI8;
+        if (d.fused) {
+            if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<W, true, false, true, kOrd>), grid, wg, 0, stream, P, order);
+            else if (level) hipLaunchKernelGGL((k_decode_paged_i8<W, true, true, true, kOrd>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged_i8<W, true, true, false, kOrd>), grid, wg, 0, stream, P, order);
+        } else {
+            if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<W, false, false, true, kOrd>), grid, wg, 0, stream, P, order);
+            else if (level) hipLaunchKernelGGL((k_decode_paged_i8<W, false, true, true, kOrd>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged_i8<W, false, true, false, kOrd>), grid, wg, 0, stream, P, order);
+        }
+    };
+    if (d.order) go(make_dispatch_order(d.order, d.num_seqs, d.num_parts));
+    else go(DispatchOrder<false>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.num_parts == 1) return e;
     if (d.fused)

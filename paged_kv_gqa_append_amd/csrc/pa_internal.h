@@ -25,6 +25,12 @@ struct AppendLaunch {
     uint32_t *flags;
 };
 
+// Bounds of a dispatch order: at most kMaxDispatchOrder (sequence, partition)
+// items (16-bit entries in the launch arguments, 2 KiB), and at most
+// kMaxOrderParts partitions per sequence (the item's low 6 bits).
+constexpr int kMaxDispatchOrder = 1024;
+constexpr int kMaxOrderParts = 64;
+
 struct DecodeLaunch {
     void *out;
     void *q;              // read-only unless fused (then rotated in place when write_q)
@@ -48,6 +54,7 @@ struct DecodeLaunch {
     float *ws_ml;         // [B][32][num_parts][2]  (max in log2 units, sum of weights)
     float *ws_acc;        // [B][32][num_parts][64]
     uint32_t *flags;
+    const int32_t *order; // host dispatch order (a checked permutation), or NULL for slot order
 };
 
 struct PrefillLaunch {

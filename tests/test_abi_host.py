@@ -45,17 +45,18 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 6
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 7
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
 
 
 def decode_call(lib, out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, B=4, mb=8, P=64, ps=16, scale=0.125,
-                odt=0, ws=None, wsb=0):
+                odt=0, ws=None, wsb=0, order=None):
     v = ctypes.c_void_p
+    op = None if order is None else np.ascontiguousarray(order, dtype=np.int32).ctypes.data_as(v)
     return lib.pa_decode_gqa(v(out), v(q), v(kp), v(vp), v(bt), v(cl), B, mb, P, ps, scale, odt, v(ws) if ws else None,
-                             wsb, None, None)
+                             wsb, None, op, None)
 
 
 def test_decode_validation(pa):
@@ -78,6 +79,26 @@ def test_decode_validation(pa):
         assert decode_call(lib, mb=mb) == pa.PA_ERR_WORKSPACE
         assert decode_call(lib, mb=mb, ws=FAKE, wsb=need - 4) == pa.PA_ERR_WORKSPACE
         assert decode_call(lib, mb=mb, ws=FAKE + 4, wsb=need) == pa.PA_ERR_WORKSPACE
+
+
+def test_dispatch_order_validation(pa):
+    """A dispatch order must be a permutation of the batch and fit the launch
+    arguments (sequences x partitions <= PA_MAX_DISPATCH_ORDER, at most 64
+    partitions); otherwise the call is refused before anything is launched."""
+    lib = pa.lib()
+    for bad in ([0, 1, 2, 2], [0, 1, 2, 4], [0, 1, 2, -1], [3, 3, 3, 3]):  # B = 4 entries each
+        assert decode_call(lib, order=bad) == pa.PA_ERR_INVALID_ARG, bad
+    pp = lib.pa_decode_partition_tokens() // 16
+    big = np.arange(1025, dtype=np.int32)
+    assert decode_call(lib, B=1025, order=big) == pa.PA_ERR_INVALID_ARG
+    # 512 sequences of 3 partitions each: 1536 items
+    assert decode_call(lib, B=512, mb=2 * pp + 1, order=np.arange(512)) == pa.PA_ERR_INVALID_ARG
+    # 65 partitions of one sequence
+    assert decode_call(lib, B=1, mb=64 * pp + 1, order=[0]) == pa.PA_ERR_INVALID_ARG
+    # the order is checked before the rest: a valid one leaves the other errors as they were
+    assert decode_call(lib, ps=32, order=[3, 2, 1, 0]) == pa.PA_ERR_UNSUPPORTED
+    assert decode_call(lib, q=0, order=[3, 2, 1, 0]) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, B=0, q=0, out=0, order=[]) == pa.PA_OK
 
 
 def test_workspace_arithmetic(pa):
@@ -144,7 +165,7 @@ def test_i8_validation(pa):
     assert app(B=0) == pa.PA_OK
 
     def dec(out=F, pool=F, B=4, mb=8, ps=16, odt=0, scale=0.125, ws=None, wsb=0):
-        return lib.pa_decode_gqa_i8(out, F, pool, F, F, B, mb, 64, ps, scale, odt, ws, wsb, None, None)
+        return lib.pa_decode_gqa_i8(out, F, pool, F, F, B, mb, 64, ps, scale, odt, ws, wsb, None, None, None)
 
     assert dec(ps=32) == pa.PA_ERR_UNSUPPORTED
     assert dec(odt=3) == pa.PA_ERR_UNSUPPORTED
@@ -157,7 +178,7 @@ def test_i8_validation(pa):
 
     def fused(rope=F, mp=64):
         return lib.pa_append_decode_gqa_i8(F, F, F, F, F, F, F, rope, 4, 8, 64, 16, mp, 0.125, 0, None, 0, None,
-                                           None)
+                                           None, None)
 
     assert fused(rope=None) == pa.PA_ERR_INVALID_ARG
     assert fused(mp=0) == pa.PA_ERR_INVALID_ARG
