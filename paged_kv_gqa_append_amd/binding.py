@@ -143,13 +143,16 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _order(dispatch_order):
-    """Host int32 copy of an optional dispatch order (kept alive by the caller for the call)."""
+    """Host int32 view or copy of an optional dispatch order, and its address (the caller keeps
+    the array alive for the call).  A contiguous int32 numpy array is used as it is."""
     if dispatch_order is None:
         return None, None
-    arr = np.ascontiguousarray(np.asarray(dispatch_order, dtype=np.int32))
+    arr = dispatch_order
+    if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
+        arr = np.ascontiguousarray(np.asarray(dispatch_order, dtype=np.int32))
     if arr.ndim != 1:
         raise ValueError("dispatch_order must be a 1-D sequence of sequence indices")
-    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+    return arr, ctypes.c_void_p(arr.ctypes.data)
 
 
 def _stream(stream) -> ctypes.c_void_p:
