@@ -508,7 +508,7 @@ def main():
     # Timed before the cold runs, after the same time-based warmup as the main figures.
     lf_ms = None
     if len(set(spec.context_lens.tolist())) > 1 and spec.num_seqs <= 1024:
-        order = np.ascontiguousarray(np.argsort(-spec.context_lens, kind="stable"), dtype=np.int32)
+        order = binding.dispatch_order_longest_first(spec.context_lens)
         lf_ms = timed(lambda: step_fused(order), n_pass, None)[0]
 
     # Cold runs for workloads whose K/V fit in the 256 MB MALL (Infinity Cache): before each

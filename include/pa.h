@@ -88,7 +88,7 @@ const char *pa_status_string(int status);
 /* ABI version of this header, bumped on any signature or layout change;
  * pa_abi_version() returns the value of the header the library was built
  * from, so a caller can refuse a library built from another header.        */
-#define PA_ABI_VERSION 7
+#define PA_ABI_VERSION 8
 int32_t pa_abi_version(void);
 
 /* Fill a HOST table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),
@@ -135,6 +135,13 @@ int32_t pa_decode_partition_tokens(void);
  * sequence, PA_ERR_INVALID_ARG when it is not a permutation, when
  * num_seqs * P exceeds PA_MAX_DISPATCH_ORDER, or when P exceeds 64.          */
 #define PA_MAX_DISPATCH_ORDER 1024
+
+/* Host helper: order[0 .. n-1] = the indices 0 .. n-1 sorted by lengths[i],
+ * longest first, equal lengths in index order (a stable sort): the dispatch
+ * order that starts long sequences first.  lengths and order are HOST arrays
+ * of n int32 (they may not overlap).  PA_ERR_INVALID_ARG for n < 0 or a NULL
+ * array with n > 0.                                                           */
+pa_status pa_dispatch_order_longest_first(const int32_t *lengths, int32_t n, int32_t *order);
 
 /* Paged GQA decode (samir-vllm, batched-decode paragraph of "Gestion de la KV
  * cache ..."; tiny-vllm ch.2, "One buffer, two roles": the attention output is

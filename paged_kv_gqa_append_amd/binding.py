@@ -31,11 +31,12 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_schedule", "pa_kvm_set_length", "pa_kvm_release", "pa_kvm_block_tables", "pa_kvm_lengths",
            "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
-           "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read")
+           "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read",
+           "pa_dispatch_order_longest_first")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class PaError(RuntimeError):
@@ -99,6 +100,8 @@ def lib():
     L.pa_argmax_workspace_bytes.argtypes = [i32, i32, i32]
     L.pa_argmax.restype = ctypes.c_int
     L.pa_argmax.argtypes = [P, P, i32, i32, i32, P, u64, P]
+    L.pa_dispatch_order_longest_first.restype = ctypes.c_int
+    L.pa_dispatch_order_longest_first.argtypes = [P, i32, P]
     L.pa_probe_stream_read.restype = ctypes.c_int
     L.pa_probe_stream_read.argtypes = [P, u64, P, P]
     i64 = ctypes.c_int64
@@ -482,6 +485,17 @@ def argmax(out_index: torch.Tensor, logits: torch.Tensor, workspace: Optional[to
     _check(lib().pa_argmax(_ptr(out_index), _ptr(logits), rows, vocab, code, _ptr(workspace), ws_bytes,
                            _stream(stream)), "pa_argmax")
     return out_index
+
+
+def dispatch_order_longest_first(lengths) -> np.ndarray:
+    """pa_dispatch_order_longest_first: batch indices by length, longest first (stable), as the
+    int32 array the decode calls take as dispatch_order."""
+    lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    order = np.empty(lens.shape[0], dtype=np.int32)
+    _check(lib().pa_dispatch_order_longest_first(ctypes.c_void_p(lens.ctypes.data), int(lens.shape[0]),
+                                                 ctypes.c_void_p(order.ctypes.data)),
+           "pa_dispatch_order_longest_first")
+    return order
 
 
 def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

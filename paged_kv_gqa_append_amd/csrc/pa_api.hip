@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pa.h"
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -274,6 +276,13 @@ pa_status pa_argmax(int32_t *out_index, const void *logits, int32_t num_rows, in
     const bool vec = aligned16(logits) && (static_cast<size_t>(vocab) * esz) % 16 == 0;
     return pa::launch_argmax(out_index, logits, num_rows, vocab, bf16, vec, workspace, stream) == hipSuccess
                ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_dispatch_order_longest_first(const int32_t *lengths, int32_t n, int32_t *order) {
+    if (n < 0 || (n > 0 && (!lengths || !order))) return PA_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order, order + n, [lengths](int32_t a, int32_t b) { return lengths[a] > lengths[b]; });
+    return PA_OK;
 }
 
 pa_status pa_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {

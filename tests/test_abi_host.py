@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 7
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 8
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -99,6 +99,18 @@ def test_dispatch_order_validation(pa):
     assert decode_call(lib, ps=32, order=[3, 2, 1, 0]) == pa.PA_ERR_UNSUPPORTED
     assert decode_call(lib, q=0, order=[3, 2, 1, 0]) == pa.PA_ERR_INVALID_ARG
     assert decode_call(lib, B=0, q=0, out=0, order=[]) == pa.PA_OK
+
+
+def test_dispatch_order_helper(pa):
+    """The longest-first helper is a stable descending sort of the lengths."""
+    rng = np.random.default_rng(5)
+    for n in (0, 1, 7, 256, 1000):
+        lens = rng.integers(1, 40, size=n).astype(np.int32)  # many ties
+        got = pa.dispatch_order_longest_first(lens)
+        assert np.array_equal(got, np.argsort(-lens.astype(np.int64), kind="stable").astype(np.int32))
+    assert pa.lib().pa_dispatch_order_longest_first(None, 3, None) == pa.PA_ERR_INVALID_ARG
+    assert pa.lib().pa_dispatch_order_longest_first(None, -1, None) == pa.PA_ERR_INVALID_ARG
+    assert pa.lib().pa_dispatch_order_longest_first(None, 0, None) == pa.PA_OK
 
 
 def test_workspace_arithmetic(pa):
