@@ -414,7 +414,7 @@ def main():
 
     from paged_kv_gqa_append_amd import binding, build
 
-    if not build.is_built():
+    if not build.is_current():
         build.build()
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))

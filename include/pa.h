@@ -49,7 +49,12 @@
  *     on the host: a bad length or page id found by a kernel is never
  *     dereferenced; the kernel skips (append) or zero-fills (decode/prefill)
  *     the affected sequence and ORs a PA_DEVERR_* bit into *device_flags when
- *     that pointer is not NULL.
+ *     that pointer is not NULL (pa_get_device_error reads it back).
+ *   Values: inputs are finite bf16; every score scale * <q, K_t> must be
+ *     finite in fp32 (|score| < 2^127), and max |V| times the context length
+ *     must stay below 2^119 (the weighted V sums are accumulated in fp32 with
+ *     weights up to 2^8: e.g. |V| < 2^108, about 3e32, at 2048 tokens).  The
+ *     outputs are then finite.
  */
 #ifndef PAGED_KV_GQA_APPEND_PA_H
 #define PAGED_KV_GQA_APPEND_PA_H
@@ -82,16 +87,44 @@ typedef enum { PA_OUT_BF16 = 0, PA_OUT_FP32 = 1 } pa_out_dtype;
 #define PA_DEVERR_CONTEXT_LEN 0x1u /* L < 1, or L beyond max_blocks*16 / max_pos */
 #define PA_DEVERR_PAGE_ID 0x2u     /* a used block-table entry outside [0, num_pages) */
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL).  Every
+ * call reports failure through its return value and the caller must not go on
+ * with what the failed call was to produce (TinyLoop, "Lifecycle and Memory
+ * Model", section "Internal allocation phases": a failed load hands back
+ * nothing and the caller must stop there; tiny-vllm ch.2 "Weight Loading and
+ * GPU Buffer Design", opening section: the device check reports a missing GPU
+ * as an error return rather than aborting).                                  */
 const char *pa_status_string(int status);
+
+/* Device-side errors, read back (debug helper; SYNCHRONISES).  The kernels
+ * never abort: a bad length or page id found in device-resident tables is
+ * flagged by OR-ing a PA_DEVERR_* bit into the caller's *device_flags word
+ * (see "Errors" above), so that, as in TinyLoop's "Internal allocation
+ * phases", the failure reaches the caller, who must not use the affected
+ * outputs.  This call waits for `stream` to drain, copies the word to the host
+ * and returns it (a combination of PA_DEVERR_* bits, 0 when nothing was
+ * flagged); with clear != 0 it also resets the word to 0, in stream order,
+ * before returning.  Returns -PA_ERR_INVALID_ARG for a NULL or misaligned
+ * pointer and -PA_ERR_HIP when the runtime fails (including an asynchronous
+ * error of earlier work on the stream).  Not for hot loops or graph capture. */
+int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t stream);
 
 /* ABI version of this header, bumped on any signature or layout change;
  * pa_abi_version() returns the value of the header the library was built
- * from, so a caller can refuse a library built from another header.        */
-#define PA_ABI_VERSION 8
+ * from, so a caller can refuse a library built from another header.  Like the
+ * fixed geometry (samir-vllm, section "Limitations et perspectives": changing
+ * the architecture means recompiling), a mismatch is refused, not adapted to. */
+#define PA_ABI_VERSION 9
 int32_t pa_abi_version(void);
 
-/* Fill a HOST table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),
+/* Identity of the sources the library was built from: the sha256 (64 hex
+ * characters, static string) of its kernel and ABI sources and compile
+ * flags, so a binding can refuse a library older than the sources beside it. */
+const char *pa_build_id(void);
+
+/* The RoPE frequency table the initialization block builds (tiny-vllm ch.2,
+ * section "What else is set up in the initialization block").  Fill a HOST
+ * table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),
  * evaluated in double precision and rounded once to fp32.  The caller copies
  * it to the device.  Frequencies are unscaled; theta = 500000 for Llama 3.
  * Returns PA_ERR_INVALID_ARG for a NULL table, max_pos < 1 or theta <= 1.     */
@@ -116,16 +149,31 @@ pa_status pa_append_kv_rope(void *q, const void *k_new, const void *v_new, void 
 /* Bytes of device workspace pa_decode_gqa needs for num_seqs sequences whose
  * block tables have max_blocks entries (0 when one context partition always
  * suffices).  The workspace holds per-partition softmax partials; it needs no
- * initialisation and its contents are dead between calls.                    */
+ * initialisation and its contents are dead between calls.  As with the
+ * engines' compute buffers, the caller allocates it once, up front, and hands
+ * it to every call (tiny-vllm ch.2, section "Preallocating the 16 compute
+ * buffers"; TinyLoop, "Lifecycle and Memory Model", section "Why this memory
+ * design exists": no allocation churn in hot paths).                         */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks);
 
-/* Tokens per context partition pa_decode_gqa uses (a multiple of 16).  It does
- * not depend on the batch, so a sequence's result does not either.           */
+/* Tokens per context partition pa_decode_gqa uses (a multiple of 16; 2048 by
+ * default, the engines' whole context window, samir-vllm "Limitations et
+ * perspectives").  It does not depend on the batch, so a sequence's result
+ * does not either (the article notes its engine's batched results may differ
+ * from single runs; this library's do not).
+ * Test switch: the environment variable PA_DECODE_PART_PAGES (1 .. 128 pages),
+ * read once per process at the first decode call, overrides the default.  It
+ * changes the summation order, hence the output bits, of every decode in the
+ * process; results stay within the same tolerance of the exact attention and
+ * remain batch-invariant within the process.  It exists to exercise the
+ * partition merge; production callers leave it unset.                        */
 int32_t pa_decode_partition_tokens(void);
 
 /* dispatch_order (every decode entry point; HOST int32[num_seqs], may be NULL):
  * the order in which the sequences' workgroups are dispatched, a permutation
- * of 0 .. num_seqs-1 (entry 0 first).  NULL dispatches in slot order.  It
+ * of 0 .. num_seqs-1 (entry 0 first).  The array must hold exactly num_seqs
+ * entries: the library reads num_seqs of them and cannot see a shorter or
+ * longer array (the Python binding refuses one whose length differs).  NULL dispatches in slot order.  It
  * changes no result: each sequence is computed the same way wherever it is
  * dispatched.  A caller that knows its lengths on the host can pass them
  * longest first, so that long sequences do not start last and form the
@@ -207,7 +255,10 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
  * symmetric fp32 scale per (token, KV head) row of 64 values:
  *   scale = max|x| / 127,  code = round-half-even(x / scale) in [-127, 127],
  * both in IEEE binary32, scale 0 and codes 0 for an all-zero row (rows must be
- * finite).  The value a code stands for is code * scale.  K rows are quantised
+ * finite; the decode accepts V over the same range as the bf16 pools, see
+ * "Values" above: the V scales reach the f16 MFMA weights through a running
+ * power-of-two exponent, so large V rows neither overflow nor lose precision).  The value a code stands for is
+ * code * scale.  K rows are quantised
  * after RoPE from the bf16-rounded rotated row (the row pa_append_kv_rope would
  * store), V rows from their bf16 input.
  *

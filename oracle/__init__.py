@@ -28,7 +28,21 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A test may point the wrapper at another build of an oracle.c copy (the mutation sweep
+# in tests/test_oracle_mutation.py); that library is loaded as it is, never rebuilt.
+_OVERRIDE = os.environ.get("PA_ORACLE_LIB")
 _lib = None
+
+CFLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra", "-fno-fast-math",
+          "-ffp-contract=off"]
+
+
+def compile_c(src: str, out: str) -> str:
+    """gcc src (an oracle.c) into the shared library out, with the oracle's flags."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
 
 OK, BAD_ARG, BAD_LEN, BAD_PAGE = 0, 1, 2, 3
 
@@ -36,11 +50,7 @@ OK, BAD_ARG, BAD_LEN, BAD_PAGE = 0, 1, 2, 3
 def build(force: bool = True) -> str:
     """Compile oracle.c with gcc (-O2, OpenMP) into oracle/liboracle.so."""
     if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
-               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
+        compile_c(_SRC, _LIB_PATH)
     return _LIB_PATH
 
 
@@ -48,9 +58,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _OVERRIDE:
+        lib = ctypes.CDLL(_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i32 = ctypes.c_int32
     dbl = ctypes.c_double

@@ -32,11 +32,11 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
            "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read",
-           "pa_dispatch_order_longest_first")
+           "pa_dispatch_order_longest_first", "pa_get_device_error", "pa_build_id")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class PaError(RuntimeError):
@@ -52,8 +52,20 @@ def _require_abi(found: int) -> None:
                            "rebuild it with paged_kv_gqa_append_amd.build.build()")
 
 
+def _require_current(built_id: str) -> None:
+    """A library built from older sources than the ones beside it would run stale kernels."""
+    from . import build as _build
+
+    want = _build.source_digest()
+    if built_id != want:
+        raise RuntimeError(f"{_LIB_PATH} was built from other sources (build id {built_id[:12]}..., the tree's "
+                           f"sources hash to {want[:12]}...): rebuild it with "
+                           "paged_kv_gqa_append_amd.build.build()")
+
+
 def lib():
-    """Load libpa.so (raises if it has not been built, or was built from another header)."""
+    """Load libpa.so (raises if it has not been built, was built from another header, or from
+    sources other than the ones in the tree)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -64,6 +76,9 @@ def lib():
     L.pa_abi_version.restype = ctypes.c_int32
     L.pa_abi_version.argtypes = []
     _require_abi(int(L.pa_abi_version()))
+    L.pa_build_id.restype = ctypes.c_char_p
+    L.pa_build_id.argtypes = []
+    _require_current(L.pa_build_id().decode())
     P, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_status_string.argtypes = [ctypes.c_int]
@@ -104,6 +119,8 @@ def lib():
     L.pa_dispatch_order_longest_first.argtypes = [P, i32, P]
     L.pa_probe_stream_read.restype = ctypes.c_int
     L.pa_probe_stream_read.argtypes = [P, u64, P, P]
+    L.pa_get_device_error.restype = i32
+    L.pa_get_device_error.argtypes = [P, i32, P]
     i64 = ctypes.c_int64
     L.pa_admission_credit_pages.restype = i64
     L.pa_admission_credit_pages.argtypes = [i32, i32, i32]
@@ -132,6 +149,16 @@ def lib():
     return L
 
 
+def get_device_error(device_flags: torch.Tensor, clear: bool = False, stream=None) -> int:
+    """pa_get_device_error: wait for the stream, return the PA_DEVERR_* bits of the caller's
+    device flag word (and reset it to 0 when ``clear``).  Synchronises: a debug helper."""
+    _expect(device_flags, "device_flags", torch.int32, (1,))
+    rc = int(lib().pa_get_device_error(_ptr(device_flags), 1 if clear else 0, _stream(stream)))
+    if rc < 0:
+        raise PaError(-rc, "pa_get_device_error")
+    return rc
+
+
 def status_string(status: int) -> str:
     return lib().pa_status_string(int(status)).decode()
 
@@ -145,16 +172,18 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _order(dispatch_order):
+def _order(dispatch_order, num_seqs: int):
     """Host int32 view or copy of an optional dispatch order, and its address (the caller keeps
-    the array alive for the call).  A contiguous int32 numpy array is used as it is."""
+    the array alive for the call).  A contiguous int32 numpy array is used as it is.  The library
+    reads exactly num_seqs entries, so an array of any other length is refused here."""
     if dispatch_order is None:
         return None, None
     arr = dispatch_order
     if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
         arr = np.ascontiguousarray(np.asarray(dispatch_order, dtype=np.int32))
-    if arr.ndim != 1:
-        raise ValueError("dispatch_order must be a 1-D sequence of sequence indices")
+    if arr.shape != (int(num_seqs),):
+        raise ValueError(f"dispatch_order must be a 1-D array of exactly num_seqs = {int(num_seqs)} sequence "
+                         f"indices, got shape {arr.shape}")
     return arr, ctypes.c_void_p(arr.ctypes.data)
 
 
@@ -254,7 +283,7 @@ def decode_gqa(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order)
+    order_arr, order_ptr = _order(dispatch_order, B)
     rc = lib().pa_decode_gqa(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
                              B, int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
                              _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, _stream(stream))
@@ -289,7 +318,7 @@ def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order)
+    order_arr, order_ptr = _order(dispatch_order, B)
     rc = lib().pa_append_decode_gqa(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                     _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
                                     int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
@@ -422,7 +451,7 @@ def decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, kv_pool_i8: torch.Tensor, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order)
+    order_arr, order_ptr = _order(dispatch_order, B)
     rc = lib().pa_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(kv_pool_i8), _ptr(block_tables), _ptr(context_lens), B,
                                 int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
                                 _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, _stream(stream))
@@ -448,7 +477,7 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order)
+    order_arr, order_ptr = _order(dispatch_order, B)
     rc = lib().pa_append_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_pool_i8),
                                        _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
                                        int(block_tables.shape[1]), num_pages, int(page_size),

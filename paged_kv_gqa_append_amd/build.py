@@ -2,7 +2,9 @@
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -34,10 +36,46 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, verbose: bool) -> str:
+def digest_inputs():
+    """Every file the library is compiled from: the kernel sources, their
+    headers and the ABI header."""
+    files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(INCLUDE, "pa.h")]
+    return files
+
+
+def source_digest() -> str:
+    """sha256 over the library's source files (names and bytes) and the compile
+    flags: the build id a library built from this tree carries."""
+    h = hashlib.sha256()
+    for f in digest_inputs():
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    h.update(repr((FLAGS, sorted(FILE_FLAGS.items()))).encode())
+    return h.hexdigest()
+
+
+def built_digest():
+    """The build id inside the built libpa.so (read from the file, not loaded), or None."""
+    try:
+        with open(LIB, "rb") as fh:
+            data = fh.read()
+    except OSError:
+        return None
+    m = re.search(rb"pa-build-id:([0-9a-f]{64})", data)
+    return m.group(1).decode() if m else None
+
+
+def is_current() -> bool:
+    """libpa.so exists and was built from the sources now in the tree."""
+    return built_digest() == source_digest()
+
+
+def _compile(src: str, verbose: bool, digest: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE, "-I", CSRC, "-c", src,
-           "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), f'-DPA_BUILD_ID="{digest}"', "-I", INCLUDE,
+           "-I", CSRC, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -47,8 +85,9 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip and link libpa.so (always recompiles)."""
     os.makedirs(OBJ_DIR, exist_ok=True)
+    digest = source_digest()
     with ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), sources()))
+        objs = list(ex.map(lambda s: _compile(s, verbose, digest), sources()))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -59,6 +98,7 @@ def build(verbose: bool = False) -> str:
 
 
 def is_built() -> bool:
+    """libpa.so exists (whatever it was built from; see is_current)."""
     return os.path.exists(LIB)
 
 

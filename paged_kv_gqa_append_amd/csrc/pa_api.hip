@@ -109,6 +109,25 @@ const char *pa_status_string(int status) {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
 
+// The build id travels in the binary behind a marker, so that the build script
+// can also read it from the file without loading the library.
+#ifndef PA_BUILD_ID
+#define PA_BUILD_ID "0000000000000000000000000000000000000000000000000000000000000000"
+#endif
+static const char kBuildIdTag[] = "pa-build-id:" PA_BUILD_ID;
+
+const char *pa_build_id(void) { return kBuildIdTag + sizeof("pa-build-id:") - 1; }
+
+int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t stream) {
+    if (!device_flags || (reinterpret_cast<uintptr_t>(device_flags) & 3u)) return -PA_ERR_INVALID_ARG;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, device_flags, sizeof word, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return -PA_ERR_HIP;
+    if (clear && hipMemsetAsync(device_flags, 0, sizeof word, stream) != hipSuccess) return -PA_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return -PA_ERR_HIP;
+    return static_cast<int32_t>(word & 0x7FFFFFFFu);
+}
+
 pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
     for (int32_t pos = 0; pos < max_pos; ++pos) {

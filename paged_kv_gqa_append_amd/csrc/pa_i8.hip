@@ -35,10 +35,13 @@
 // and the output subtracts 1152 * the sum of the fed weights, taken by the
 // same MFMA against a ones column.  q enters as f16 after a power-of-two
 // scaling (exact) that puts its largest element in [2^14, 2^15).  Weights
-// P' = 2^(x - m) * V scale are fed as an f16 pair hi + lo (two MFMA passes,
-// about 22 significant bits, so the weights' rounding stays ~2^-22 of |V|);
-// the running sum uses the fp32 2^(x - m).  P' stays below 2^8 * V scale, so
-// V rows must hold |values| < 65504 * 127 / 2^8 (about 32000) for hi to fit f16.
+// P' = 2^(x - m) * V scale * 2^-ve are fed as an f16 pair hi + lo (two MFMA
+// passes, about 22 significant bits, so the weights' rounding stays ~2^-22 of
+// |V|); the running sum uses the fp32 2^(x - m).  ve >= 0 is a wave-uniform
+// exponent raised lazily, like the running max, whenever a live token's V
+// scale exceeds 2^(ve + 7); with 2^(x - m) <= 2^8 the weights then stay below
+// 2^15 and hi never overflows f16, for any finite bf16 V row.  Raising ve
+// halves the accumulators exactly; the wave epilogue multiplies by 2^ve.
 // Online softmax (log2 units, lazy max), wave and partition merges follow the
 // bf16 kernel's.  The grid size chooses the cache hint on the code loads and
 // whether wave priorities are levelled; neither changes the arithmetic.
@@ -463,6 +466,11 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     for (int n = 0; n < 5; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t one2 = 0x3C003C00u;  // f16 1.0 twice
     const half4 ones = __builtin_bit_cast(half4, u32x2{one2, one2});
+    // V scales enter the weights as vs * 2^-ve (wave-uniform ve >= 0, raised
+    // lazily): every live scale seen so far is below vlim = 2^(ve + 7).
+    int ve = 0;
+    float vmul = 1.0f;    // 2^-ve
+    float vlim = 128.0f;  // 2^(ve + 7)
 
     auto process = [&](const I8Page &r, bool last, int p) {
         // scores of tokens 4qd + i (i < 4) for column hh
@@ -496,12 +504,34 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
                 for (int n = 0; n < 5; ++n) acc[n][i] *= fi;
             }
         }
+        // V scales of the live tokens (a dead slot's scale may be anything)
+        float vsl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vsl[i] = (last && dead[i]) ? 0.0f : r.vs[i];
+        const float vmx = fmaxf(fmaxf(vsl[0], vsl[1]), fmaxf(vsl[2], vsl[3]));
+        if (__builtin_amdgcn_ballot_w64(vmx > vlim)) {
+            // rare: raise ve so that the page's largest scale times 2^-ve < 2^7
+            // (every lane of a quarter holds the same 4 scales, so the max over
+            // the quarters is the page's, the same in every lane)
+            const float wmx = __builtin_bit_cast(
+                float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, max_quarters(vmx))));
+            int e = 0;
+            (void)frexpf(wmx, &e);  // wmx in [2^(e-1), 2^e), e >= ve + 8
+            const int ve_new = e - 7;
+            const float f = ldexpf(1.0f, ve - ve_new);
+#pragma unroll
+            for (int n = 0; n < 5; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+            ve = ve_new;
+            vmul = ldexpf(1.0f, -ve);
+            vlim = ldexpf(1.0f, ve + 7);
+        }
         float pw[4], pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             pw[i] = fast_exp2(x[i] - m_run);
-            pv[i] = pw[i] * r.vs[i];
-            if (last && dead[i]) pv[i] = 0.0f;  // a dead slot's scale may be anything
+            pv[i] = (last && dead[i]) ? 0.0f : pw[i] * (vsl[i] * vmul);
         }
         l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
         // weights as an f16 pair hi + lo (lo = the rounding remainder of hi)
@@ -581,11 +611,12 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     if (pg1 == n_pages && p == n_pages - 1) process_last(cur, p);  // the sequence's last page
     // ---- wave epilogue ---------------------------------------------------------
     const float l_tot = sum_quarters(l_run);
-    if (lane < 16) {  // O minus 1152 x (sum of the fed weights), per head
+    if (lane < 16) {  // (O minus 1152 x the sum of the fed weights) x 2^ve, per head
+        const float vback = ldexpf(1.0f, ve);
 #pragma unroll
         for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_acc[w][i][16 * n + hh] = fmaf(-kOffsetF16, acc[4][i], acc[n][i]);
+            for (int i = 0; i < 4; ++i) s_acc[w][i][16 * n + hh] = fmaf(-kOffsetF16, acc[4][i], acc[n][i]) * vback;
     }
     if (lane < kGroup) {
         s_m[w][lane] = m_run;

@@ -344,14 +344,21 @@ def batch256_spec(seed: int = 3, num_layers: int = 16, num_seqs: int = 256) -> D
                           outlier_slots=outl)
 
 
-def fill_pool_device(spec: DeviceCaseSpec, device, which: str, chunk_pages: int = 8192):
-    """Draw one pool (``which`` in {"k", "v"}) on the device: N(0,1) -> (x20 outlier rows) -> bf16."""
+def fill_pool_device(spec: DeviceCaseSpec, device, which: str, chunk_pages: int = 8192, out=None):
+    """Draw one pool (``which`` in {"k", "v"}) on the device: N(0,1) -> (x20 outlier rows) -> bf16.
+    ``out``: an existing bf16 [num_pages][8][16][64] device tensor to fill instead of a new one."""
     import torch
 
     tid = _T_KPOOL if which == "k" else _T_VPOOL
     gen = torch.Generator(device=device)
     gen.manual_seed(int(np.random.SeedSequence([spec.seed, tid]).generate_state(1)[0]))
-    pool = torch.empty((spec.num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    shape = (spec.num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM)
+    if out is None:
+        pool = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    else:
+        if tuple(out.shape) != shape or out.dtype != torch.bfloat16:
+            raise ValueError(f"out must be bf16 {shape}, got {out.dtype} {tuple(out.shape)}")
+        pool = out
     mult = None
     if spec.outlier_slots is not None and len(spec.outlier_slots):
         mult = torch.ones(spec.num_pages * PAGE_SIZE, dtype=torch.float32, device=device)

@@ -14,12 +14,114 @@ def dev():
     return torch.device("cuda", 0)
 
 
+# ---- guard bands -------------------------------------------------------------
+# Every device buffer the GPU tests hand to the library (inputs, outputs, pools,
+# tables, flags) is the middle of a larger allocation whose first and last
+# GUARD_BYTES hold a fixed canary: bytes A5 7F repeated, which read as NaN in
+# bf16 (0x7FA5) and fp32 (0x7FA57FA5).  A kernel store that runs past an output
+# row, a (page, head) tile or a chunk lands in a canary, and so does a read-
+# modify-write of a neighbouring buffer; check_guards(), run after every GPU
+# test (tests/conftest.py), finds it.  The canaries are never legitimately
+# written, so one check at the end of a test covers every call it made,
+# aliased and device-error calls included.
+GUARD_BYTES = 4096
+_GUARD_PATTERN = np.tile(np.array([0xA5, 0x7F], np.uint8), GUARD_BYTES // 2)
+_guarded = []
+
+
+def guarded_empty(shape, dtype) -> torch.Tensor:
+    """Uninitialised device tensor of shape/dtype between two canary regions (16-byte aligned)."""
+    shape = tuple(int(x) for x in shape)
+    el = torch.empty((), dtype=dtype).element_size()
+    nbytes = int(np.prod(shape, dtype=np.int64)) * el
+    tail = GUARD_BYTES + (-nbytes) % 16
+    buf = torch.empty(GUARD_BYTES + nbytes + tail, dtype=torch.uint8, device=dev())
+    pat = torch.from_numpy(np.resize(_GUARD_PATTERN, tail)).to(dev())
+    buf[:GUARD_BYTES] = pat[:GUARD_BYTES]
+    buf[GUARD_BYTES + nbytes:] = pat
+    _guarded.append((buf, nbytes, tail))
+    return buf[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(shape)
+
+
+def guarded_full(shape, value, dtype) -> torch.Tensor:
+    return guarded_empty(shape, dtype).fill_(value)
+
+
+def guarded_zeros(shape, dtype) -> torch.Tensor:
+    return guarded_full(shape, 0, dtype)
+
+
+def guarded_clone(t: torch.Tensor) -> torch.Tensor:
+    return guarded_empty(t.shape, t.dtype).copy_(t)
+
+
+def guarded_flags() -> torch.Tensor:
+    """A device_flags word (int32, zero)."""
+    return guarded_zeros((1,), torch.int32)
+
+
+def check_guards() -> int:
+    """Assert every canary written since the last check is intact; forget the buffers.
+    Returns how many buffers were checked."""
+    n = len(_guarded)
+    if not n:
+        return 0
+    torch.cuda.synchronize()
+    bad = []
+    for buf, nbytes, tail in _guarded:
+        head = buf[:GUARD_BYTES].cpu().numpy()
+        back = buf[GUARD_BYTES + nbytes:].cpu().numpy()
+        if not np.array_equal(head, _GUARD_PATTERN):
+            bad.append(f"{nbytes}-byte buffer: {int((head != _GUARD_PATTERN).sum())} canary bytes changed before it")
+        if not np.array_equal(back, np.resize(_GUARD_PATTERN, tail)):
+            bad.append(f"{nbytes}-byte buffer: {int((back != np.resize(_GUARD_PATTERN, tail)).sum())} canary bytes "
+                       "changed after it")
+    _guarded.clear()
+    assert not bad, "guard band overwritten: " + "; ".join(bad)
+    return n
+
+
 def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev())
+    a = np.ascontiguousarray(bits).view(np.int16)
+    return guarded_empty(a.shape, torch.bfloat16).copy_(torch.from_numpy(a).view(torch.bfloat16))
 
 
 def to_dev_i32(a: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return guarded_empty(a.shape, torch.int32).copy_(torch.from_numpy(a))
+
+
+def to_dev_u8(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    return guarded_empty(a.shape, torch.uint8).copy_(torch.from_numpy(a))
+
+
+def to_dev_f32(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return guarded_empty(a.shape, torch.float32).copy_(torch.from_numpy(a))
+
+
+def guarded_workspace(num_seqs: int, max_blocks: int):
+    """The decode workspace (pa_decode_workspace_bytes), between canaries; None when none is needed."""
+    from paged_kv_gqa_append_amd import binding
+
+    n = binding.decode_workspace_bytes(num_seqs, max_blocks)
+    return None if n == 0 else guarded_empty((n // 4,), torch.float32)
+
+
+def guarded_argmax_workspace(rows: int, vocab: int, dtype):
+    """The argmax workspace (zeroed once, as its contract asks), between canaries; None when none is needed."""
+    from paged_kv_gqa_append_amd import binding
+
+    code = binding.PA_LOGITS_BF16 if dtype == torch.bfloat16 else binding.PA_LOGITS_FP32
+    n = int(binding.lib().pa_argmax_workspace_bytes(int(rows), int(vocab), code))
+    return None if n == 0 else guarded_zeros((n // 8,), torch.int64)
+
+
+def guarded_pool(spec, which: str) -> torch.Tensor:
+    """A full-size seeded pool (workloads.fill_pool_device) drawn into a guarded buffer."""
+    pool = guarded_empty((spec.num_pages, W.NUM_KV_HEADS, W.PAGE_SIZE, W.HEAD_DIM), torch.bfloat16)
+    return W.fill_pool_device(spec, dev(), which, out=pool)
 
 
 def to_host_bits(t: torch.Tensor) -> np.ndarray:
@@ -48,17 +150,42 @@ def bf16_ulp(bits: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
 
 
-def assert_rope_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, max_abs_input: float, what=""):
+def pair_magnitude(input_bits: np.ndarray) -> np.ndarray:
+    """|x_i| + |x_{i+32}| of every element's rotate-half pair (last axis 64), per element."""
+    x = np.abs(W.bf16_bits_to_f32(input_bits).astype(np.float64))
+    p = x[..., :32] + x[..., 32:]
+    return np.concatenate([p, p], axis=-1)
+
+
+def assert_rope_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, input_bits: np.ndarray, what=""):
     """Rotated bf16 rows: the device rotates in fp32 with a rounded (cos, sin)
-    table, the oracle in fp64; each result is rounded once to bf16.  They may
-    differ by one bf16 step plus the fp32 evaluation error of x_i cos - x_j sin,
-    at most ~2^-22 (|x_i| + |x_j|) <= 2^-21 max|x|, which spans several steps
-    only when the two terms cancel to a tiny result."""
+    table, the oracle in fp64; each result is rounded once to bf16.  The
+    device's value of an element of pair (x_i, x_{i+32}) is within
+    3 * 2^-24 (|x_i| + |x_{i+32}|) of the exact rotation (the table entries, the
+    product and the fused multiply-add each round once, relative 2^-24, and
+    |cos|, |sin| <= 1), so after both roundings the two may differ by one bf16
+    step plus 2^-22 (|x_i| + |x_{i+32}|), the pair's own inputs.  That spans
+    several steps only when the two terms cancel to a tiny result.
+    input_bits: the un-rotated rows (bf16 bits), the same shape as the results;
+    for elements that were not rotated (copied pool rows) pass the row itself,
+    which both sides hold bit for bit."""
+    assert gpu_bits.shape == ref_bits.shape == input_bits.shape, (gpu_bits.shape, ref_bits.shape, input_bits.shape)
     g = W.bf16_bits_to_f32(gpu_bits).astype(np.float64)
     r = W.bf16_bits_to_f32(ref_bits).astype(np.float64)
-    bound = bf16_ulp(ref_bits) + 2.0 ** -21 * max_abs_input
+    bound = bf16_ulp(ref_bits) + 2.0 ** -22 * pair_magnitude(input_bits)
     bad = np.abs(g - r) > bound
-    assert not bad.any(), f"{what}: {int(bad.sum())} rotated elements outside 1 ulp + fp32 bound"
+    both_nan = np.isnan(g) & np.isnan(r)
+    bad &= ~both_nan
+    assert not bad.any(), f"{what}: {int(bad.sum())} rotated elements outside 1 ulp + the pair's fp32 bound"
+
+
+def rope_input_pool(pool_bits: np.ndarray, writes) -> np.ndarray:
+    """The un-rotated inputs of a K pool after appends: a copy of the pool before them with
+    each written slot's row replaced by its pre-RoPE K rows.  writes: (page, slot, rows[8][64])."""
+    out = pool_bits.copy()
+    for page, slot, rows in writes:
+        out[int(page), :, int(slot)] = rows
+    return out
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, tol, what=""):
@@ -78,7 +205,7 @@ def assert_close(got: np.ndarray, ref: np.ndarray, tol, what=""):
 def rope(max_pos=W.MAX_CONTEXT + 64):
     from paged_kv_gqa_append_amd import binding
 
-    return binding.rope_table(max_pos, W.ROPE_THETA, dev())
+    return guarded_clone(binding.rope_table(max_pos, W.ROPE_THETA, dev()))
 
 
 class DeviceCase:
@@ -94,4 +221,4 @@ class DeviceCase:
         self.v_new = to_dev_bf16(case.v_new[layer])
         self.bt = to_dev_i32(case.block_tables[layer])
         self.lens = to_dev_i32(case.context_lens)
-        self.flags = torch.zeros(1, dtype=torch.int32, device=dev())
+        self.flags = guarded_flags()

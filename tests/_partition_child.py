@@ -16,6 +16,7 @@ import torch  # noqa: E402
 
 import oracle  # noqa: E402
 from _gpu_helpers import TOL_BF16, TOL_FP32, DeviceCase, assert_close, dev, rope, to_dev_bf16, to_dev_i32, to_host_f64  # noqa: E402,E501
+from _gpu_helpers import guarded_empty, guarded_workspace, to_dev_u8, check_guards  # noqa: E402
 from paged_kv_gqa_append_amd import binding  # noqa: E402
 from paged_kv_gqa_append_amd import workloads as W  # noqa: E402
 
@@ -27,10 +28,10 @@ def main():
     lens = [1, 16, 17, 129, 500, 1023, 2048, 2049, 3000]
     case = W.make_decode_case("sweep", 81, lens, dist="normal", max_blocks=200)
     table = rope(max_pos=3300)
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
     # bf16: decode alone (fp32 out) and append + decode (bf16 out)
     d = DeviceCase(case)
-    out = torch.empty((case.num_seqs, 32, 64), dtype=torch.float32, device=dev())
+    out = guarded_empty((case.num_seqs, 32, 64), torch.float32)
     binding.decode_gqa(out, d.q, d.k_pool, d.v_pool, d.bt, d.lens, case.scale, workspace=ws, device_flags=d.flags)
     torch.cuda.synchronize()
     ref, rc = oracle.decode_gqa(case.q[0], case.k_pool, case.v_pool, case.block_tables[0], case.context_lens,
@@ -38,7 +39,7 @@ def main():
     assert rc == oracle.OK and int(d.flags.item()) == 0
     assert_close(to_host_f64(out), ref, TOL_FP32, f"bf16 decode, partition {part_tokens}")
     d = DeviceCase(case)
-    out = torch.empty((case.num_seqs, 32, 64), dtype=torch.bfloat16, device=dev())
+    out = guarded_empty((case.num_seqs, 32, 64), torch.bfloat16)
     binding.append_decode_gqa(out, d.q, d.k_new, d.v_new, d.k_pool, d.v_pool, d.bt, d.lens, table, case.scale,
                               workspace=ws, device_flags=d.flags)
     torch.cuda.synchronize()
@@ -50,8 +51,8 @@ def main():
     assert_close(to_host_f64(out), ref, TOL_BF16, f"bf16 append + decode, partition {part_tokens}")
     # INT8: append + decode (fp32 out)
     pool_h = oracle.quantize_pages_i8(case.k_pool, case.v_pool)
-    pool = torch.from_numpy(pool_h.copy()).to(dev())
-    out = torch.empty((case.num_seqs, 32, 64), dtype=torch.float32, device=dev())
+    pool = to_dev_u8(pool_h)
+    out = guarded_empty((case.num_seqs, 32, 64), torch.float32)
     binding.append_decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0]),
                                  pool, to_dev_i32(case.block_tables[0]), to_dev_i32(case.context_lens), table,
                                  case.scale, workspace=ws)
@@ -62,6 +63,7 @@ def main():
     ref, rc = oracle.decode_gqa_i8(oq, opool, case.block_tables[0], case.context_lens, case.num_pages, case.scale)
     assert rc == oracle.OK
     assert_close(to_host_f64(out), ref, TOL_FP32, f"INT8 append + decode, partition {part_tokens}")
+    check_guards()
     print(json.dumps({"partition_tokens": part_tokens, "ok": True}), flush=True)
 
 

@@ -24,3 +24,15 @@ def oracle_lib():
 
     oracle._load()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _guard_bands(request):
+    """After every GPU test: the canaries around every device buffer it handed to the
+    library (tests/_gpu_helpers.py, guarded_*) must be intact."""
+    yield
+    if request.node.get_closest_marker("gpu") is None:
+        return
+    from _gpu_helpers import check_guards
+
+    check_guards()

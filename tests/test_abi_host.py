@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "pa.h")
 def pa():
     from paged_kv_gqa_append_amd import binding, build
 
-    if not build.is_built():
+    if not build.is_current():
         build.build()
     binding.lib()
     return binding
@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 8
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 9
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -263,3 +263,84 @@ def test_binding_refuses_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "libpa.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         binding.lib()
+
+
+def test_device_error_readback_validation(pa):
+    """pa_get_device_error refuses a NULL or misaligned flag word before touching the runtime."""
+    lib = pa.lib()
+    assert lib.pa_get_device_error(None, 0, None) == -pa.PA_ERR_INVALID_ARG
+    assert lib.pa_get_device_error(ctypes.c_void_p(FAKE + 2), 1, None) == -pa.PA_ERR_INVALID_ARG
+
+
+def test_build_id_matches_tree(pa):
+    """The library in the tree was built from the sources in the tree: its embedded build id
+    (read through the ABI and from the file) is the digest of today's sources and flags."""
+    from paged_kv_gqa_append_amd import build
+
+    got = pa.lib().pa_build_id().decode()
+    assert re.fullmatch(r"[0-9a-f]{64}", got)
+    assert got == build.source_digest() == build.built_digest()
+    assert build.is_current()
+
+
+def test_stale_library_is_refused(pa, monkeypatch):
+    """A build id that differs from the sources' digest makes the binding refuse the library."""
+    from paged_kv_gqa_append_amd import binding
+
+    binding._require_current(__import__("paged_kv_gqa_append_amd.build", fromlist=["x"]).source_digest())
+    with pytest.raises(RuntimeError, match="rebuild"):
+        binding._require_current("0" * 64)
+
+
+def test_digest_tracks_sources(tmp_path, monkeypatch):
+    """The digest covers the kernel sources, their headers and the ABI header: a copy of the tree
+    hashes the same, and a one-byte change to any of those files changes it."""
+    import shutil
+
+    from paged_kv_gqa_append_amd import build
+
+    base = build.source_digest()
+    rel = [os.path.relpath(f, build.ROOT) for f in build.digest_inputs()]
+    assert "include/pa.h" in rel and any(r.endswith(".h") and "csrc" in r for r in rel)
+    root = tmp_path / "tree"
+    shutil.copytree(os.path.join(build.ROOT, "paged_kv_gqa_append_amd", "csrc"),
+                    root / "paged_kv_gqa_append_amd" / "csrc")
+    shutil.copytree(os.path.join(build.ROOT, "include"), root / "include")
+    monkeypatch.setattr(build, "ROOT", str(root))
+    monkeypatch.setattr(build, "CSRC", str(root / "paged_kv_gqa_append_amd" / "csrc"))
+    monkeypatch.setattr(build, "INCLUDE", str(root / "include"))
+    assert build.source_digest() == base
+    for r in (rel[0], "paged_kv_gqa_append_amd/csrc/pa_decode_core.h", "include/pa.h"):
+        f = root / r
+        data = f.read_bytes()
+        f.write_bytes(data + b"\n")
+        assert build.source_digest() != base, r
+        f.write_bytes(data)
+    assert build.source_digest() == base
+
+
+def test_dispatch_order_length_refused(pa):
+    """The library reads exactly num_seqs order entries through a bare pointer, so the binding
+    refuses a shorter or longer array before calling it (host tensors: nothing is launched)."""
+    import torch
+
+    B, mb, P = 3, 2, 8
+    kp = torch.zeros((P, 8, 16, 64), dtype=torch.bfloat16)
+    q = torch.zeros((B, 32, 64), dtype=torch.bfloat16)
+    out = torch.zeros((B, 32, 64), dtype=torch.bfloat16)
+    bt = torch.zeros((B, mb), dtype=torch.int32)
+    lens = torch.ones(B, dtype=torch.int32)
+    kn = torch.zeros((B, 8, 64), dtype=torch.bfloat16)
+    table = torch.zeros((64, 32, 2), dtype=torch.float32)
+    i8 = torch.zeros((P, 8, 2176), dtype=torch.uint8)
+    for bad in ([1, 0], [2, 1, 0, 3], [[0, 1, 2]]):
+        with pytest.raises(ValueError, match="exactly num_seqs"):
+            pa.decode_gqa(out, q, kp, kp, bt, lens, dispatch_order=bad)
+        with pytest.raises(ValueError, match="exactly num_seqs"):
+            pa.append_decode_gqa(out, q, kn, kn, kp, kp, bt, lens, table, dispatch_order=bad)
+        with pytest.raises(ValueError, match="exactly num_seqs"):
+            pa.decode_gqa_i8(out, q, i8, bt, lens, dispatch_order=bad)
+        with pytest.raises(ValueError, match="exactly num_seqs"):
+            pa.append_decode_gqa_i8(out, q, kn, kn, i8, bt, lens, table, dispatch_order=bad)
+    arr, ptr = pa._order(np.array([2, 0, 1], np.int32), B)
+    assert arr.shape == (3,) and ptr.value == arr.ctypes.data

@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from _gpu_helpers import DeviceCase, assert_rope_close, dev, rope, to_dev_i32, to_host_bits
+from _gpu_helpers import guarded_flags, rope_input_pool
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -44,12 +45,13 @@ def check(case, d, kp, vp, q, with_q=True):
     for s, L in enumerate(case.context_lens):
         appended[case.block_tables[0, s, (L - 1) // 16], (L - 1) % 16] = True
     assert not np.any(diff.transpose(0, 2, 1, 3)[~appended]), "bytes outside the appended slots changed"
-    xmax = float(np.abs(W.bf16_bits_to_f32(np.concatenate([case.k_new[0].ravel(), case.q[0].ravel()]))).max())
-    assert_rope_close(gk, kp, xmax, "K pool")
+    writes = [(case.block_tables[0, s, (L - 1) // 16], (L - 1) % 16, case.k_new[0][s])
+              for s, L in enumerate(case.context_lens)]
+    assert_rope_close(gk, kp, rope_input_pool(case.k_pool, writes), "K pool")
     # the appended slots really changed (they held NaN poison or other data)
     assert np.array_equal(np.any(gk != case.k_pool, axis=(1, 3)), appended)
     if with_q:
-        assert_rope_close(gq, q, xmax, "rotated q")
+        assert_rope_close(gq, q, case.q[0], "rotated q")
     else:
         assert np.array_equal(gq, case.q[0])
     assert int(d.flags.item()) == 0
@@ -106,7 +108,7 @@ def test_append_device_errors_leave_pool_untouched(table):
     assert np.array_equal(gq[0], case.q[0, 0]) and np.array_equal(gq[1], case.q[0, 1])
     # position beyond the rope table is a length error as well
     short = rope(max_pos=16)
-    f2 = torch.zeros(1, dtype=torch.int32, device=dev())
+    f2 = guarded_flags()
     binding.append_kv_rope(None, d.k_new, d.v_new, d.k_pool, d.v_pool, to_dev_i32(case.block_tables[0]),
                            to_dev_i32(case.context_lens), short, device_flags=f2)
     torch.cuda.synchronize()

@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from _gpu_helpers import dev
+from _gpu_helpers import guarded_empty, guarded_full, guarded_argmax_workspace, to_dev_bf16, to_dev_f32
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -22,16 +23,16 @@ def run(x32, dtype, offset=0):
     rows, vocab = x32.shape
     if dtype == torch.bfloat16:
         host = W.f32_to_bf16_bits(x32)
-        flat = torch.empty(rows * vocab + offset, dtype=torch.bfloat16, device=dev())
+        flat = guarded_empty((rows * vocab + offset,), torch.bfloat16)
         flat[offset:] = torch.from_numpy(host.view(np.int16).ravel()).view(torch.bfloat16).to(dev())
         ref = oracle.argmax(host)
     else:
-        flat = torch.empty(rows * vocab + offset, dtype=torch.float32, device=dev())
+        flat = guarded_empty((rows * vocab + offset,), torch.float32)
         flat[offset:] = torch.from_numpy(x32.ravel()).to(dev())
         ref = oracle.argmax(x32)
     logits = flat[offset:].view(rows, vocab)
-    out = torch.full((rows,), -7, dtype=torch.int32, device=dev())
-    binding.argmax(out, logits, workspace=binding.argmax_workspace(rows, vocab, dtype, dev()))
+    out = guarded_full((rows,), -7, torch.int32)
+    binding.argmax(out, logits, workspace=guarded_argmax_workspace(rows, vocab, dtype))
     torch.cuda.synchronize()
     return out.cpu().numpy(), ref
 
@@ -70,19 +71,19 @@ def test_argmax_workspace_reused_and_left_zero(dtype):
     one stream: every call matches the oracle and the workspace ends all zero
     (the last chunk of each row resets the row's key and arrival count)."""
     rows0, vocab0 = 40, W.VOCAB_SIZE
-    ws = binding.argmax_workspace(rows0, vocab0, dtype, dev())
+    ws = guarded_argmax_workspace(rows0, vocab0, dtype)
     assert ws is not None and ws.numel() == 2 * rows0
     for k, (rows, vocab) in enumerate([(40, W.VOCAB_SIZE), (40, W.VOCAB_SIZE), (17, 70001), (3, 16385)]):
         print(f"argmax reuse call {k}: rows={rows} vocab={vocab} dtype={dtype}", flush=True)
         x = W.argmax_logits(93 + k, rows, vocab)
         if dtype == torch.bfloat16:
             host = W.f32_to_bf16_bits(x)
-            logits = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).to(dev())
+            logits = to_dev_bf16(host)
             ref = oracle.argmax(host)
         else:
-            logits = torch.from_numpy(x).to(dev())
+            logits = to_dev_f32(x)
             ref = oracle.argmax(x)
-        out = torch.full((rows,), -7, dtype=torch.int32, device=dev())
+        out = guarded_full((rows,), -7, torch.int32)
         binding.argmax(out, logits, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), ref), f"call {k}"

@@ -12,6 +12,7 @@ import torch
 import oracle
 from _gpu_helpers import (TOL_BF16, TOL_FP32, DeviceCase, assert_close, dev, rope, to_dev_bf16, to_dev_i32,
                           to_host_bits, to_host_f64)
+from _gpu_helpers import guarded_empty, guarded_full, guarded_clone, guarded_workspace
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -24,8 +25,8 @@ def gpu_decode(d: DeviceCase, out_dtype=torch.bfloat16, q=None, out=None):
     case = d.case
     q = d.q if q is None else q
     if out is None:
-        out = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+        out = guarded_empty((case.num_seqs, 32, 64), out_dtype)
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
     binding.decode_gqa(out, q, d.k_pool, d.v_pool, d.bt, d.lens, case.scale, workspace=ws, device_flags=d.flags)
     torch.cuda.synchronize()
     return out
@@ -104,7 +105,7 @@ def test_output_may_alias_q():
     case = CASES["edges"]()
     d = DeviceCase(case)
     sep = to_host_bits(gpu_decode(d, torch.bfloat16))
-    q_alias = d.q.clone()
+    q_alias = guarded_clone(d.q)
     gpu_decode(d, torch.bfloat16, q=q_alias, out=q_alias)
     assert np.array_equal(to_host_bits(q_alias), sep)
 
@@ -158,9 +159,32 @@ def test_device_errors_zero_fill_and_flag():
     bt = case.block_tables[0].copy()
     bt[3, 40] = -1              # a used entry of a multi-partition sequence
     d.lens, d.bt = to_dev_i32(lens), to_dev_i32(bt)
-    out = torch.full((4, 32, 64), 7.0, dtype=torch.float32, device=dev())
+    out = guarded_full((4, 32, 64), 7.0, torch.float32)
     gpu_decode(d, out=out)
     got = to_host_f64(out)
     assert int(d.flags.item()) == binding.PA_DEVERR_CONTEXT_LEN | binding.PA_DEVERR_PAGE_ID
     assert np.all(got[0] == 0) and np.all(got[2] == 0) and np.all(got[3] == 0)
     assert_close(got[1], ref[1], TOL_FP32, "healthy sequence next to bad ones")
+
+
+def test_device_error_read_back():
+    """pa_get_device_error returns the bits a kernel flagged (after draining the stream), resets
+    the word when asked, and reads 0 after a clean call."""
+    case = W.make_decode_case("err_rb", 56, [40, 600, 17], dist="normal", max_blocks=64)
+    d = DeviceCase(case)
+    out = guarded_empty((3, 32, 64), torch.bfloat16)
+    gpu_decode(d, out=out)  # clean
+    assert binding.get_device_error(d.flags) == 0
+    bt = case.block_tables[0].copy()
+    bt[1, 7] = case.num_pages + 3  # a used page id outside the pool
+    d.bt = to_dev_i32(bt)
+    gpu_decode(d, out=out)
+    assert binding.get_device_error(d.flags) == binding.PA_DEVERR_PAGE_ID
+    assert binding.get_device_error(d.flags, clear=True) == binding.PA_DEVERR_PAGE_ID
+    assert binding.get_device_error(d.flags) == 0
+    lens = case.context_lens.copy()
+    lens[2] = 0
+    d.lens, d.bt = to_dev_i32(lens), to_dev_i32(case.block_tables[0])
+    gpu_decode(d, out=out)
+    assert binding.get_device_error(d.flags, clear=True) == binding.PA_DEVERR_CONTEXT_LEN
+    assert int(d.flags.item()) == 0

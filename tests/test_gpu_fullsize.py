@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from _gpu_helpers import TOL_BF16, assert_close, assert_rope_close, dev, to_host_bits, to_host_f64
+from _gpu_helpers import guarded_empty, guarded_flags, guarded_workspace, rope, guarded_pool, to_dev_i32, to_dev_bf16
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -22,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 def up(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev())
+    return to_dev_bf16(bits)
 
 
 def compact(spec, layer, seqs, k_pool, v_pool):
@@ -40,18 +41,18 @@ def compact(spec, layer, seqs, k_pool, v_pool):
 
 def run_case(spec, layer, seqs):
     print(f"full-size case={spec.name} layer={layer} sampled={list(seqs)}", flush=True)
-    k_pool = W.fill_pool_device(spec, dev(), "k")
-    v_pool = W.fill_pool_device(spec, dev(), "v")
+    k_pool = guarded_pool(spec, "k")
+    v_pool = guarded_pool(spec, "v")
     q, kn, vn = spec.host_rows(layer)
     kp, vp, bt_small, used = compact(spec, layer, seqs, k_pool, v_pool)  # before the launch
     dq = up(q)
-    out = torch.empty((spec.num_seqs, 32, 64), dtype=torch.bfloat16, device=dev())
-    table = binding.rope_table(2048 + 64, spec.theta, dev())
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    out = guarded_empty((spec.num_seqs, 32, 64), torch.bfloat16)
+    table = rope(2048 + 64)
+    flags = guarded_flags()
     binding.append_decode_gqa(out, dq, up(kn), up(vn), k_pool, v_pool,
-                              torch.from_numpy(spec.block_tables[layer]).to(dev()),
-                              torch.from_numpy(spec.context_lens).to(dev()), table, spec.scale,
-                              workspace=binding.decode_workspace(spec.num_seqs, spec.max_blocks, dev()),
+                              to_dev_i32(spec.block_tables[layer]),
+                              to_dev_i32(spec.context_lens), table, spec.scale,
+                              workspace=guarded_workspace(spec.num_seqs, spec.max_blocks),
                               device_flags=flags)
     torch.cuda.synchronize()
     assert int(flags.item()) == 0
@@ -65,13 +66,12 @@ def run_case(spec, layer, seqs):
     got = to_host_f64(out)[seqs]
     err = assert_close(got, ref, TOL_BF16, spec.name)
     # rotated q and the appended K rows (1 ulp + fp32 bound), V rows exact
-    xmax = float(np.abs(W.bf16_bits_to_f32(np.concatenate([q.ravel(), kn.ravel()]))).max())
-    assert_rope_close(to_host_bits(dq)[seqs], oq, xmax, "rotated q")
+    assert_rope_close(to_host_bits(dq)[seqs], oq, q[seqs], "rotated q")
     gk = to_host_bits(k_pool.index_select(0, torch.from_numpy(used).to(dev())))
     gv = to_host_bits(v_pool.index_select(0, torch.from_numpy(used).to(dev())))
     for i, L in enumerate(lens):
         pg, sl = bt_small[i, (L - 1) // 16], (L - 1) % 16
-        assert_rope_close(gk[pg, :, sl], kp[pg, :, sl], xmax, "appended K")
+        assert_rope_close(gk[pg, :, sl], kp[pg, :, sl], kn[seqs][i], "appended K")
         assert np.array_equal(gv[pg, :, sl], vp[pg, :, sl])
     del k_pool, v_pool
     torch.cuda.empty_cache()

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from _gpu_helpers import TOL_BF16, TOL_FP32, DeviceCase, assert_close, dev, rope, to_dev_i32, to_host_bits, to_host_f64
+from _gpu_helpers import guarded_empty, guarded_full, guarded_workspace
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -35,8 +36,8 @@ def table():
 
 def run_fused(case, table, out_dtype, alias=False):
     d = DeviceCase(case)
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
-    out = d.q if alias else torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
+    out = d.q if alias else guarded_empty((case.num_seqs, 32, 64), out_dtype)
     binding.append_decode_gqa(out, d.q, d.k_new, d.v_new, d.k_pool, d.v_pool, d.bt, d.lens, table, case.scale,
                               workspace=ws, device_flags=d.flags)
     torch.cuda.synchronize()
@@ -45,9 +46,9 @@ def run_fused(case, table, out_dtype, alias=False):
 
 def run_separate(case, table, out_dtype):
     d = DeviceCase(case)
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
     binding.append_kv_rope(d.q, d.k_new, d.v_new, d.k_pool, d.v_pool, d.bt, d.lens, table, device_flags=d.flags)
-    out = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    out = guarded_empty((case.num_seqs, 32, 64), out_dtype)
     binding.decode_gqa(out, d.q, d.k_pool, d.v_pool, d.bt, d.lens, case.scale, workspace=ws, device_flags=d.flags)
     torch.cuda.synchronize()
     return d, out
@@ -88,9 +89,9 @@ def test_fused_output_may_alias_q(table, name):
 def test_decode_long_contexts_against_oracle(table):
     case = CASES["long"]()
     d = DeviceCase(case)
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
     assert ws is not None  # 260 blocks need more than one partition
-    out = torch.empty((case.num_seqs, 32, 64), dtype=torch.float32, device=dev())
+    out = guarded_empty((case.num_seqs, 32, 64), torch.float32)
     binding.decode_gqa(out, d.q, d.k_pool, d.v_pool, d.bt, d.lens, case.scale, workspace=ws, device_flags=d.flags)
     torch.cuda.synchronize()
     ref, rc = oracle.decode_gqa(case.q[0], case.k_pool, case.v_pool, case.block_tables[0], case.context_lens,
@@ -109,7 +110,7 @@ def test_fused_device_errors(table):
     d.lens, d.bt = to_dev_i32(lens), to_dev_i32(bt)
     short = rope(max_pos=600)   # sequences 1 (pos 599 ok), 3 (pos 999) and ... beyond the table
     before_k = to_host_bits(d.k_pool)
-    out = torch.full((5, 32, 64), 7.0, dtype=torch.float32, device=dev())
+    out = guarded_full((5, 32, 64), 7.0, torch.float32)
     binding.append_decode_gqa(out, d.q, d.k_new, d.v_new, d.k_pool, d.v_pool, d.bt, d.lens, short, case.scale,
                               device_flags=d.flags)
     torch.cuda.synchronize()
@@ -132,7 +133,7 @@ def test_fused_device_errors(table):
     # a bad page id alone
     d2 = DeviceCase(case)
     d2.bt = to_dev_i32(bt)
-    out2 = torch.full((5, 32, 64), 7.0, dtype=torch.float32, device=dev())
+    out2 = guarded_full((5, 32, 64), 7.0, torch.float32)
     binding.append_decode_gqa(out2, d2.q, d2.k_new, d2.v_new, d2.k_pool, d2.v_pool, d2.bt, d2.lens, table,
                               case.scale, device_flags=d2.flags)
     torch.cuda.synchronize()

@@ -27,6 +27,7 @@ import torch
 import oracle
 from _gpu_helpers import (TOL_BF16, TOL_FP32, assert_close, assert_rope_close, dev, rope, to_dev_bf16, to_dev_i32,
                           to_host_bits, to_host_f64)
+from _gpu_helpers import guarded_empty, guarded_full, guarded_flags, to_dev_u8, guarded_workspace, guarded_pool, pair_magnitude
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -74,10 +75,6 @@ def host_i8(case, poison=True):
     return pool
 
 
-def to_dev_u8(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
-
-
 def oracle_decode_i8(case, pool, q_bits=None):
     out, rc = oracle.decode_gqa_i8(case.q[0] if q_bits is None else q_bits, pool, case.block_tables[0],
                                    case.context_lens, case.num_pages, case.scale)
@@ -109,7 +106,7 @@ def test_quantize_pages_bitexact():
     print(f"quantize pages P={P} listed={len(ids)}", flush=True)
     # listed pages only
     pool = to_dev_u8(start)
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    flags = guarded_flags()
     binding.quantize_pages_i8(pool, to_dev_bf16(kp), to_dev_bf16(vp), to_dev_i32(ids), device_flags=flags)
     torch.cuda.synchronize()
     want = start.copy()
@@ -138,15 +135,43 @@ def test_decode_i8_parity(name, out_dtype):
     case = CASES[name]()
     print(f"i8 decode parity case={name} B={case.num_seqs} out={out_dtype}", flush=True)
     pool = host_i8(case)
-    out = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    out = guarded_empty((case.num_seqs, 32, 64), out_dtype)
+    flags = guarded_flags()
     binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(case.block_tables[0]),
                           to_dev_i32(case.context_lens), case.scale,
-                          workspace=binding.decode_workspace(case.num_seqs, case.max_blocks, dev()),
+                          workspace=guarded_workspace(case.num_seqs, case.max_blocks),
                           device_flags=flags)
     torch.cuda.synchronize()
     got = to_host_f64(out)
     assert_close(got, oracle_decode_i8(case, pool), TOL_BF16 if out_dtype == torch.bfloat16 else TOL_FP32, name)
+    assert int(flags.item()) == 0
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_i8_wide_v_range(out_dtype):
+    """V rows far beyond what an f16 weight times a V scale can hold without an exponent
+    offset (|v| ~ 4e4, 1e6 and 1e30, the f16 limit of the plain form being about 3.2e4) mixed
+    with ordinary rows and rows of 1e-6, in the same pages and sequences, some past one
+    partition: every output within tolerance of the oracle over the same INT8 pool."""
+    lens = [40, 600, 2048, 17, 2500]
+    case = W.make_decode_case("wide_v", 76, lens, dist="normal", max_blocks=160, poison=False)
+    rng = np.random.default_rng(77)
+    rows = W.bf16_bits_to_f32(case.v_pool).astype(np.float64)  # [P][8][16][64]
+    factor = rng.choice([1.0, 1.0, 4.0e4, 1.0e6, 1.0e-6, 1.0e30], size=rows.shape[:3], p=[.5, .2, .1, .1, .08, .02])
+    vp = W.f32_to_bf16_bits((rows * factor[..., None]).astype(np.float32))
+    case.v_pool = vp
+    print(f"i8 wide V range B={case.num_seqs} out={out_dtype} max|v|={np.abs(rows * factor[..., None]).max():.3g}",
+          flush=True)
+    pool = host_i8(case)
+    out = guarded_empty((case.num_seqs, 32, 64), out_dtype)
+    flags = guarded_flags()
+    binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(case.block_tables[0]),
+                          to_dev_i32(case.context_lens), case.scale,
+                          workspace=guarded_workspace(case.num_seqs, case.max_blocks), device_flags=flags)
+    torch.cuda.synchronize()
+    ref = oracle_decode_i8(case, pool)
+    assert np.abs(ref).max() > 1e20  # the huge rows do reach the outputs
+    assert_close(to_host_f64(out), ref, TOL_BF16 if out_dtype == torch.bfloat16 else TOL_FP32, "wide V range")
     assert int(flags.item()) == 0
 
 
@@ -184,7 +209,7 @@ def test_append_i8_against_oracle():
     table = rope()
     q = to_dev_bf16(case.q[0])
     dpool = to_dev_u8(pool)
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    flags = guarded_flags()
     binding.append_kv_rope_i8(q, to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0]), dpool,
                               to_dev_i32(case.block_tables[0]), to_dev_i32(case.context_lens), table,
                               device_flags=flags)
@@ -212,15 +237,13 @@ def test_append_i8_against_oracle():
             gc, gs = read_row(got, pg, j, t, "k")
             rc_, rs = read_row(ref, pg, j, t, "k")
             y = oracle.rope_head(kx, pos, case.theta)
-            xmax = float(np.abs(W.bf16_bits_to_f32(kx)).max())
             assert abs(float(gs) - float(rs)) <= float(rs) * 2.0 ** -7
             err = np.abs(gc.astype(np.float64) * float(gs) - y)
-            assert np.all(err <= float(gs) * (0.5 + 2.0 ** -16) + 2.0 ** -7 * np.abs(y) + 2.0 ** -21 * xmax)
+            assert np.all(err <= float(gs) * (0.5 + 2.0 ** -16) + 2.0 ** -7 * np.abs(y) + 2.0 ** -22 * pair_magnitude(kx))
     diff = got != ref
     assert not (diff & ~allowed).any(), f"{int((diff & ~allowed).sum())} bytes differ outside the allowed K rows"
     print(f"appended K rows: {n_exact} bit-exact by construction, {n_bound} checked by bound", flush=True)
-    xmax = float(np.abs(W.bf16_bits_to_f32(case.q[0])).max())
-    assert_rope_close(to_host_bits(q), oq, xmax, "rotated q")
+    assert_rope_close(to_host_bits(q), oq, case.q[0], "rotated q")
 
 
 @pytest.mark.parametrize("name", ["tiny", "edges", "long"])
@@ -234,15 +257,15 @@ def test_fused_i8_equals_separate(name, out_dtype):
     table = rope(4200)
     bt, lens = to_dev_i32(case.block_tables[0]), to_dev_i32(case.context_lens)
     kn, vn = to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0])
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
     # separate
     q1, p1 = to_dev_bf16(case.q[0]), to_dev_u8(pool)
-    o1 = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    o1 = guarded_empty((case.num_seqs, 32, 64), out_dtype)
     binding.append_kv_rope_i8(q1, kn, vn, p1, bt, lens, table)
     binding.decode_gqa_i8(o1, q1, p1, bt, lens, case.scale, workspace=ws)
     # fused
     q2, p2 = to_dev_bf16(case.q[0]), to_dev_u8(pool)
-    o2 = torch.empty((case.num_seqs, 32, 64), dtype=out_dtype, device=dev())
+    o2 = guarded_empty((case.num_seqs, 32, 64), out_dtype)
     binding.append_decode_gqa_i8(o2, q2, kn, vn, p2, bt, lens, table, case.scale, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
@@ -272,7 +295,7 @@ def test_single_token_returns_its_v():
     value below 1280 x scale, so |out - code x scale| < 2^-12 x scale."""
     case = W.make_decode_case("one", 76, [1] * 5, dist="normal")
     pool = host_i8(case)
-    out = torch.empty((5, 32, 64), dtype=torch.float32, device=dev())
+    out = guarded_empty((5, 32, 64), torch.float32)
     binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(case.block_tables[0]),
                           to_dev_i32(case.context_lens), case.scale)
     torch.cuda.synchronize()
@@ -292,8 +315,8 @@ def test_i8_device_errors():
     lens = case.context_lens.copy()
     lens[0] = 0                 # bad length
     bt[1, 1] = case.num_pages   # bad page id in the used range
-    out = torch.full((3, 32, 64), 7.0, dtype=torch.float32, device=dev())
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    out = guarded_full((3, 32, 64), 7.0, torch.float32)
+    flags = guarded_flags()
     binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(bt), to_dev_i32(lens),
                           case.scale, device_flags=flags)
     torch.cuda.synchronize()
@@ -332,8 +355,8 @@ def _full_size_i8(spec, layer, seqs, what):
     """The benchmark's INT8 step on one layer of a full-size workload, sampled sequences checked
     against the oracle on bf16 pages copied to the host before any of our kernels ran."""
     print(f"i8 full-size {what} layer={layer} sampled={list(seqs)}", flush=True)
-    k_pool = W.fill_pool_device(spec, dev(), "k")
-    v_pool = W.fill_pool_device(spec, dev(), "v")
+    k_pool = guarded_pool(spec, "k")
+    v_pool = guarded_pool(spec, "v")
     bt = spec.block_tables[layer][seqs]
     used = np.unique(bt[bt >= 0])
     idx = torch.from_numpy(used).to(dev())
@@ -350,12 +373,12 @@ def _full_size_i8(spec, layer, seqs, what):
     assert np.array_equal(pool.index_select(0, idx).cpu().numpy(), ref_pool)
     q, kn, vn = spec.host_rows(layer)
     dq = to_dev_bf16(q)
-    out = torch.empty((spec.num_seqs, 32, 64), dtype=torch.bfloat16, device=dev())
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
+    out = guarded_empty((spec.num_seqs, 32, 64), torch.bfloat16)
+    flags = guarded_flags()
     binding.append_decode_gqa_i8(out, dq, to_dev_bf16(kn), to_dev_bf16(vn), pool,
                                  to_dev_i32(spec.block_tables[layer]), to_dev_i32(spec.context_lens),
-                                 binding.rope_table(2048 + 64, spec.theta, dev()), spec.scale,
-                                 workspace=binding.decode_workspace(spec.num_seqs, spec.max_blocks, dev()),
+                                 rope(2048 + 64), spec.scale,
+                                 workspace=guarded_workspace(spec.num_seqs, spec.max_blocks),
                                  device_flags=flags)
     torch.cuda.synchronize()
     assert int(flags.item()) == 0
@@ -366,8 +389,7 @@ def _full_size_i8(spec, layer, seqs, what):
     ref, rc = oracle.decode_gqa_i8(oq, ref_pool, bt_small, lens, len(used), spec.scale)
     assert rc == oracle.OK
     assert_close(to_host_f64(out)[seqs], ref, TOL_BF16, what)
-    xmax = float(np.abs(W.bf16_bits_to_f32(q)).max())
-    assert_rope_close(to_host_bits(dq)[seqs], oq, xmax, "rotated q")
+    assert_rope_close(to_host_bits(dq)[seqs], oq, q[seqs], "rotated q")
     del pool
     torch.cuda.empty_cache()
 

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 from _gpu_helpers import TOL_BF16, assert_close, dev, rope, to_dev_bf16, to_dev_i32, to_host_bits
+from _gpu_helpers import guarded_empty, guarded_workspace, to_dev_u8
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -33,8 +34,8 @@ def run(case, kv, fused, pools, table):
     q = to_dev_bf16(case.q[0])
     bt, lens = to_dev_i32(case.block_tables[0]), to_dev_i32(case.context_lens)
     kn, vn = to_dev_bf16(case.k_new[0]), to_dev_bf16(case.v_new[0])
-    out = torch.empty((case.num_seqs, 32, 64), dtype=torch.bfloat16, device=dev())
-    ws = binding.decode_workspace(case.num_seqs, case.max_blocks, dev())
+    out = guarded_empty((case.num_seqs, 32, 64), torch.bfloat16)
+    ws = guarded_workspace(case.num_seqs, case.max_blocks)
     if kv == "int8":
         if fused:
             binding.append_decode_gqa_i8(out, q, kn, vn, pools[0], bt, lens, table, case.scale, workspace=ws)
@@ -52,7 +53,7 @@ def run(case, kv, fused, pools, table):
 
 def device_pools(case, kv, host_i8):
     if kv == "int8":
-        return [torch.from_numpy(host_i8.copy()).to(dev())]
+        return [to_dev_u8(host_i8)]
     return [to_dev_bf16(case.k_pool), to_dev_bf16(case.v_pool)]
 
 

@@ -19,6 +19,7 @@ import torch
 import oracle
 from _gpu_helpers import (TOL_BF16, assert_close, assert_rope_close, dev, rope, to_dev_bf16, to_dev_i32,
                           to_host_bits, to_host_f64)
+from _gpu_helpers import guarded_empty, guarded_flags, guarded_workspace, rope_input_pool
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -45,9 +46,9 @@ def test_manager_driven_decode_loop(batching):
     vp_host = bf16(rng, (P, 8, 16, 64))
     kp, vp = to_dev_bf16(kp_host), to_dev_bf16(vp_host)
     kp_ref, vp_ref = kp_host.copy(), vp_host.copy()
-    flags = torch.zeros(1, dtype=torch.int32, device=dev())
-    ws = binding.decode_workspace(SLOTS, MB, dev())
-    max_abs = 0.0
+    k_writes = []  # (page, slot, pre-RoPE K rows) of every append, in order
+    flags = guarded_flags()
+    ws = guarded_workspace(SLOTS, MB)
     decoded = prefilled = 0
     for step in range(200):
         for slot in m.schedule():
@@ -60,10 +61,9 @@ def test_manager_driven_decode_loop(batching):
                 bt = bt_all[layer, slot:slot + 1]
                 q = bf16(rng, (1, prompt, 32, 64))
                 kc, vc = bf16(rng, (1, prompt, 8, 64)), bf16(rng, (1, prompt, 8, 64))
-                max_abs = max(max_abs, float(np.abs(W.bf16_bits_to_f32(kc)).max()),
-                              float(np.abs(W.bf16_bits_to_f32(q)).max()))
+                k_writes += [(bt[0, i // 16], i % 16, kc[0, i]) for i in range(prompt)]
                 qd = to_dev_bf16(q)
-                out = torch.empty_like(qd)
+                out = guarded_empty(qd.shape, qd.dtype)
                 binding.prefill_chunk(out, qd, to_dev_bf16(kc), to_dev_bf16(vc), kp, vp, to_dev_i32(bt),
                                       to_dev_i32(np.zeros(1, np.int32)), table, SCALE, device_flags=flags)
                 q_ref = q.copy()
@@ -85,10 +85,9 @@ def test_manager_driven_decode_loop(batching):
                 bt = np.ascontiguousarray(bt_all[layer, active])
                 q = bf16(rng, (len(active), 32, 64))
                 kn, vn = bf16(rng, (len(active), 8, 64)), bf16(rng, (len(active), 8, 64))
-                max_abs = max(max_abs, float(np.abs(W.bf16_bits_to_f32(kn)).max()),
-                              float(np.abs(W.bf16_bits_to_f32(q)).max()))
+                k_writes += [(bt[i, (L[i] - 1) // 16], (L[i] - 1) % 16, kn[i]) for i in range(len(active))]
                 qd = to_dev_bf16(q)
-                out = torch.empty_like(qd)
+                out = guarded_empty(qd.shape, qd.dtype)
                 binding.append_decode_gqa(out, qd, to_dev_bf16(kn), to_dev_bf16(vn), kp, vp, to_dev_i32(bt),
                                           to_dev_i32(L), table, SCALE, workspace=ws, device_flags=flags)
                 q_ref = q.copy()
@@ -109,4 +108,4 @@ def test_manager_driven_decode_loop(batching):
     assert m.free_pages == P and m.reserved_pages == 0
     # whole pools: V copies are exact, rotated K rows within the fp32 rotation bound
     assert np.array_equal(to_host_bits(vp), vp_ref)
-    assert_rope_close(to_host_bits(kp), kp_ref, max_abs, "K pool")
+    assert_rope_close(to_host_bits(kp), kp_ref, rope_input_pool(kp_host, k_writes), "K pool")

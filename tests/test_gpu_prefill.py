@@ -12,6 +12,7 @@ import torch
 import oracle
 from _gpu_helpers import (TOL_BF16, TOL_FP32, assert_close, assert_rope_close, dev, rope, to_dev_bf16,
                           to_dev_i32, to_host_bits, to_host_f64)
+from _gpu_helpers import guarded_empty, guarded_full, guarded_flags, rope_input_pool
 from paged_kv_gqa_append_amd import binding
 from paged_kv_gqa_append_amd import workloads as W
 
@@ -28,11 +29,11 @@ class DevPrefill:
         self.vp = to_dev_bf16(c.v_pool)
         self.bt = to_dev_i32(c.block_tables)
         self.prefix = to_dev_i32(c.prefix_lens)
-        self.flags = torch.zeros(1, dtype=torch.int32, device=dev())
+        self.flags = guarded_flags()
 
     def run(self, out_dtype=torch.bfloat16, table=None, alias=False):
         table = rope(max_pos=4200) if table is None else table
-        out = self.q if alias else torch.empty(self.q.shape, dtype=out_dtype, device=dev())
+        out = self.q if alias else guarded_empty(self.q.shape, out_dtype)
         binding.prefill_chunk(out, self.q, self.kc, self.vc, self.kp, self.vp, self.bt, self.prefix, table,
                               self.c.scale, device_flags=self.flags)
         torch.cuda.synchronize()
@@ -45,6 +46,14 @@ def oracle_all(c):
                                    c.theta, c.scale)
     assert rc == oracle.OK
     return out, q, kp, vp
+
+
+
+def chunk_inputs(c):
+    """Pre-RoPE K rows of the chunk at their slots, over the pool as it was before the call."""
+    writes = [(c.block_tables[s, (P0 + i) // 16], (P0 + i) % 16, c.k_chunk[s, i])
+              for s, P0 in enumerate(c.prefix_lens) for i in range(c.chunk_len)]
+    return rope_input_pool(c.k_pool, writes)
 
 
 SMALL = {
@@ -69,8 +78,7 @@ def test_prefill_small_against_oracle(name, out_dtype):
     # the append part: pools and rotated q
     gk, gv, gq = to_host_bits(d.kp), to_host_bits(d.vp), to_host_bits(d.q)
     assert np.array_equal(gv, ovp)
-    xmax = float(np.abs(W.bf16_bits_to_f32(np.concatenate([c.k_chunk.ravel(), c.q.ravel()]))).max())
-    assert_rope_close(gk, okp, xmax, "K pool")
+    assert_rope_close(gk, okp, chunk_inputs(c), "K pool")
     diff_slots = np.any(gk != okp, axis=(1, 3))
     written = np.zeros_like(diff_slots)
     for s, P0 in enumerate(c.prefix_lens):
@@ -78,7 +86,7 @@ def test_prefill_small_against_oracle(name, out_dtype):
             t = P0 + i
             written[c.block_tables[s, t // 16], t % 16] = True
     assert not np.any(diff_slots & ~written), "bytes outside the chunk's slots differ"
-    assert_rope_close(gq, oq, xmax, "rotated q")
+    assert_rope_close(gq, oq, c.q, "rotated q")
 
 
 def test_prefill_output_may_alias_q():
@@ -122,8 +130,7 @@ def test_prefill_config_full_size_sampled_rows():
         ref, rc = oracle.decode_gqa(np.ascontiguousarray(q[:, i]), kp, vp, c.block_tables, lens, c.num_pages, c.scale)
         assert rc == oracle.OK
         assert_close(got[:, i], ref, TOL_BF16, f"row {i}")
-    xmax = float(np.abs(W.bf16_bits_to_f32(c.k_chunk)).max())
-    assert_rope_close(to_host_bits(d.kp), kp, xmax, "K pool")
+    assert_rope_close(to_host_bits(d.kp), kp, chunk_inputs(c), "K pool")
     assert np.array_equal(to_host_bits(d.vp), vp)
 
 
@@ -135,7 +142,7 @@ def test_prefill_device_errors():
     bt = c.block_tables.copy()
     bt[2, 1] = c.num_pages + 5       # bad page among sequence 2's used pages
     d.prefix, d.bt = to_dev_i32(prefix), to_dev_i32(bt)
-    out = torch.full(d.q.shape, 3.0, dtype=torch.float32, device=dev())
+    out = guarded_full(d.q.shape, 3.0, torch.float32)
     binding.prefill_chunk(out, d.q, d.kc, d.vc, d.kp, d.vp, d.bt, d.prefix, rope(max_pos=4200), c.scale,
                           device_flags=d.flags)
     torch.cuda.synchronize()

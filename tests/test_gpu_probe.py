@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from _gpu_helpers import dev
+from _gpu_helpers import guarded_zeros, guarded_flags, to_dev_i32
 from paged_kv_gqa_append_amd import binding
 
 pytestmark = pytest.mark.gpu
@@ -44,14 +45,14 @@ def positions(n_vec):
 @pytest.mark.parametrize("n_vec", [1, 37, 256 * 8 * 3 + 5, 256 * 8 * 2048 + 999])
 def test_probe_reads_every_vector(n_vec):
     print(f"probe: {n_vec} vectors", flush=True)
-    buf = torch.zeros((n_vec, 4), dtype=torch.int32, device=dev())
-    sink = torch.zeros(1, dtype=torch.int32, device=dev())
+    buf = guarded_zeros((n_vec, 4), torch.int32)
+    sink = guarded_flags()
     binding.probe_stream_read(buf, sink)
     torch.cuda.synchronize()
     assert int(sink.cpu()[0]) == 0, "sink written for an all-zero buffer"
     words = np.array([0x01234567, 0x89ABCDEF, 0x0F1E2D3C, 0], dtype=np.uint32)
     words[3] = np.uint32(MAGIC) ^ words[0] ^ words[1] ^ words[2]
-    magic_vec = torch.from_numpy(words.view(np.int32)).to(dev())
+    magic_vec = to_dev_i32(words.view(np.int32))
     for p in positions(n_vec):
         buf[p] = magic_vec
         sink.zero_()

@@ -20,7 +20,7 @@ import pytest
 def pa():
     from paged_kv_gqa_append_amd import binding, build
 
-    if not build.is_built():
+    if not build.is_current():
         build.build()
     binding.lib()
     return binding
