@@ -256,8 +256,12 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
  *   scale = max|x| / 127,  code = round-half-even(x / scale) in [-127, 127],
  * both in IEEE binary32, scale 0 and codes 0 for an all-zero row (rows must be
  * finite; the decode accepts V over the same range as the bf16 pools, see
- * "Values" above: the V scales reach the f16 MFMA weights through a running
- * power-of-two exponent, so large V rows neither overflow nor lose precision).  The value a code stands for is
+ * "Values" above).  Accuracy: the products run on f16 MFMAs; the weights
+ * times the V scales reach them through one running power-of-two exponent
+ * per wave, so they never overflow, and a (sequence, KV head)'s outputs are
+ * within the usual rounding of the exact attention plus 2^-16 of the largest
+ * |V| it attends (rows about 2^30 below that largest one lose precision
+ * first; with V rows of ordinary spread the extra term is negligible).  The value a code stands for is
  * code * scale.  K rows are quantised
  * after RoPE from the bf16-rounded rotated row (the row pa_append_kv_rope would
  * store), V rows from their bf16 input.

@@ -28,12 +28,15 @@
 //   O[16][64] += P'[16][16 tokens] . V[16 tokens][64] four v_mfma_f32_16x16x16_f16,
 //       whose A operand is exactly the lane's 4 weights from S^T (rows 0-3
 //       are the 4 heads; rows 4-15 are never read).
-// Codes enter the MFMAs as f16 values 1152 + code: the byte code ^ 0x80 (= code
-// + 128) under an f16 exponent pattern 0x64 is 1024 + code + 128, built with
-// one v_perm per pair, exactly.  The offsets come out again exactly where they
-// went in: the score subtracts 1152 * <q, 1> (an MFMA over a key row of 1152s),
-// and the output subtracts 1152 * the sum of the fed weights, taken by the
-// same MFMA against a ones column.  q enters as f16 after a power-of-two
+// Codes become f16 values 1152 + code: the byte code ^ 0x80 (= code + 128)
+// under an f16 exponent pattern 0x64 is 1024 + code + 128, built with one
+// v_perm per pair, exactly.  K codes enter the MFMAs so; the score subtracts
+// 1152 * <q, 1> (an MFMA over a key row of 1152s), which is exact up to the
+// score's own fp32 rounding.  V codes lose the offset before the MFMA (one
+// packed f16 subtraction per pair, exact: the result is the code itself), so
+// the output sums carry no 1152 * weight terms: with them, a row of large
+// values whose small elements quantise to code 0 would leave fp32 rounding
+// noise of the large row's size in those elements.  q enters as f16 after a power-of-two
 // scaling (exact) that puts its largest element in [2^14, 2^15).  Weights
 // P' = 2^(x - m) * V scale * 2^-ve are fed as an f16 pair hi + lo (two MFMA
 // passes, about 22 significant bits, so the weights' rounding stays ~2^-22 of
@@ -106,10 +109,14 @@ __device__ __forceinline__ half8 codes8_to_f16(uint32_t w0, uint32_t w1) {
     codes_to_f16x4(w1, c, d);
     return __builtin_bit_cast(half8, u32x4{a, b, c, d});
 }
-__device__ __forceinline__ half4 codes4_to_f16(uint32_t w) {
+// 4 codes -> the f16 values of the codes themselves (1152 + code, minus 1152
+// in packed f16: exact, every integer in [-127, 127] being an f16).
+__device__ __forceinline__ half4 codes4_to_f16_signed(uint32_t w) {
     uint32_t a, b;
     codes_to_f16x4(w, a, b);
-    return __builtin_bit_cast(half4, u32x2{a, b});
+    const half4 off = {static_cast<_Float16>(-kOffsetF16), static_cast<_Float16>(-kOffsetF16),
+                       static_cast<_Float16>(-kOffsetF16), static_cast<_Float16>(-kOffsetF16)};
+    return __builtin_bit_cast(half4, u32x2{a, b}) + off;
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
@@ -459,13 +466,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
 
     float m_run = kNegBig;  // running max (log2 units) of head hh
     float l_run = 0.0f;     // sum of 2^(x - m) over the lane's tokens
-    // acc[n]: O[head 4qd + r][dim 16n + hh] (rows 0-3, lanes 0-15, are the
-    // heads); acc[4]: the fed weights' sum of head 4qd + r (the 1152 offset)
-    f32x4 acc[5];
+    // acc[n]: O[head 4qd + r][dim 16n + hh] (rows 0-3, lanes 0-15, are the heads)
+    f32x4 acc[4];
 #pragma unroll
-    for (int n = 0; n < 5; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t one2 = 0x3C003C00u;  // f16 1.0 twice
-    const half4 ones = __builtin_bit_cast(half4, u32x2{one2, one2});
+    for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     // V scales enter the weights as vs * 2^-ve (wave-uniform ve >= 0, raised
     // lazily): every live scale seen so far is below vlim = 2^(ve + 7).
     int ve = 0;
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
             for (int i = 0; i < 4; ++i) {
                 const float fi = lane_value(f, i);
 #pragma unroll
-                for (int n = 0; n < 5; ++n) acc[n][i] *= fi;
+                for (int n = 0; n < 4; ++n) acc[n][i] *= fi;
             }
         }
         // V scales of the live tokens (a dead slot's scale may be anything)
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
             const int ve_new = e - 7;
             const float f = ldexpf(1.0f, ve - ve_new);
 #pragma unroll
-            for (int n = 0; n < 5; ++n)
+            for (int n = 0; n < 4; ++n)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[n][i] *= f;
             ve = ve_new;
@@ -542,15 +546,13 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         const uint32_t l23 = pack_f16x2(pv[2] - static_cast<float>(e23[0]), pv[3] - static_cast<float>(e23[1]));
         const half4 ph = __builtin_bit_cast(half4, u32x2{h01, h23});
         const half4 pl = __builtin_bit_cast(half4, u32x2{l01, l23});
-        const half4 vb[4] = {codes4_to_f16(r.v.x), codes4_to_f16(r.v.y), codes4_to_f16(r.v.z),
-                             codes4_to_f16(r.v.w)};
+        const half4 vb[4] = {codes4_to_f16_signed(r.v.x), codes4_to_f16_signed(r.v.y),
+                             codes4_to_f16_signed(r.v.z), codes4_to_f16_signed(r.v.w)};
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb[n], acc[n], 0, 0, 0);
             acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb[n], acc[n], 0, 0, 0);
         }
-        acc[4] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, ones, acc[4], 0, 0, 0);
-        acc[4] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, ones, acc[4], 0, 0, 0);
     };
     auto process_last = [&](I8Page r, int p) {
         if (kFused) {  // patch the appended token's codes and scales into the registers
@@ -611,12 +613,12 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     if (pg1 == n_pages && p == n_pages - 1) process_last(cur, p);  // the sequence's last page
     // ---- wave epilogue ---------------------------------------------------------
     const float l_tot = sum_quarters(l_run);
-    if (lane < 16) {  // (O minus 1152 x the sum of the fed weights) x 2^ve, per head
+    if (lane < 16) {  // O x 2^ve, per head
         const float vback = ldexpf(1.0f, ve);
 #pragma unroll
         for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_acc[w][i][16 * n + hh] = fmaf(-kOffsetF16, acc[4][i], acc[n][i]) * vback;
+            for (int i = 0; i < 4; ++i) s_acc[w][i][16 * n + hh] = acc[n][i] * vback;
     }
     if (lane < kGroup) {
         s_m[w][lane] = m_run;
