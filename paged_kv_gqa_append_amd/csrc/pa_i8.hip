@@ -473,8 +473,8 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     // V scales enter the weights as vs * 2^-ve (wave-uniform ve >= 0, raised
     // lazily): every live scale seen so far is below vlim = 2^(ve + 7).
     int ve = 0;
-    float vmul = 1.0f;    // 2^-ve
-    float vlim = 128.0f;  // 2^(ve + 7)
+    float vmul = 1.0f;                                       // 2^-ve
+    uint32_t vlim_bits = __builtin_bit_cast(uint32_t, 128.0f);  // 2^(ve + 7), as bits
 
     auto process = [&](const I8Page &r, bool last, int p) {
         // scores of tokens 4qd + i (i < 4) for column hh
@@ -494,42 +494,53 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         }
         // lazy running max of head hh (uniform over the 4 lanes of column hh)
         const float xm = max_quarters(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        const bool need = xm > m_run + kRescaleLog2;
-        if (__builtin_amdgcn_ballot_w64(need && head_lane)) {
-            const float mn = need ? xm : m_run;
-            const float f = fast_exp2(m_run - mn);
-            m_run = mn;
-            l_run *= f;
-            // accumulator row i of lanes 0-15 is head i: its factor is lane i's
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float fi = lane_value(f, i);
-#pragma unroll
-                for (int n = 0; n < 4; ++n) acc[n][i] *= fi;
-            }
-        }
-        // V scales of the live tokens (a dead slot's scale may be anything)
+        const bool need = (xm > m_run + kRescaleLog2) && head_lane;
+        // V scales of the live tokens (a dead slot's scale may be anything);
+        // vneed: one of them exceeds 2^(ve + 7).  The scales are >= 0, so
+        // their bit patterns order as unsigned integers the way the values do
+        // (an integer max needs no NaN-quieting of its loaded operands).
         float vsl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vsl[i] = (last && dead[i]) ? 0.0f : r.vs[i];
-        const float vmx = fmaxf(fmaxf(vsl[0], vsl[1]), fmaxf(vsl[2], vsl[3]));
-        if (__builtin_amdgcn_ballot_w64(vmx > vlim)) {
-            // rare: raise ve so that the page's largest scale times 2^-ve < 2^7
-            // (every lane of a quarter holds the same 4 scales, so the max over
-            // the quarters is the page's, the same in every lane)
-            const float wmx = __builtin_bit_cast(
-                float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, max_quarters(vmx))));
-            int e = 0;
-            (void)frexpf(wmx, &e);  // wmx in [2^(e-1), 2^e), e >= ve + 8
-            const int ve_new = e - 7;
-            const float f = ldexpf(1.0f, ve - ve_new);
+        const uint32_t vmx = max(max(__builtin_bit_cast(uint32_t, vsl[0]), __builtin_bit_cast(uint32_t, vsl[1])),
+                                 max(__builtin_bit_cast(uint32_t, vsl[2]), __builtin_bit_cast(uint32_t, vsl[3])));
+        const bool vneed = vmx > vlim_bits;
+        // one ballot and one branch per page for both rare events
+        if (__builtin_amdgcn_ballot_w64(need || vneed)) {
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = need ? xm : m_run;
+                const float f = fast_exp2(m_run - mn);
+                m_run = mn;
+                l_run *= f;
+                // accumulator row i of lanes 0-15 is head i: its factor is lane i's
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
+                for (int i = 0; i < 4; ++i) {
+                    const float fi = lane_value(f, i);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[n][i] *= f;
-            ve = ve_new;
-            vmul = ldexpf(1.0f, -ve);
-            vlim = ldexpf(1.0f, ve + 7);
+                    for (int n = 0; n < 4; ++n) acc[n][i] *= fi;
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(vneed)) {
+                // raise ve so that the page's largest scale times 2^-ve < 2^7
+                // (every lane of a quarter holds the same 4 scales, so the max
+                // over the quarters is the page's, the same in every lane)
+                const float wmx = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readfirstlane(
+                               __builtin_bit_cast(int, max_quarters(__builtin_bit_cast(float, vmx)))));
+                int e = 0;
+                (void)frexpf(wmx, &e);  // wmx in [2^(e-1), 2^e), e >= ve + 8
+                const int ve_new = e - 7;
+                if (ve_new > ve) {     // (not for a NaN scale, which the contract excludes)
+                    const float f = ldexpf(1.0f, ve - ve_new);
+#pragma unroll
+                    for (int n = 0; n < 4; ++n)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+                    ve = ve_new;
+                    vmul = ldexpf(1.0f, -ve);
+                    vlim_bits = __builtin_bit_cast(uint32_t, ldexpf(1.0f, ve + 7));
+                }
+            }
         }
         float pw[4], pv[4];
 #pragma unroll
