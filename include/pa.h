@@ -114,7 +114,7 @@ int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t s
  * from, so a caller can refuse a library built from another header.  Like the
  * fixed geometry (samir-vllm, section "Limitations et perspectives": changing
  * the architecture means recompiling), a mismatch is refused, not adapted to. */
-#define PA_ABI_VERSION 9
+#define PA_ABI_VERSION 10
 int32_t pa_abi_version(void);
 
 /* Identity of the sources the library was built from: the sha256 (64 hex
@@ -225,6 +225,29 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
                                int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                int32_t out_dtype, void *workspace, size_t workspace_bytes,
                                uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
+
+/* pa_append_decode_gqa without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: the decode partials
+ * go to a scratch array of PA_NOALLOC_SCRATCH_BYTES that the library holds in
+ * every GPU it runs on (static device memory, kept until the process ends).
+ * Everything else, results included, is exactly pa_append_decode_gqa's.
+ * Limit: pa_decode_workspace_bytes(num_seqs, max_blocks) must not exceed
+ * PA_NOALLOC_SCRATCH_BYTES (8 MiB: for example 64 sequences of up to 30720
+ * tokens, or 256 of up to 6144), else PA_ERR_WORKSPACE before anything runs.
+ * The scratch needs no initialisation and holds nothing between calls, but it
+ * is one array per GPU: calls on one GPU whose executions overlap (on
+ * different streams, or concurrently from several host threads on streams
+ * that are not ordered) race on it and must be serialised by the caller.
+ * `stream` must belong to the current device.  PA_ERR_HIP if the scratch
+ * cannot be located on the current device.                                  */
+#define PA_NOALLOC_SCRATCH_BYTES (8u << 20)
+pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, const void *v_new, void *k_pool,
+                                       void *v_pool, const int32_t *block_tables, const int32_t *context_lens,
+                                       const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                       int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
+                                       int32_t out_dtype, uint32_t *device_flags, const int32_t *dispatch_order,
+                                       hipStream_t stream);
 
 /* Chunked prefill (TinyLoop, section "prefill_chunk and scratch residency":
  * the prompt is processed in row chunks; samir-vllm: the prompt's pages are

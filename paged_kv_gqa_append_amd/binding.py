@@ -32,11 +32,12 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_slot_request", "pa_kvm_slot_budget", "pa_kvm_free_pages", "pa_kvm_reserved_pages",
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
            "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read",
-           "pa_dispatch_order_longest_first", "pa_get_device_error", "pa_build_id")
+           "pa_dispatch_order_longest_first", "pa_get_device_error", "pa_build_id",
+           "pa_append_decode_gqa_noalloc")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class PaError(RuntimeError):
@@ -97,6 +98,9 @@ def lib():
     L.pa_append_decode_gqa.restype = ctypes.c_int
     L.pa_append_decode_gqa.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
                                        u64, P, P, P]
+    L.pa_append_decode_gqa_noalloc.restype = ctypes.c_int
+    L.pa_append_decode_gqa_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float,
+                                               i32, P, P, P]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
                                    P, P]
@@ -325,6 +329,41 @@ def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
                                     float(scale), odt, _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr,
                                     _stream(stream))
     _check(rc, "pa_append_decode_gqa")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # PA_NOALLOC_SCRATCH_BYTES
+
+
+def append_decode_gqa_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                              k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, rope_cos_sin: torch.Tensor, scale: float = 0.125,
+                              device_flags: Optional[torch.Tensor] = None, page_size: int = 16,
+                              dispatch_order=None, stream=None) -> torch.Tensor:
+    """pa_append_decode_gqa_noalloc: pa_append_decode_gqa with the library's own per-GPU scratch
+    in place of a workspace (nothing is allocated; calls on one GPU must not overlap)."""
+    num_pages = _pool_checks(k_pool, v_pool)
+    dev = k_pool.device
+    _expect(context_lens, "context_lens", torch.int32, device=dev)
+    B = int(context_lens.shape[0])
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
+    _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    odt = _out_dtype(out)
+    _expect(out, "out", out.dtype, (B, 32, 64), dev)
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    order_arr, order_ptr = _order(dispatch_order, B)
+    rc = lib().pa_append_decode_gqa_noalloc(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                            _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+                                            _ptr(rope_cos_sin), B, int(block_tables.shape[1]), num_pages,
+                                            int(page_size), int(rope_cos_sin.shape[0]), float(scale), odt,
+                                            _ptr(device_flags), order_ptr, _stream(stream))
+    _check(rc, "pa_append_decode_gqa_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pa.h"
 #include "pa_device.h"
@@ -89,6 +90,32 @@ pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new
     d.flags = device_flags;
     d.order = order;
     return (i8 ? pa::launch_decode_i8(d, stream) : pa::launch_decode(d, stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// ---- the no-allocation decode entry point's scratch ------------------------
+// Decode partials of pa_append_decode_gqa_noalloc live in this file-scope
+// device array instead of a caller workspace: PA_NOALLOC_SCRATCH_BYTES per
+// GPU, held by each GPU the library runs on until the process ends.  In host
+// code the array's name is only a stand-in; the device address is looked up
+// once per device with hipGetSymbolAddress (with that device current) and
+// kept in g_scratch_ptr, and only that pointer is ever handed to a kernel.
+static __device__ __align__(256) float scratch[PA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The scratch array's device address on the current device (nullptr on failure).
+void *scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -188,6 +215,26 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
     return decode_common(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin, num_seqs,
                          max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace, workspace_bytes,
                          device_flags, dispatch_order, stream, true);
+}
+
+pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, const void *v_new, void *k_pool,
+                                       void *v_pool, const int32_t *block_tables, const int32_t *context_lens,
+                                       const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                       int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
+                                       int32_t out_dtype, uint32_t *device_flags, const int32_t *dispatch_order,
+                                       hipStream_t stream) {
+    // Sizes first, so that an oversized call fails before anything else.
+    const size_t need = pa_decode_workspace_bytes(num_seqs, max_blocks);
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        ws = scratch_on_current_device();
+        if (!ws) return PA_ERR_HIP;
+    }
+    return decode_common(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin, num_seqs,
+                         max_blocks, num_pages, page_size, max_pos, scale, out_dtype, ws,
+                         need > 0 ? static_cast<size_t>(PA_NOALLOC_SCRATCH_BYTES) : 0, device_flags, dispatch_order,
+                         stream, true);
 }
 
 pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool, void *v_pool,

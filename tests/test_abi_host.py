@@ -45,7 +45,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 9
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 10
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -344,3 +344,28 @@ def test_dispatch_order_length_refused(pa):
             pa.append_decode_gqa_i8(out, q, kn, kn, i8, bt, lens, table, dispatch_order=bad)
     arr, ptr = pa._order(np.array([2, 0, 1], np.int32), B)
     assert arr.shape == (3,) and ptr.value == arr.ctypes.data
+
+
+def test_noalloc_size_limit(pa):
+    """pa_append_decode_gqa_noalloc refuses a batch whose partials exceed its scratch before
+    anything else happens (the fake pointers are never touched), and validates arguments like
+    pa_append_decode_gqa when no scratch is needed."""
+    lib = pa.lib()
+    v = ctypes.c_void_p
+    F = v(FAKE)
+    pp = lib.pa_decode_partition_tokens() // 16
+
+    def na(B=4, mb=8, ps=16, mp=64, q=F, rope=F):
+        return lib.pa_append_decode_gqa_noalloc(F, q, F, F, F, F, F, F, rope, B, mb, 64, ps, mp, 0.125, 0, None,
+                                                None, None)
+
+    assert lib.pa_decode_workspace_bytes(64, 16 * pp + 1) > pa.NOALLOC_SCRATCH_BYTES
+    assert na(B=64, mb=16 * pp + 1) == pa.PA_ERR_WORKSPACE
+    assert lib.pa_decode_workspace_bytes(64, 15 * pp) <= pa.NOALLOC_SCRATCH_BYTES
+    assert na(ps=32) == pa.PA_ERR_UNSUPPORTED
+    assert na(mp=0) == pa.PA_ERR_INVALID_ARG
+    assert na(q=None) == pa.PA_ERR_INVALID_ARG
+    assert na(rope=None) == pa.PA_ERR_INVALID_ARG
+    assert na(B=0) == pa.PA_OK
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_SCRATCH_BYTES
