@@ -49,11 +49,13 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRows = 64;                   // chunk positions per workgroup
+#ifndef PA_PREFILL_SUB
+#define PA_PREFILL_SUB 1
+#endif
+constexpr int kSub = PA_PREFILL_SUB;        // 32-row sub-tiles per wave
+constexpr int kRows = 32 * kSub;            // chunk positions per workgroup
 constexpr int kKB = 32;                     // keys per block
-constexpr int kKStride = 72;                // bf16 per K row in LDS (64 + 8 pad: conflict-free fragment reads)
-constexpr int kKBuf = kKB * kKStride;       // bf16 per K buffer
-constexpr int kVBuf = kD * 20;              // 32-bit words per V^T buffer (64 rows of 5 units)
+constexpr int kBlockBytes = kKB * kD * 2;  // one K or V block in LDS: 32 rows of 128 bytes
 constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -72,6 +74,39 @@ __device__ __forceinline__ float partner32(float v) {
     return __lane_id() < 32 ? __builtin_bit_cast(float, r1) : __builtin_bit_cast(float, r0);
 }
 
+// max(v, value of lane l^32) in every lane: after the swap one register holds
+// the lower lane's value and the other the upper one's, in both halves, so no
+// select is needed.
+__device__ __forceinline__ float max_partner32(float v) {
+    const unsigned a = __builtin_bit_cast(unsigned, v);
+    unsigned b = a;
+    asm volatile("" : "+v"(b));
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
+// One 16-byte direct-to-LDS load per lane (global_load_lds_dwordx4): lane l's
+// 16 bytes at gbase + voff (bytes) land at LDS byte address lds + 16 l.  It is
+// issued through inline assembly so that the compiler, which cannot tell which
+// LDS buffer it fills, does not hold LDS reads of the other buffers behind it;
+// the kernel waits for these loads itself (vmcnt) before the barrier that
+// publishes a buffer.  M0 carries the LDS address; its previous value is kept
+// and restored, since the compiler may hold one there.  gbase and lds must be
+// wave-uniform.
+__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %1\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(gbase), "v"(voff), "s"(lds)
+        : "memory");
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -81,33 +116,33 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Slot of key k (0..31) in a V^T row: bits 2 and 3 swapped.  Lane half g of
-// the P.V MFMA over keys 16b..16b+15 holds the weights of keys
-// 16b + 4g + {0..3, 8..11}; with this order they sit in slots 16b + 8g .. +7.
-__device__ __forceinline__ int vt_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// K and V blocks in LDS: 32 rows (keys) of 128 bytes, as in the pool, with the
+// 16-byte chunk c of row r stored at chunk position c ^ (r & 7).  Direct-to-LDS
+// loads write each wave's 8 rows as one contiguous kilobyte (lane l fetches the
+// chunk that belongs at position l), and the swizzle spreads the fragment reads
+// (one chunk column of many rows) over the banks.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
-// 16-byte unit of V^T row d (0..63) that holds slot chunk ch (slots 8ch..8ch+7).
-// Rows are 5 units apart (one unit of padding): the MFMA fragment reads (16
-// consecutive rows, one unit each) then fall in distinct banks, and the
-// transposing stores (4 rows 8 apart, 16 words each, per instruction) meet at
-// most two to a bank instead of four.
-__device__ __forceinline__ int vt_unit(int d, int ch) { return d * 5 + ch; }
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// acc + the sum of the 8 bf16 weights (dot2 against (1, 1): exact products,
-// fp32 sums), as two independent chains.
-__device__ __forceinline__ float sum8_bf16(bf16x8 v, float acc) {
-    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc, false);
-    float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, 0.0f, false);
-    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, a, false);
-    b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, b, false);
-    return a + b;
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i names the 4 consecutive elements of row i/4 of a 4 x 16 block
+// (columns 4(i%4)..+3), and lane j receives column j of the block, rows 0..3.
+__device__ __forceinline__ bf16x4 read_tr16(const unsigned char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
 }
 
-// Two 16-byte global loads per thread stage one K/V block (see load_block).
-struct Stage {
-    u32x4 a, b;
-};
+// acc + the sum of the 8 bf16 weights (dot2 against (1, 1): exact products,
+// fp32 sums), one chain.
+__device__ __forceinline__ float sum8_bf16(bf16x8 v, float acc) {
+    const bf16x2 one2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, acc, false);
+    return acc;
+}
 
 }  // namespace
 
@@ -167,36 +202,61 @@ __device__ __forceinline__ void load_q_rotated(const PrefillParams &P, int s, in
     }
 }
 
-// One 32-key block for both sub-tiles of this wave.  sk: K rows [key][72],
-// svt: V^T in swizzled 16-byte units.  pos0: absolute position of this lane's
-// query in sub-tile 0 (sub-tile 1 is +32).  mask: some key of the block may
-// lie past a row's position or past the sequence (wave-uniform); dead keys get
-// score -inf, hence weight exactly 0 (c > 0).
-template <bool kHiLo>
-__device__ __forceinline__ void attend_block(const uint16_t *sk, const uint32_t *svt, int lane, int kb, bool mask,
-                                             const bf16x8 (&qf)[2][4], f32x16 (&o)[2][2], float (&m)[2],
-                                             float (&l)[2], int pos0, int total, float c, float thr) {
+// The fragments of one 32-key block, read from LDS (sk, sv: the block's K and
+// V rows, swizzled, see swz).
+//   kf: K as the A operand of S^T = K Q^T: key l%32, dims 16kk + 8(l/32) .. +7.
+//   vf: V^T as the A operand of O^T += V^T P^T over keys 16sb..16sb+15: lane l
+//       holds dim 32db + l%32 of the keys its P^T operand pairs with.  The score
+//       registers give lane half h the keys 16sb + 4h + {0..3} and
+//       16sb + 4h + {8..11} (registers 8sb .. 8sb+7), so two transposing reads
+//       of 4 rows each fetch exactly those keys for 16 consecutive dims.
+__device__ __forceinline__ void read_k(const unsigned char *sk, int lane, bf16x8 (&kf)[4]) {
     const int qc = lane & 31, half = lane >> 5;
-    bf16x8 kf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sk + qc * kKStride + 16 * kk + 8 * half));
-    f32x16 st[2];
+        kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sk + swz(qc, 2 * kk + half)));
+}
+__device__ __forceinline__ void read_v(const unsigned char *sv, int lane, bf16x8 (&vf)[2][2]) {
+    const int half = lane >> 5;
+    const int rq = (lane & 15) >> 2;  // row within the 4-row block
+    const int col0 = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int col = 32 * db + col0;
+            const int r0 = 16 * sb + 4 * half + rq;
+            const bf16x4 lo = read_tr16(sv + swz(r0, col >> 3) + ((col & 7) << 1));
+            const bf16x4 hi = read_tr16(sv + swz(r0 + 8, col >> 3) + ((col & 7) << 1));
+            vf[db][sb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+}
+
+// One 32-key block for the wave's sub-tiles, from its K fragments (read_k) and
+// the block's V rows in LDS (read here, after the S^T products are issued, so
+// the K and V fragments are never held at once).
+// pos0: absolute position of this lane's query in sub-tile 0 (sub-tile 1 is
+// +32).  mask: some key of the block may lie past a row's position or past the
+// sequence (wave-uniform); dead keys get score -inf, hence weight exactly 0
+// (c > 0).
+template <bool kHiLo>
+__device__ __forceinline__ void attend_block(const bf16x8 (&kf)[4], const unsigned char *sv, int lane, int kb,
+                                             bool mask, const bf16x8 (&qf)[kSub][4], f32x16 (&o)[kSub][2],
+                                             float (&m)[kSub], float (&mt)[kSub], float (&mc)[kSub],
+                                             float (&l)[kSub], int pos0, int total, float c, float thr) {
+    const int half = lane >> 5;
+    f32x16 st[kSub];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
         st[u] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) st[u] = mfma32(kf[kk], qf[u][kk], st[u]);
     }
     bf16x8 vf[2][2];
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-            vf[db][sb] = as_bf16x8(*reinterpret_cast<const u32x4 *>(svt + 4 * vt_unit(32 * db + qc, 2 * sb + half)));
+    read_v(sv, lane, vf);
 
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kSub; ++u) {
         float x[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[v] = st[u][v];
@@ -210,8 +270,9 @@ __device__ __forceinline__ void attend_block(const uint16_t *sk, const uint32_t 
 #pragma unroll
         for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, x[v]), x[v + 1]);
         mx = fmaxf(mx, x[15]);
-        mx = fmaxf(mx, partner32(mx));
-        const bool need = !(mx <= m[u] + thr);  // also true on the first block (m = -inf)
+        mx = max_partner32(mx);
+        // mt = m + thr; also true on the first live block (m = mt = -inf)
+        const bool need = !(mx <= mt[u]);
         if (__builtin_amdgcn_ballot_w64(need)) {
             // rare after the first block: keep it a branch (the barrier stops
             // the compiler from multiplying the accumulators unconditionally)
@@ -221,20 +282,21 @@ __device__ __forceinline__ void attend_block(const uint16_t *sk, const uint32_t 
             // factor is 0 when m was -inf
             const float f = need ? fast_exp2((m[u] - mx) * c) : 1.0f;
             m[u] = need ? mx : m[u];
+            mt[u] = m[u] + thr;
+            // m is still -inf only if no key so far is live for this row (a
+            // key half can start past a row's position): every score is -inf
+            // then, and offset 0 keeps their weights at 0 instead of -inf + inf.
+            mc[u] = m[u] > -INFINITY ? m[u] * c : 0.0f;
             l[u] *= f;
             o[u][0] *= f;
             o[u][1] *= f;
         }
-        // m is still -inf only if no key so far is live for this row (a key
-        // half can start past a row's position): every score is -inf then,
-        // and offset 0 keeps their weights at 0 instead of -inf + inf.
-        const float mc = m[u] > -INFINITY ? m[u] * c : 0.0f;
         bf16x8 pb[2], pl[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[8 * sb + e], c, -mc));
+            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[8 * sb + e], c, -mc[u]));
             uint32_t wh[4], wl[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
@@ -261,19 +323,19 @@ __device__ __forceinline__ void attend_block(const uint16_t *sk, const uint32_t 
 
 }  // namespace
 
-// LDS layout of one workgroup: two key halves, each with double-buffered K
-// and V^T blocks; after the block loop the same bytes hold the second half's
-// partial results for the merge.
-constexpr int kKBufBytes = kKBuf * 2;
-constexpr int kVBufBytes = kVBuf * 4;
-constexpr int kHalfBytes = 2 * (kKBufBytes + kVBufBytes);
+// LDS layout of one workgroup: two key halves, each with kNBuf K and V block
+// buffers; after the block loop the same bytes hold the second half's partial
+// results for the merge.
+constexpr int kNBuf = 4;                                // K/V blocks in LDS per key half (3 in flight)
+constexpr int kHalfBytes = 2 * kNBuf * kBlockBytes;     // per key half: K and V, kNBuf buffers each
 constexpr int kStageBytes = 2 * kHalfBytes;
-constexpr int kMergeOBytes = 4 * 2 * 64 * 32 * 4;   // 4 waves x 2 sub-tiles x 64 lanes x 32 floats
-constexpr int kMergeMLBytes = 4 * 2 * 64 * 2 * 4;   // (m, l) per lane and sub-tile
+constexpr int kMergeOBytes = 4 * kSub * 64 * 32 * 4;   // 4 waves x sub-tiles x 64 lanes x 32 floats
+constexpr int kMergeMLBytes = 4 * kSub * 64 * 2 * 4;   // (m, l) per lane and sub-tile
 constexpr int kSmemBytes = kStageBytes > kMergeOBytes + kMergeMLBytes ? kStageBytes : kMergeOBytes + kMergeMLBytes;
 
 template <bool kHiLo>
-__global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
+// kSub == 1: two workgroups per CU, so each SIMD holds 4 waves (<= 128 VGPRs)
+__global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(PrefillParams P) {
     // ids -> (sequence, KV head, tile): the 8 low id bits pick the XCD, which
     // is also the KV head, so every tile of (s, j) runs on XCD j; the longest
     // tiles (highest positions) go first.
@@ -316,7 +378,7 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
         // are valid), then zero-fill this tile's rows of this head.  The first
         // key half's waves do it.
         if (kh != 0) return;
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kSub; ++u) {
             const int i = row0 + 32 * u + qc;
             if (i >= C) continue;
             const int64_t pos = static_cast<int64_t>(prefix) + i;
@@ -344,10 +406,10 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
     }
 
     // ---- rotated q fragments of both sub-tiles --------------------------------
-    bf16x8 qf[2][4];
+    bf16x8 qf[kSub][4];
     int pos0 = 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kSub; ++u) {
         const int i = row0 + 32 * u + qc;
         const int i_c = min(i, C - 1);  // padding rows compute on the last row, never stored
         if (u == 0) pos0 = prefix + i_c;
@@ -371,126 +433,109 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
     // first block that needs the causal / length mask for some row of the tile
     const int first_masked = (prefix + row0) / kKB;
 
-    unsigned char *my_half = s_raw + kh * kHalfBytes;
-    uint16_t *s_k0 = reinterpret_cast<uint16_t *>(my_half);
-    uint16_t *s_k1 = reinterpret_cast<uint16_t *>(my_half + kKBufBytes);
-    uint32_t *s_v0 = reinterpret_cast<uint32_t *>(my_half + 2 * kKBufBytes);
-    uint32_t *s_v1 = reinterpret_cast<uint32_t *>(my_half + 2 * kKBufBytes + kVBufBytes);
+    // LDS of this key half: K buffers 0 .. kNBuf-1, then V buffers (kBlockBytes
+    // each), addressed by arithmetic on the shared array (so every access is
+    // known to be an LDS access)
+    const int half_off = kh * kHalfBytes;
+    auto k_buf = [&](int buf) { return s_raw + half_off + buf * kBlockBytes; };
+    auto v_buf = [&](int buf) { return s_raw + half_off + (kNBuf + buf) * kBlockBytes; };
+    const uint32_t lds_half = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(s_raw + half_off)));
 
-    // Staging roles within a key half (256 threads): threads 0..127 move K
-    // (key st&31, d 8p..8p+7 and 32+8p..+7 with p = st>>5), threads 128..255
-    // move V (keys 2kp, 2kp+1 with kp = u&15, d 8c..8c+7 with c = u>>4).  Every
-    // thread issues the same two loads; dead keys (>= total) read a live row so
-    // no NaN reaches the MFMA; blocks past the half's range are clamped.
-    const int st_id = tid & 255;
-    const bool is_k = st_id < 128;
-    const int u_t = st_id & 127;
+    // Staging: the 4 waves of a key half each bring 8 keys (rows 8wq .. 8wq+7
+    // of the block) of K and of V straight into LDS, one 16-byte direct-to-LDS
+    // load per lane and tensor: lane l fills chunk position l%8 of row l/8,
+    // which holds the row's chunk (l%8) ^ (row & 7) (see swz).  The 8 rows lie
+    // in one page, so the page base is scalar and each lane adds a fixed
+    // offset.  Dead keys (>= total) fetch the first row of the same page (a
+    // live one), or of the sequence's first page when the whole page lies past
+    // the sequence, so no NaN reaches the MFMAs; blocks past the half's range
+    // are clamped (re-read, never used).
+    const int wq = w & 3;
     const int64_t tile_j = static_cast<int64_t>(j) * kTile;
-    const uint16_t *pool = is_k ? P.k_pool : P.v_pool;
-    auto load_block = [&](int kbl) -> Stage {
+    const int st_row = 8 * wq + (lane >> 3);
+    const uint32_t st_chunk_b = static_cast<uint32_t>(((lane & 7) ^ (st_row & 7)) * 16);
+    const uint32_t st_off_live = static_cast<uint32_t>((8 * (wq & 1) + (lane >> 3)) * kD * 2) + st_chunk_b;
+    // The page of this wave's 8 rows of block kb_begin + i, held by lane i (read
+    // back with readlane, so staging waits for no LDS read); blocks from 64 on
+    // (contexts past 4096 keys) look theirs up in LDS.
+    auto page_of = [&](int kb) {
+        const int idx = 2 * kb + (wq >> 1);
+        return s_pages[idx < n_pages ? idx : 0];
+    };
+    const int my_page = page_of(min(kb_begin + lane, nb - 1));
+    auto stage_block = [&](int kbl, int buf) {
         const int kb = min(kb_begin + kbl, nb - 1);
-        int key0, key1, d0, d1;
-        if (is_k) {
-            key0 = key1 = kb * kKB + (u_t & 31);
-            d0 = 8 * (u_t >> 5);
-            d1 = d0 + 32;
-        } else {
-            key0 = kb * kKB + 2 * (u_t & 15);
-            key1 = key0 + 1;
-            d0 = d1 = 8 * (u_t >> 4);
-        }
-        key0 = key0 < total ? key0 : 0;
-        key1 = key1 < total ? key1 : key0;
-        const uint16_t *r0 = pool + static_cast<int64_t>(s_pages[key0 >> 4]) * kPageElems + tile_j + (key0 & 15) * kD;
-        const uint16_t *r1 = pool + static_cast<int64_t>(s_pages[key1 >> 4]) * kPageElems + tile_j + (key1 & 15) * kD;
-        Stage st;
-        st.a = *reinterpret_cast<const u32x4 *>(r0 + d0);
-        st.b = *reinterpret_cast<const u32x4 *>(r1 + d1);
-        return st;
+        const int page = __builtin_amdgcn_readfirstlane(kbl < 64 ? __builtin_amdgcn_readlane(my_page, kbl)
+                                                                   : page_of(kb));
+        const int64_t base = static_cast<int64_t>(page) * kPageElems + tile_j;
+        const uint32_t voff = kb * kKB + st_row < total ? st_off_live : st_chunk_b;
+        const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_half + buf * kBlockBytes + wq * 8 * 128);
+        dma16(P.k_pool + base, voff, lds_k);
+        dma16(P.v_pool + base, voff, lds_k + kNBuf * kBlockBytes);
     };
-    auto store_block = [&](const Stage &st, uint16_t *sk, uint32_t *svt) {
-        if (is_k) {
-            uint16_t *dst = sk + (u_t & 31) * kKStride + 8 * (u_t >> 5);
-            *reinterpret_cast<u32x4 *>(dst) = st.a;
-            *reinterpret_cast<u32x4 *>(dst + 32) = st.b;
-        } else {
-            const int slot = vt_slot(2 * (u_t & 15));
-            const int c8 = u_t >> 4;
-            const uint32_t ra[4] = {st.a.x, st.a.y, st.a.z, st.a.w};
-            const uint32_t rb[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
+
+    f32x16 o[kSub][2];
+    float m[kSub], mt[kSub], mc[kSub], l[kSub];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = 8 * c8 + e;
-                // (V[2kp][d], V[2kp+1][d]) as one word: low halves or high halves
-                const uint32_t wv = (e & 1) ? __builtin_amdgcn_perm(rb[e >> 1], ra[e >> 1], 0x07060302u)
-                                            : __builtin_amdgcn_perm(rb[e >> 1], ra[e >> 1], 0x05040100u);
-                svt[4 * vt_unit(d, slot >> 3) + ((slot & 7) >> 1)] = wv;
-            }
-        }
-    };
-
-    f32x16 o[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
-    float m[2] = {-INFINITY, -INFINITY};
-    float l[2] = {0.0f, 0.0f};
-    auto attend = [&](int kbl, const uint16_t *sk, const uint32_t *svt) {
-        if (kbl >= kb_count) return;  // the second half may run out first
-        const int kb = kb_begin + kbl;
-        attend_block<kHiLo>(sk, svt, lane, kb, kb >= first_masked, qf, o, m, l, pos0, total, P.c, P.thr);
-    };
-
-    // Two register stages in flight: while block kb is consumed from LDS,
-    // block kb+1 waits in registers and block kb+2 is being loaded.  Both key
-    // halves run the same trip count (nb0) so that their barriers pair up.
-    Stage sa = load_block(0);
-    Stage sb = load_block(1);
-    store_block(sa, s_k0, s_v0);
-    __syncthreads();
-    sa = load_block(2);
-    // Within one barrier interval the staging of the next block and the use of
-    // the current one are independent, so the two key halves take them in
-    // opposite orders: the second half's MFMAs then start while the first
-    // half's waves (which share its SIMDs) are in their softmax, instead of
-    // both halves contending for the MFMA unit and then for the VALU.
-    for (int kbl = 0;; kbl += 2) {
-        if (kh == 0) {
-            attend(kbl, s_k0, s_v0);
-            store_block(sb, s_k1, s_v1);
-        } else {
-            store_block(sb, s_k1, s_v1);
-            attend(kbl, s_k0, s_v0);
-        }
-        __syncthreads();
-        if (kbl + 1 >= nb0) break;
-        sb = load_block(kbl + 3);
-        if (kh == 0) {
-            attend(kbl + 1, s_k1, s_v1);
-            store_block(sa, s_k0, s_v0);
-        } else {
-            store_block(sa, s_k0, s_v0);
-            attend(kbl + 1, s_k1, s_v1);
-        }
-        __syncthreads();
-        if (kbl + 2 >= nb0) break;
-        sa = load_block(kbl + 4);
+    for (int u = 0; u < kSub; ++u) {
+        o[u][0] = f32x16{};
+        o[u][1] = f32x16{};
+        m[u] = -INFINITY;
+        mt[u] = -INFINITY;
+        mc[u] = 0.0f;
+        l[u] = 0.0f;
     }
+
+    // Block kbl is read from buffer kbl % kNBuf while blocks kbl+1 .. kbl+3 land
+    // in the others (the loads of block kbl+3 are issued right after the K
+    // fragments of block kbl are read).  One barrier per block:
+    // before it each wave waits until its loads of block kbl+1 have landed (at
+    // most the two blocks after it, 4 loads, still in flight), and after it
+    // every wave is done with the buffer the next loads overwrite.  Both key
+    // halves run the same trip count (nb0) so that their barriers pair up; the
+    // second half may run out of blocks first.
+#pragma unroll
+    for (int b = 0; b < kNBuf - 1; ++b)
+        if (b < nb0) stage_block(b, b);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kbl = 0;; ++kbl) {
+        bf16x8 kf[4];
+        const int buf = kbl & (kNBuf - 1);
+        read_k(k_buf(buf), lane, kf);
+        const bool more = kbl + kNBuf - 1 < nb0;
+        if (more) stage_block(kbl + kNBuf - 1, (kbl + kNBuf - 1) & (kNBuf - 1));
+        if (kbl < kb_count) {
+            const int kb = kb_begin + kbl;
+            attend_block<kHiLo>(kf, v_buf(buf), lane, kb, kb >= first_masked, qf, o, m, mt, mc, l, pos0, total,
+                                P.c, P.thr);
+        }
+        if (kbl + 1 >= nb0) break;
+        // block kbl+1's loads are the oldest of this wave's in flight: with a
+        // full pipeline, 2 blocks (4 loads) were issued after them
+        if (more) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    __syncthreads();
 
     // ---- merge the two key halves through LDS ---------------------------------
     // slot of this lane's results: (head-in-group, sub-tile, lane); lane-major
     float *mo = reinterpret_cast<float *>(s_raw);
     float *mml = reinterpret_cast<float *>(s_raw + kMergeOBytes);
-    const int wq = w & 3;
     if (kh == 1) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float *dst = mo + ((wq * 2 + u) * 64 + lane) * 32;
+        for (int u = 0; u < kSub; ++u) {
+            float *dst = mo + ((wq * kSub + u) * 64 + lane) * 32;
 #pragma unroll
             for (int db = 0; db < 2; ++db)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
                     *reinterpret_cast<f32x4 *>(dst + 16 * db + 4 * r4) =
                         f32x4{o[u][db][4 * r4], o[u][db][4 * r4 + 1], o[u][db][4 * r4 + 2], o[u][db][4 * r4 + 3]};
-            mml[((wq * 2 + u) * 64 + lane) * 2] = m[u];
-            mml[((wq * 2 + u) * 64 + lane) * 2 + 1] = l[u];
+            mml[((wq * kSub + u) * 64 + lane) * 2] = m[u];
+            mml[((wq * kSub + u) * 64 + lane) * 2 + 1] = l[u];
         }
     }
     __syncthreads();
@@ -499,7 +544,7 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
     // ---- rotated q back in place (unless out aliases q) -------------------------
     if (P.write_q) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kSub; ++u) {
             const int i = row0 + 32 * u + qc;
             if (i >= C) continue;
             uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
@@ -513,10 +558,10 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillParams P) {
 
     // ---- out[s][i][h][d] = O^T[d][query] / l, d = 32db + 8r4 + 4*half + r ------
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const float *src = mo + ((wq * 2 + u) * 64 + lane) * 32;
-        const float mB = mml[((wq * 2 + u) * 64 + lane) * 2];
-        const float lB = mml[((wq * 2 + u) * 64 + lane) * 2 + 1];
+    for (int u = 0; u < kSub; ++u) {
+        const float *src = mo + ((wq * kSub + u) * 64 + lane) * 32;
+        const float mB = mml[((wq * kSub + u) * 64 + lane) * 2];
+        const float lB = mml[((wq * kSub + u) * 64 + lane) * 2 + 1];
         const float mt = fmaxf(m[u], mB);  // finite: the first half always holds key 0
         const float fA = fast_exp2((m[u] - mt) * P.c);
         const float fB = fast_exp2((mB - mt) * P.c);  // 0 when the second half had no block
