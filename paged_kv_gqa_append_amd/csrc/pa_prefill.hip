@@ -12,29 +12,34 @@
 // 512 x 512 x 32 score buffer, ch.2 buffer table).
 //
 // Work decomposition
-//   One workgroup per (sequence, KV head j, tile of 64 chunk positions); its 4
-//   waves are the 4 query heads of that KV head, and each wave carries its 64
-//   rows as two 32-row sub-tiles, so every K/V fragment a wave reads from LDS
-//   feeds 2 x 32 query rows.  Keys go 32 at a time (two pages).  Workgroup ids
-//   are mapped so that all tiles of one (sequence, KV head) land on the same
-//   XCD (ids are dealt to the 8 XCDs round-robin) and share its L2.
+//   One workgroup of 8 waves per (sequence, KV head j, tile of 32 chunk
+//   positions; built with PA_PREFILL_SUB=2, 64 positions as two 32-row
+//   sub-tiles per wave, one workgroup per CU).  Waves 0-3 are the 4 query
+//   heads of that KV head over the first half of the tile's key blocks, waves
+//   4-7 the same heads over the second half; the two partial results are
+//   merged through LDS at the end, each half finishing 32 of the 64 output
+//   dims.  Two workgroups share a CU (4 waves per SIMD, <= 128 VGPRs).  Keys
+//   go 32 at a time (two pages).
+//   Workgroup ids are mapped so that all tiles of one (sequence, KV head) land
+//   on the same XCD (ids are dealt to the 8 XCDs round-robin) and share its
+//   L2; the longest tiles start first.
 //   Scores are computed transposed, S^T = K Q^T (32 keys x 32 queries): in the
 //   MFMA result layout a lane holds 16 keys of ONE query (lane l: query l%32,
 //   keys 8i + 4(l/32) + r in register 4i+r), so the online softmax is
 //   lane-local plus one exchange with lane l^32.  The output is accumulated
 //   transposed too, O^T = V^T P^T (64 d x 32 queries): the same lane-per-query
 //   layout, so rescaling is lane-local.  P^T is the MFMA B operand straight
-//   from the score registers; V^T is staged in LDS with its key slots permuted
-//   to match (bits 2 and 3 of the key swapped), so each A fragment is one
-//   16-byte LDS read.
-//   K/V blocks are double-buffered in LDS and prefetched two blocks ahead
-//   through registers; one barrier per block.
-//   Softmax in log2 units with a lazy running max (rescale only when a block
-//   exceeds it by more than 2^8): per score one max, one fused multiply-add,
-//   one exp2, a packed bf16 conversion and half a dot2 for the row sum, which
-//   is taken over the same bf16 weights the P.V product uses.  With fp32
-//   output the weights are fed as a bf16 hi/lo pair (two MFMAs) so they keep
-//   ~16 significant bits.
+//   from the score registers; the V^T fragments come from natural V rows in
+//   LDS through transposing LDS reads.
+//   K/V blocks go from the pool straight into LDS (direct-to-LDS loads, no
+//   staging registers), four buffers per key half with three blocks in
+//   flight; one barrier per block.
+//   Softmax in log2 units against a lazily kept integer reference: per score
+//   one fused multiply-add, one exp2, half a packed bf16 conversion and half a
+//   dot2 for the row sum (taken over the same bf16 weights the P.V product
+//   uses); the block maximum is needed only when the weights outgrow 2^8.
+//   With fp32 output the weights are fed as a bf16 hi/lo pair (two MFMAs) so
+//   they keep ~16 significant bits.
 //   q is rotated here, from the fp32 cos/sin table, with the same expressions
 //   as the append kernel; the rotated row is written back to q unless out
 //   aliases q.
@@ -56,7 +61,6 @@ constexpr int kSub = PA_PREFILL_SUB;        // 32-row sub-tiles per wave
 constexpr int kRows = 32 * kSub;            // chunk positions per workgroup
 constexpr int kKB = 32;                     // keys per block
 constexpr int kBlockBytes = kKB * kD * 2;  // one K or V block in LDS: 32 rows of 128 bytes
-constexpr float kRescaleLog2 = 8.0f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -117,11 +121,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 }
 
 // K and V blocks in LDS: 32 rows (keys) of 128 bytes, as in the pool, with the
-// 16-byte chunk c of row r stored at chunk position c ^ (r & 7).  Direct-to-LDS
-// loads write each wave's 8 rows as one contiguous kilobyte (lane l fetches the
-// chunk that belongs at position l), and the swizzle spreads the fragment reads
-// (one chunk column of many rows) over the banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of row r stored at chunk position c ^ f(r), where
+// f(r) = 2 (r mod 4) + (r / 4 mod 2) is a permutation of 0..7 over any 8
+// consecutive rows.  Direct-to-LDS loads write each wave's 8 rows as one
+// contiguous kilobyte (lane l fetches the chunk that belongs at position l),
+// and the swizzle spreads the fragment reads over the 32 banks: a K read (one
+// chunk of 8 consecutive rows per 8 lanes) meets 8 positions, and so does a
+// transposing V read (chunks 2i, 2i+1 of 4 rows 4j..4j+3 per 16 lanes).
+__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ swz_f(row)) << 4); }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -162,7 +170,6 @@ struct PrefillParams {
     int write_q;
     int neg;        // scale < 0: q is negated for the products and c = |scale| log2(e)
     float c;        // |scale| * log2(e)
-    float thr;      // lazy-rescale threshold in raw score units (2^8 in log2 units)
     int out_fp32;
     uint32_t *flags;
 };
@@ -170,28 +177,35 @@ struct PrefillParams {
 namespace {
 
 // Rotated q fragments of one 32-row sub-tile (MFMA B operand): this lane's
-// query row i_c, d = 16kk + 8*half .. +7.  Pairs (d, d+32) are kk and kk+2 of
-// the same lane.
-__device__ __forceinline__ void load_q_rotated(const PrefillParams &P, int s, int h, int i_c, int pos_c, int half,
-                                               u32x4 (&rq)[4]) {
-    const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * P.chunk_len + i_c) * kHQ + h) * kD;
+// query row, d = 16kk + 8*half .. +7.  Pairs (d, d+32) are kk and kk+2 of the
+// same lane.  The loads (q row and the position's (cos, sin) entries) and the
+// arithmetic are separate steps, so the loads can be issued early.
+struct QRaw {
     u32x4 raw[4];
+    f32x4 t[2][4];
+};
+__device__ __forceinline__ QRaw load_q_raw(const PrefillParams &P, int s, int h, int i_c, int pos_c, int half) {
+    QRaw r;
+    const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * P.chunk_len + i_c) * kHQ + h) * kD;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) raw[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * half);
+    for (int kk = 0; kk < 4; ++kk) r.raw[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * half);
     const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD;  // [32][2]
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int i0 = 16 * kk + 8 * half;  // first pair of this fragment
-        f32x4 t[4];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] = *reinterpret_cast<const f32x4 *>(cs + 2 * i0 + 4 * r);
-        const uint32_t lo[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
-        const uint32_t hi[4] = {raw[kk + 2].x, raw[kk + 2].y, raw[kk + 2].z, raw[kk + 2].w};
+        for (int e = 0; e < 4; ++e) r.t[kk][e] = *reinterpret_cast<const f32x4 *>(cs + 2 * (16 * kk + 8 * half) + 4 * e);
+    return r;
+}
+__device__ __forceinline__ void rotate_q(const QRaw &r, u32x4 (&rq)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const uint32_t lo[4] = {r.raw[kk].x, r.raw[kk].y, r.raw[kk].z, r.raw[kk].w};
+        const uint32_t hi[4] = {r.raw[kk + 2].x, r.raw[kk + 2].y, r.raw[kk + 2].z, r.raw[kk + 2].w};
         uint32_t ylo[4], yhi[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-            // pairs i0 + 2*e2 (low bf16 of each word) and i0 + 2*e2 + 1 (high bf16)
-            const float c0 = t[e2][0], s0 = t[e2][1], c1 = t[e2][2], s1 = t[e2][3];
+            // pairs i0 + 2*e2 (low bf16 of each word) and i0 + 2*e2 + 1 (high bf16), i0 = 16kk + 8half
+            const float c0 = r.t[kk][e2][0], s0 = r.t[kk][e2][1], c1 = r.t[kk][e2][2], s1 = r.t[kk][e2][3];
             const float a0 = bf16_lo(lo[e2]), b0 = bf16_lo(hi[e2]);
             const float a1 = bf16_hi(lo[e2]), b1 = bf16_hi(hi[e2]);
             ylo[e2] = pack_bf16x2(rope_lo(a0, b0, c0, s0), rope_lo(a1, b1, c1, s1));
@@ -200,6 +214,10 @@ __device__ __forceinline__ void load_q_rotated(const PrefillParams &P, int s, in
         rq[kk] = u32x4{ylo[0], ylo[1], ylo[2], ylo[3]};
         rq[kk + 2] = u32x4{yhi[0], yhi[1], yhi[2], yhi[3]};
     }
+}
+__device__ __forceinline__ void load_q_rotated(const PrefillParams &P, int s, int h, int i_c, int pos_c, int half,
+                                               u32x4 (&rq)[4]) {
+    rotate_q(load_q_raw(P, s, h, i_c, pos_c, half), rq);
 }
 
 // The fragments of one 32-key block, read from LDS (sk, sv: the block's K and
@@ -232,92 +250,128 @@ __device__ __forceinline__ void read_v(const unsigned char *sv, int lane, bf16x8
         }
 }
 
+// Scores of one 32-key block for sub-tile u (S^T = K Q^T), with dead keys at
+// -inf.  pos0: absolute position of this lane's query in sub-tile 0 (sub-tile
+// 1 is +32).  mask: some key of the block may lie past a row's position or past
+// the sequence (wave-uniform).
+__device__ __forceinline__ void block_scores(const bf16x8 (&kf)[4], const bf16x8 (&qf)[4], int half, int kb,
+                                             bool mask, int lim_pos, float (&x)[16]) {
+    f32x16 st = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) st = mfma32(kf[kk], qf[kk], st);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = st[v];
+    if (mask) {
+        // key kb*32 + 8(v/4) + 4*half + v%4 is live iff <= lim_pos
+        const int lim = lim_pos - kb * kKB - 4 * half;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3)) > lim ? -INFINITY : x[v];
+    }
+}
+
+// Weights exp2(t - d) of the lane's 16 log-weights t as bf16 (and, for fp32
+// output, the bf16 remainders), and their sum over the same bf16 values.
+template <bool kHiLo>
+__device__ __forceinline__ float block_weights(const float (&t)[16], float d, bf16x8 (&pb)[2], bf16x8 (&pl)[2]) {
+    float bs = 0.0f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(t[8 * sb + e] - d);
+        uint32_t wh[4], wl[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            wh[e2] = cvt_pk_bf16(p[2 * e2], p[2 * e2 + 1]);
+            if (kHiLo) wl[e2] = cvt_pk_bf16(p[2 * e2] - bf16_lo(wh[e2]), p[2 * e2 + 1] - bf16_hi(wh[e2]));
+        }
+        pb[sb] = as_bf16x8(u32x4{wh[0], wh[1], wh[2], wh[3]});
+        bs = sum8_bf16(pb[sb], bs);
+        if (kHiLo) {
+            pl[sb] = as_bf16x8(u32x4{wl[0], wl[1], wl[2], wl[3]});
+            bs = sum8_bf16(pl[sb], bs);
+        }
+    }
+    return bs;
+}
+
+// O^T += V^T P^T for one sub-tile (both 32-dim halves, both 16-key steps).
+template <bool kHiLo>
+__device__ __forceinline__ void pv_products(const bf16x8 (&vf)[2][2], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
+                                            f32x16 (&o)[2]) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            o[db] = mfma32(vf[db][sb], pb[sb], o[db]);
+            if (kHiLo) o[db] = mfma32(vf[db][sb], pl[sb], o[db]);
+        }
+}
+
 // One 32-key block for the wave's sub-tiles, from its K fragments (read_k) and
-// the block's V rows in LDS (read here, after the S^T products are issued, so
+// the block's V rows in LDS (sv, read after the S^T products are issued, so
 // the K and V fragments are never held at once).
-// pos0: absolute position of this lane's query in sub-tile 0 (sub-tile 1 is
-// +32).  mask: some key of the block may lie past a row's position or past the
-// sequence (wave-uniform); dead keys get score -inf, hence weight exactly 0
-// (c > 0).
+//
+// Softmax in log2 units against a lazily kept, integer-valued reference ref
+// (-inf while none of the row's keys so far is live; mc = ref, or 0 then): the
+// log-weights are t = c x - mc.  The usual step needs no block maximum: the
+// weights exp2(t) are accepted when the lane's 16 of them sum to at most 2^8
+// (so each is at most 2^8; an overflow or NaN fails the test too).  Otherwise,
+// and on a key half's first block (first, uniform), the reference moves up by
+// d = ceil of the row's largest t where that is positive (or is set to it when
+// the row had none), O and l are multiplied by 2^-d, and the weights are taken
+// again as exp2(t - d) (each <= 1 then).  Integer references keep every factor
+// an exact power of two.  Dead keys have x = -inf, hence t = -inf and weight 0.
 template <bool kHiLo>
 __device__ __forceinline__ void attend_block(const bf16x8 (&kf)[4], const unsigned char *sv, int lane, int kb,
-                                             bool mask, const bf16x8 (&qf)[kSub][4], f32x16 (&o)[kSub][2],
-                                             float (&m)[kSub], float (&mt)[kSub], float (&mc)[kSub],
-                                             float (&l)[kSub], int pos0, int total, float c, float thr) {
+                                             bool mask, bool first, const bf16x8 (&qf)[kSub][4],
+                                             f32x16 (&o)[kSub][2], float (&ref)[kSub], float (&l)[kSub], int pos0,
+                                             int total, float c) {
     const int half = lane >> 5;
-    f32x16 st[kSub];
+    float t[kSub][16];
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-        st[u] = f32x16{};
+        float x[16];
+        block_scores(kf, qf[u], half, kb, mask, min(pos0 + 32 * u, total - 1), x);
+        const float mc = ref[u] > -INFINITY ? ref[u] : 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st[u] = mfma32(kf[kk], qf[u][kk], st[u]);
+        for (int v = 0; v < 16; ++v) t[u][v] = fmaf(x[v], c, -mc);
     }
     bf16x8 vf[2][2];
     read_v(sv, lane, vf);
 
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-        float x[16];
+        bf16x8 pb[2], pl[2];
+        float bs = block_weights<kHiLo>(t[u], 0.0f, pb, pl);
+        if (first || __builtin_amdgcn_ballot_w64(!(bs <= 256.0f))) {
+            float tmax = t[u][0];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = st[u][v];
-        if (mask) {
-            // key kb*32 + 8(v/4) + 4*half + v%4 is live iff <= min(pos, total-1)
-            const int lim = min(pos0 + 32 * u, total - 1) - kb * kKB - 4 * half;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3)) > lim ? -INFINITY : x[v];
-        }
-        float mx = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-        for (int v = 3; v < 15; v += 2) mx = fmaxf(fmaxf(mx, x[v]), x[v + 1]);
-        mx = fmaxf(mx, x[15]);
-        mx = max_partner32(mx);
-        // mt = m + thr; also true on the first live block (m = mt = -inf)
-        const bool need = !(mx <= mt[u]);
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            // rare after the first block: keep it a branch (the barrier stops
-            // the compiler from multiplying the accumulators unconditionally)
-            asm volatile("" ::: "memory");
-            // lanes that do not need it keep m and factor 1 (their m may be
-            // -inf, and -inf - -inf must not reach the exp); otherwise the
-            // factor is 0 when m was -inf
-            const float f = need ? fast_exp2((m[u] - mx) * c) : 1.0f;
-            m[u] = need ? mx : m[u];
-            mt[u] = m[u] + thr;
-            // m is still -inf only if no key so far is live for this row (a
-            // key half can start past a row's position): every score is -inf
-            // then, and offset 0 keeps their weights at 0 instead of -inf + inf.
-            mc[u] = m[u] > -INFINITY ? m[u] * c : 0.0f;
+            for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, t[u][v]);
+            tmax = max_partner32(tmax);
+            const bool has = ref[u] > -INFINITY;
+            const bool live = tmax > -INFINITY;
+            float d = 0.0f, f = 1.0f;
+            if (has) {
+                if (tmax > 0.0f) {
+                    const float r_new = ref[u] + ceilf(tmax);
+                    d = r_new - ref[u];
+                    ref[u] = r_new;
+                    f = fast_exp2(-d);
+                }
+            } else if (live) {
+                // first live key of the row: O and l are still 0
+                d = ceilf(tmax);
+                ref[u] = d;
+                f = 0.0f;
+            }
             l[u] *= f;
             o[u][0] *= f;
             o[u][1] *= f;
+            bs = block_weights<kHiLo>(t[u], d, pb, pl);
         }
-        bf16x8 pb[2], pl[2];
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(x[8 * sb + e], c, -mc[u]));
-            uint32_t wh[4], wl[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                wh[e2] = cvt_pk_bf16(p[2 * e2], p[2 * e2 + 1]);
-                if (kHiLo)
-                    wl[e2] = cvt_pk_bf16(p[2 * e2] - bf16_lo(wh[e2]), p[2 * e2 + 1] - bf16_hi(wh[e2]));
-            }
-            pb[sb] = as_bf16x8(u32x4{wh[0], wh[1], wh[2], wh[3]});
-            l[u] = sum8_bf16(pb[sb], l[u]);
-            if (kHiLo) {
-                pl[sb] = as_bf16x8(u32x4{wl[0], wl[1], wl[2], wl[3]});
-                l[u] = sum8_bf16(pl[sb], l[u]);
-            }
-        }
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                o[u][db] = mfma32(vf[db][sb], pb[sb], o[u][db]);
-                if (kHiLo) o[u][db] = mfma32(vf[db][sb], pl[sb], o[u][db]);
-            }
+        l[u] += bs;
+        pv_products<kHiLo>(vf, pb, pl, o[u]);
     }
 }
 
@@ -329,8 +383,8 @@ __device__ __forceinline__ void attend_block(const bf16x8 (&kf)[4], const unsign
 constexpr int kNBuf = 4;                                // K/V blocks in LDS per key half (3 in flight)
 constexpr int kHalfBytes = 2 * kNBuf * kBlockBytes;     // per key half: K and V, kNBuf buffers each
 constexpr int kStageBytes = 2 * kHalfBytes;
-constexpr int kMergeOBytes = 4 * kSub * 64 * 32 * 4;   // 4 waves x sub-tiles x 64 lanes x 32 floats
-constexpr int kMergeMLBytes = 4 * kSub * 64 * 2 * 4;   // (m, l) per lane and sub-tile
+constexpr int kMergeOBytes = 8 * kSub * 64 * 16 * 4;   // 8 waves x sub-tiles x 64 lanes x 16 floats
+constexpr int kMergeMLBytes = 8 * kSub * 64 * 2 * 4;   // (m, l) per wave, lane and sub-tile
 constexpr int kSmemBytes = kStageBytes > kMergeOBytes + kMergeMLBytes ? kStageBytes : kMergeOBytes + kMergeMLBytes;
 
 template <bool kHiLo>
@@ -358,22 +412,97 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
     __shared__ int s_pages[kMaxBlocksPrefill];
     __shared__ __align__(16) unsigned char s_raw[kSmemBytes];
 
-    // ---- validation: the whole sequence's pages ------------------------------
+    // ---- prologue ----------------------------------------------------------------
+    // Every WG starts at once, so each dependent round trip to memory here adds
+    // to the whole call.  After the prefix length, the loads that do not depend
+    // on validation all go out together: the block table (one entry per thread,
+    // for validation and for LDS), this lane's q row and (cos, sin) entries, the
+    // page ids of the first blocks and those blocks' K/V (direct to LDS).  All
+    // addresses are clamped into their arrays, so a sequence that then fails
+    // validation has read only valid memory; its results are never used.
     const int prefix = P.prefix_lens[s];
     const int64_t lim = min(static_cast<int64_t>(P.max_blocks) * kPage, static_cast<int64_t>(P.max_pos));
     const bool len_ok = prefix >= 0 && static_cast<int64_t>(prefix) + C <= lim;
     const int total = len_ok ? prefix + C : 0;
-    const int n_pages = (total + kPage - 1) / kPage;
+    const int n_pages = (total + kPage - 1) / kPage;  // <= kMaxBlocksPrefill = the WG's thread count
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
-    int bad = 0;
-    for (int b = tid; b < n_pages; b += 512) {
-        const int pid = bt_row[b];
-        s_pages[b] = pid;
-        bad |= (pid < 0) | (pid >= P.num_pages);
+    int pid = 0;
+    if (tid < n_pages) pid = bt_row[tid];
+
+    // block ranges: keys needed by this tile are 0 .. prefix + last valid row
+    const int prefix_c = len_ok ? prefix : 0;
+    const int last_key = prefix_c + min(row0 + kRows, C) - 1;
+    const int nb = last_key / kKB + 1;
+    const int nb0 = (nb + 1) / 2;  // blocks of the first key half (the loop trip count)
+    const int kb_begin = kh ? nb0 : 0;
+    const int kb_count = kh ? nb - nb0 : nb0;
+    // first block that needs the causal / length mask for some row of the tile
+    const int first_masked = (prefix_c + row0) / kKB;
+
+    // q rows of the sub-tiles (padding rows compute on the last row, never
+    // stored; sub-tile 1 of a partly padded tile overshoots, and keys >= total
+    // are masked anyway)
+    QRaw qraw[kSub];
+    int pos0 = 0;
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+        const int i_c = min(row0 + 32 * u + qc, C - 1);
+        if (u == 0) pos0 = prefix_c + i_c;
+        const int pos_c = min(max(prefix_c + i_c, 0), P.max_pos - 1);
+        qraw[u] = load_q_raw(P, s, h, i_c, pos_c, half);
     }
+
+    // LDS of this key half: K buffers 0 .. kNBuf-1, then V buffers (kBlockBytes
+    // each), addressed by arithmetic on the shared array (so every access is
+    // known to be an LDS access)
+    const int half_off = kh * kHalfBytes;
+    auto k_buf = [&](int buf) { return s_raw + half_off + buf * kBlockBytes; };
+    auto v_buf = [&](int buf) { return s_raw + half_off + (kNBuf + buf) * kBlockBytes; };
+    const uint32_t lds_half = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(s_raw + half_off)));
+
+    // Staging: the 4 waves of a key half each bring 8 keys (rows 8wq .. 8wq+7
+    // of the block) of K and of V straight into LDS, one 16-byte direct-to-LDS
+    // load per lane and tensor: lane l fills chunk position l%8 of row l/8,
+    // which holds the row's chunk (l%8) ^ f(row) (see swz).  The 8 rows lie
+    // in one page, so the page base is scalar and each lane adds a fixed
+    // offset.  Dead keys (>= total) fetch the first row of the same page (a
+    // live one), or of the sequence's first page when the whole page lies past
+    // the sequence, so no NaN reaches the MFMAs; blocks past the half's range
+    // are clamped (re-read, never used).
+    const int wq = w & 3;
+    const int64_t tile_j = static_cast<int64_t>(j) * kTile;
+    const int st_row = 8 * wq + (lane >> 3);
+    const uint32_t st_chunk_b = static_cast<uint32_t>(((lane & 7) ^ swz_f(st_row)) * 16);
+    const uint32_t st_off_live = static_cast<uint32_t>((8 * (wq & 1) + (lane >> 3)) * kD * 2) + st_chunk_b;
+    auto stage_with = [&](int kbl, int buf, int page) {
+        const int kb = min(kb_begin + kbl, nb - 1);
+        const int64_t base = static_cast<int64_t>(page) * kPageElems + tile_j;
+        const uint32_t voff = kb * kKB + st_row < total ? st_off_live : st_chunk_b;
+        const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_half + buf * kBlockBytes + wq * 8 * 128);
+        dma16(P.k_pool + base, voff, lds_k);
+        dma16(P.v_pool + base, voff, lds_k + kNBuf * kBlockBytes);
+    };
+    // the first blocks, from page ids read straight from the table (scalar
+    // loads; ids clamped into the pool)
+#pragma unroll
+    for (int b = 0; b < kNBuf - 1; ++b) {
+        if (b < nb0) {
+            const int idx = min(2 * min(kb_begin + b, nb - 1) + (wq >> 1), P.max_blocks - 1);
+            const int idx_c = idx < n_pages ? idx : 0;
+            int page = bt_row[__builtin_amdgcn_readfirstlane(idx_c)];
+            page = min(max(page, 0), P.num_pages - 1);
+            stage_with(b, b, __builtin_amdgcn_readfirstlane(page));
+        }
+    }
+
+    // ---- validation: the whole sequence's pages ------------------------------
+    if (tid < n_pages) s_pages[tid] = pid;
+    const int bad = (tid < n_pages) && (pid < 0 || pid >= P.num_pages);
     const bool ok = len_ok && __syncthreads_or(bad) == 0;
 
     if (!ok) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
         // Rotate q where the append would have (the token's position and page
         // are valid), then zero-fill this tile's rows of this head.  The first
         // key half's waves do it.
@@ -384,8 +513,8 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
             const int64_t pos = static_cast<int64_t>(prefix) + i;
             bool tok_ok = prefix >= 0 && pos < lim;
             if (tok_ok) {
-                const int pid = bt_row[pos >> 4];
-                tok_ok = pid >= 0 && pid < P.num_pages;
+                const int pid_t = bt_row[pos >> 4];
+                tok_ok = pid_t >= 0 && pid_t < P.num_pages;
             }
             if (P.write_q && tok_ok) {
                 u32x4 rq[4];
@@ -405,60 +534,19 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
         return;
     }
 
-    // ---- rotated q fragments of both sub-tiles --------------------------------
+    // ---- rotated q fragments --------------------------------------------------
     bf16x8 qf[kSub][4];
-    int pos0 = 0;
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-        const int i = row0 + 32 * u + qc;
-        const int i_c = min(i, C - 1);  // padding rows compute on the last row, never stored
-        if (u == 0) pos0 = prefix + i_c;
         u32x4 rq[4];
-        load_q_rotated(P, s, h, i_c, prefix + i_c, half, rq);
+        rotate_q(qraw[u], rq);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) qf[u][kk] = as_bf16x8(P.neg ? (rq[kk] ^ 0x80008000u) : rq[kk]);
     }
-    // The rotated rows are written back only after the final barrier: both
-    // key halves read the same q rows here.
-    // sub-tile 1 of a partly padded tile: pos0 + 32 overshoots; keys >= total
-    // are masked anyway, and its rows are not stored.
 
-    // ---- block ranges -----------------------------------------------------------
-    // keys needed by this tile: 0 .. prefix + last valid row
-    const int last_key = prefix + min(row0 + kRows, C) - 1;
-    const int nb = last_key / kKB + 1;
-    const int nb0 = (nb + 1) / 2;          // blocks of the first key half (the loop trip count)
-    const int kb_begin = kh ? nb0 : 0;
-    const int kb_count = kh ? nb - nb0 : nb0;
-    // first block that needs the causal / length mask for some row of the tile
-    const int first_masked = (prefix + row0) / kKB;
-
-    // LDS of this key half: K buffers 0 .. kNBuf-1, then V buffers (kBlockBytes
-    // each), addressed by arithmetic on the shared array (so every access is
-    // known to be an LDS access)
-    const int half_off = kh * kHalfBytes;
-    auto k_buf = [&](int buf) { return s_raw + half_off + buf * kBlockBytes; };
-    auto v_buf = [&](int buf) { return s_raw + half_off + (kNBuf + buf) * kBlockBytes; };
-    const uint32_t lds_half = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(s_raw + half_off)));
-
-    // Staging: the 4 waves of a key half each bring 8 keys (rows 8wq .. 8wq+7
-    // of the block) of K and of V straight into LDS, one 16-byte direct-to-LDS
-    // load per lane and tensor: lane l fills chunk position l%8 of row l/8,
-    // which holds the row's chunk (l%8) ^ (row & 7) (see swz).  The 8 rows lie
-    // in one page, so the page base is scalar and each lane adds a fixed
-    // offset.  Dead keys (>= total) fetch the first row of the same page (a
-    // live one), or of the sequence's first page when the whole page lies past
-    // the sequence, so no NaN reaches the MFMAs; blocks past the half's range
-    // are clamped (re-read, never used).
-    const int wq = w & 3;
-    const int64_t tile_j = static_cast<int64_t>(j) * kTile;
-    const int st_row = 8 * wq + (lane >> 3);
-    const uint32_t st_chunk_b = static_cast<uint32_t>(((lane & 7) ^ (st_row & 7)) * 16);
-    const uint32_t st_off_live = static_cast<uint32_t>((8 * (wq & 1) + (lane >> 3)) * kD * 2) + st_chunk_b;
     // The page of this wave's 8 rows of block kb_begin + i, held by lane i (read
-    // back with readlane, so staging waits for no LDS read); blocks from 64 on
-    // (contexts past 4096 keys) look theirs up in LDS.
+    // back with readlane, so staging in the loop waits for no LDS read); blocks
+    // from 64 on (contexts past 4096 keys) look theirs up in LDS.
     auto page_of = [&](int kb) {
         const int idx = 2 * kb + (wq >> 1);
         return s_pages[idx < n_pages ? idx : 0];
@@ -468,81 +556,27 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
         const int kb = min(kb_begin + kbl, nb - 1);
         const int page = __builtin_amdgcn_readfirstlane(kbl < 64 ? __builtin_amdgcn_readlane(my_page, kbl)
                                                                    : page_of(kb));
-        const int64_t base = static_cast<int64_t>(page) * kPageElems + tile_j;
-        const uint32_t voff = kb * kKB + st_row < total ? st_off_live : st_chunk_b;
-        const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_half + buf * kBlockBytes + wq * 8 * 128);
-        dma16(P.k_pool + base, voff, lds_k);
-        dma16(P.v_pool + base, voff, lds_k + kNBuf * kBlockBytes);
+        stage_with(kbl, buf, page);
     };
 
     f32x16 o[kSub][2];
-    float m[kSub], mt[kSub], mc[kSub], l[kSub];
+    float ref[kSub], l[kSub];
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
         o[u][0] = f32x16{};
         o[u][1] = f32x16{};
-        m[u] = -INFINITY;
-        mt[u] = -INFINITY;
-        mc[u] = 0.0f;
+        ref[u] = -INFINITY;
         l[u] = 0.0f;
     }
 
-    // Block kbl is read from buffer kbl % kNBuf while blocks kbl+1 .. kbl+3 land
-    // in the others (the loads of block kbl+3 are issued right after the K
-    // fragments of block kbl are read).  One barrier per block:
-    // before it each wave waits until its loads of block kbl+1 have landed (at
-    // most the two blocks after it, 4 loads, still in flight), and after it
-    // every wave is done with the buffer the next loads overwrite.  Both key
-    // halves run the same trip count (nb0) so that their barriers pair up; the
-    // second half may run out of blocks first.
-#pragma unroll
-    for (int b = 0; b < kNBuf - 1; ++b)
-        if (b < nb0) stage_block(b, b);
+    // the first blocks have landed (and the q loads); publish them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    for (int kbl = 0;; ++kbl) {
-        bf16x8 kf[4];
-        const int buf = kbl & (kNBuf - 1);
-        read_k(k_buf(buf), lane, kf);
-        const bool more = kbl + kNBuf - 1 < nb0;
-        if (more) stage_block(kbl + kNBuf - 1, (kbl + kNBuf - 1) & (kNBuf - 1));
-        if (kbl < kb_count) {
-            const int kb = kb_begin + kbl;
-            attend_block<kHiLo>(kf, v_buf(buf), lane, kb, kb >= first_masked, qf, o, m, mt, mc, l, pos0, total,
-                                P.c, P.thr);
-        }
-        if (kbl + 1 >= nb0) break;
-        // block kbl+1's loads are the oldest of this wave's in flight: with a
-        // full pipeline, 2 blocks (4 loads) were issued after them
-        if (more) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
-    __syncthreads();
-
-    // ---- merge the two key halves through LDS ---------------------------------
-    // slot of this lane's results: (head-in-group, sub-tile, lane); lane-major
-    float *mo = reinterpret_cast<float *>(s_raw);
-    float *mml = reinterpret_cast<float *>(s_raw + kMergeOBytes);
-    if (kh == 1) {
-#pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            float *dst = mo + ((wq * kSub + u) * 64 + lane) * 32;
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    *reinterpret_cast<f32x4 *>(dst + 16 * db + 4 * r4) =
-                        f32x4{o[u][db][4 * r4], o[u][db][4 * r4 + 1], o[u][db][4 * r4 + 2], o[u][db][4 * r4 + 3]};
-            mml[((wq * kSub + u) * 64 + lane) * 2] = m[u];
-            mml[((wq * kSub + u) * 64 + lane) * 2 + 1] = l[u];
-        }
-    }
-    __syncthreads();
-    if (kh == 1) return;
 
     // ---- rotated q back in place (unless out aliases q) -------------------------
-    if (P.write_q) {
+    // Every wave has read its q rows by now (the barrier above follows their
+    // use), so the first key half writes them back here, under the main loop.
+    if (P.write_q && kh == 0) {
 #pragma unroll
         for (int u = 0; u < kSub; ++u) {
             const int i = row0 + 32 * u + qc;
@@ -556,37 +590,86 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
         }
     }
 
-    // ---- out[s][i][h][d] = O^T[d][query] / l, d = 32db + 8r4 + 4*half + r ------
+    // Block kbl is read from buffer kbl % kNBuf while blocks kbl+1 .. kbl+3 land
+    // in the others (the loads of block kbl+3 are issued right after the K
+    // fragments of block kbl are read).  One barrier per block: before it each
+    // wave waits until its loads of block kbl+1 have landed (at most the two
+    // blocks after it, 4 loads, still in flight), and after it every wave is
+    // done with the buffer the next loads overwrite.  Both key halves run the
+    // same trip count (nb0) so that their barriers pair up; the second half may
+    // run out of blocks first.
+    for (int kbl = 0;; ++kbl) {
+        bf16x8 kf[4];
+        const int buf = kbl & (kNBuf - 1);
+        read_k(k_buf(buf), lane, kf);
+        const bool more = kbl + kNBuf - 1 < nb0;
+        if (more) stage_block(kbl + kNBuf - 1, (kbl + kNBuf - 1) & (kNBuf - 1));
+        if (kbl < kb_count) {
+            const int kb = kb_begin + kbl;
+            attend_block<kHiLo>(kf, v_buf(buf), lane, kb, kb >= first_masked, kbl == 0, qf, o, ref, l, pos0, total,
+                                P.c);
+        }
+        if (kbl + 1 >= nb0) break;
+        // block kbl+1's loads are the oldest of this wave's in flight: with a
+        // full pipeline, 2 blocks (4 loads) were issued after them
+        if (more) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    __syncthreads();
+
+    // ---- merge the two key halves through LDS -----------------------------------
+    // Key half kh finalizes dims 32kh .. 32kh+31: each wave leaves the other
+    // half's dims of its partial O^T, with its (m, l), in LDS.  Slot:
+    // (key half, head-in-group, sub-tile, lane), 16 floats.
+    float *mo = reinterpret_cast<float *>(s_raw);
+    float *mml = reinterpret_cast<float *>(s_raw + kMergeOBytes);
+    auto slot = [&](int half_k, int u) { return ((half_k * 4 + wq) * kSub + u) * 64 + lane; };
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
-        const float *src = mo + ((wq * kSub + u) * 64 + lane) * 32;
-        const float mB = mml[((wq * kSub + u) * 64 + lane) * 2];
-        const float lB = mml[((wq * kSub + u) * 64 + lane) * 2 + 1];
-        const float mt = fmaxf(m[u], mB);  // finite: the first half always holds key 0
-        const float fA = fast_exp2((m[u] - mt) * P.c);
-        const float fB = fast_exp2((mB - mt) * P.c);  // 0 when the second half had no block
+        const f32x16 give = kh ? o[u][0] : o[u][1];
+        float *dst = mo + slot(kh, u) * 16;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<f32x4 *>(dst + 4 * r4) = f32x4{give[4 * r4], give[4 * r4 + 1], give[4 * r4 + 2],
+                                                             give[4 * r4 + 3]};
+        mml[slot(kh, u) * 2] = ref[u];
+        mml[slot(kh, u) * 2 + 1] = l[u];
+    }
+    __syncthreads();
+
+    // ---- out[s][i][h][d] = O^T[d][query] / l, d = 32kh + 8r4 + 4*half + r ------
+    const int oh = 1 - kh;
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+        const float *src = mo + slot(oh, u) * 16;
+        const float rB = mml[slot(oh, u) * 2];
+        const float lB = mml[slot(oh, u) * 2 + 1];
+        // finite: the first half always holds key 0; a half that had no live
+        // key for a row has reference -inf and weight 0
+        const float rx = fmaxf(ref[u], rB);
+        const float fA = fast_exp2(ref[u] - rx);
+        const float fB = fast_exp2(rB - rx);
         const float lh = l[u] * fA + lB * fB;
         const float l_tot = lh + partner32(lh);
         const int i = row0 + 32 * u + qc;
         if (i >= C) continue;
         const float inv = 1.0f / l_tot;
+        const f32x16 mine = kh ? o[u][1] : o[u][0];
         const int64_t orow = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 16 * db + 4 * r4);
-                const int d = 32 * db + 8 * r4 + 4 * half;
-                const float y0 = (o[u][db][4 * r4] * fA + ob[0] * fB) * inv;
-                const float y1 = (o[u][db][4 * r4 + 1] * fA + ob[1] * fB) * inv;
-                const float y2 = (o[u][db][4 * r4 + 2] * fA + ob[2] * fB) * inv;
-                const float y3 = (o[u][db][4 * r4 + 3] * fA + ob[3] * fB) * inv;
-                if (P.out_fp32) {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
-                } else {
-                    const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
-                }
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 4 * r4);
+            const int d = 32 * kh + 8 * r4 + 4 * half;
+            const float y0 = (mine[4 * r4] * fA + ob[0] * fB) * inv;
+            const float y1 = (mine[4 * r4 + 1] * fA + ob[1] * fB) * inv;
+            const float y2 = (mine[4 * r4 + 2] * fA + ob[2] * fB) * inv;
+            const float y3 = (mine[4 * r4 + 3] * fA + ob[3] * fB) * inv;
+            if (P.out_fp32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
+            } else {
+                const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
             }
         }
     }
@@ -616,7 +699,6 @@ hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream) 
     const float c = p.scale * 1.4426950408889634f;
     P.neg = c < 0.0f;
     P.c = fmaxf(fabsf(c), 1e-30f);
-    P.thr = kRescaleLog2 / P.c;
     P.out_fp32 = p.out_fp32;
     P.flags = p.flags;
     const int64_t blocks = static_cast<int64_t>(p.num_seqs) * kHKV * P.n_tiles;
