@@ -29,7 +29,7 @@
  *   q              : [num_seqs][32][64] bf16; q head h reads KV head h/4.
  *   k_new, v_new   : [num_seqs][8][64] bf16 (the decode-time K/V batch buffers
  *                    of tiny-vllm, BATCH_SIZE x KV_DIM).
- *   rope_cos_sin   : [max_pos][32][2] fp32: (cos, sin) of pos * w_i,
+ *   rope_cos_sin   : [max_pos][32][2] fp64: (cos, sin) of pos * w_i,
  *                    w_i = theta^(-2i/64); pair i rotates elements (i, i+32)
  *                    ("rotate-half").  Build it with pa_rope_table_fill_host.
  *
@@ -114,7 +114,7 @@ int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t s
  * from, so a caller can refuse a library built from another header.  Like the
  * fixed geometry (samir-vllm, section "Limitations et perspectives": changing
  * the architecture means recompiling), a mismatch is refused, not adapted to. */
-#define PA_ABI_VERSION 10
+#define PA_ABI_VERSION 11
 int32_t pa_abi_version(void);
 
 /* Identity of the sources the library was built from: the sha256 (64 hex
@@ -124,11 +124,11 @@ const char *pa_build_id(void);
 
 /* The RoPE frequency table the initialization block builds (tiny-vllm ch.2,
  * section "What else is set up in the initialization block").  Fill a HOST
- * table [max_pos][32][2] fp32 with (cos, sin)(pos * theta^(-2i/64)),
- * evaluated in double precision and rounded once to fp32.  The caller copies
- * it to the device.  Frequencies are unscaled; theta = 500000 for Llama 3.
+ * table [max_pos][32][2] fp64 with (cos, sin)(a), a = pos * pow(theta,
+ * -2i/64), each a double operation of the C library.  The caller copies it to
+ * the device.  Frequencies are unscaled; theta = 500000 for Llama 3.
  * Returns PA_ERR_INVALID_ARG for a NULL table, max_pos < 1 or theta <= 1.     */
-pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta);
+pa_status pa_rope_table_fill_host(double *cos_sin_host, int32_t max_pos, double theta);
 
 /* Decode-time KV append (samir-vllm, section "Gestion de la KV cache ...": each
  * new token is written at its absolute RoPE position).  For every sequence s,
@@ -137,12 +137,15 @@ pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double t
  *   v_pool[page][j][slot][:] = v_new[s][j][:]                           (copy)
  *   q[s][h][:] = bf16_rne(rope(q[s][h][:], pos)) in place, h < 32 (skipped when
  *   q is NULL).
- * Rotation is fp32 (table values, fused multiply-add), stored once, RNE.
+ * Rotation in fp64 from the table values, every product and the sum rounded
+ * on its own (no fused multiply-add), then rounded once to bf16 (RNE): the
+ * operations of the plain double-precision definition, so the stored rows are
+ * bitwise those of such an evaluation.
  * Device errors: L < 1 or pos >= min(max_blocks*16, max_pos) -> CONTEXT_LEN,
  * page id out of range -> PAGE_ID; that sequence is left untouched.           */
 pa_status pa_append_kv_rope(void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
                             const int32_t *block_tables, const int32_t *context_lens,
-                            const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                            const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                             int32_t num_pages, int32_t page_size, int32_t max_pos,
                             uint32_t *device_flags, hipStream_t stream);
 
@@ -214,14 +217,14 @@ pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void
  * the sequence's pages).  Arguments are the union of the two calls; q holds the
  * UN-rotated query and receives the rotated one in place (unless out == q, in
  * which case it receives the attention output).  Results are bitwise those of
- * the two separate calls: the same fp32 rotation and bf16 rounding, and the
+ * the two separate calls: the same fp64 rotation and bf16 rounding, and the
  * appended K/V row is written to its slot exactly as pa_append_kv_rope does.
  * Device errors: the union of both calls' (L-1 >= max_pos also counts as
  * CONTEXT_LEN); a failing sequence is neither appended nor attended, its out
  * rows are zero-filled.                                                        */
 pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
                                const int32_t *block_tables, const int32_t *context_lens,
-                               const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                               const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                int32_t out_dtype, void *workspace, size_t workspace_bytes,
                                uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
@@ -244,7 +247,7 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
 #define PA_NOALLOC_SCRATCH_BYTES (8u << 20)
 pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, const void *v_new, void *k_pool,
                                        void *v_pool, const int32_t *block_tables, const int32_t *context_lens,
-                                       const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                       const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                        int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                        int32_t out_dtype, uint32_t *device_flags, const int32_t *dispatch_order,
                                        hipStream_t stream);
@@ -267,7 +270,7 @@ pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, co
  * is set.                                                                       */
 pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool,
                            void *v_pool, const int32_t *block_tables, const int32_t *prefix_lens,
-                           const float *rope_cos_sin, int32_t num_seqs, int32_t chunk_len,
+                           const double *rope_cos_sin, int32_t num_seqs, int32_t chunk_len,
                            int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                            float scale, int32_t out_dtype, uint32_t *device_flags, hipStream_t stream);
 
@@ -321,7 +324,7 @@ pa_status pa_quantize_pages_i8(void *kv_pool_i8, const void *k_pool, const void 
  * pa_append_kv_rope (skipped when q is NULL).  Device errors as there.        */
 pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
                                const int32_t *block_tables, const int32_t *context_lens,
-                               const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                               const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                int32_t num_pages, int32_t page_size, int32_t max_pos,
                                uint32_t *device_flags, hipStream_t stream);
 
@@ -337,7 +340,7 @@ pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, con
  * pa_append_decode_gqa.                                                       */
 pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
                                   const int32_t *block_tables, const int32_t *context_lens,
-                                  const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                  const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                   int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
                                   uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);

@@ -37,7 +37,7 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class PaError(RuntimeError):
@@ -211,8 +211,8 @@ def _expect(t: torch.Tensor, name: str, dtype, shape=None, device=None) -> None:
 
 
 def rope_table(max_pos: int, theta: float = _w.ROPE_THETA, device="cuda") -> torch.Tensor:
-    """[max_pos][32][2] fp32 (cos, sin) table, filled by the library on the host, then uploaded."""
-    host = np.empty((max_pos, _w.HEAD_DIM // 2, 2), dtype=np.float32)
+    """[max_pos][32][2] fp64 (cos, sin) table, filled by the library on the host, then uploaded."""
+    host = np.empty((max_pos, _w.HEAD_DIM // 2, 2), dtype=np.float64)
     _check(lib().pa_rope_table_fill_host(host.ctypes.data_as(ctypes.c_void_p), int(max_pos), float(theta)),
            "pa_rope_table_fill_host")
     return torch.from_numpy(host).to(device)
@@ -255,7 +255,7 @@ def append_kv_rope(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: torch.
     _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
     if q is not None:
         _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
-    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
     rc = lib().pa_append_kv_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
@@ -311,7 +311,7 @@ def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
     _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
     _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
     _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
-    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
     if out.dtype == torch.bfloat16:
         odt = PA_OUT_BF16
     elif out.dtype == torch.float32:
@@ -352,7 +352,7 @@ def append_decode_gqa_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.T
     _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
     _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
     _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
-    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
     odt = _out_dtype(out)
     _expect(out, "out", out.dtype, (B, 32, 64), dev)
     if device_flags is not None:
@@ -385,7 +385,7 @@ def prefill_chunk(out: torch.Tensor, q: torch.Tensor, k_chunk: torch.Tensor, v_c
     _expect(block_tables, "block_tables", torch.int32, device=dev)
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [num_seqs][max_blocks]")
-    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
     if out.dtype == torch.bfloat16:
         odt = PA_OUT_BF16
     elif out.dtype == torch.float32:
@@ -467,7 +467,7 @@ def append_kv_rope_i8(q: Optional[torch.Tensor], k_new: torch.Tensor, v_new: tor
     _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
     if q is not None:
         _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
-    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
     rc = lib().pa_append_kv_rope_i8(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_pool_i8), _ptr(block_tables),
@@ -510,7 +510,7 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
     _expect(q, "q", torch.bfloat16, (B, 32, 64), dev)
     _expect(k_new, "k_new", torch.bfloat16, (B, 8, 64), dev)
     _expect(v_new, "v_new", torch.bfloat16, (B, 8, 64), dev)
-    _expect(rope_cos_sin, "rope_cos_sin", torch.float32, device=dev)
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
     odt = _out_dtype(out)
     _expect(out, "out", out.dtype, (B, 32, 64), dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

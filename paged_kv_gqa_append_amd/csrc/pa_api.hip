@@ -40,7 +40,7 @@ bool is_permutation(const int32_t *order, int32_t n) {
 // Shared argument checks and launch of the plain and the append-fused decode,
 // over bf16 pools (k_pool, v_pool) or an INT8 tile pool (k_pool; v_pool unused).
 pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
-                        const int32_t *block_tables, const int32_t *context_lens, const float *rope,
+                        const int32_t *block_tables, const int32_t *context_lens, const double *rope,
                         int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                         float scale, int32_t out_dtype, void *workspace, size_t workspace_bytes,
                         uint32_t *device_flags, const int32_t *order, hipStream_t stream, bool fused,
@@ -155,21 +155,21 @@ int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t s
     return static_cast<int32_t>(word & 0x7FFFFFFFu);
 }
 
-pa_status pa_rope_table_fill_host(float *cos_sin_host, int32_t max_pos, double theta) {
+pa_status pa_rope_table_fill_host(double *cos_sin_host, int32_t max_pos, double theta) {
     if (!cos_sin_host || max_pos < 1 || !(theta > 1.0)) return PA_ERR_INVALID_ARG;
     for (int32_t pos = 0; pos < max_pos; ++pos) {
         for (int i = 0; i < PA_HEAD_DIM / 2; ++i) {
             const double w = pow(theta, -(2.0 * i) / PA_HEAD_DIM);
             const double a = static_cast<double>(pos) * w;
-            cos_sin_host[(static_cast<int64_t>(pos) * (PA_HEAD_DIM / 2) + i) * 2] = static_cast<float>(cos(a));
-            cos_sin_host[(static_cast<int64_t>(pos) * (PA_HEAD_DIM / 2) + i) * 2 + 1] = static_cast<float>(sin(a));
+            cos_sin_host[(static_cast<int64_t>(pos) * (PA_HEAD_DIM / 2) + i) * 2] = cos(a);
+            cos_sin_host[(static_cast<int64_t>(pos) * (PA_HEAD_DIM / 2) + i) * 2 + 1] = sin(a);
         }
     }
     return PA_OK;
 }
 
 pa_status pa_append_kv_rope(void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
-                            const int32_t *block_tables, const int32_t *context_lens, const float *rope_cos_sin,
+                            const int32_t *block_tables, const int32_t *context_lens, const double *rope_cos_sin,
                             int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size,
                             int32_t max_pos, uint32_t *device_flags, hipStream_t stream) {
     if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1) return PA_ERR_INVALID_ARG;
@@ -207,7 +207,7 @@ pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void
 }
 
 pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
-                               const int32_t *block_tables, const int32_t *context_lens, const float *rope_cos_sin,
+                               const int32_t *block_tables, const int32_t *context_lens, const double *rope_cos_sin,
                                int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size,
                                int32_t max_pos, float scale, int32_t out_dtype, void *workspace,
                                size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
@@ -219,7 +219,7 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
 
 pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, const void *v_new, void *k_pool,
                                        void *v_pool, const int32_t *block_tables, const int32_t *context_lens,
-                                       const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                       const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                        int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                        int32_t out_dtype, uint32_t *device_flags, const int32_t *dispatch_order,
                                        hipStream_t stream) {
@@ -238,7 +238,7 @@ pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, co
 }
 
 pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool, void *v_pool,
-                           const int32_t *block_tables, const int32_t *prefix_lens, const float *rope_cos_sin,
+                           const int32_t *block_tables, const int32_t *prefix_lens, const double *rope_cos_sin,
                            int32_t num_seqs, int32_t chunk_len, int32_t max_blocks, int32_t num_pages,
                            int32_t page_size, int32_t max_pos, float scale, int32_t out_dtype,
                            uint32_t *device_flags, hipStream_t stream) {
@@ -253,12 +253,12 @@ pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(k_pool) ||
         !aligned16(v_pool) || !aligned16(block_tables) || !aligned16(prefix_lens) || !aligned16(rope_cos_sin))
         return PA_ERR_INVALID_ARG;
-    // K/V rows of the chunk go into their pages first (q is rotated by the
-    // attention kernel itself, which reads it anyway).
-    pa::AppendLaunch a{nullptr, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin,
+    // K/V rows of the chunk go into their pages and the chunk's q rows are
+    // rotated in place first; the attention kernel reads q rotated.
+    pa::AppendLaunch a{q, k_chunk, v_chunk, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin,
                        num_seqs, chunk_len, 1, max_blocks, num_pages, max_pos, device_flags};
     if (pa::launch_append_rope(a, stream) != hipSuccess) return PA_ERR_HIP;
-    pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, rope_cos_sin, num_seqs, chunk_len,
+    pa::PrefillLaunch p{out, q, k_pool, v_pool, block_tables, prefix_lens, num_seqs, chunk_len,
                         max_blocks, num_pages, max_pos, scale, out_dtype == PA_OUT_FP32, device_flags};
     return pa::launch_prefill_attention(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -281,7 +281,7 @@ pa_status pa_quantize_pages_i8(void *kv_pool_i8, const void *k_pool, const void 
 
 pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
                                const int32_t *block_tables, const int32_t *context_lens,
-                               const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                               const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                int32_t num_pages, int32_t page_size, int32_t max_pos,
                                uint32_t *device_flags, hipStream_t stream) {
     if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1) return PA_ERR_INVALID_ARG;
@@ -308,7 +308,7 @@ pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, con
 
 pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
                                   const int32_t *block_tables, const int32_t *context_lens,
-                                  const float *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
+                                  const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                   int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
                                   uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream) {

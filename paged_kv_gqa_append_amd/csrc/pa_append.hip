@@ -4,8 +4,8 @@
 // batching": a new token's K and V go into the page that the sequence's block
 // table names for its position, at the absolute RoPE position.  One workgroup
 // per appended token: it resolves (page, slot) once, rotates the 8 K heads and
-// (optionally) the 32 q heads with the fp32 cos/sin table row of that
-// position, and copies V verbatim.  The kernel moves ~6 KiB per token, so it is
+// (optionally) the 32 q heads with the fp64 cos/sin table row of that
+// position (rope_pair_bf16), and copies V verbatim.  The kernel moves ~6 KiB per token, so it is
 // bound by launch latency, not bandwidth; it stays simple and fully coalesced
 // (consecutive lanes touch consecutive bf16 elements).
 #include "pa_device.h"
@@ -13,12 +13,12 @@
 
 namespace pa {
 
-// Rotate-half pair (x_i, x_{i+32}) by (c, s): (x_i c - x_{i+32} s, x_{i+32} c + x_i s).
-__device__ __forceinline__ void rope_pair(const uint16_t *src, uint16_t *dst, int i, float c, float s) {
-    const float x0 = bf16_to_f32(src[i]);
-    const float x1 = bf16_to_f32(src[i + kD / 2]);
-    dst[i] = f32_to_bf16(rope_lo(x0, x1, c, s));
-    dst[i + kD / 2] = f32_to_bf16(rope_hi(x0, x1, c, s));
+// Rotate-half pair (x_i, x_{i+32}) of a row by (c, s) (rope_pair_bf16).
+__device__ __forceinline__ void rope_pair(const uint16_t *src, uint16_t *dst, int i, double c, double s) {
+    uint16_t lo, hi;
+    rope_pair_bf16(bf16_to_f32(src[i]), bf16_to_f32(src[i + kD / 2]), c, s, lo, hi);
+    dst[i] = lo;
+    dst[i + kD / 2] = hi;
 }
 
 // token = blockIdx.x = s * tokens_per_seq + i.
@@ -27,7 +27,7 @@ __device__ __forceinline__ void rope_pair(const uint16_t *src, uint16_t *dst, in
 __global__ __launch_bounds__(256) void k_append_rope(uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
                                                      const uint16_t *__restrict__ v_new, uint16_t *__restrict__ k_pool,
                                                      uint16_t *__restrict__ v_pool, const int32_t *__restrict__ bt,
-                                                     const int32_t *__restrict__ lens, const float *__restrict__ rope,
+                                                     const int32_t *__restrict__ lens, const double *__restrict__ rope,
                                                      int tokens_per_seq, int prefix_mode, int max_blocks, int num_pages,
                                                      int max_pos, uint32_t *__restrict__ flags) {
     const int tok = blockIdx.x;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_append_rope(uint16_t *__restrict__ q, c
         return;
     }
     const int slot = static_cast<int>(pos & (kPage - 1));
-    const float *cs = rope + pos * kD;  // [32][2]
+    const double *cs = rope + pos * kD;  // [32][2]
     const int t = threadIdx.x;
 
     // K: 8 heads x 32 pairs, one pair per thread.

@@ -7,7 +7,7 @@
 // "Gestion de la KV cache ...": attention reads only the sequence's own
 // pages, accumulates weighted V, concatenates nothing and stores no scores).
 // The fused variant first appends the new token at position L-1 exactly as
-// pa_append_kv_rope does (same fp32 rotation, same bf16 rounding) and rotates
+// pa_append_kv_rope does (same fp64 rotation, same bf16 rounding) and rotates
 // q in registers, so its results are bitwise those of append-then-decode.
 //
 // Work decomposition
@@ -139,10 +139,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P,
     __builtin_amdgcn_sched_barrier(0);
     // fused: the (cos, sin) of pair pr at position L-1, clamped into the table
     // (a bad L is rejected below, before anything computed from it is used)
-    float co = 0.0f, si = 0.0f;
+    double co = 0.0, si = 0.0;
     if (kFused) {
         const int pos_c = min(max(pos, 0), P.max_pos - 1);
-        const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD + 2 * pr;
+        const double *cs = P.rope + static_cast<int64_t>(pos_c) * kD + 2 * pr;
         co = cs[0];
         si = cs[1];
     }
@@ -171,13 +171,12 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P,
     KVRegs cur = load_tile(first_id >= 0 && first_id < P.num_pages ? first_id : 0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // fused: rotation once per workgroup, one pair per thread, into LDS (same
-    // fp32 operations as k_append_rope)
+    // fused: rotation once per workgroup, one pair per thread, into LDS (the
+    // rope_pair_bf16 of k_append_rope)
     if (kFused && tid < 192) {
         if (tid < 160) {
             uint16_t *dst = tid < 128 ? &s_q[tid >> 5][0] : &s_newk[0];
-            dst[pr] = f32_to_bf16(fmaf(x0, co, -(x1 * si)));
-            dst[pr + 32] = f32_to_bf16(fmaf(x1, co, x0 * si));
+            rope_pair_bf16(x0, x1, co, si, dst[pr], dst[pr + 32]);
         } else {
             reinterpret_cast<uint32_t *>(s_newv)[pr] = vword;
         }

@@ -234,7 +234,7 @@ struct DecodeParams {
     uint16_t *v_pool;
     const int32_t *bt;
     const int32_t *lens;
-    const float *rope;
+    const double *rope;
     int max_blocks;
     int num_pages;
     int max_pos;
@@ -279,14 +279,14 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams P) {
     if (kFused && P.write_q) {
         const int pos = L - 1;
         const int i = d & 31;
-        const float co = P.rope[static_cast<int64_t>(pos) * kD + 2 * i];
-        const float si = P.rope[static_cast<int64_t>(pos) * kD + 2 * i + 1];
+        const double co = P.rope[static_cast<int64_t>(pos) * kD + 2 * i];
+        const double si = P.rope[static_cast<int64_t>(pos) * kD + 2 * i + 1];
         uint16_t *qr = P.q + o - d;
-        const float xv = bf16_to_f32(qr[d]);
-        const float pv = bf16_to_f32(qr[d ^ 32]);
-        const float y = d >= 32 ? fmaf(xv, co, pv * si) : fmaf(xv, co, -(pv * si));
+        // pair (i, i + 32): this thread keeps the half it owns
+        uint16_t lo, hi;
+        rope_pair_bf16(bf16_to_f32(qr[i]), bf16_to_f32(qr[i + 32]), co, si, lo, hi);
         __syncthreads();  // both halves read before either is written
-        qr[d] = f32_to_bf16(y);
+        qr[d] = d >= 32 ? hi : lo;
     }
     const float r = A / Ls;
     if (P.out_fp32) static_cast<float *>(P.out)[o] = r;

@@ -69,11 +69,40 @@ __device__ __forceinline__ float sum_lanes8(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The bf16 nearest to the double x, ties to even, in one rounding step: x's
+// binade has bf16 spacing 2^(e-8) for 2^(e-1) <= |x| < 2^e (2^-133 below
+// 2^-126); x is scaled by the spacing, rounded to an integer (ties to even) and
+// scaled back, all exact in double, and the result is a binary32 whose low 16
+// bits are zero.  NaN gives 0x7FC0, magnitudes that round to 2^128 or more give
+// infinity.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+    if (__builtin_isnan(x)) return 0x7FC0;
+    if (__builtin_isinf(x)) return x > 0.0 ? 0x7F80 : 0xFF80;
+    if (x == 0.0) return __builtin_signbit(x) ? 0x8000 : 0x0000;
+    int e;
+    (void)__builtin_frexp(__builtin_fabs(x), &e);
+    const int qexp = max(e - 8, -133);
+    const double y = __builtin_ldexp(__builtin_rint(__builtin_ldexp(x, -qexp)), qexp);
+    if (__builtin_fabs(y) >= 0x1p128) return x > 0.0 ? 0x7F80 : 0xFF80;
+    return static_cast<uint16_t>(__builtin_bit_cast(uint32_t, static_cast<float>(y)) >> 16);
+}
+
 // Rotate-half RoPE of the pair (x_i, x_{i+32}) by (c, s) = (cos, sin) of
-// pos * theta^(-2i/64): (x_i c - x_{i+32} s, x_{i+32} c + x_i s), one fused
-// multiply-add each.  Every kernel that rotates uses these two expressions, so
-// a row rotated by any of them has the same bits.
-__device__ __forceinline__ float rope_lo(float x0, float x1, float c, float s) { return fmaf(x0, c, -(x1 * s)); }
-__device__ __forceinline__ float rope_hi(float x0, float x1, float c, float s) { return fmaf(x1, c, x0 * s); }
+// pos * theta^(-2i/64), both doubles from the table:
+//     (x_i c - x_{i+32} s,  x_{i+32} c + x_i s),
+// evaluated in double with every product and the sum rounded on its own (no
+// fused multiply-add), then rounded once to bf16.  These are the operations of
+// the plain fp64 definition, so the rotated rows are bitwise those of an exact
+// evaluation rounded the same way, and every kernel that rotates uses this one
+// function.
+__device__ __forceinline__ void rope_pair_bf16(float x0, float x1, double c, double s, uint16_t &lo, uint16_t &hi) {
+    const double a = x0, b = x1;
+    double p0 = a * c, p1 = b * s, p2 = b * c, p3 = a * s;
+    // The products leave through an empty asm, so the compiler (built with
+    // contraction on) cannot fuse them into the sums.
+    asm("" : "+v"(p0), "+v"(p1), "+v"(p2), "+v"(p3));
+    lo = f64_to_bf16(p0 - p1);
+    hi = f64_to_bf16(p2 + p3);
+}
 
 }  // namespace pa

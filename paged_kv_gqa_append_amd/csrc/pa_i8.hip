@@ -129,7 +129,7 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
                                                         const uint16_t *__restrict__ v_new, uint8_t *__restrict__ pool,
                                                         const int32_t *__restrict__ bt, const int32_t *__restrict__ lens,
-                                                        const float *__restrict__ rope, int max_blocks, int num_pages,
+                                                        const double *__restrict__ rope, int max_blocks, int num_pages,
                                                         int max_pos, uint32_t *__restrict__ flags) {
     const int s = blockIdx.x;
     const int64_t len = lens[s];
@@ -144,17 +144,17 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
         return;
     }
     const int slot = static_cast<int>(pos & (kPage - 1));
-    const float *cs = rope + pos * kD;  // [32][2]
+    const double *cs = rope + pos * kD;  // [32][2]
     const int t = threadIdx.x;
     const int j = t >> 5, p = t & 31;
     uint8_t *tile = pool + (static_cast<int64_t>(page) * kHKV + j) * kI8Tile;
     {
         // K: rotate the pair, round to bf16 (the stored row of the bf16 format), quantise the row
         const uint16_t *src = k_new + (static_cast<int64_t>(s) * kHKV + j) * kD;
-        const float x0 = bf16_to_f32(src[p]), x1 = bf16_to_f32(src[p + 32]);
-        const float c = cs[2 * p], sn = cs[2 * p + 1];
-        const float y0 = bf16_to_f32(f32_to_bf16(rope_lo(x0, x1, c, sn)));
-        const float y1 = bf16_to_f32(f32_to_bf16(rope_hi(x0, x1, c, sn)));
+        uint16_t b0, b1;
+        rope_pair_bf16(bf16_to_f32(src[p]), bf16_to_f32(src[p + 32]), cs[2 * p], cs[2 * p + 1], b0, b1);
+        const float y0 = bf16_to_f32(b0);
+        const float y1 = bf16_to_f32(b1);
         const float sc = max_lanes32(fmaxf(fabsf(y0), fabsf(y1))) / 127.0f;
         tile[i8_kpos(slot, p)] = static_cast<uint8_t>(quant_code(y0, sc));
         tile[i8_kpos(slot, p + 32)] = static_cast<uint8_t>(quant_code(y1, sc));
@@ -175,10 +175,10 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
             const int idx = t + 256 * r;
             const int h = idx >> 5, pp = idx & 31;
             uint16_t *row = q + (static_cast<int64_t>(s) * kHQ + h) * kD;
-            const float x0 = bf16_to_f32(row[pp]), x1 = bf16_to_f32(row[pp + 32]);
-            const float c = cs[2 * pp], sn = cs[2 * pp + 1];
-            row[pp] = f32_to_bf16(rope_lo(x0, x1, c, sn));
-            row[pp + 32] = f32_to_bf16(rope_hi(x0, x1, c, sn));
+            uint16_t b0, b1;
+            rope_pair_bf16(bf16_to_f32(row[pp]), bf16_to_f32(row[pp + 32]), cs[2 * pp], cs[2 * pp + 1], b0, b1);
+            row[pp] = b0;
+            row[pp + 32] = b1;
         }
     }
 }
@@ -332,10 +332,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         qraw1 = head_lane ? b : qraw1;
     }
     __builtin_amdgcn_sched_barrier(0);
-    float co = 0.0f, si = 0.0f;
+    double co = 0.0, si = 0.0;
     if (kFused) {
         const int pos_c = min(max(pos, 0), P.max_pos - 1);
-        const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD + 2 * pr;
+        const double *cs = P.rope + static_cast<int64_t>(pos_c) * kD + 2 * pr;
         co = cs[0];
         si = cs[1];
     }
@@ -365,13 +365,15 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
     // (lanes 0-31, pair pr) and takes the new V row (lanes 32-63, elements
     // 2pr, 2pr+1), then quantises both rows exactly as k_append_rope_i8 does.
     if (kFused && tid < 192) {
+        uint16_t r0 = 0, r1 = 0;
+        if (tid < 160) rope_pair_bf16(x0, x1, co, si, r0, r1);
         if (tid < 128) {
-            s_q[tid >> 5][pr] = f32_to_bf16(rope_lo(x0, x1, co, si));
-            s_q[tid >> 5][pr + 32] = f32_to_bf16(rope_hi(x0, x1, co, si));
+            s_q[tid >> 5][pr] = r0;
+            s_q[tid >> 5][pr + 32] = r1;
         } else {
             const bool is_k = tid < 160;
-            const float e0 = is_k ? bf16_to_f32(f32_to_bf16(rope_lo(x0, x1, co, si))) : bf16_lo(vword);
-            const float e1 = is_k ? bf16_to_f32(f32_to_bf16(rope_hi(x0, x1, co, si))) : bf16_hi(vword);
+            const float e0 = is_k ? bf16_to_f32(r0) : bf16_lo(vword);
+            const float e1 = is_k ? bf16_to_f32(r1) : bf16_hi(vword);
             const float sc = max_lanes32(fmaxf(fabsf(e0), fabsf(e1))) / 127.0f;
             const int c0 = quant_code(e0, sc), c1 = quant_code(e1, sc);
             if (is_k) {

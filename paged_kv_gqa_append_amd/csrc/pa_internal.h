@@ -15,7 +15,7 @@ struct AppendLaunch {
     void *v_pool;
     const int32_t *block_tables;
     const int32_t *lens;  // context lengths (decode) or prefix lengths (prefill)
-    const float *rope;
+    const double *rope;
     int num_seqs;
     int tokens_per_seq;
     int prefix_mode;      // 0: pos = lens[s]-1, 1: pos = lens[s]+i
@@ -36,7 +36,7 @@ struct DecodeLaunch {
     void *q;              // read-only unless fused (then rotated in place when write_q)
     const void *k_new;    // fused only
     const void *v_new;    // fused only
-    const float *rope;    // fused only
+    const double *rope;    // fused only
     int max_pos;          // fused only
     int fused;            // 1: append the token at L-1 and rotate q first
     int write_q;          // fused only: store the rotated q (out does not alias q)
@@ -59,12 +59,11 @@ struct DecodeLaunch {
 
 struct PrefillLaunch {
     void *out;
-    void *q;              // un-rotated; rotated in place unless out == q
+    const void *q;        // rotated (by the append kernel of the same call)
     const void *k_pool;
     const void *v_pool;
     const int32_t *block_tables;
     const int32_t *prefix_lens;
-    const float *rope;
     int num_seqs;
     int chunk_len;
     int max_blocks;

@@ -4,8 +4,9 @@
 // What is computed (TinyLoop, section "prefill_chunk and scratch residency":
 // the prompt is processed in row chunks; samir-vllm, "Gestion de la KV cache
 // ...": the prompt's pages are filled during prefill): after the chunk's K/V
-// rows have been appended (k_append_rope, prefix mode), every chunk query at
-// absolute position p = prefix + i is rotated at p and attends to keys 0..p
+// rows have been appended and the chunk's q rows rotated in place
+// (k_append_rope, prefix mode), every chunk query at absolute position
+// p = prefix + i, rotated at p, attends to keys 0..p
 // of its sequence, read through the block table:
 //     out[s][i][h] = sum_t softmax_t(scale <rope(q[s][i][h], p), K_t>) V_t,  t <= p.
 // No score matrix is stored (contrast tiny-vllm's prefill, which keeps a
@@ -40,9 +41,8 @@
 //   uses); the block maximum is needed only when the weights outgrow 2^8.
 //   With fp32 output the weights are fed as a bf16 hi/lo pair (two MFMAs) so
 //   they keep ~16 significant bits.
-//   q is rotated here, from the fp32 cos/sin table, with the same expressions
-//   as the append kernel; the rotated row is written back to q unless out
-//   aliases q.
+//   q arrives rotated (the append kernel of the same call rotates it in place
+//   before this kernel runs; with out == q the output then overwrites it).
 #include <math.h>
 
 #include "pa_device.h"
@@ -156,18 +156,16 @@ __device__ __forceinline__ float sum8_bf16(bf16x8 v, float acc) {
 
 struct PrefillParams {
     void *out;
-    uint16_t *q;
+    const uint16_t *q;
     const uint16_t *k_pool;
     const uint16_t *v_pool;
     const int32_t *bt;
     const int32_t *prefix_lens;
-    const float *rope;
     int chunk_len;
     int max_blocks;
     int num_pages;
     int max_pos;
     int n_tiles;
-    int write_q;
     int neg;        // scale < 0: q is negated for the products and c = |scale| log2(e)
     float c;        // |scale| * log2(e)
     int out_fp32;
@@ -176,48 +174,13 @@ struct PrefillParams {
 
 namespace {
 
-// Rotated q fragments of one 32-row sub-tile (MFMA B operand): this lane's
-// query row, d = 16kk + 8*half .. +7.  Pairs (d, d+32) are kk and kk+2 of the
-// same lane.  The loads (q row and the position's (cos, sin) entries) and the
-// arithmetic are separate steps, so the loads can be issued early.
-struct QRaw {
-    u32x4 raw[4];
-    f32x4 t[2][4];
-};
-__device__ __forceinline__ QRaw load_q_raw(const PrefillParams &P, int s, int h, int i_c, int pos_c, int half) {
-    QRaw r;
+// q fragments of one 32-row sub-tile (MFMA B operand, as stored: the append
+// kernel has rotated the rows already): this lane's query row, dims
+// 16kk + 8*half .. +7.
+__device__ __forceinline__ void load_q(const PrefillParams &P, int s, int h, int i_c, int half, u32x4 (&raw)[4]) {
     const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * P.chunk_len + i_c) * kHQ + h) * kD;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) r.raw[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * half);
-    const float *cs = P.rope + static_cast<int64_t>(pos_c) * kD;  // [32][2]
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r.t[kk][e] = *reinterpret_cast<const f32x4 *>(cs + 2 * (16 * kk + 8 * half) + 4 * e);
-    return r;
-}
-__device__ __forceinline__ void rotate_q(const QRaw &r, u32x4 (&rq)[4]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const uint32_t lo[4] = {r.raw[kk].x, r.raw[kk].y, r.raw[kk].z, r.raw[kk].w};
-        const uint32_t hi[4] = {r.raw[kk + 2].x, r.raw[kk + 2].y, r.raw[kk + 2].z, r.raw[kk + 2].w};
-        uint32_t ylo[4], yhi[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            // pairs i0 + 2*e2 (low bf16 of each word) and i0 + 2*e2 + 1 (high bf16), i0 = 16kk + 8half
-            const float c0 = r.t[kk][e2][0], s0 = r.t[kk][e2][1], c1 = r.t[kk][e2][2], s1 = r.t[kk][e2][3];
-            const float a0 = bf16_lo(lo[e2]), b0 = bf16_lo(hi[e2]);
-            const float a1 = bf16_hi(lo[e2]), b1 = bf16_hi(hi[e2]);
-            ylo[e2] = pack_bf16x2(rope_lo(a0, b0, c0, s0), rope_lo(a1, b1, c1, s1));
-            yhi[e2] = pack_bf16x2(rope_hi(a0, b0, c0, s0), rope_hi(a1, b1, c1, s1));
-        }
-        rq[kk] = u32x4{ylo[0], ylo[1], ylo[2], ylo[3]};
-        rq[kk + 2] = u32x4{yhi[0], yhi[1], yhi[2], yhi[3]};
-    }
-}
-__device__ __forceinline__ void load_q_rotated(const PrefillParams &P, int s, int h, int i_c, int pos_c, int half,
-                                               u32x4 (&rq)[4]) {
-    rotate_q(load_q_raw(P, s, h, i_c, pos_c, half), rq);
+    for (int kk = 0; kk < 4; ++kk) raw[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * half);
 }
 
 // The fragments of one 32-key block, read from LDS (sk, sv: the block's K and
@@ -442,14 +405,13 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
     // q rows of the sub-tiles (padding rows compute on the last row, never
     // stored; sub-tile 1 of a partly padded tile overshoots, and keys >= total
     // are masked anyway)
-    QRaw qraw[kSub];
+    u32x4 qraw[kSub][4];
     int pos0 = 0;
 #pragma unroll
     for (int u = 0; u < kSub; ++u) {
         const int i_c = min(row0 + 32 * u + qc, C - 1);
         if (u == 0) pos0 = prefix_c + i_c;
-        const int pos_c = min(max(prefix_c + i_c, 0), P.max_pos - 1);
-        qraw[u] = load_q_raw(P, s, h, i_c, pos_c, half);
+        load_q(P, s, h, i_c, half, qraw[u]);
     }
 
     // LDS of this key half: K buffers 0 .. kNBuf-1, then V buffers (kBlockBytes
@@ -503,26 +465,11 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
 
     if (!ok) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
-        // Rotate q where the append would have (the token's position and page
-        // are valid), then zero-fill this tile's rows of this head.  The first
-        // key half's waves do it.
+        // zero-fill this tile's rows of this head (the first key half's waves)
         if (kh != 0) return;
         for (int u = 0; u < kSub; ++u) {
             const int i = row0 + 32 * u + qc;
             if (i >= C) continue;
-            const int64_t pos = static_cast<int64_t>(prefix) + i;
-            bool tok_ok = prefix >= 0 && pos < lim;
-            if (tok_ok) {
-                const int pid_t = bt_row[pos >> 4];
-                tok_ok = pid_t >= 0 && pid_t < P.num_pages;
-            }
-            if (P.write_q && tok_ok) {
-                u32x4 rq[4];
-                load_q_rotated(P, s, h, i, static_cast<int>(pos), half, rq);
-                uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) *reinterpret_cast<u32x4 *>(qrow + 16 * kk + 8 * half) = rq[kk];
-            }
             const int64_t o = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD + 32 * half;
             for (int d = 0; d < 32; ++d) {
                 if (P.out_fp32) static_cast<float *>(P.out)[o + d] = 0.0f;
@@ -534,15 +481,12 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
         return;
     }
 
-    // ---- rotated q fragments --------------------------------------------------
+    // ---- q fragments (negated for scale < 0) -----------------------------------
     bf16x8 qf[kSub][4];
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        u32x4 rq[4];
-        rotate_q(qraw[u], rq);
+    for (int u = 0; u < kSub; ++u)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[u][kk] = as_bf16x8(P.neg ? (rq[kk] ^ 0x80008000u) : rq[kk]);
-    }
+        for (int kk = 0; kk < 4; ++kk) qf[u][kk] = as_bf16x8(P.neg ? (qraw[u][kk] ^ 0x80008000u) : qraw[u][kk]);
 
     // The page of this wave's 8 rows of block kb_begin + i, held by lane i (read
     // back with readlane, so staging in the loop waits for no LDS read); blocks
@@ -572,23 +516,6 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
     // the first blocks have landed (and the q loads); publish them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-
-    // ---- rotated q back in place (unless out aliases q) -------------------------
-    // Every wave has read its q rows by now (the barrier above follows their
-    // use), so the first key half writes them back here, under the main loop.
-    if (P.write_q && kh == 0) {
-#pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-            const int i = row0 + 32 * u + qc;
-            if (i >= C) continue;
-            uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const u32x4 v = __builtin_bit_cast(u32x4, qf[u][kk]);
-                *reinterpret_cast<u32x4 *>(qrow + 16 * kk + 8 * half) = P.neg ? (v ^ 0x80008000u) : v;
-            }
-        }
-    }
 
     // Block kbl is read from buffer kbl % kNBuf while blocks kbl+1 .. kbl+3 land
     // in the others (the loads of block kbl+3 are issued right after the K
@@ -680,18 +607,16 @@ hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream) 
     if (p.max_blocks > kMaxBlocksPrefill) return hipErrorInvalidValue;
     PrefillParams P{};
     P.out = p.out;
-    P.q = static_cast<uint16_t *>(p.q);
+    P.q = static_cast<const uint16_t *>(p.q);
     P.k_pool = static_cast<const uint16_t *>(p.k_pool);
     P.v_pool = static_cast<const uint16_t *>(p.v_pool);
     P.bt = p.block_tables;
     P.prefix_lens = p.prefix_lens;
-    P.rope = p.rope;
     P.chunk_len = p.chunk_len;
     P.max_blocks = p.max_blocks;
     P.num_pages = p.num_pages;
     P.max_pos = p.max_pos;
     P.n_tiles = (p.chunk_len + kRows - 1) / kRows;
-    P.write_q = p.out != p.q;
     // Scores are taken in units of c = |scale| log2(e) (q is negated when
     // scale < 0).  c is kept >= 1e-30 so that a masked score of -inf always
     // maps to weight 0; for scale == 0 the weights are then exp2(~0) = 1, the

@@ -150,42 +150,18 @@ def bf16_ulp(bits: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
 
 
-def pair_magnitude(input_bits: np.ndarray) -> np.ndarray:
-    """|x_i| + |x_{i+32}| of every element's rotate-half pair (last axis 64), per element."""
-    x = np.abs(W.bf16_bits_to_f32(input_bits).astype(np.float64))
-    p = x[..., :32] + x[..., 32:]
-    return np.concatenate([p, p], axis=-1)
-
-
-def assert_rope_close(gpu_bits: np.ndarray, ref_bits: np.ndarray, input_bits: np.ndarray, what=""):
-    """Rotated bf16 rows: the device rotates in fp32 with a rounded (cos, sin)
-    table, the oracle in fp64; each result is rounded once to bf16.  The
-    device's value of an element of pair (x_i, x_{i+32}) is within
-    3 * 2^-24 (|x_i| + |x_{i+32}|) of the exact rotation (the table entries, the
-    product and the fused multiply-add each round once, relative 2^-24, and
-    |cos|, |sin| <= 1), so after both roundings the two may differ by one bf16
-    step plus 2^-22 (|x_i| + |x_{i+32}|), the pair's own inputs.  That spans
-    several steps only when the two terms cancel to a tiny result.
-    input_bits: the un-rotated rows (bf16 bits), the same shape as the results;
-    for elements that were not rotated (copied pool rows) pass the row itself,
-    which both sides hold bit for bit."""
-    assert gpu_bits.shape == ref_bits.shape == input_bits.shape, (gpu_bits.shape, ref_bits.shape, input_bits.shape)
-    g = W.bf16_bits_to_f32(gpu_bits).astype(np.float64)
-    r = W.bf16_bits_to_f32(ref_bits).astype(np.float64)
-    bound = bf16_ulp(ref_bits) + 2.0 ** -22 * pair_magnitude(input_bits)
-    bad = np.abs(g - r) > bound
-    both_nan = np.isnan(g) & np.isnan(r)
-    bad &= ~both_nan
-    assert not bad.any(), f"{what}: {int(bad.sum())} rotated elements outside 1 ulp + the pair's fp32 bound"
-
-
-def rope_input_pool(pool_bits: np.ndarray, writes) -> np.ndarray:
-    """The un-rotated inputs of a K pool after appends: a copy of the pool before them with
-    each written slot's row replaced by its pre-RoPE K rows.  writes: (page, slot, rows[8][64])."""
-    out = pool_bits.copy()
-    for page, slot, rows in writes:
-        out[int(page), :, int(slot)] = rows
-    return out
+def assert_rope_equal(gpu_bits: np.ndarray, ref_bits: np.ndarray, what=""):
+    """Rotated bf16 rows (and every other byte of the arrays) bit for bit: the
+    device evaluates the rotation with the fp64 operations of the oracle's
+    definition (each product and the sum rounded on its own, then one rounding
+    to bf16) from a table of the same libm values, so nothing may differ."""
+    assert gpu_bits.shape == ref_bits.shape, (gpu_bits.shape, ref_bits.shape)
+    bad = gpu_bits != ref_bits
+    if bad.any():
+        i = np.argmax(bad)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements differ; first at "
+                             f"{np.unravel_index(i, bad.shape)}: gpu {int(gpu_bits.flat[i]):#06x} "
+                             f"ref {int(ref_bits.flat[i]):#06x}")
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, tol, what=""):

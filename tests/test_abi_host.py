@@ -6,6 +6,7 @@
 * workspace sizing and the fp64 -> fp32 RoPE table builder.
 """
 import ctypes
+import math
 import os
 import re
 
@@ -45,7 +46,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 10
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 11
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -236,12 +237,14 @@ def test_stream_read_probe_validation(pa):
 
 
 def test_rope_table_fill(pa):
-    t = np.empty((300, 32, 2), np.float32)
+    """The table holds the C library's double cos / sin of pos * pow(theta, -2i/64) exactly
+    (Python's math module calls the same libm)."""
+    t = np.empty((300, 32, 2), np.float64)
     assert pa.lib().pa_rope_table_fill_host(t.ctypes.data_as(ctypes.c_void_p), 300, 500000.0) == 0
-    pos = np.arange(300)[:, None].astype(np.float64)
-    w = 500000.0 ** (-2.0 * np.arange(32) / 64.0)
-    assert np.array_equal(t[..., 0], np.cos(pos * w).astype(np.float32))
-    assert np.array_equal(t[..., 1], np.sin(pos * w).astype(np.float32))
+    for pos in range(300):
+        for i in range(32):
+            a = float(pos) * math.pow(500000.0, -(2.0 * i) / 64.0)
+            assert t[pos, i, 0] == math.cos(a) and t[pos, i, 1] == math.sin(a), (pos, i)
     assert pa.lib().pa_rope_table_fill_host(None, 3, 500000.0) == pa.PA_ERR_INVALID_ARG
     assert pa.lib().pa_rope_table_fill_host(t.ctypes.data_as(ctypes.c_void_p), 0, 500000.0) == pa.PA_ERR_INVALID_ARG
 
@@ -331,7 +334,7 @@ def test_dispatch_order_length_refused(pa):
     bt = torch.zeros((B, mb), dtype=torch.int32)
     lens = torch.ones(B, dtype=torch.int32)
     kn = torch.zeros((B, 8, 64), dtype=torch.bfloat16)
-    table = torch.zeros((64, 32, 2), dtype=torch.float32)
+    table = torch.zeros((64, 32, 2), dtype=torch.float64)
     i8 = torch.zeros((P, 8, 2176), dtype=torch.uint8)
     for bad in ([1, 0], [2, 1, 0, 3], [[0, 1, 2]]):
         with pytest.raises(ValueError, match="exactly num_seqs"):

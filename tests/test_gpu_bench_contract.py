@@ -3,9 +3,11 @@ round-end driver reads (metric, value, unit, n_gpus, steps, warmup,
 ms_per_step, higher_is_better, scaling, vs_baseline, dtype, data, config with
 its workload), the roofline object (bound, achieved, peak, unit, frac =
 achieved / peak, traffic, and the read ceiling beside it) and the CPU
-baseline (the oracle, its thread count and sample).  The tiny decode workload
-and the argmax line run in child processes, one after the other, with short
-step counts."""
+baseline (the oracle, its thread count and sample), and the accuracy stamp
+(the outputs of a call made after the timed steps against the oracle: within
+the bf16 tolerance, or no argmax index differing).  The tiny decode workload,
+the prefill and the argmax line run in child processes, one after the other,
+with short step counts."""
 import json
 import os
 import subprocess
@@ -39,6 +41,11 @@ def check_common(line, steps, unit, bound):
     assert "traffic" in r
     cb = line["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    acc = line["accuracy"]
+    if "index_mismatches" in acc:
+        assert acc["index_mismatches"] == 0
+    else:
+        assert acc["within_tol"] and acc["max_err_over_tol"] <= 1.0 and acc["elements"] > 0
 
 
 def test_decode_line():
@@ -56,3 +63,12 @@ def test_argmax_line():
     print("bench contract: argmax", flush=True)
     line = run_bench("--config", "argmax", "--steps", "3", "--warmup", "2", "--cpu-seconds", "1")
     check_common(line, 3, "GB/s", "hbm")
+    # the roofline is the cold figure (logits from HBM); the warm one is beside it
+    assert line["value"] == line["roofline"]["achieved"] and line["warm"]["value"] > 0
+
+
+def test_prefill_line():
+    print("bench contract: prefill", flush=True)
+    line = run_bench("--config", "prefill", "--steps", "3", "--warmup", "2", "--cpu-seconds", "1")
+    check_common(line, 3, "TFLOP/s", "mfma")
+    assert line["accuracy"]["elements"] == 4 * 512 * 32 * 64
