@@ -12,10 +12,11 @@
   1e-2 + 1e-2|ref|, fp32 out 2e-3 + 2e-3|ref|); the fused call is bitwise the
   two separate calls; contexts past one partition; unused slots hold NaN scales
   and random codes.
-* Full size: the batch-64 x 2048 workload's pool quantised on the device is
-  bit-identical, on sampled sequences' pages, to the oracle's quantisation of
-  the same bf16 pages (copied to the host before any of our kernels ran), and
-  the fused decode matches the oracle on those sequences.
+* Full size: the batch-64 x 2048 and ragged batch-256 workloads' pools
+  quantised on the device are bit-identical, on whole layers' pages, to the
+  oracle's quantisation of the same bf16 pages (copied to the host before any
+  of our kernels ran); the fused append + decode matches the oracle on every
+  sequence of those layers, and the pool after the append bit for bit.
 The INT8 pools the oracle reads are built on the host by the oracle itself.
 """
 import numpy as np
@@ -335,57 +336,61 @@ def test_i8_device_errors():
     assert np.array_equal(got_pool, ref_pool)
 
 
-def _full_size_i8(spec, layer, seqs, what):
-    """The benchmark's INT8 step on one layer of a full-size workload, sampled sequences checked
+def _full_size_i8(spec, layers, what):
+    """The benchmark's INT8 step on whole layers of a full-size workload, every sequence checked
     against the oracle on bf16 pages copied to the host before any of our kernels ran."""
-    print(f"i8 full-size {what} layer={layer} sampled={list(seqs)}", flush=True)
     k_pool = guarded_pool(spec, "k")
     v_pool = guarded_pool(spec, "v")
-    bt = spec.block_tables[layer][seqs]
-    used = np.unique(bt[bt >= 0])
-    idx = torch.from_numpy(used).to(dev())
-    kp = to_host_bits(k_pool.index_select(0, idx)).copy()   # bf16 pages, before any of our kernels
-    vp = to_host_bits(v_pool.index_select(0, idx)).copy()
-    remap = np.full(spec.num_pages, -1, np.int64)
-    remap[used] = np.arange(len(used))
-    bt_small = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+    seqs = np.arange(spec.num_seqs)
+    host = []
+    for layer in layers:
+        bt = spec.block_tables[layer][seqs]
+        used = np.unique(bt[bt >= 0])
+        idx = torch.from_numpy(used).to(dev())
+        kp = to_host_bits(k_pool.index_select(0, idx)).copy()   # bf16 pages, before any of our kernels
+        vp = to_host_bits(v_pool.index_select(0, idx)).copy()
+        remap = np.full(spec.num_pages, -1, np.int64)
+        remap[used] = np.arange(len(used))
+        bt_small = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1).astype(np.int32)
+        host.append((layer, used, idx, kp, vp, bt_small))
     pool = binding.i8_pool(spec.num_pages, dev())
     binding.quantize_pages_i8(pool, k_pool, v_pool)
     del k_pool, v_pool
     torch.cuda.empty_cache()
-    ref_pool = oracle.quantize_pages_i8(kp, vp)
-    assert np.array_equal(pool.index_select(0, idx).cpu().numpy(), ref_pool)
-    q, kn, vn = spec.host_rows(layer)
-    dq = to_dev_bf16(q)
-    out = guarded_empty((spec.num_seqs, 32, 64), torch.bfloat16)
-    flags = guarded_flags()
-    binding.append_decode_gqa_i8(out, dq, to_dev_bf16(kn), to_dev_bf16(vn), pool,
-                                 to_dev_i32(spec.block_tables[layer]), to_dev_i32(spec.context_lens),
-                                 rope(2048 + 64), spec.scale,
-                                 workspace=guarded_workspace(spec.num_seqs, spec.max_blocks),
-                                 device_flags=flags)
-    torch.cuda.synchronize()
-    assert int(flags.item()) == 0
-    lens = spec.context_lens[seqs].copy()
-    oq = q[seqs].copy()
-    assert oracle.append_kv_rope_i8(oq, kn[seqs].copy(), vn[seqs].copy(), ref_pool, bt_small, lens, len(used),
-                                    spec.theta) == oracle.OK
-    ref, rc = oracle.decode_gqa_i8(oq, ref_pool, bt_small, lens, len(used), spec.scale)
-    assert rc == oracle.OK
-    assert_close(to_host_f64(out)[seqs], ref, TOL_BF16, what)
-    assert_rope_equal(to_host_bits(dq)[seqs], oq, "rotated q")
+    table = rope(2048 + 64)
+    ws = guarded_workspace(spec.num_seqs, spec.max_blocks)
+    for layer, used, idx, kp, vp, bt_small in host:
+        print(f"i8 full-size {what} layer={layer}: all {spec.num_seqs} sequences", flush=True)
+        ref_pool = oracle.quantize_pages_i8(kp, vp)
+        assert np.array_equal(pool.index_select(0, idx).cpu().numpy(), ref_pool)
+        q, kn, vn = spec.host_rows(layer)
+        dq = to_dev_bf16(q)
+        out = guarded_empty((spec.num_seqs, 32, 64), torch.bfloat16)
+        flags = guarded_flags()
+        binding.append_decode_gqa_i8(out, dq, to_dev_bf16(kn), to_dev_bf16(vn), pool,
+                                     to_dev_i32(spec.block_tables[layer]), to_dev_i32(spec.context_lens),
+                                     table, spec.scale, workspace=ws, device_flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0
+        lens = spec.context_lens.copy()
+        oq = q.copy()
+        assert oracle.append_kv_rope_i8(oq, kn.copy(), vn.copy(), ref_pool, bt_small, lens, len(used),
+                                        spec.theta) == oracle.OK
+        ref, rc = oracle.decode_gqa_i8(oq, ref_pool, bt_small, lens, len(used), spec.scale)
+        assert rc == oracle.OK
+        assert_close(to_host_f64(out), ref, TOL_BF16, f"{what} layer {layer}")
+        assert_rope_equal(to_host_bits(dq), oq, "rotated q")
+        # the pool after the append (the new K/V codes and scales), bit for bit
+        assert np.array_equal(pool.index_select(0, idx).cpu().numpy(), ref_pool)
     del pool
     torch.cuda.empty_cache()
 
 
-def test_batch64_i8_full_size_sampled():
+def test_batch64_i8_full_size_two_layers():
     """64 x 2048 tokens: the launch reads its codes with the non-temporal hint (512 workgroups)."""
-    _full_size_i8(W.batch64_spec(), 9, np.array([0, 5, 31, 62]), "batch64 i8")
+    _full_size_i8(W.batch64_spec(), [0, 9], "batch64 i8")
 
 
-def test_batch256_i8_full_size_sampled():
+def test_batch256_i8_full_size_one_layer():
     """The ragged, fragmented 256-sequence workload with 1 % outlier rows (2048 workgroups)."""
-    spec = W.batch256_spec()
-    lens = spec.context_lens
-    seqs = np.unique(np.array([0, int(np.argmax(lens)), int(np.argmin(lens)), 100, 255]))
-    _full_size_i8(spec, 11, seqs, "batch256 i8")
+    _full_size_i8(W.batch256_spec(), [11], "batch256 i8")

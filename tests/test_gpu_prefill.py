@@ -102,28 +102,18 @@ def test_prefill_chunk_of_one_matches_decode():
     assert_close(got, ref, TOL_FP32, "chunk of one")
 
 
-def test_prefill_config_full_size_sampled_rows():
-    """4 sequences x (1536 cached + 512 chunk): every row checked where it is cheap, sampled otherwise."""
+def test_prefill_config_full_size_all_rows():
+    """4 sequences x (1536 cached + 512 chunk), in the benchmark's launch: every row of every
+    sequence against the oracle's prefill, and the pools and rotated q bit for bit."""
     c = W.prefill_config()
     d = DevPrefill(c)
     got = to_host_f64(d.run(torch.bfloat16))
     assert int(d.flags.item()) == 0
-    # oracle: append the whole chunk, then decode the sampled rows (row i == decode at L = prefix + i + 1)
-    q, kp, vp = c.q.copy(), c.k_pool.copy(), c.v_pool.copy()
-    for i in range(c.chunk_len):
-        lens = (c.prefix_lens + i + 1).astype(np.int32)
-        qi = np.ascontiguousarray(q[:, i])
-        assert oracle.append_kv_rope(qi, np.ascontiguousarray(c.k_chunk[:, i]), np.ascontiguousarray(c.v_chunk[:, i]),
-                                     kp, vp, c.block_tables, lens, c.num_pages, c.theta) == oracle.OK
-        q[:, i] = qi
-    rows = [0, 1, 31, 32, 33, 255, 256, 300, 480, 510, 511]
-    for i in rows:
-        lens = (c.prefix_lens + i + 1).astype(np.int32)
-        ref, rc = oracle.decode_gqa(np.ascontiguousarray(q[:, i]), kp, vp, c.block_tables, lens, c.num_pages, c.scale)
-        assert rc == oracle.OK
-        assert_close(got[:, i], ref, TOL_BF16, f"row {i}")
-    assert_rope_equal(to_host_bits(d.kp), kp, "K pool")
-    assert np.array_equal(to_host_bits(d.vp), vp)
+    ref, oq, okp, ovp = oracle_all(c)
+    assert_close(got, ref, TOL_BF16, "prefill config, all rows")
+    assert_rope_equal(to_host_bits(d.kp), okp, "K pool")
+    assert np.array_equal(to_host_bits(d.vp), ovp)
+    assert_rope_equal(to_host_bits(d.q), oq, "rotated q")
 
 
 def test_prefill_device_errors():
