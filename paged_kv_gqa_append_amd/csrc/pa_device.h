@@ -73,18 +73,15 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // binade has bf16 spacing 2^(e-8) for 2^(e-1) <= |x| < 2^e (2^-133 below
 // 2^-126); x is scaled by the spacing, rounded to an integer (ties to even) and
 // scaled back, all exact in double, and the result is a binary32 whose low 16
-// bits are zero.  NaN gives 0x7FC0, magnitudes that round to 2^128 or more give
-// infinity.
+// bits are zero.  Without branches: zeros and infinities pass through the
+// scaling unchanged (their exponent reads as 0), a result of 2^128 or more
+// converts to infinity, and NaN gives 0x7FC0.
 __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-    if (__builtin_isnan(x)) return 0x7FC0;
-    if (__builtin_isinf(x)) return x > 0.0 ? 0x7F80 : 0xFF80;
-    if (x == 0.0) return __builtin_signbit(x) ? 0x8000 : 0x0000;
-    int e;
-    (void)__builtin_frexp(__builtin_fabs(x), &e);
+    const int e = __builtin_amdgcn_frexp_exp(x);
     const int qexp = max(e - 8, -133);
     const double y = __builtin_ldexp(__builtin_rint(__builtin_ldexp(x, -qexp)), qexp);
-    if (__builtin_fabs(y) >= 0x1p128) return x > 0.0 ? 0x7F80 : 0xFF80;
-    return static_cast<uint16_t>(__builtin_bit_cast(uint32_t, static_cast<float>(y)) >> 16);
+    const uint16_t b = static_cast<uint16_t>(__builtin_bit_cast(uint32_t, static_cast<float>(y)) >> 16);
+    return __builtin_isnan(x) ? static_cast<uint16_t>(0x7FC0) : b;
 }
 
 // Rotate-half RoPE of the pair (x_i, x_{i+32}) by (c, s) = (cos, sin) of
