@@ -13,12 +13,24 @@
 
 namespace pa {
 
-// Rotate-half pair (x_i, x_{i+32}) of a row by (c, s) (rope_pair_bf16).
-__device__ __forceinline__ void rope_pair(const uint16_t *src, uint16_t *dst, int i, double c, double s) {
-    uint16_t lo, hi;
-    rope_pair_bf16(bf16_to_f32(src[i]), bf16_to_f32(src[i + kD / 2]), c, s, lo, hi);
-    dst[i] = lo;
-    dst[i + kD / 2] = hi;
+// Rotate-half pairs i0 .. i0+3 of a row (with their partners i0+32 .. i0+35)
+// by the (cos, sin) entries cs[2i], cs[2i+1] (rope_pair_bf16): 8-byte row loads
+// and stores, 16-byte table loads.
+__device__ __forceinline__ void rope_unit4(const uint16_t *src, uint16_t *dst, int i0, const double *cs) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(src + i0);
+    const uint2 b = *reinterpret_cast<const uint2 *>(src + i0 + kD / 2);
+    const double2 t0 = *reinterpret_cast<const double2 *>(cs + 2 * i0);
+    const double2 t1 = *reinterpret_cast<const double2 *>(cs + 2 * i0 + 2);
+    const double2 t2 = *reinterpret_cast<const double2 *>(cs + 2 * i0 + 4);
+    const double2 t3 = *reinterpret_cast<const double2 *>(cs + 2 * i0 + 6);
+    uint16_t lo[4], hi[4];
+    rope_pair_bf16(bf16_lo(a.x), bf16_lo(b.x), t0.x, t0.y, lo[0], hi[0]);
+    rope_pair_bf16(bf16_hi(a.x), bf16_hi(b.x), t1.x, t1.y, lo[1], hi[1]);
+    rope_pair_bf16(bf16_lo(a.y), bf16_lo(b.y), t2.x, t2.y, lo[2], hi[2]);
+    rope_pair_bf16(bf16_hi(a.y), bf16_hi(b.y), t3.x, t3.y, lo[3], hi[3]);
+    *reinterpret_cast<uint2 *>(dst + i0) = uint2{lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16)};
+    *reinterpret_cast<uint2 *>(dst + i0 + kD / 2) =
+        uint2{hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16)};
 }
 
 // token = blockIdx.x = s * tokens_per_seq + i.
@@ -49,29 +61,24 @@ __global__ __launch_bounds__(256) void k_append_rope(uint16_t *__restrict__ q, c
     const double *cs = rope + pos * kD;  // [32][2]
     const int t = threadIdx.x;
 
-    // K: 8 heads x 32 pairs, one pair per thread.
-    {
-        const int j = t >> 5, p = t & 31;
+    // Work in units of 4 pairs: K is 8 heads x 8 units (threads 0..63), V 8 heads
+    // x 8 sixteen-byte chunks copied verbatim (threads 64..127), q 32 heads x 8
+    // units in place (one per thread).
+    if (t < 64) {
+        const int j = t >> 3, i0 = 4 * (t & 7);
         const uint16_t *src = k_new + (static_cast<int64_t>(tok) * kHKV + j) * kD;
         uint16_t *dst = k_pool + ((static_cast<int64_t>(page) * kHKV + j) * kPage + slot) * kD;
-        rope_pair(src, dst, p, cs[2 * p], cs[2 * p + 1]);
+        rope_unit4(src, dst, i0, cs);
+    } else if (t < 128) {
+        const int j = (t - 64) >> 3, c = (t - 64) & 7;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(v_new + (static_cast<int64_t>(tok) * kHKV + j) * kD);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(v_pool + ((static_cast<int64_t>(page) * kHKV + j) * kPage + slot) * kD);
+        dst[c] = src[c];
     }
-    // V: 8 heads x 64 elements, two per thread, verbatim.
-    {
-        const int j = t >> 5, w = t & 31;
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(v_new + (static_cast<int64_t>(tok) * kHKV + j) * kD);
-        uint32_t *dst = reinterpret_cast<uint32_t *>(v_pool + ((static_cast<int64_t>(page) * kHKV + j) * kPage + slot) * kD);
-        dst[w] = src[w];
-    }
-    // q: 32 heads x 32 pairs, four per thread, in place.
     if (q) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int idx = t + 256 * r;
-            const int h = idx >> 5, p = idx & 31;
-            uint16_t *row = q + (static_cast<int64_t>(tok) * kHQ + h) * kD;
-            rope_pair(row, row, p, cs[2 * p], cs[2 * p + 1]);
-        }
+        const int h = t >> 3, i0 = 4 * (t & 7);
+        uint16_t *row = q + (static_cast<int64_t>(tok) * kHQ + h) * kD;
+        rope_unit4(row, row, i0, cs);
     }
 }
 
