@@ -14,13 +14,11 @@
 //
 // Work decomposition
 //   One workgroup of 8 waves per (sequence, KV head j, tile of 32 chunk
-//   positions; built with PA_PREFILL_SUB=2, 64 positions as two 32-row
-//   sub-tiles per wave, one workgroup per CU).  Waves 0-3 are the 4 query
-//   heads of that KV head over the first half of the tile's key blocks, waves
-//   4-7 the same heads over the second half; the two partial results are
-//   merged through LDS at the end, each half finishing 32 of the 64 output
-//   dims.  Two workgroups share a CU (4 waves per SIMD, <= 128 VGPRs).  Keys
-//   go 32 at a time (two pages).
+//   positions).  Waves 0-3 are the 4 query heads of that KV head over the
+//   first half of the tile's key blocks, waves 4-7 the same heads over the
+//   second half; the two partial results are merged through LDS at the end,
+//   each half finishing 32 of the 64 output dims.  Two workgroups share a CU
+//   (4 waves per SIMD, <= 128 VGPRs).  Keys go 32 at a time (two pages).
 //   Workgroup ids are mapped so that all tiles of one (sequence, KV head) land
 //   on the same XCD (ids are dealt to the 8 XCDs round-robin) and share its
 //   L2; the longest tiles start first.
@@ -35,6 +33,11 @@
 //   K/V blocks go from the pool straight into LDS (direct-to-LDS loads, no
 //   staging registers), four buffers per key half with three blocks in
 //   flight; one barrier per block.
+//   The loop is software-pipelined by one block: while the weights of block
+//   b are formed (exp2, bf16 packing, row sums: VALU work), the score MFMAs
+//   of block b+1 run, and the P.V MFMAs of block b overlap the scaling of
+//   block b+1's scores; scheduling groups pin that interleave so that the
+//   matrix and vector units of one wave work at the same time.
 //   Softmax in log2 units against a lazily kept integer reference: per score
 //   one fused multiply-add, one exp2, half a packed bf16 conversion and half a
 //   dot2 for the row sum (taken over the same bf16 weights the P.V product
@@ -54,11 +57,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-#ifndef PA_PREFILL_SUB
-#define PA_PREFILL_SUB 1
-#endif
-constexpr int kSub = PA_PREFILL_SUB;        // 32-row sub-tiles per wave
-constexpr int kRows = 32 * kSub;            // chunk positions per workgroup
+constexpr int kRows = 32;                   // chunk positions per workgroup (one 32-row tile per wave)
 constexpr int kKB = 32;                     // keys per block
 constexpr int kBlockBytes = kKB * kD * 2;  // one K or V block in LDS: 32 rows of 128 bytes
 
@@ -213,23 +212,13 @@ __device__ __forceinline__ void read_v(const unsigned char *sv, int lane, bf16x8
         }
 }
 
-// Scores of one 32-key block for sub-tile u (S^T = K Q^T), with dead keys at
-// -inf.  pos0: absolute position of this lane's query in sub-tile 0 (sub-tile
-// 1 is +32).  mask: some key of the block may lie past a row's position or past
-// the sequence (wave-uniform).
-__device__ __forceinline__ void block_scores(const bf16x8 (&kf)[4], const bf16x8 (&qf)[4], int half, int kb,
-                                             bool mask, int lim_pos, float (&x)[16]) {
-    f32x16 st = f32x16{};
+// Dead keys of a block get log-weight -inf, hence weight exactly 0: key
+// kb*32 + 8(v/4) + 4*half + v%4 of register v is live iff <= lim_pos (the
+// row's position, or the sequence's last key).
+__device__ __forceinline__ void mask_block(float (&t)[16], int half, int kb, int lim_pos) {
+    const int lim = lim_pos - kb * kKB - 4 * half;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) st = mfma32(kf[kk], qf[kk], st);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) x[v] = st[v];
-    if (mask) {
-        // key kb*32 + 8(v/4) + 4*half + v%4 is live iff <= lim_pos
-        const int lim = lim_pos - kb * kKB - 4 * half;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] = (8 * (v >> 2) + (v & 3)) > lim ? -INFINITY : x[v];
-    }
+    for (int v = 0; v < 16; ++v) t[v] = (8 * (v >> 2) + (v & 3)) > lim ? -INFINITY : t[v];
 }
 
 // Weights exp2(t - d) of the lane's 16 log-weights t as bf16 (and, for fp32
@@ -258,84 +247,57 @@ __device__ __forceinline__ float block_weights(const float (&t)[16], float d, bf
     return bs;
 }
 
-// O^T += V^T P^T for one sub-tile (both 32-dim halves, both 16-key steps).
+// O^T += V^T P^T for the wave's tile (both 32-dim halves, both 16-key steps),
+// ordered so that the two products chained on one accumulator are not
+// adjacent.
 template <bool kHiLo>
 __device__ __forceinline__ void pv_products(const bf16x8 (&vf)[2][2], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
                                             f32x16 (&o)[2]) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
+        for (int db = 0; db < 2; ++db) {
             o[db] = mfma32(vf[db][sb], pb[sb], o[db]);
             if (kHiLo) o[db] = mfma32(vf[db][sb], pl[sb], o[db]);
         }
 }
 
-// One 32-key block for the wave's sub-tiles, from its K fragments (read_k) and
-// the block's V rows in LDS (sv, read after the S^T products are issued, so
-// the K and V fragments are never held at once).
-//
 // Softmax in log2 units against a lazily kept, integer-valued reference ref
 // (-inf while none of the row's keys so far is live; mc = ref, or 0 then): the
-// log-weights are t = c x - mc.  The usual step needs no block maximum: the
-// weights exp2(t) are accepted when the lane's 16 of them sum to at most 2^8
-// (so each is at most 2^8; an overflow or NaN fails the test too).  Otherwise,
-// and on a key half's first block (first, uniform), the reference moves up by
-// d = ceil of the row's largest t where that is positive (or is set to it when
-// the row had none), O and l are multiplied by 2^-d, and the weights are taken
-// again as exp2(t - d) (each <= 1 then).  Integer references keep every factor
-// an exact power of two.  Dead keys have x = -inf, hence t = -inf and weight 0.
+// log-weights are t = c x - mc.  The usual block needs no maximum: the weights
+// exp2(t) are accepted when the lane's 16 of them sum to at most 2^8 (so each
+// is at most 2^8; an overflow or NaN fails the test too).  Otherwise, and on a
+// key half's first block, slow_path moves the reference up by d = ceil of the
+// row's largest t where that is positive (or sets it when the row had none),
+// multiplies O and l by 2^-d and takes the weights again as exp2(t - d) (each
+// <= 1 then).  Integer references keep every factor an exact power of two.
 template <bool kHiLo>
-__device__ __forceinline__ void attend_block(const bf16x8 (&kf)[4], const unsigned char *sv, int lane, int kb,
-                                             bool mask, bool first, const bf16x8 (&qf)[kSub][4],
-                                             f32x16 (&o)[kSub][2], float (&ref)[kSub], float (&l)[kSub], int pos0,
-                                             int total, float c) {
-    const int half = lane >> 5;
-    float t[kSub][16];
+__device__ __forceinline__ float slow_path(const float (&t)[16], float &ref, float &l, f32x16 (&o)[2],
+                                           bf16x8 (&pb)[2], bf16x8 (&pl)[2]) {
+    float tmax = t[0];
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        float x[16];
-        block_scores(kf, qf[u], half, kb, mask, min(pos0 + 32 * u, total - 1), x);
-        const float mc = ref[u] > -INFINITY ? ref[u] : 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) t[u][v] = fmaf(x[v], c, -mc);
-    }
-    bf16x8 vf[2][2];
-    read_v(sv, lane, vf);
-
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        bf16x8 pb[2], pl[2];
-        float bs = block_weights<kHiLo>(t[u], 0.0f, pb, pl);
-        if (first || __builtin_amdgcn_ballot_w64(!(bs <= 256.0f))) {
-            float tmax = t[u][0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, t[u][v]);
-            tmax = max_partner32(tmax);
-            const bool has = ref[u] > -INFINITY;
-            const bool live = tmax > -INFINITY;
-            float d = 0.0f, f = 1.0f;
-            if (has) {
-                if (tmax > 0.0f) {
-                    const float r_new = ref[u] + ceilf(tmax);
-                    d = r_new - ref[u];
-                    ref[u] = r_new;
-                    f = fast_exp2(-d);
-                }
-            } else if (live) {
-                // first live key of the row: O and l are still 0
-                d = ceilf(tmax);
-                ref[u] = d;
-                f = 0.0f;
-            }
-            l[u] *= f;
-            o[u][0] *= f;
-            o[u][1] *= f;
-            bs = block_weights<kHiLo>(t[u], d, pb, pl);
+    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, t[v]);
+    tmax = max_partner32(tmax);
+    const bool has = ref > -INFINITY;
+    const bool live = tmax > -INFINITY;
+    float d = 0.0f, f = 1.0f;
+    if (has) {
+        if (tmax > 0.0f) {
+            const float r_new = ref + ceilf(tmax);
+            d = r_new - ref;
+            ref = r_new;
+            f = fast_exp2(-d);
         }
-        l[u] += bs;
-        pv_products<kHiLo>(vf, pb, pl, o[u]);
+    } else if (live) {
+        // first live key of the row: O and l are still 0
+        d = ceilf(tmax);
+        ref = d;
+        f = 0.0f;
     }
+    l *= f;
+    o[0] *= f;
+    o[1] *= f;
+    return block_weights<kHiLo>(t, d, pb, pl);
 }
 
 }  // namespace
@@ -346,13 +308,13 @@ __device__ __forceinline__ void attend_block(const bf16x8 (&kf)[4], const unsign
 constexpr int kNBuf = 4;                                // K/V blocks in LDS per key half (3 in flight)
 constexpr int kHalfBytes = 2 * kNBuf * kBlockBytes;     // per key half: K and V, kNBuf buffers each
 constexpr int kStageBytes = 2 * kHalfBytes;
-constexpr int kMergeOBytes = 8 * kSub * 64 * 16 * 4;   // 8 waves x sub-tiles x 64 lanes x 16 floats
-constexpr int kMergeMLBytes = 8 * kSub * 64 * 2 * 4;   // (m, l) per wave, lane and sub-tile
+constexpr int kMergeOBytes = 8 * 64 * 16 * 4;   // 8 waves x 64 lanes x 16 floats
+constexpr int kMergeMLBytes = 8 * 64 * 2 * 4;   // (reference, l) per wave and lane
 constexpr int kSmemBytes = kStageBytes > kMergeOBytes + kMergeMLBytes ? kStageBytes : kMergeOBytes + kMergeMLBytes;
 
 template <bool kHiLo>
-// kSub == 1: two workgroups per CU, so each SIMD holds 4 waves (<= 128 VGPRs)
-__global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(PrefillParams P) {
+// two workgroups per CU, so each SIMD holds 4 waves (<= 128 VGPRs)
+__global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     // ids -> (sequence, KV head, tile): the 8 low id bits pick the XCD, which
     // is also the KV head, so every tile of (s, j) runs on XCD j; the longest
     // tiles (highest positions) go first.
@@ -402,17 +364,11 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
     // first block that needs the causal / length mask for some row of the tile
     const int first_masked = (prefix_c + row0) / kKB;
 
-    // q rows of the sub-tiles (padding rows compute on the last row, never
-    // stored; sub-tile 1 of a partly padded tile overshoots, and keys >= total
-    // are masked anyway)
-    u32x4 qraw[kSub][4];
-    int pos0 = 0;
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        const int i_c = min(row0 + 32 * u + qc, C - 1);
-        if (u == 0) pos0 = prefix_c + i_c;
-        load_q(P, s, h, i_c, half, qraw[u]);
-    }
+    // this lane's q row (padding rows compute on the last row, never stored)
+    u32x4 qraw[4];
+    const int i_c = min(row0 + qc, C - 1);
+    const int pos0 = prefix_c + i_c;
+    load_q(P, s, h, i_c, half, qraw);
 
     // LDS of this key half: K buffers 0 .. kNBuf-1, then V buffers (kBlockBytes
     // each), addressed by arithmetic on the shared array (so every access is
@@ -467,9 +423,8 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
         // zero-fill this tile's rows of this head (the first key half's waves)
         if (kh != 0) return;
-        for (int u = 0; u < kSub; ++u) {
-            const int i = row0 + 32 * u + qc;
-            if (i >= C) continue;
+        const int i = row0 + qc;
+        if (i < C) {
             const int64_t o = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD + 32 * half;
             for (int d = 0; d < 32; ++d) {
                 if (P.out_fp32) static_cast<float *>(P.out)[o + d] = 0.0f;
@@ -482,11 +437,9 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
     }
 
     // ---- q fragments (negated for scale < 0) -----------------------------------
-    bf16x8 qf[kSub][4];
+    bf16x8 qf[4];
 #pragma unroll
-    for (int u = 0; u < kSub; ++u)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qf[u][kk] = as_bf16x8(P.neg ? (qraw[u][kk] ^ 0x80008000u) : qraw[u][kk]);
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(P.neg ? (qraw[kk] ^ 0x80008000u) : qraw[kk]);
 
     // The page of this wave's 8 rows of block kb_begin + i, held by lane i (read
     // back with readlane, so staging in the loop waits for no LDS read); blocks
@@ -503,43 +456,85 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
         stage_with(kbl, buf, page);
     };
 
-    f32x16 o[kSub][2];
-    float ref[kSub], l[kSub];
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        o[u][0] = f32x16{};
-        o[u][1] = f32x16{};
-        ref[u] = -INFINITY;
-        l[u] = 0.0f;
-    }
+    f32x16 o[2] = {f32x16{}, f32x16{}};
+    float ref = -INFINITY, l = 0.0f;
+    const int lim_pos = min(pos0, total - 1);
 
     // the first blocks have landed (and the q loads); publish them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // Block kbl is read from buffer kbl % kNBuf while blocks kbl+1 .. kbl+3 land
-    // in the others (the loads of block kbl+3 are issued right after the K
-    // fragments of block kbl are read).  One barrier per block: before it each
-    // wave waits until its loads of block kbl+1 have landed (at most the two
-    // blocks after it, 4 loads, still in flight), and after it every wave is
-    // done with the buffer the next loads overwrite.  Both key halves run the
-    // same trip count (nb0) so that their barriers pair up; the second half may
-    // run out of blocks first.
-    for (int kbl = 0;; ++kbl) {
+    // Software pipeline over this half's blocks.  Iteration kbl: (A) the S^T
+    // products of block kbl+1 go out with the weights of block kbl interleaved
+    // between them (each product waits for the one before it on the same
+    // accumulator, so the VALU work fills the wait); (B) after the rare
+    // rescale, the P.V products of block kbl go out with the log-weights of
+    // block kbl+1 interleaved.  Block b is in buffer b % kNBuf; the loads of
+    // block kbl+3 go into the buffer of block kbl-1, which every wave finished
+    // before the last barrier.  One barrier per block: before it each wave
+    // waits until its loads of block kbl+2 (whose K the next iteration reads)
+    // have landed, at most the block after it (2 loads) still in flight.  Both
+    // key halves run the same trip count (nb0) so that their barriers pair up;
+    // the second half may run out of blocks first (its extra iterations compute
+    // on stale buffers and keep nothing).
+    float t[16];  // log-weights of the block being finished
+    {
         bf16x8 kf[4];
-        const int buf = kbl & (kNBuf - 1);
-        read_k(k_buf(buf), lane, kf);
+        read_k(k_buf(0), lane, kf);
+        f32x16 st = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) st = mfma32(kf[kk], qf[kk], st);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) t[v] = st[v] * P.c;  // reference 0 (ref is -inf)
+        if (kb_begin >= first_masked) mask_block(t, half, kb_begin, lim_pos);
+    }
+    for (int kbl = 0;; ++kbl) {
         const bool more = kbl + kNBuf - 1 < nb0;
         if (more) stage_block(kbl + kNBuf - 1, (kbl + kNBuf - 1) & (kNBuf - 1));
+
+        // ---- (A) next block's S^T, this block's weights
+        bf16x8 kf[4];
+        read_k(k_buf((kbl + 1) & (kNBuf - 1)), lane, kf);
+        bf16x8 pb[2], pl[2];
+        float bs = block_weights<kHiLo>(t, 0.0f, pb, pl);
+        f32x16 sn = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) sn = mfma32(kf[kk], qf[kk], sn);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the K fragment reads
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x002, kHiLo ? 12 : 8, 0);  // weights
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one S^T product
+        }
+        // the weights are used only on the live path below: an empty asm that
+        // reads them keeps the compiler from moving their computation there,
+        // out of reach of the products they are interleaved with
+        asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[0])), "v"(__builtin_bit_cast(u32x4, pb[1])), "v"(bs));
+        if (kHiLo) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pl[0])), "v"(__builtin_bit_cast(u32x4, pl[1])));
+
         if (kbl < kb_count) {
-            const int kb = kb_begin + kbl;
-            attend_block<kHiLo>(kf, v_buf(buf), lane, kb, kb >= first_masked, kbl == 0, qf, o, ref, l, pos0, total,
-                                P.c);
+            if (kbl == 0 || __builtin_amdgcn_ballot_w64(!(bs <= 256.0f)))
+                bs = slow_path<kHiLo>(t, ref, l, o, pb, pl);
+            l += bs;
+
+            // ---- (B) this block's P.V, next block's log-weights
+            bf16x8 vf[2][2];
+            read_v(v_buf(kbl & (kNBuf - 1)), lane, vf);
+            pv_products<kHiLo>(vf, pb, pl, o);
+            const float mc = ref > -INFINITY ? ref : 0.0f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t[v] = fmaf(sn[v], P.c, -mc);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);  // the V fragment reads
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);              // log-weights
+                __builtin_amdgcn_sched_group_barrier(0x008, kHiLo ? 2 : 1, 1);  // P.V products
+            }
+            const int kbn = kb_begin + kbl + 1;
+            if (kbn >= first_masked) mask_block(t, half, kbn, lim_pos);
         }
         if (kbl + 1 >= nb0) break;
-        // block kbl+1's loads are the oldest of this wave's in flight: with a
-        // full pipeline, 2 blocks (4 loads) were issued after them
-        if (more) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        if (more) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
@@ -547,57 +542,53 @@ __global__ __launch_bounds__(512, kSub == 1 ? 4 : 1) void k_prefill_attn(Prefill
 
     // ---- merge the two key halves through LDS -----------------------------------
     // Key half kh finalizes dims 32kh .. 32kh+31: each wave leaves the other
-    // half's dims of its partial O^T, with its (m, l), in LDS.  Slot:
-    // (key half, head-in-group, sub-tile, lane), 16 floats.
+    // half's dims of its partial O^T, with its (reference, l), in LDS.  Slot:
+    // (key half, head-in-group, lane), 16 floats.
     float *mo = reinterpret_cast<float *>(s_raw);
     float *mml = reinterpret_cast<float *>(s_raw + kMergeOBytes);
-    auto slot = [&](int half_k, int u) { return ((half_k * 4 + wq) * kSub + u) * 64 + lane; };
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        const f32x16 give = kh ? o[u][0] : o[u][1];
-        float *dst = mo + slot(kh, u) * 16;
+    auto slot = [&](int half_k) { return (half_k * 4 + wq) * 64 + lane; };
+    {
+        const f32x16 give = kh ? o[0] : o[1];
+        float *dst = mo + slot(kh) * 16;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             *reinterpret_cast<f32x4 *>(dst + 4 * r4) = f32x4{give[4 * r4], give[4 * r4 + 1], give[4 * r4 + 2],
                                                              give[4 * r4 + 3]};
-        mml[slot(kh, u) * 2] = ref[u];
-        mml[slot(kh, u) * 2 + 1] = l[u];
+        mml[slot(kh) * 2] = ref;
+        mml[slot(kh) * 2 + 1] = l;
     }
     __syncthreads();
 
     // ---- out[s][i][h][d] = O^T[d][query] / l, d = 32kh + 8r4 + 4*half + r ------
     const int oh = 1 - kh;
+    const float *src = mo + slot(oh) * 16;
+    const float rB = mml[slot(oh) * 2];
+    const float lB = mml[slot(oh) * 2 + 1];
+    // finite: the first half always holds key 0; a half that had no live key
+    // for a row has reference -inf and weight 0
+    const float rx = fmaxf(ref, rB);
+    const float fA = fast_exp2(ref - rx);
+    const float fB = fast_exp2(rB - rx);
+    const float lh = l * fA + lB * fB;
+    const float l_tot = lh + partner32(lh);
+    const int i = row0 + qc;
+    if (i >= C) return;
+    const float inv = 1.0f / l_tot;
+    const f32x16 mine = kh ? o[1] : o[0];
+    const int64_t orow = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-        const float *src = mo + slot(oh, u) * 16;
-        const float rB = mml[slot(oh, u) * 2];
-        const float lB = mml[slot(oh, u) * 2 + 1];
-        // finite: the first half always holds key 0; a half that had no live
-        // key for a row has reference -inf and weight 0
-        const float rx = fmaxf(ref[u], rB);
-        const float fA = fast_exp2(ref[u] - rx);
-        const float fB = fast_exp2(rB - rx);
-        const float lh = l[u] * fA + lB * fB;
-        const float l_tot = lh + partner32(lh);
-        const int i = row0 + 32 * u + qc;
-        if (i >= C) continue;
-        const float inv = 1.0f / l_tot;
-        const f32x16 mine = kh ? o[u][1] : o[u][0];
-        const int64_t orow = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 4 * r4);
-            const int d = 32 * kh + 8 * r4 + 4 * half;
-            const float y0 = (mine[4 * r4] * fA + ob[0] * fB) * inv;
-            const float y1 = (mine[4 * r4 + 1] * fA + ob[1] * fB) * inv;
-            const float y2 = (mine[4 * r4 + 2] * fA + ob[2] * fB) * inv;
-            const float y3 = (mine[4 * r4 + 3] * fA + ob[3] * fB) * inv;
-            if (P.out_fp32) {
-                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
-            } else {
-                const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
-            }
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 4 * r4);
+        const int d = 32 * kh + 8 * r4 + 4 * half;
+        const float y0 = (mine[4 * r4] * fA + ob[0] * fB) * inv;
+        const float y1 = (mine[4 * r4 + 1] * fA + ob[1] * fB) * inv;
+        const float y2 = (mine[4 * r4 + 2] * fA + ob[2] * fB) * inv;
+        const float y3 = (mine[4 * r4 + 3] * fA + ob[3] * fB) * inv;
+        if (P.out_fp32) {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
+        } else {
+            const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
         }
     }
 }
