@@ -305,6 +305,7 @@ __device__ __forceinline__ float slow_path(const float (&t)[16], float &ref, flo
 // LDS layout of one workgroup: two key halves, each with kNBuf K and V block
 // buffers; after the block loop the same bytes hold the second half's partial
 // results for the merge.
+constexpr int kCuPerXcd = 32;  // gfx950: 8 XCDs x 32 CUs
 constexpr int kNBuf = 4;                                // K/V blocks in LDS per key half (3 in flight)
 constexpr int kHalfBytes = 2 * kNBuf * kBlockBytes;     // per key half: K and V, kNBuf buffers each
 constexpr int kStageBytes = 2 * kHalfBytes;
@@ -315,13 +316,20 @@ constexpr int kSmemBytes = kStageBytes > kMergeOBytes + kMergeMLBytes ? kStageBy
 template <bool kHiLo>
 // two workgroups per CU, so each SIMD holds 4 waves (<= 128 VGPRs)
 __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
-    // ids -> (sequence, KV head, tile): the 8 low id bits pick the XCD, which
-    // is also the KV head, so every tile of (s, j) runs on XCD j; the longest
-    // tiles (highest positions) go first.
+    // ids -> (sequence, KV head, tile): the 3 low id bits pick the XCD, which
+    // is also the KV head, so every tile of (s, j) runs on XCD j.  An XCD's
+    // workgroups are dealt to its 32 CUs in turn, so its p-th workgroup shares
+    // a CU with the (p+32)-th: the first 32 take the work list longest first
+    // and the next 32 in the reverse order, so that each CU pairs a long tile
+    // with a short one (rank r: sequence r / n_tiles, tiles from the highest
+    // positions down).
     const int bid = blockIdx.x;
-    const int mq = bid >> 3;
-    const int sj = (bid & 7) + 8 * (mq / P.n_tiles);
-    const int tile = P.n_tiles - 1 - (mq % P.n_tiles);
+    const int p = bid >> 3;
+    const int base = p & ~(kCuPerXcd - 1);
+    const int span = min(static_cast<int>(gridDim.x >> 3) - base, kCuPerXcd);  // a last turn may be short
+    const int rank = ((p / kCuPerXcd) & 1) ? base + span - 1 - (p - base) : p;
+    const int sj = (bid & 7) + 8 * (rank / P.n_tiles);
+    const int tile = P.n_tiles - 1 - (rank % P.n_tiles);
     const int j = sj & (kHKV - 1);
     const int s = sj >> 3;
     const int tid = threadIdx.x;
