@@ -13,12 +13,13 @@
 // 512 x 512 x 32 score buffer, ch.2 buffer table).
 //
 // Work decomposition
-//   One workgroup of 8 waves per (sequence, KV head j, tile of 32 chunk
-//   positions).  Waves 0-3 are the 4 query heads of that KV head over the
-//   first half of the tile's key blocks, waves 4-7 the same heads over the
-//   second half; the two partial results are merged through LDS at the end,
-//   each half finishing 32 of the 64 output dims.  Two workgroups share a CU
-//   (4 waves per SIMD, <= 128 VGPRs).  Keys go 32 at a time (two pages).
+//   One workgroup of 4 waves per (sequence, KV head j, tile of 32 chunk
+//   positions).  Each wave holds two of the 4 query heads of that KV head
+//   (two independent streams that share every K and V fragment); waves 0-1
+//   take the first half of the tile's key blocks, waves 2-3 the second half.
+//   The two partial results are merged through LDS at the end, each half
+//   finishing 32 of the 64 output dims.  Two workgroups share a CU (2 waves
+//   per SIMD, <= 256 VGPRs).  Keys go 32 at a time (two pages).
 //   Workgroup ids are mapped so that all tiles of one (sequence, KV head) land
 //   on the same XCD (ids are dealt to the 8 XCDs round-robin) and share its
 //   L2; the longest tiles start first.
@@ -37,7 +38,8 @@
 //   b are formed (exp2, bf16 packing, row sums: VALU work), the score MFMAs
 //   of block b+1 run, and the P.V MFMAs of block b overlap the scaling of
 //   block b+1's scores; scheduling groups pin that interleave so that the
-//   matrix and vector units of one wave work at the same time.
+//   matrix and vector units of one wave work at the same time, and the two
+//   streams' products alternate so that none waits for the one before it.
 //   Softmax in log2 units against a lazily kept integer reference: per score
 //   one fused multiply-add, one exp2, half a packed bf16 conversion and half a
 //   dot2 for the row sum (taken over the same bf16 weights the P.V product
@@ -303,19 +305,21 @@ __device__ __forceinline__ float slow_path(const float (&t)[16], float &ref, flo
 }  // namespace
 
 // LDS layout of one workgroup: two key halves, each with kNBuf K and V block
-// buffers; after the block loop the same bytes hold the second half's partial
-// results for the merge.
-constexpr int kCuPerXcd = 32;  // gfx950: 8 XCDs x 32 CUs
+// buffers; after the block loop the same bytes hold the partial results the
+// two halves exchange.
+constexpr int kCuPerXcd = 32;                           // gfx950: 8 XCDs x 32 CUs
+constexpr int kThreads = 256;                           // 4 waves: 2 head pairs x 2 key halves
 constexpr int kNBuf = 4;                                // K/V blocks in LDS per key half (3 in flight)
 constexpr int kHalfBytes = 2 * kNBuf * kBlockBytes;     // per key half: K and V, kNBuf buffers each
 constexpr int kStageBytes = 2 * kHalfBytes;
-constexpr int kMergeOBytes = 8 * 64 * 16 * 4;   // 8 waves x 64 lanes x 16 floats
-constexpr int kMergeMLBytes = 8 * 64 * 2 * 4;   // (reference, l) per wave and lane
+constexpr int kMergeOBytes = 4 * 2 * 64 * 16 * 4;   // 4 waves x 2 heads x 64 lanes x 16 floats
+constexpr int kMergeMLBytes = 4 * 2 * 64 * 2 * 4;   // (reference, l) per wave, head and lane
 constexpr int kSmemBytes = kStageBytes > kMergeOBytes + kMergeMLBytes ? kStageBytes : kMergeOBytes + kMergeMLBytes;
+static_assert(kMaxBlocksPrefill <= 2 * kThreads, "page validation takes two table entries per thread");
 
 template <bool kHiLo>
-// two workgroups per CU, so each SIMD holds 4 waves (<= 128 VGPRs)
-__global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
+// two workgroups per CU, so each SIMD holds 2 waves (<= 256 VGPRs)
+__global__ __launch_bounds__(kThreads, 2) void k_prefill_attn(PrefillParams P) {
     // ids -> (sequence, KV head, tile): the 3 low id bits pick the XCD, which
     // is also the KV head, so every tile of (s, j) runs on XCD j.  An XCD's
     // workgroups are dealt to its 32 CUs in turn, so its p-th workgroup shares
@@ -335,8 +339,9 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int kh = w >> 2;            // key half: waves 0-3 take the first half of the blocks, 4-7 the rest
-    const int h = j * kGroup + (w & 3);
+    const int hp = w & 1;             // head pair: query heads 2hp and 2hp+1 of the group, the wave's two streams
+    const int kh = w >> 1;            // key half: waves 0-1 take the first half of the blocks, 2-3 the rest
+    const int h0 = j * kGroup + 2 * hp;
     const int C = P.chunk_len;
     const int row0 = tile * kRows;
     const int qc = lane & 31;
@@ -348,19 +353,20 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     // ---- prologue ----------------------------------------------------------------
     // Every WG starts at once, so each dependent round trip to memory here adds
     // to the whole call.  After the prefix length, the loads that do not depend
-    // on validation all go out together: the block table (one entry per thread,
-    // for validation and for LDS), this lane's q row and (cos, sin) entries, the
-    // page ids of the first blocks and those blocks' K/V (direct to LDS).  All
-    // addresses are clamped into their arrays, so a sequence that then fails
-    // validation has read only valid memory; its results are never used.
+    // on validation all go out together: the block table (two entries per
+    // thread, for validation and for LDS), this lane's q rows, the page ids of
+    // the first blocks and those blocks' K/V (direct to LDS).  All addresses
+    // are clamped into their arrays, so a sequence that then fails validation
+    // has read only valid memory; its results are never used.
     const int prefix = P.prefix_lens[s];
     const int64_t lim = min(static_cast<int64_t>(P.max_blocks) * kPage, static_cast<int64_t>(P.max_pos));
     const bool len_ok = prefix >= 0 && static_cast<int64_t>(prefix) + C <= lim;
     const int total = len_ok ? prefix + C : 0;
-    const int n_pages = (total + kPage - 1) / kPage;  // <= kMaxBlocksPrefill = the WG's thread count
+    const int n_pages = (total + kPage - 1) / kPage;  // <= kMaxBlocksPrefill = twice the WG's thread count
     const int32_t *bt_row = P.bt + static_cast<int64_t>(s) * P.max_blocks;
-    int pid = 0;
-    if (tid < n_pages) pid = bt_row[tid];
+    int pid0 = 0, pid1 = 0;
+    if (tid < n_pages) pid0 = bt_row[tid];
+    if (tid + kThreads < n_pages) pid1 = bt_row[tid + kThreads];
 
     // block ranges: keys needed by this tile are 0 .. prefix + last valid row
     const int prefix_c = len_ok ? prefix : 0;
@@ -372,11 +378,13 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     // first block that needs the causal / length mask for some row of the tile
     const int first_masked = (prefix_c + row0) / kKB;
 
-    // this lane's q row (padding rows compute on the last row, never stored)
-    u32x4 qraw[4];
+    // this lane's q rows of both heads (padding rows compute on the last row,
+    // never stored)
+    u32x4 qraw[2][4];
     const int i_c = min(row0 + qc, C - 1);
     const int pos0 = prefix_c + i_c;
-    load_q(P, s, h, i_c, half, qraw);
+    load_q(P, s, h0, i_c, half, qraw[0]);
+    load_q(P, s, h0 + 1, i_c, half, qraw[1]);
 
     // LDS of this key half: K buffers 0 .. kNBuf-1, then V buffers (kBlockBytes
     // each), addressed by arithmetic on the shared array (so every access is
@@ -387,34 +395,37 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     const uint32_t lds_half = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(s_raw + half_off)));
 
-    // Staging: the 4 waves of a key half each bring 8 keys (rows 8wq .. 8wq+7
-    // of the block) of K and of V straight into LDS, one 16-byte direct-to-LDS
-    // load per lane and tensor: lane l fills chunk position l%8 of row l/8,
-    // which holds the row's chunk (l%8) ^ f(row) (see swz).  The 8 rows lie
-    // in one page, so the page base is scalar and each lane adds a fixed
-    // offset.  Dead keys (>= total) fetch the first row of the same page (a
+    // Staging: the 2 waves of a key half each bring one page of the block
+    // (wave hp: keys 16hp .. 16hp+15, page 2kb + hp) of K and of V straight
+    // into LDS, two 16-byte direct-to-LDS loads per lane and tensor: load r,
+    // lane l fills chunk position l%8 of block row 16hp + 8r + l/8, which holds
+    // the row's chunk (l%8) ^ f(row) (see swz; f depends on the row mod 8
+    // only).  Dead keys (>= total) fetch the first row of the same page (a
     // live one), or of the sequence's first page when the whole page lies past
     // the sequence, so no NaN reaches the MFMAs; blocks past the half's range
     // are clamped (re-read, never used).
-    const int wq = w & 3;
     const int64_t tile_j = static_cast<int64_t>(j) * kTile;
-    const int st_row = 8 * wq + (lane >> 3);
-    const uint32_t st_chunk_b = static_cast<uint32_t>(((lane & 7) ^ swz_f(st_row)) * 16);
-    const uint32_t st_off_live = static_cast<uint32_t>((8 * (wq & 1) + (lane >> 3)) * kD * 2) + st_chunk_b;
+    const int st_row8 = lane >> 3;
+    const uint32_t st_chunk_b = static_cast<uint32_t>(((lane & 7) ^ swz_f(st_row8)) * 16);
     auto stage_with = [&](int kbl, int buf, int page) {
         const int kb = min(kb_begin + kbl, nb - 1);
         const int64_t base = static_cast<int64_t>(page) * kPageElems + tile_j;
-        const uint32_t voff = kb * kKB + st_row < total ? st_off_live : st_chunk_b;
-        const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_half + buf * kBlockBytes + wq * 8 * 128);
-        dma16(P.k_pool + base, voff, lds_k);
-        dma16(P.v_pool + base, voff, lds_k + kNBuf * kBlockBytes);
+        const int key0 = kb * kKB + 16 * hp + st_row8;
+        const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_half + buf * kBlockBytes + hp * 16 * 128);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const uint32_t voff =
+                key0 + 8 * r < total ? static_cast<uint32_t>((8 * r + st_row8) * kD * 2) + st_chunk_b : st_chunk_b;
+            dma16(P.k_pool + base, voff, lds_k + r * 1024);
+            dma16(P.v_pool + base, voff, lds_k + r * 1024 + kNBuf * kBlockBytes);
+        }
     };
     // the first blocks, from page ids read straight from the table (scalar
     // loads; ids clamped into the pool)
 #pragma unroll
     for (int b = 0; b < kNBuf - 1; ++b) {
         if (b < nb0) {
-            const int idx = min(2 * min(kb_begin + b, nb - 1) + (wq >> 1), P.max_blocks - 1);
+            const int idx = min(2 * min(kb_begin + b, nb - 1) + hp, P.max_blocks - 1);
             const int idx_c = idx < n_pages ? idx : 0;
             int page = bt_row[__builtin_amdgcn_readfirstlane(idx_c)];
             page = min(max(page, 0), P.num_pages - 1);
@@ -423,20 +434,24 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     }
 
     // ---- validation: the whole sequence's pages ------------------------------
-    if (tid < n_pages) s_pages[tid] = pid;
-    const int bad = (tid < n_pages) && (pid < 0 || pid >= P.num_pages);
+    if (tid < n_pages) s_pages[tid] = pid0;
+    if (tid + kThreads < n_pages) s_pages[tid + kThreads] = pid1;
+    const int bad = ((tid < n_pages) && (pid0 < 0 || pid0 >= P.num_pages)) ||
+                    ((tid + kThreads < n_pages) && (pid1 < 0 || pid1 >= P.num_pages));
     const bool ok = len_ok && __syncthreads_or(bad) == 0;
 
     if (!ok) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
-        // zero-fill this tile's rows of this head (the first key half's waves)
+        // zero-fill this tile's rows of both heads (the first key half's waves)
         if (kh != 0) return;
         const int i = row0 + qc;
         if (i < C) {
-            const int64_t o = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD + 32 * half;
-            for (int d = 0; d < 32; ++d) {
-                if (P.out_fp32) static_cast<float *>(P.out)[o + d] = 0.0f;
-                else static_cast<uint16_t *>(P.out)[o + d] = 0;
+            for (int u = 0; u < 2; ++u) {
+                const int64_t o = ((static_cast<int64_t>(s) * C + i) * kHQ + h0 + u) * kD + 32 * half;
+                for (int d = 0; d < 32; ++d) {
+                    if (P.out_fp32) static_cast<float *>(P.out)[o + d] = 0.0f;
+                    else static_cast<uint16_t *>(P.out)[o + d] = 0;
+                }
             }
         }
         if (tid == 0 && j == 0 && tile == P.n_tiles - 1 && P.flags)
@@ -445,15 +460,17 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
     }
 
     // ---- q fragments (negated for scale < 0) -----------------------------------
-    bf16x8 qf[4];
+    bf16x8 qf[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(P.neg ? (qraw[kk] ^ 0x80008000u) : qraw[kk]);
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qf[u][kk] = as_bf16x8(P.neg ? (qraw[u][kk] ^ 0x80008000u) : qraw[u][kk]);
 
-    // The page of this wave's 8 rows of block kb_begin + i, held by lane i (read
-    // back with readlane, so staging in the loop waits for no LDS read); blocks
-    // from 64 on (contexts past 4096 keys) look theirs up in LDS.
+    // The page of this wave's 16 rows of block kb_begin + i, held by lane i
+    // (read back with readlane, so staging in the loop waits for no LDS read);
+    // blocks from 64 on (contexts past 4096 keys) look theirs up in LDS.
     auto page_of = [&](int kb) {
-        const int idx = 2 * kb + (wq >> 1);
+        const int idx = 2 * kb + hp;
         return s_pages[idx < n_pages ? idx : 0];
     };
     const int my_page = page_of(min(kb_begin + lane, nb - 1));
@@ -464,37 +481,43 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
         stage_with(kbl, buf, page);
     };
 
-    f32x16 o[2] = {f32x16{}, f32x16{}};
-    float ref = -INFINITY, l = 0.0f;
+    f32x16 o[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
+    float ref[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
     const int lim_pos = min(pos0, total - 1);
 
     // the first blocks have landed (and the q loads); publish them
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // Software pipeline over this half's blocks.  Iteration kbl: (A) the S^T
-    // products of block kbl+1 go out with the weights of block kbl interleaved
-    // between them (each product waits for the one before it on the same
-    // accumulator, so the VALU work fills the wait); (B) after the rare
-    // rescale, the P.V products of block kbl go out with the log-weights of
-    // block kbl+1 interleaved.  Block b is in buffer b % kNBuf; the loads of
-    // block kbl+3 go into the buffer of block kbl-1, which every wave finished
-    // before the last barrier.  One barrier per block: before it each wave
-    // waits until its loads of block kbl+2 (whose K the next iteration reads)
-    // have landed, at most the block after it (2 loads) still in flight.  Both
-    // key halves run the same trip count (nb0) so that their barriers pair up;
-    // the second half may run out of blocks first (its extra iterations compute
-    // on stale buffers and keep nothing).
-    float t[16];  // log-weights of the block being finished
+    // Software pipeline over this half's blocks, two heads (streams) per wave
+    // sharing every K and V fragment.  Iteration kbl: (A) the S^T products of
+    // block kbl+1 for both heads go out with the weights of block kbl
+    // interleaved between them (the two heads' products alternate, so each
+    // waits for no other); (B) after the rare rescales, the P.V products of
+    // block kbl go out with the log-weights of block kbl+1 interleaved.  Block
+    // b is in buffer b % kNBuf; the loads of block kbl+3 go into the buffer of
+    // block kbl-1, which every wave finished before the last barrier.  One
+    // barrier per block: before it each wave waits until its loads of block
+    // kbl+2 (whose K the next iteration reads) have landed, at most the block
+    // after it (4 loads) still in flight.  Both key halves run the same trip
+    // count (nb0) so that their barriers pair up; the second half may run out
+    // of blocks first (its extra iterations compute on stale buffers and keep
+    // nothing).
+    float t[2][16];  // log-weights of the block being finished, per head
     {
         bf16x8 kf[4];
         read_k(k_buf(0), lane, kf);
-        f32x16 st = f32x16{};
+        f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) st = mfma32(kf[kk], qf[kk], st);
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) t[v] = st[v] * P.c;  // reference 0 (ref is -inf)
-        if (kb_begin >= first_masked) mask_block(t, half, kb_begin, lim_pos);
+            for (int u = 0; u < 2; ++u) st[u] = mfma32(kf[kk], qf[u][kk], st[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t[u][v] = st[u][v] * P.c;  // reference 0 (ref is -inf)
+            if (kb_begin >= first_masked) mask_block(t[u], half, kb_begin, lim_pos);
+        }
     }
     for (int kbl = 0;; ++kbl) {
         const bool more = kbl + kNBuf - 1 < nb0;
@@ -503,100 +526,134 @@ __global__ __launch_bounds__(512, 4) void k_prefill_attn(PrefillParams P) {
         // ---- (A) next block's S^T, this block's weights
         bf16x8 kf[4];
         read_k(k_buf((kbl + 1) & (kNBuf - 1)), lane, kf);
-        bf16x8 pb[2], pl[2];
-        float bs = block_weights<kHiLo>(t, 0.0f, pb, pl);
-        f32x16 sn = f32x16{};
+        bf16x8 pb[2][2], pl[2][2];
+        float bs[2];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) sn = mfma32(kf[kk], qf[kk], sn);
+        for (int u = 0; u < 2; ++u) bs[u] = block_weights<kHiLo>(t[u], 0.0f, pb[u], pl[u]);
+        f32x16 sn[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) sn[u] = mfma32(kf[kk], qf[u][kk], sn[u]);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // the K fragment reads
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < 8; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x002, kHiLo ? 12 : 8, 0);  // weights
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one S^T product
         }
         // the weights are used only on the live path below: an empty asm that
         // reads them keeps the compiler from moving their computation there,
         // out of reach of the products they are interleaved with
-        asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[0])), "v"(__builtin_bit_cast(u32x4, pb[1])), "v"(bs));
-        if (kHiLo) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pl[0])), "v"(__builtin_bit_cast(u32x4, pl[1])));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pb[u][0])), "v"(__builtin_bit_cast(u32x4, pb[u][1])),
+                         "v"(bs[u]));
+            if (kHiLo)
+                asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pl[u][0])), "v"(__builtin_bit_cast(u32x4, pl[u][1])));
+        }
 
         if (kbl < kb_count) {
-            if (kbl == 0 || __builtin_amdgcn_ballot_w64(!(bs <= 256.0f)))
-                bs = slow_path<kHiLo>(t, ref, l, o, pb, pl);
-            l += bs;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (kbl == 0 || __builtin_amdgcn_ballot_w64(!(bs[u] <= 256.0f)))
+                    bs[u] = slow_path<kHiLo>(t[u], ref[u], l[u], o[u], pb[u], pl[u]);
+                l[u] += bs[u];
+            }
 
             // ---- (B) this block's P.V, next block's log-weights
             bf16x8 vf[2][2];
             read_v(v_buf(kbl & (kNBuf - 1)), lane, vf);
-            pv_products<kHiLo>(vf, pb, pl, o);
-            const float mc = ref > -INFINITY ? ref : 0.0f;
+            // products chained on one accumulator are 4 apart
 #pragma unroll
-            for (int v = 0; v < 16; ++v) t[v] = fmaf(sn[v], P.c, -mc);
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int db = 0; db < 2; ++db) {
+                        o[u][db] = mfma32(vf[db][sb], pb[u][sb], o[u][db]);
+                        if (kHiLo) o[u][db] = mfma32(vf[db][sb], pl[u][sb], o[u][db]);
+                    }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float mc = ref[u] > -INFINITY ? ref[u] : 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) t[u][v] = fmaf(sn[u][v], P.c, -mc);
+            }
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);  // the V fragment reads
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < 8; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);              // log-weights
                 __builtin_amdgcn_sched_group_barrier(0x008, kHiLo ? 2 : 1, 1);  // P.V products
             }
             const int kbn = kb_begin + kbl + 1;
-            if (kbn >= first_masked) mask_block(t, half, kbn, lim_pos);
+            if (kbn >= first_masked) {
+                mask_block(t[0], half, kbn, lim_pos);
+                mask_block(t[1], half, kbn, lim_pos);
+            }
         }
         if (kbl + 1 >= nb0) break;
-        if (more) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        if (more) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
     __syncthreads();
 
     // ---- merge the two key halves through LDS -----------------------------------
-    // Key half kh finalizes dims 32kh .. 32kh+31: each wave leaves the other
-    // half's dims of its partial O^T, with its (reference, l), in LDS.  Slot:
-    // (key half, head-in-group, lane), 16 floats.
+    // Key half kh finalizes dims 32kh .. 32kh+31 of both heads: each wave
+    // leaves the other half's dims of its partial O^T, with its (reference, l),
+    // in LDS.  Slot: (key half, head pair, head, lane), 16 floats.
     float *mo = reinterpret_cast<float *>(s_raw);
     float *mml = reinterpret_cast<float *>(s_raw + kMergeOBytes);
-    auto slot = [&](int half_k) { return (half_k * 4 + wq) * 64 + lane; };
-    {
-        const f32x16 give = kh ? o[0] : o[1];
-        float *dst = mo + slot(kh) * 16;
+    auto slot = [&](int half_k, int u) { return ((half_k * 2 + hp) * 2 + u) * 64 + lane; };
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const f32x16 give = kh ? o[u][0] : o[u][1];
+        float *dst = mo + slot(kh, u) * 16;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             *reinterpret_cast<f32x4 *>(dst + 4 * r4) = f32x4{give[4 * r4], give[4 * r4 + 1], give[4 * r4 + 2],
                                                              give[4 * r4 + 3]};
-        mml[slot(kh) * 2] = ref;
-        mml[slot(kh) * 2 + 1] = l;
+        mml[slot(kh, u) * 2] = ref[u];
+        mml[slot(kh, u) * 2 + 1] = l[u];
     }
     __syncthreads();
 
     // ---- out[s][i][h][d] = O^T[d][query] / l, d = 32kh + 8r4 + 4*half + r ------
     const int oh = 1 - kh;
-    const float *src = mo + slot(oh) * 16;
-    const float rB = mml[slot(oh) * 2];
-    const float lB = mml[slot(oh) * 2 + 1];
-    // finite: the first half always holds key 0; a half that had no live key
-    // for a row has reference -inf and weight 0
-    const float rx = fmaxf(ref, rB);
-    const float fA = fast_exp2(ref - rx);
-    const float fB = fast_exp2(rB - rx);
-    const float lh = l * fA + lB * fB;
-    const float l_tot = lh + partner32(lh);
+    float fA[2], fB[2], inv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const float rB = mml[slot(oh, u) * 2];
+        const float lB = mml[slot(oh, u) * 2 + 1];
+        // finite: the first half always holds key 0; a half that had no live
+        // key for a row has reference -inf and weight 0
+        const float rx = fmaxf(ref[u], rB);
+        fA[u] = fast_exp2(ref[u] - rx);
+        fB[u] = fast_exp2(rB - rx);
+        const float lh = l[u] * fA[u] + lB * fB[u];
+        inv[u] = 1.0f / (lh + partner32(lh));  // every lane takes part in the exchange
+    }
     const int i = row0 + qc;
     if (i >= C) return;
-    const float inv = 1.0f / l_tot;
-    const f32x16 mine = kh ? o[1] : o[0];
-    const int64_t orow = ((static_cast<int64_t>(s) * C + i) * kHQ + h) * kD;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 4 * r4);
-        const int d = 32 * kh + 8 * r4 + 4 * half;
-        const float y0 = (mine[4 * r4] * fA + ob[0] * fB) * inv;
-        const float y1 = (mine[4 * r4 + 1] * fA + ob[1] * fB) * inv;
-        const float y2 = (mine[4 * r4 + 2] * fA + ob[2] * fB) * inv;
-        const float y3 = (mine[4 * r4 + 3] * fA + ob[3] * fB) * inv;
-        if (P.out_fp32) {
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
-        } else {
-            const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
+    for (int u = 0; u < 2; ++u) {
+        const float *src = mo + slot(oh, u) * 16;
+        const f32x16 mine = kh ? o[u][1] : o[u][0];
+        const int64_t orow = ((static_cast<int64_t>(s) * C + i) * kHQ + h0 + u) * kD;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 ob = *reinterpret_cast<const f32x4 *>(src + 4 * r4);
+            const int d = 32 * kh + 8 * r4 + 4 * half;
+            const float y0 = (mine[4 * r4] * fA[u] + ob[0] * fB[u]) * inv[u];
+            const float y1 = (mine[4 * r4 + 1] * fA[u] + ob[1] * fB[u]) * inv[u];
+            const float y2 = (mine[4 * r4 + 2] * fA[u] + ob[2] * fB[u]) * inv[u];
+            const float y3 = (mine[4 * r4 + 3] * fA[u] + ob[3] * fB[u]) * inv[u];
+            if (P.out_fp32) {
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(P.out) + orow + d) = f32x4{y0, y1, y2, y3};
+            } else {
+                const uint2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P.out) + orow + d) = pk;
+            }
         }
     }
 }
@@ -627,9 +684,9 @@ hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream) 
     P.flags = p.flags;
     const int64_t blocks = static_cast<int64_t>(p.num_seqs) * kHKV * P.n_tiles;
     if (p.out_fp32)
-        hipLaunchKernelGGL(k_prefill_attn<true>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, P);
+        hipLaunchKernelGGL(k_prefill_attn<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, P);
     else
-        hipLaunchKernelGGL(k_prefill_attn<false>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, stream, P);
+        hipLaunchKernelGGL(k_prefill_attn<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, P);
     return hipGetLastError();
 }
 
