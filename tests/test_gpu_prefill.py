@@ -116,6 +116,42 @@ def test_prefill_config_full_size_all_rows():
     assert_rope_equal(to_host_bits(d.q), oq, "rotated q")
 
 
+def _all_rows_case(c, table=None):
+    """Run one case on the GPU and return it with the oracle's output, rotated q and pools."""
+    d = DevPrefill(c)
+    got = to_host_f64(d.run(torch.bfloat16, table=table))
+    assert int(d.flags.item()) == 0
+    ref, oq, okp, ovp = oracle_all(c)
+    return d, got, ref, oq, okp, ovp
+
+
+@pytest.mark.parametrize("prefix,chunk", [([0, 3, 60], 512), ([5, 0, 17, 40, 2], 448)])
+def test_prefill_workgroup_turns(prefix, chunk):
+    """Workgroup ids are dealt to an XCD's 32 CUs in turns, every second turn in reverse order.
+    Grids with 48 workgroups per XCD (3 sequences x 16 tiles: the reversed turn only half full) and
+    70 (5 x 14: three turns, the last one short) must still cover every (sequence, KV head, tile)
+    once: every row against the oracle, pools and rotated q bit for bit."""
+    c = W.make_prefill_case("turns", 83 + len(prefix), prefix, chunk, poison=True)
+    d, got, ref, oq, okp, ovp = _all_rows_case(c)
+    assert_close(got, ref, TOL_BF16, f"{len(prefix)} x {chunk}, all rows")
+    assert_rope_equal(to_host_bits(d.kp), okp, "K pool")
+    assert np.array_equal(to_host_bits(d.vp), ovp)
+    assert_rope_equal(to_host_bits(d.q), oq, "rotated q")
+
+
+def test_prefill_past_4096_keys():
+    """Contexts of 4,548 and 6,048 keys: a key half then has more than 64 blocks, whose page ids
+    the kernel looks up in LDS instead of keeping them in lanes, and a sequence has more pages
+    than the workgroup has threads (two block-table entries per thread in validation)."""
+    c = W.make_prefill_case("long", 84, [4500, 6000, 100], 48, poison=True)
+    assert c.max_blocks > 256
+    d, got, ref, oq, okp, ovp = _all_rows_case(c, table=rope(max_pos=6200))
+    assert_close(got, ref, TOL_BF16, "contexts past 4096 keys")
+    assert_rope_equal(to_host_bits(d.kp), okp, "K pool")
+    assert np.array_equal(to_host_bits(d.vp), ovp)
+    assert_rope_equal(to_host_bits(d.q), oq, "rotated q")
+
+
 def test_prefill_device_errors():
     c = W.make_prefill_case("err", 82, [10, 20, 30], 16, poison=True)
     d = DevPrefill(c)
