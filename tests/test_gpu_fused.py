@@ -86,6 +86,31 @@ def test_fused_output_may_alias_q(table, name):
     assert np.array_equal(to_host_bits(out), to_host_bits(sep))
 
 
+VERY_LONG = [32768, 20001, 1, 4097]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_fused_very_long_contexts(out_dtype):
+    """Contexts up to 32,768 tokens (16 partitions of 128 pages; 2,048-entry block-table rows, which
+    validation reads in steps of the workgroup's 512 threads): fused equals append-then-decode bit
+    for bit, and both are within tolerance of the oracle."""
+    case = W.make_decode_case("very_long", 65, VERY_LONG, dist="normal", max_blocks=2048)
+    table = rope(max_pos=32768 + 64)
+    fa, oa = run_fused(case, table, out_dtype)
+    sb, ob = run_separate(case, table, out_dtype)
+    assert int(fa.flags.item()) == 0 and int(sb.flags.item()) == 0
+    assert np.array_equal(to_host_bits(fa.k_pool), to_host_bits(sb.k_pool)), "K pool differs"
+    assert np.array_equal(to_host_bits(fa.q), to_host_bits(sb.q)), "rotated q differs"
+    got = to_host_f64(oa)
+    assert np.array_equal(got, to_host_f64(ob)), "output differs from append-then-decode"
+    kp, vp, q = case.k_pool.copy(), case.v_pool.copy(), case.q[0].copy()
+    assert oracle.append_kv_rope(q, case.k_new[0], case.v_new[0], kp, vp, case.block_tables[0], case.context_lens,
+                                 case.num_pages, case.theta) == oracle.OK
+    ref, rc = oracle.decode_gqa(q, kp, vp, case.block_tables[0], case.context_lens, case.num_pages, case.scale)
+    assert rc == oracle.OK
+    assert_close(got, ref, TOL_BF16 if out_dtype == torch.bfloat16 else TOL_FP32, "very long")
+
+
 def test_decode_long_contexts_against_oracle(table):
     case = CASES["long"]()
     d = DeviceCase(case)

@@ -146,6 +146,23 @@ def test_decode_i8_parity(name, out_dtype):
     assert int(flags.item()) == 0
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_decode_i8_very_long_contexts(out_dtype):
+    """Contexts up to 32,768 tokens over INT8 pages: 16 partitions of 128 pages and their merge,
+    2,048-entry block-table rows."""
+    case = W.make_decode_case("very_long", 75, [32768, 20001, 1, 4097], dist="normal", max_blocks=2048)
+    pool = host_i8(case)
+    out = guarded_empty((case.num_seqs, 32, 64), out_dtype)
+    flags = guarded_flags()
+    binding.decode_gqa_i8(out, to_dev_bf16(case.q[0]), to_dev_u8(pool), to_dev_i32(case.block_tables[0]),
+                          to_dev_i32(case.context_lens), case.scale,
+                          workspace=guarded_workspace(case.num_seqs, case.max_blocks), device_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    assert_close(to_host_f64(out), oracle_decode_i8(case, pool), TOL_BF16 if out_dtype == torch.bfloat16 else TOL_FP32,
+                 "very long")
+
+
 WIDE_V = {
     # |v| up to 1e6 (the plain f16 form of the weights overflowed past about 3.2e4), with rows of
     # 1e-6: every output within the stated tolerance
