@@ -152,6 +152,21 @@ def test_prefill_past_4096_keys():
     assert_rope_equal(to_host_bits(d.q), oq, "rotated q")
 
 
+def test_prefill_batch_invariance():
+    """A sequence's rows come out bit for bit the same alone and inside a batch (the workgroup order
+    changes with the grid; the arithmetic of a tile does not)."""
+    c = W.make_prefill_case("inv", 85, [7, 300, 40, 1030, 0], 70, poison=True)
+    batch = to_host_bits(DevPrefill(c).run(torch.float32))
+    for s in range(c.num_seqs):
+        one = W.PrefillCase(name="one", num_seqs=1, chunk_len=c.chunk_len, max_blocks=c.max_blocks,
+                            num_pages=c.num_pages, prefix_lens=c.prefix_lens[s:s + 1].copy(),
+                            block_tables=c.block_tables[s:s + 1].copy(), q=c.q[s:s + 1].copy(),
+                            k_chunk=c.k_chunk[s:s + 1].copy(), v_chunk=c.v_chunk[s:s + 1].copy(),
+                            k_pool=c.k_pool, v_pool=c.v_pool)
+        alone = to_host_bits(DevPrefill(one).run(torch.float32))
+        assert np.array_equal(alone[0], batch[s]), f"sequence {s}"
+
+
 def test_prefill_device_errors():
     c = W.make_prefill_case("err", 82, [10, 20, 30], 16, poison=True)
     d = DevPrefill(c)
