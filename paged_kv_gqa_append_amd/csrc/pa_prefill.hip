@@ -175,9 +175,9 @@ struct PrefillParams {
 
 namespace {
 
-// q fragments of one 32-row sub-tile (MFMA B operand, as stored: the append
-// kernel has rotated the rows already): this lane's query row, dims
-// 16kk + 8*half .. +7.
+// q fragments of one head over the workgroup's 32 rows (MFMA B operand, as
+// stored: the append kernel has rotated the rows already): this lane's query
+// row, dims 16kk + 8*half .. +7.
 __device__ __forceinline__ void load_q(const PrefillParams &P, int s, int h, int i_c, int half, u32x4 (&raw)[4]) {
     const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * P.chunk_len + i_c) * kHQ + h) * kD;
 #pragma unroll
@@ -247,21 +247,6 @@ __device__ __forceinline__ float block_weights(const float (&t)[16], float d, bf
         }
     }
     return bs;
-}
-
-// O^T += V^T P^T for the wave's tile (both 32-dim halves, both 16-key steps),
-// ordered so that the two products chained on one accumulator are not
-// adjacent.
-template <bool kHiLo>
-__device__ __forceinline__ void pv_products(const bf16x8 (&vf)[2][2], const bf16x8 (&pb)[2], const bf16x8 (&pl)[2],
-                                            f32x16 (&o)[2]) {
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            o[db] = mfma32(vf[db][sb], pb[sb], o[db]);
-            if (kHiLo) o[db] = mfma32(vf[db][sb], pl[sb], o[db]);
-        }
 }
 
 // Softmax in log2 units against a lazily kept, integer-valued reference ref
