@@ -45,6 +45,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+# decode workgroups resident at once: 2 per CU (8 waves each, at most 4 waves per SIMD), 256 CUs
+RESIDENT_DECODE_WGS = 512
 # sources each fused decode kernel is compiled from (its traffic figure is tied to them),
 # and the committed rocprofv3 summary that holds that figure
 TRAFFIC = {
@@ -421,38 +423,55 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
             binding.append_decode_gqa(L["out"], L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens,
                                       table, spec.scale, workspace=ws, dispatch_order=order, stream=stream)
 
+    # A batch whose workgroups outnumber the 512 that stay resident on the GPU (2 per CU) is
+    # dispatched longest first, from an order computed on the device from the device-resident
+    # lengths once per step (pa_order_by_length, inside the timed step) and read by every
+    # layer's launch; a smaller batch starts all its workgroups at once and runs in slot order.
+    parts = -(-spec.max_blocks * 16 // binding.decode_partition_tokens())
+    use_order = spec.num_seqs * 8 * parts > RESIDENT_DECODE_WGS
+    order_buf = torch.empty(spec.num_seqs, dtype=torch.int32, device=device)
+
+    def make_order():
+        return binding.order_by_length(lens, spec.max_blocks, order_buf, stream=stream) if use_order else None
+
     def step_fused(order=None):
         for l in range(spec.num_layers):
             call_layer(l, order)
 
+    def step_main():
+        step_fused(make_order())
+
     def step_separate():
+        order = make_order()
         for L in layers:
             if i8:
                 binding.append_kv_rope_i8(L["q"], L["k_new"], L["v_new"], pool, L["bt"], lens, table, stream=stream)
                 binding.decode_gqa_i8(L["out"], L["q"], pool, L["bt"], lens, spec.scale, workspace=ws,
-                                      stream=stream)
+                                      dispatch_order=order, stream=stream)
             else:
                 binding.append_kv_rope(L["q"], L["k_new"], L["v_new"], k_pool, v_pool, L["bt"], lens, table,
                                        stream=stream)
                 binding.decode_gqa(L["out"], L["q"], k_pool, v_pool, L["bt"], lens, spec.scale, workspace=ws,
-                                   stream=stream)
+                                   dispatch_order=order, stream=stream)
 
     # a secondary one-layer workload takes 200 timed steps (a step is ~10 us)
     steps = max(args.steps, 200) if spec.num_layers == 1 and not headline else args.steps
     separate = args.path == "separate"
-    step = step_separate if separate else step_fused
+    step = step_separate if separate else step_main
     ms, warm = timed_steps(step, steps, args.warmup, torch, stream)
     n_pass = max(3, args.steps // 2)
     other_ms = None
     if headline:
-        other_ms = timed_steps(step_fused if separate else step_separate, max(3, steps // 2), 2, torch, stream)[0]
+        other_ms = timed_steps(step_main if separate else step_separate, max(3, steps // 2), 2, torch, stream)[0]
 
-    # Kernel duration for the roofline.  With the fused path the timed region above is
-    # nothing but the fused kernel, num_layers launches per step back to back on the
-    # launch stream, so its mean per launch (gaps included) is ms / num_layers.  With the
-    # separate path the fused kernel is timed the same way in a pass of its own.
-    dec_ms_mean = ms / spec.num_layers if not separate else \
-        timed_steps(step_fused, n_pass, 1, torch, stream)[0] / spec.num_layers
+    # Kernel duration for the roofline.  With the fused path in slot order the timed region
+    # above is nothing but the fused kernel, num_layers launches per step back to back on the
+    # launch stream, so its mean per launch (gaps included) is ms / num_layers.  Otherwise (the
+    # step also computes its order, or runs the separate calls) the fused kernel is timed the
+    # same way in a pass of its own, with the order computed once before it.
+    fixed_order = make_order()
+    dec_ms_mean = ms / spec.num_layers if not (separate or use_order) else \
+        timed_steps(lambda: step_fused(fixed_order), n_pass, 1, torch, stream)[0] / spec.num_layers
     # Median per launch: one event pair per step of a further pass (steps of many launches
     # only, where the events' own cost is small against the step).
     seq_ms = []
@@ -461,20 +480,21 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            step_fused()
+            step_fused(fixed_order)
             b.record(stream)
             torch.cuda.synchronize()
             seq_ms.append(a.elapsed_time(b))
 
-    # Ragged batches: the fused step with the sequences dispatched longest first (the
-    # dispatch_order argument; same results bit for bit).  The host sort runs inside every
-    # timed step, as a server whose lengths change each step would run it.  The library
-    # takes at most 1024 (sequence, partition) work items in an ordered dispatch.
-    lf_ms = None
-    parts = -(-spec.max_blocks * 16 // binding.decode_partition_tokens())
-    if len(set(spec.context_lens.tolist())) > 1 and spec.num_seqs * parts <= 1024:
-        lf_ms = timed_steps(lambda: step_fused(binding.dispatch_order_longest_first(spec.context_lens)), n_pass,
-                            None, torch, stream)[0]
+    # Ordered batches, for comparison: the same fused step in slot order (no order), and with
+    # the host's longest-first order (dispatch_order from pa_dispatch_order_longest_first, the
+    # host sort inside every timed step; the launch arguments take at most 1024 (sequence,
+    # partition) items).
+    slot_ms = lf_ms = None
+    if use_order:
+        slot_ms = timed_steps(step_fused, n_pass, None, torch, stream)[0]
+        if spec.num_seqs * parts <= 1024:
+            lf_ms = timed_steps(lambda: step_fused(binding.dispatch_order_longest_first(spec.context_lens)), n_pass,
+                                None, torch, stream)[0]
 
     # Cold runs for workloads whose K/V fit in the 256 MB MALL (Infinity Cache).
     kv_step = spec.kv_bytes() // 2048 * KV_TOKEN_BYTES[kv]
@@ -495,7 +515,9 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
                    "step": ("per layer: pa_append_decode_gqa%s (append + RoPE + decode, one launch)" % sfx
                             if not separate else
                             "per layer: pa_append_kv_rope%s then pa_decode_gqa%s" % (sfx, sfx)),
-                   "decode_partition_tokens": binding.decode_partition_tokens()},
+                   "decode_partition_tokens": binding.decode_partition_tokens(),
+                   "dispatch": ("longest first: pa_order_by_length on the device once per step (in the timed "
+                                "step), its order passed to every layer's launch" if use_order else "slot order")},
         "kv_bytes_per_step": kv_step,
         "roofline": {"bound": "hbm",
                      "kernel": ("k_decode_paged_i8<8,true,nt> (pa_append_decode_gqa_i8)" if i8 else
@@ -520,13 +542,18 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
                                            "distinct_chunks_per_step": ceil_chunks,
                                            "frac_of_peak": round(ceil_gbps / HBM_PEAK_GBPS, 4),
                                            "decode_frac_of_stream_read": round(dec_gbps / ceil_gbps, 4)})
+    def order_figure(m, note):
+        return {"ms_per_step": round(m, 5), "value": round(kv_step / (m * 1e-3) / 1e9, 2), "unit": "GB/s",
+                "tokens_per_s": round(spec.num_seqs / (m * 1e-3), 1),
+                "mean_launch_us": round(m / spec.num_layers * 1e3, 2),
+                "frac": round(kv_launch / (m / spec.num_layers * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "note": note}
+
+    if slot_ms is not None:
+        res["slot_order"] = order_figure(slot_ms, "the fused step without an order: workgroups dealt in batch order")
     if lf_ms is not None:
-        res["longest_first"] = {"ms_per_step": round(lf_ms, 5), "value": round(kv_step / (lf_ms * 1e-3) / 1e9, 2),
-                                "unit": "GB/s", "tokens_per_s": round(spec.num_seqs / (lf_ms * 1e-3), 1),
-                                "mean_launch_us": round(lf_ms / spec.num_layers * 1e3, 2),
-                                "frac": round(kv_launch / (lf_ms / spec.num_layers * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                "note": "fused step with dispatch_order = sequences by length, longest first; the "
-                                        "host sort (pa_dispatch_order_longest_first) runs inside every timed step"}
+        res["longest_first"] = order_figure(lf_ms, "fused step with a host dispatch_order = sequences by length, "
+                                                   "longest first; the host sort (pa_dispatch_order_longest_first) "
+                                                   "runs inside every timed step")
     if cold_ms is not None:
         res["cold"] = {"ms_per_step": round(cold_ms, 5), "value": round(kv_step / (cold_ms * 1e-3) / 1e9, 2),
                        "unit": "GB/s", "pct_hbm_peak": round(100.0 * kv_step / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
@@ -535,7 +562,8 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
                                "the MALL; the main figures are warm"}
     if not args.no_accuracy:
         acc_layers = [0, spec.num_layers - 1] if spec.num_layers > 1 else [0]
-        res["accuracy"] = decode_accuracy(spec, k_pool, v_pool, rows, layers, call_layer, acc_layers, kv, stream)
+        res["accuracy"] = decode_accuracy(spec, k_pool, v_pool, rows, layers, lambda l: call_layer(l, make_order()),
+                                          acc_layers, kv, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, k_pool, v_pool, rows, cpu_seconds, kv)
     del spec, k_pool, v_pool, layers, pool, ws

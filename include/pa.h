@@ -86,6 +86,7 @@ typedef enum { PA_OUT_BF16 = 0, PA_OUT_FP32 = 1 } pa_out_dtype;
 /* Bits a kernel ORs into *device_flags (caller-owned uint32, may be NULL). */
 #define PA_DEVERR_CONTEXT_LEN 0x1u /* L < 1, or L beyond max_blocks*16 / max_pos */
 #define PA_DEVERR_PAGE_ID 0x2u     /* a used block-table entry outside [0, num_pages) */
+#define PA_DEVERR_DISPATCH_ORDER 0x4u /* a device_order entry outside [0, num_seqs)      */
 
 /* Human-readable name of a status code (static string, never NULL).  Every
  * call reports failure through its return value and the caller must not go on
@@ -114,7 +115,7 @@ int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t s
  * from, so a caller can refuse a library built from another header.  Like the
  * fixed geometry (samir-vllm, section "Limitations et perspectives": changing
  * the architecture means recompiling), a mismatch is refused, not adapted to. */
-#define PA_ABI_VERSION 11
+#define PA_ABI_VERSION 12
 int32_t pa_abi_version(void);
 
 /* Identity of the sources the library was built from: the sha256 (64 hex
@@ -194,6 +195,37 @@ int32_t pa_decode_partition_tokens(void);
  * array with n > 0.                                                           */
 pa_status pa_dispatch_order_longest_first(const int32_t *lengths, int32_t n, int32_t *order);
 
+/* device_order (every decode entry point; DEVICE int32[num_seqs], may be NULL;
+ * not together with dispatch_order, PA_ERR_INVALID_ARG): the same as
+ * dispatch_order, read by the kernels from device memory, so that an order
+ * computed on the device (pa_order_by_length) needs no copy to the host and
+ * one order serves every layer of a step.  Workgroups of the i-th dispatched
+ * item serve sequence device_order[i / P], partition i % P.  It must be a
+ * permutation of 0 .. num_seqs-1: the host cannot check device memory, so a
+ * repeated entry leaves some sequence unserved, unflagged (pa_order_by_length
+ * always writes a permutation).  An entry outside [0, num_seqs) is never
+ * dereferenced: its workgroups do nothing and OR PA_DEVERR_DISPATCH_ORDER into
+ * *device_flags; the whole call's outputs are then unusable.  Any num_seqs
+ * and any P; 16-byte aligned.                                                */
+
+/* The longest-first order of a ragged batch, computed on the device (a
+ * continuous-batching decode batch mixes contexts of very different lengths:
+ * samir-vllm, "Gestion de la KV cache et strategies de batching", admission as
+ * soon as a request's page budget is free).  Writes order[0 .. num_seqs-1]
+ * (DEVICE int32) from context_lens (DEVICE int32[num_seqs]): the sequences by
+ * length class, longest class first, index order within a class, where class
+ * c of a valid length L (1 <= L <= 16 * max_blocks) is (ceil(L/16) - 1) /
+ * ceil(max_blocks/64), 64 classes across the table width; an invalid length
+ * has class 0, the last (the decode rejects it as usual).  Pass the result as
+ * device_order to every decode of the step: starting the long contexts first
+ * keeps them from forming the launch's tail, and changes no result.  One
+ * workgroup on `stream`, nothing allocated; the lengths must not change
+ * between this call and the decodes that use its order (stream order).
+ * PA_ERR_INVALID_ARG for num_seqs outside [0, PA_MAX_DISPATCH_ORDER],
+ * max_blocks < 1, a NULL or misaligned array, or arrays that overlap.        */
+pa_status pa_order_by_length(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t *order,
+                             hipStream_t stream);
+
 /* Paged GQA decode (samir-vllm, batched-decode paragraph of "Gestion de la KV
  * cache ..."; tiny-vllm ch.2, "One buffer, two roles": the attention output is
  * written over the q buffer).  For each s, h < 32, j = h/4, L = context_lens[s]:
@@ -209,7 +241,8 @@ pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void
                         const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
                         int32_t max_blocks, int32_t num_pages, int32_t page_size, float scale,
                         int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                        uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
+                        uint32_t *device_flags, const int32_t *dispatch_order, const int32_t *device_order,
+                        hipStream_t stream);
 
 /* One decode step of a layer in a single launch: pa_append_kv_rope followed by
  * pa_decode_gqa, fused (samir-vllm, "Gestion de la KV cache ...": the new
@@ -227,7 +260,8 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
                                const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                               uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
+                               uint32_t *device_flags, const int32_t *dispatch_order, const int32_t *device_order,
+                               hipStream_t stream);
 
 /* pa_append_decode_gqa without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
@@ -250,7 +284,7 @@ pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, co
                                        const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                        int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                        int32_t out_dtype, uint32_t *device_flags, const int32_t *dispatch_order,
-                                       hipStream_t stream);
+                                       const int32_t *device_order, hipStream_t stream);
 
 /* Chunked prefill (TinyLoop, section "prefill_chunk and scratch residency":
  * the prompt is processed in row chunks; samir-vllm: the prompt's pages are
@@ -333,7 +367,8 @@ pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, vo
 pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, const int32_t *block_tables,
                            const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
                            int32_t page_size, float scale, int32_t out_dtype, void *workspace,
-                           size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
+                           size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
+                           const int32_t *device_order, hipStream_t stream);
 
 /* pa_append_kv_rope_i8 followed by pa_decode_gqa_i8 in one launch, bitwise equal
  * to the two calls (same rotation, rounding and quantisation); q as in
@@ -343,7 +378,8 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
                                   const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                   int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                                  uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream);
+                                  uint32_t *device_flags, const int32_t *dispatch_order,
+                                  const int32_t *device_order, hipStream_t stream);
 
 /* --------------------------------------------------------------- argmax --
  * Greedy next-token choice on the GPU (samir-vllm, section "Architecture et

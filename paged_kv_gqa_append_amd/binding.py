@@ -23,7 +23,7 @@ _lib = None
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_REJECTED = range(6)
 PA_BATCH_CONTINUOUS, PA_BATCH_STATIC = 0, 1
 PA_OUT_BF16, PA_OUT_FP32 = 0, 1
-PA_DEVERR_CONTEXT_LEN, PA_DEVERR_PAGE_ID = 0x1, 0x2
+PA_DEVERR_CONTEXT_LEN, PA_DEVERR_PAGE_ID, PA_DEVERR_DISPATCH_ORDER = 0x1, 0x2, 0x4
 
 EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_append_kv_rope",
            "pa_decode_workspace_bytes", "pa_decode_partition_tokens", "pa_decode_gqa", "pa_append_decode_gqa",
@@ -33,11 +33,11 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
            "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read",
            "pa_dispatch_order_longest_first", "pa_get_device_error", "pa_build_id",
-           "pa_append_decode_gqa_noalloc")
+           "pa_append_decode_gqa_noalloc", "pa_order_by_length")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 
 class PaError(RuntimeError):
@@ -94,13 +94,13 @@ def lib():
     L.pa_decode_partition_tokens.restype = i32
     L.pa_decode_partition_tokens.argtypes = []
     L.pa_decode_gqa.restype = ctypes.c_int
-    L.pa_decode_gqa.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P, P]
+    L.pa_decode_gqa.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P, P, P]
     L.pa_append_decode_gqa.restype = ctypes.c_int
     L.pa_append_decode_gqa.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
-                                       u64, P, P, P]
+                                       u64, P, P, P, P]
     L.pa_append_decode_gqa_noalloc.restype = ctypes.c_int
     L.pa_append_decode_gqa_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float,
-                                               i32, P, P, P]
+                                               i32, P, P, P, P]
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
                                    P, P]
@@ -111,16 +111,18 @@ def lib():
     L.pa_append_kv_rope_i8.restype = ctypes.c_int
     L.pa_append_kv_rope_i8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P]
     L.pa_decode_gqa_i8.restype = ctypes.c_int
-    L.pa_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P, P]
+    L.pa_decode_gqa_i8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float, i32, P, u64, P, P, P, P]
     L.pa_append_decode_gqa_i8.restype = ctypes.c_int
     L.pa_append_decode_gqa_i8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
-                                          u64, P, P, P]
+                                          u64, P, P, P, P]
     L.pa_argmax_workspace_bytes.restype = u64
     L.pa_argmax_workspace_bytes.argtypes = [i32, i32, i32]
     L.pa_argmax.restype = ctypes.c_int
     L.pa_argmax.argtypes = [P, P, i32, i32, i32, P, u64, P]
     L.pa_dispatch_order_longest_first.restype = ctypes.c_int
     L.pa_dispatch_order_longest_first.argtypes = [P, i32, P]
+    L.pa_order_by_length.restype = ctypes.c_int
+    L.pa_order_by_length.argtypes = [P, i32, i32, P, P]
     L.pa_probe_stream_read.restype = ctypes.c_int
     L.pa_probe_stream_read.argtypes = [P, u64, P, P]
     L.pa_get_device_error.restype = i32
@@ -176,19 +178,24 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _order(dispatch_order, num_seqs: int):
-    """Host int32 view or copy of an optional dispatch order, and its address (the caller keeps
-    the array alive for the call).  A contiguous int32 numpy array is used as it is.  The library
-    reads exactly num_seqs entries, so an array of any other length is refused here."""
+def _order(dispatch_order, num_seqs: int, device=None):
+    """The two order arguments of a decode call, (keep-alive, host pointer, device pointer), from
+    an optional dispatch order.  A torch tensor on the call's device is a device order
+    (int32[num_seqs], e.g. from order_by_length), passed as device_order; anything else is a host
+    order: a contiguous int32 numpy array is used as it is, other sequences are copied.  The
+    library reads exactly num_seqs entries, so an order of any other length is refused here."""
     if dispatch_order is None:
-        return None, None
+        return None, None, None
+    if isinstance(dispatch_order, torch.Tensor):
+        _expect(dispatch_order, "dispatch_order", torch.int32, (int(num_seqs),), device)
+        return dispatch_order, None, _ptr(dispatch_order)
     arr = dispatch_order
     if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
         arr = np.ascontiguousarray(np.asarray(dispatch_order, dtype=np.int32))
     if arr.shape != (int(num_seqs),):
         raise ValueError(f"dispatch_order must be a 1-D array of exactly num_seqs = {int(num_seqs)} sequence "
                          f"indices, got shape {arr.shape}")
-    return arr, ctypes.c_void_p(arr.ctypes.data)
+    return arr, ctypes.c_void_p(arr.ctypes.data), None
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -287,10 +294,10 @@ def decode_gqa(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order, B)
+    order_keep, order_ptr, order_dev = _order(dispatch_order, B, dev)
     rc = lib().pa_decode_gqa(_ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
                              B, int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
-                             _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, _stream(stream))
+                             _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, order_dev, _stream(stream))
     _check(rc, "pa_decode_gqa")
     return out
 
@@ -322,12 +329,12 @@ def append_decode_gqa(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor, v
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order, B)
+    order_keep, order_ptr, order_dev = _order(dispatch_order, B, dev)
     rc = lib().pa_append_decode_gqa(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
                                     _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
                                     int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
                                     float(scale), odt, _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr,
-                                    _stream(stream))
+                                    order_dev, _stream(stream))
     _check(rc, "pa_append_decode_gqa")
     return out
 
@@ -357,12 +364,12 @@ def append_decode_gqa_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.T
     _expect(out, "out", out.dtype, (B, 32, 64), dev)
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order, B)
+    order_keep, order_ptr, order_dev = _order(dispatch_order, B, dev)
     rc = lib().pa_append_decode_gqa_noalloc(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
                                             _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
                                             _ptr(rope_cos_sin), B, int(block_tables.shape[1]), num_pages,
                                             int(page_size), int(rope_cos_sin.shape[0]), float(scale), odt,
-                                            _ptr(device_flags), order_ptr, _stream(stream))
+                                            _ptr(device_flags), order_ptr, order_dev, _stream(stream))
     _check(rc, "pa_append_decode_gqa_noalloc")
     return out
 
@@ -490,10 +497,10 @@ def decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, kv_pool_i8: torch.Tensor, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order, B)
+    order_keep, order_ptr, order_dev = _order(dispatch_order, B, dev)
     rc = lib().pa_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(kv_pool_i8), _ptr(block_tables), _ptr(context_lens), B,
                                 int(block_tables.shape[1]), num_pages, int(page_size), float(scale), odt,
-                                _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, _stream(stream))
+                                _ptr(workspace), ws_bytes, _ptr(device_flags), order_ptr, order_dev, _stream(stream))
     _check(rc, "pa_decode_gqa_i8")
     return out
 
@@ -516,12 +523,12 @@ def append_decode_gqa_i8(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if device_flags is not None:
         _expect(device_flags, "device_flags", torch.int32, (1,), dev)
-    order_arr, order_ptr = _order(dispatch_order, B)
+    order_keep, order_ptr, order_dev = _order(dispatch_order, B, dev)
     rc = lib().pa_append_decode_gqa_i8(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_pool_i8),
                                        _ptr(block_tables), _ptr(context_lens), _ptr(rope_cos_sin), B,
                                        int(block_tables.shape[1]), num_pages, int(page_size),
                                        int(rope_cos_sin.shape[0]), float(scale), odt, _ptr(workspace), ws_bytes,
-                                       _ptr(device_flags), order_ptr, _stream(stream))
+                                       _ptr(device_flags), order_ptr, order_dev, _stream(stream))
     _check(rc, "pa_append_decode_gqa_i8")
     return out
 
@@ -563,6 +570,23 @@ def dispatch_order_longest_first(lengths) -> np.ndarray:
     _check(lib().pa_dispatch_order_longest_first(ctypes.c_void_p(lens.ctypes.data), int(lens.shape[0]),
                                                  ctypes.c_void_p(order.ctypes.data)),
            "pa_dispatch_order_longest_first")
+    return order
+
+
+def order_by_length(context_lens: torch.Tensor, max_blocks: int, order: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """pa_order_by_length: the sequences longest first (64 length classes across max_blocks pages,
+    index order within a class), computed on the device into ``order`` (int32[num_seqs], a new
+    tensor when None).  Pass it as ``dispatch_order`` to the decode calls of the step."""
+    _expect(context_lens, "context_lens", torch.int32)
+    if context_lens.dim() != 1:
+        raise ValueError("context_lens must be [num_seqs]")
+    n = int(context_lens.shape[0])
+    if order is None:
+        order = torch.empty(n, dtype=torch.int32, device=context_lens.device)
+    _expect(order, "order", torch.int32, (n,), context_lens.device)
+    _check(lib().pa_order_by_length(_ptr(context_lens), n, int(max_blocks), _ptr(order), _stream(stream)),
+           "pa_order_by_length")
     return order
 
 

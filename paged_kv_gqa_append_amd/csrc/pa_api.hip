@@ -43,10 +43,11 @@ pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new
                         const int32_t *block_tables, const int32_t *context_lens, const double *rope,
                         int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size, int32_t max_pos,
                         float scale, int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                        uint32_t *device_flags, const int32_t *order, hipStream_t stream, bool fused,
-                        bool i8 = false) {
+                        uint32_t *device_flags, const int32_t *order, const int32_t *order_dev,
+                        hipStream_t stream, bool fused, bool i8 = false) {
     if (i8) v_pool = k_pool;
     if (num_seqs < 0 || max_blocks < 1 || num_pages < 1 || !isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (order && order_dev) return PA_ERR_INVALID_ARG;
     if (order && (!is_permutation(order, num_seqs) || decode_num_parts(max_blocks) > pa::kMaxOrderParts ||
                   static_cast<int64_t>(num_seqs) * decode_num_parts(max_blocks) > PA_MAX_DISPATCH_ORDER))
         return PA_ERR_INVALID_ARG;
@@ -56,7 +57,7 @@ pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(block_tables) ||
-        !aligned16(context_lens))
+        !aligned16(context_lens) || !aligned16(order_dev))
         return PA_ERR_INVALID_ARG;
     if (fused && (!k_new || !v_new || !rope || !aligned16(k_new) || !aligned16(v_new) || !aligned16(rope)))
         return PA_ERR_INVALID_ARG;
@@ -89,6 +90,7 @@ pa_status decode_common(void *out, void *q, const void *k_new, const void *v_new
     d.ws_acc = need ? ws + rows * 2 : nullptr;
     d.flags = device_flags;
     d.order = order;
+    d.order_dev = order_dev;
     return (i8 ? pa::launch_decode_i8(d, stream) : pa::launch_decode(d, stream)) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -199,11 +201,11 @@ pa_status pa_decode_gqa(void *out, const void *q, const void *k_pool, const void
                         const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
                         int32_t max_blocks, int32_t num_pages, int32_t page_size, float scale, int32_t out_dtype,
                         void *workspace, size_t workspace_bytes, uint32_t *device_flags,
-                        const int32_t *dispatch_order, hipStream_t stream) {
+                        const int32_t *dispatch_order, const int32_t *device_order, hipStream_t stream) {
     return decode_common(out, const_cast<void *>(q), nullptr, nullptr, const_cast<void *>(k_pool),
                          const_cast<void *>(v_pool), block_tables, context_lens, nullptr, num_seqs, max_blocks,
                          num_pages, page_size, 0, scale, out_dtype, workspace, workspace_bytes, device_flags,
-                         dispatch_order, stream, false);
+                         dispatch_order, device_order, stream, false);
 }
 
 pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void *v_new, void *k_pool, void *v_pool,
@@ -211,10 +213,10 @@ pa_status pa_append_decode_gqa(void *out, void *q, const void *k_new, const void
                                int32_t num_seqs, int32_t max_blocks, int32_t num_pages, int32_t page_size,
                                int32_t max_pos, float scale, int32_t out_dtype, void *workspace,
                                size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
-                               hipStream_t stream) {
+                               const int32_t *device_order, hipStream_t stream) {
     return decode_common(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin, num_seqs,
                          max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace, workspace_bytes,
-                         device_flags, dispatch_order, stream, true);
+                         device_flags, dispatch_order, device_order, stream, true);
 }
 
 pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, const void *v_new, void *k_pool,
@@ -222,7 +224,7 @@ pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, co
                                        const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                        int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                        int32_t out_dtype, uint32_t *device_flags, const int32_t *dispatch_order,
-                                       hipStream_t stream) {
+                                       const int32_t *device_order, hipStream_t stream) {
     // Sizes first, so that an oversized call fails before anything else.
     const size_t need = pa_decode_workspace_bytes(num_seqs, max_blocks);
     if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
@@ -234,7 +236,7 @@ pa_status pa_append_decode_gqa_noalloc(void *out, void *q, const void *k_new, co
     return decode_common(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, rope_cos_sin, num_seqs,
                          max_blocks, num_pages, page_size, max_pos, scale, out_dtype, ws,
                          need > 0 ? static_cast<size_t>(PA_NOALLOC_SCRATCH_BYTES) : 0, device_flags, dispatch_order,
-                         stream, true);
+                         device_order, stream, true);
 }
 
 pa_status pa_prefill_chunk(void *out, void *q, const void *k_chunk, const void *v_chunk, void *k_pool, void *v_pool,
@@ -300,10 +302,11 @@ pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, con
                            const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
                            int32_t page_size, float scale, int32_t out_dtype, void *workspace,
                            size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
-                           hipStream_t stream) {
+                           const int32_t *device_order, hipStream_t stream) {
     return decode_common(out, const_cast<void *>(q), nullptr, nullptr, const_cast<void *>(kv_pool_i8), nullptr,
                          block_tables, context_lens, nullptr, num_seqs, max_blocks, num_pages, page_size, 0, scale,
-                         out_dtype, workspace, workspace_bytes, device_flags, dispatch_order, stream, false, true);
+                         out_dtype, workspace, workspace_bytes, device_flags, dispatch_order, device_order, stream,
+                         false, true);
 }
 
 pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
@@ -311,10 +314,11 @@ pa_status pa_append_decode_gqa_i8(void *out, void *q, const void *k_new, const v
                                   const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,
                                   int32_t num_pages, int32_t page_size, int32_t max_pos, float scale,
                                   int32_t out_dtype, void *workspace, size_t workspace_bytes,
-                                  uint32_t *device_flags, const int32_t *dispatch_order, hipStream_t stream) {
+                                  uint32_t *device_flags, const int32_t *dispatch_order,
+                                  const int32_t *device_order, hipStream_t stream) {
     return decode_common(out, q, k_new, v_new, kv_pool_i8, nullptr, block_tables, context_lens, rope_cos_sin,
                          num_seqs, max_blocks, num_pages, page_size, max_pos, scale, out_dtype, workspace,
-                         workspace_bytes, device_flags, dispatch_order, stream, true, true);
+                         workspace_bytes, device_flags, dispatch_order, device_order, stream, true, true);
 }
 
 size_t pa_argmax_workspace_bytes(int32_t num_rows, int32_t vocab, int32_t logits_dtype) {
@@ -349,6 +353,18 @@ pa_status pa_dispatch_order_longest_first(const int32_t *lengths, int32_t n, int
     for (int32_t i = 0; i < n; ++i) order[i] = i;
     std::stable_sort(order, order + n, [lengths](int32_t a, int32_t b) { return lengths[a] > lengths[b]; });
     return PA_OK;
+}
+
+pa_status pa_order_by_length(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t *order,
+                             hipStream_t stream) {
+    if (num_seqs < 0 || num_seqs > PA_MAX_DISPATCH_ORDER || max_blocks < 1) return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PA_OK;
+    if (!context_lens || !order || !aligned16(context_lens) || !aligned16(order)) return PA_ERR_INVALID_ARG;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(context_lens), b = reinterpret_cast<uintptr_t>(order);
+    const uintptr_t bytes = static_cast<uintptr_t>(num_seqs) * sizeof(int32_t);
+    if (a < b + bytes && b < a + bytes) return PA_ERR_INVALID_ARG;
+    return pa::launch_order_by_length(context_lens, num_seqs, max_blocks, order, stream) == hipSuccess ? PA_OK
+                                                                                                       : PA_ERR_HIP;
 }
 
 pa_status pa_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {

@@ -56,14 +56,18 @@
 
 namespace pa {
 
-template <int kWaves, bool kFused, bool kRows, bool kOrd>
-__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P, DispatchOrder<kOrd> order) {
+template <int kWaves, bool kFused, bool kRows, class Ord>
+__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P, Ord order) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
     const WgCoords wc = wg_coords(order, P.num_parts);
     const int part = wc.part;
     const int j = wc.j;
-    const int s = wc.s;
+    // A device order entry outside the batch is never used as an index: the
+    // workgroup reads sequence 0's rows instead (always valid to read) and
+    // leaves at the validation below, having written nothing.
+    const bool order_ok = order_entry_ok(order, wc.s);
+    const int s = order_ok ? wc.s : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -194,6 +198,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P,
         if (len_ok && rel >= 0 && rel == my_idx && rel < slice) s_app_page = my_id;
     }
     bool ok = len_ok && (__syncthreads_or(bad) == 0);
+    if (!order_ok) {  // uniform over the workgroup
+        if (tid == 0 && P.flags) atomicOr(P.flags, kDevErrDispatchOrder);
+        return;
+    }
     if (ok && n_parts_s > 1) {  // long context: the whole row decides, as in every partition
         int bad_row = 0;
         for (int b = tid; b < n_pages; b += kThreads) {
@@ -440,16 +448,17 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream) {
     const bool rows = blocks >= kNtMinBlocks;
     const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWaves);
     auto go = [&](auto order) {
-        constexpr bool kOrd = !std::is_empty_v<decltype(order)>;
+        using Ord = decltype(order);
         if (d.fused) {
-            if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, true, kOrd>), grid, wg, 0, stream, P, order);
-            else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, false, kOrd>), grid, wg, 0, stream, P, order);
+            if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, true, Ord>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, true, false, Ord>), grid, wg, 0, stream, P, order);
         } else {
-            if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, true, kOrd>), grid, wg, 0, stream, P, order);
-            else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, false, kOrd>), grid, wg, 0, stream, P, order);
+            if (rows) hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, true, Ord>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged<kDecodeWaves, false, false, Ord>), grid, wg, 0, stream, P, order);
         }
     };
     if (d.order) go(make_dispatch_order(d.order, d.num_seqs, d.num_parts));
+    else if (d.order_dev) go(DeviceOrder{d.order_dev, d.num_seqs});
     else go(DispatchOrder<false>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.num_parts == 1) return e;

@@ -46,6 +46,18 @@ struct DispatchOrder<true> {
     uint16_t item[kMaxDispatchOrder];
 };
 
+// A dispatch order in device memory, int32[n] (pa_order_by_length writes
+// one): workgroups 8i .. 8i+7 serve partition i % num_parts of sequence
+// ord[i / num_parts].  One uniform load, L2-resident after the launch's first
+// workgroups, stands before the block-table row; against the order in the
+// launch arguments it also keeps the arguments small (2 KiB less to set up per
+// launch).  An entry outside [0, n) makes its workgroups flag the error and
+// do nothing else.
+struct DeviceOrder {
+    const int32_t *ord;
+    int n;
+};
+
 struct WgCoords {
     int s, j, part;
 };
@@ -60,6 +72,21 @@ __device__ __forceinline__ WgCoords wg_coords(const DispatchOrder<kOrd> &o, int 
         const int sj = b / num_parts;
         return {sj >> 3, sj & (kHKV - 1), b % num_parts};
     }
+}
+
+__device__ __forceinline__ WgCoords wg_coords(const DeviceOrder &o, int num_parts) {
+    const int b = blockIdx.x;
+    const int i = b >> 3;
+    const int r = num_parts == 1 ? i : i / num_parts;
+    const int s = __builtin_amdgcn_readfirstlane(o.ord[r]);
+    return {s, b & (kHKV - 1), i - r * num_parts};
+}
+
+// whether the workgroup's sequence index came from a valid order entry
+template <class Ord>
+__device__ __forceinline__ bool order_entry_ok(const Ord &o, int s) {
+    if constexpr (std::is_same_v<Ord, DeviceOrder>) return static_cast<unsigned>(s) < static_cast<unsigned>(o.n);
+    else return true;
 }
 
 // The ordered form for a host-checked permutation of the n sequences, with

@@ -16,6 +16,7 @@ constexpr int kPageElems = kHKV * kTile;   // elements of one page (all heads)
 
 constexpr uint32_t kDevErrContextLen = 0x1u;
 constexpr uint32_t kDevErrPageId = 0x2u;
+constexpr uint32_t kDevErrDispatchOrder = 0x4u;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -266,14 +266,18 @@ __device__ __forceinline__ float max_quarters(float v) {
 // out (as in the bf16 kernel).  The s_setprio instructions also constrain how
 // the compiler schedules the page loop, so the form without them is kept for
 // grids where levelling does not pay (see launch_decode_i8).
-template <int kWaves, bool kFused, bool kNt, bool kLevel, bool kOrd>
-__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P, DispatchOrder<kOrd> order) {
+template <int kWaves, bool kFused, bool kNt, bool kLevel, class Ord>
+__global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams P, Ord order) {
     constexpr int kThreads = 64 * kWaves;
     static_assert(kMaxPartPages <= 64 * kWaves, "one page id per lane must cover a partition");
     const WgCoords wc = wg_coords(order, P.num_parts);
     const int part = wc.part;
     const int j = wc.j;
-    const int s = wc.s;
+    // A device order entry outside the batch is never used as an index: the
+    // workgroup reads sequence 0's rows instead (always valid to read) and
+    // leaves at the validation below, having written nothing.
+    const bool order_ok = order_entry_ok(order, wc.s);
+    const int s = order_ok ? wc.s : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -398,6 +402,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
         if (len_ok && rel >= 0 && rel == my_idx && rel < slice) s_app_page = my_id;
     }
     bool ok = len_ok && (__syncthreads_or(bad) == 0);
+    if (!order_ok) {  // uniform over the workgroup
+        if (tid == 0 && P.flags) atomicOr(P.flags, kDevErrDispatchOrder);
+        return;
+    }
     if (ok && n_parts_s > 1) {
         int bad_row = 0;
         for (int b = tid; b < n_pages; b += kThreads) {
@@ -747,19 +755,20 @@ hipError_t launch_decode_i8(const DecodeLaunch &d, hipStream_t stream) {
     const bool level = blocks <= kPrioMaxBlocksI8;
     const dim3 grid(static_cast<unsigned>(blocks)), wg(64 * kDecodeWavesI8);
     auto go = [&](auto order) {
-        constexpr bool kOrd = !std::is_empty_v<decltype(order)>;
+        using Ord = decltype(order);
         constexpr int W = kDecodeWavesI8;
         if (d.fused) {
-            if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<W, true, false, true, kOrd>), grid, wg, 0, stream, P, order);
-            else if (level) hipLaunchKernelGGL((k_decode_paged_i8<W, true, true, true, kOrd>), grid, wg, 0, stream, P, order);
-            else hipLaunchKernelGGL((k_decode_paged_i8<W, true, true, false, kOrd>), grid, wg, 0, stream, P, order);
+            if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<W, true, false, true, Ord>), grid, wg, 0, stream, P, order);
+            else if (level) hipLaunchKernelGGL((k_decode_paged_i8<W, true, true, true, Ord>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged_i8<W, true, true, false, Ord>), grid, wg, 0, stream, P, order);
         } else {
-            if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<W, false, false, true, kOrd>), grid, wg, 0, stream, P, order);
-            else if (level) hipLaunchKernelGGL((k_decode_paged_i8<W, false, true, true, kOrd>), grid, wg, 0, stream, P, order);
-            else hipLaunchKernelGGL((k_decode_paged_i8<W, false, true, false, kOrd>), grid, wg, 0, stream, P, order);
+            if (!nt) hipLaunchKernelGGL((k_decode_paged_i8<W, false, false, true, Ord>), grid, wg, 0, stream, P, order);
+            else if (level) hipLaunchKernelGGL((k_decode_paged_i8<W, false, true, true, Ord>), grid, wg, 0, stream, P, order);
+            else hipLaunchKernelGGL((k_decode_paged_i8<W, false, true, false, Ord>), grid, wg, 0, stream, P, order);
         }
     };
     if (d.order) go(make_dispatch_order(d.order, d.num_seqs, d.num_parts));
+    else if (d.order_dev) go(DeviceOrder{d.order_dev, d.num_seqs});
     else go(DispatchOrder<false>{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || d.num_parts == 1) return e;

@@ -54,7 +54,8 @@ struct DecodeLaunch {
     float *ws_ml;         // [B][32][num_parts][2]  (max in log2 units, sum of weights)
     float *ws_acc;        // [B][32][num_parts][64]
     uint32_t *flags;
-    const int32_t *order; // host dispatch order (a checked permutation), or NULL for slot order
+    const int32_t *order; // host dispatch order (a checked permutation), or NULL
+    const int32_t *order_dev; // device dispatch order int32[num_seqs], or NULL (not with order)
 };
 
 struct PrefillLaunch {
@@ -83,6 +84,9 @@ int decode_part_pages();
 
 hipError_t launch_append_rope(const AppendLaunch &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+// A longest-first dispatch order of n <= kMaxDispatchOrder sequences, written
+// on the device from their device-resident lengths (pa_order_by_length).
+hipError_t launch_order_by_length(const int32_t *lens, int n, int max_blocks, int32_t *order, hipStream_t stream);
 hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream);
 
 // INT8 K/V pages (pa_i8.hip).  The tile pool travels in k_pool; v_pool is unused.

@@ -46,18 +46,18 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 11
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 12
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
 
 
 def decode_call(lib, out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, B=4, mb=8, P=64, ps=16, scale=0.125,
-                odt=0, ws=None, wsb=0, order=None):
+                odt=0, ws=None, wsb=0, order=None, dorder=None):
     v = ctypes.c_void_p
     op = None if order is None else np.ascontiguousarray(order, dtype=np.int32).ctypes.data_as(v)
     return lib.pa_decode_gqa(v(out), v(q), v(kp), v(vp), v(bt), v(cl), B, mb, P, ps, scale, odt, v(ws) if ws else None,
-                             wsb, None, op, None)
+                             wsb, None, op, v(dorder) if dorder else None, None)
 
 
 def test_decode_validation(pa):
@@ -100,6 +100,43 @@ def test_dispatch_order_validation(pa):
     assert decode_call(lib, ps=32, order=[3, 2, 1, 0]) == pa.PA_ERR_UNSUPPORTED
     assert decode_call(lib, q=0, order=[3, 2, 1, 0]) == pa.PA_ERR_INVALID_ARG
     assert decode_call(lib, B=0, q=0, out=0, order=[]) == pa.PA_OK
+
+
+def test_device_order_validation(pa):
+    """A device order is not checked on the host beyond its pointer: it may not come with a host
+    order, and it must be 16-byte aligned; with any number of sequences and partitions it is
+    otherwise accepted (the fake pointers below fail later checks, so nothing is launched)."""
+    lib = pa.lib()
+    assert decode_call(lib, order=[0, 1, 2, 3], dorder=FAKE) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, q=0, dorder=FAKE + 4) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, ps=32, dorder=FAKE) == pa.PA_ERR_UNSUPPORTED  # the order passes, the page size fails
+    pp = lib.pa_decode_partition_tokens() // 16
+    need = lib.pa_decode_workspace_bytes(2000, 70 * pp)
+    assert decode_call(lib, B=2000, mb=70 * pp, dorder=FAKE) == pa.PA_ERR_WORKSPACE  # no 1024-item bound
+    assert decode_call(lib, B=2000, mb=70 * pp, dorder=FAKE, ws=FAKE, wsb=need, q=0) == pa.PA_ERR_INVALID_ARG
+    assert decode_call(lib, B=0, q=0, out=0, dorder=FAKE) == pa.PA_OK
+
+
+def test_order_by_length_validation(pa):
+    """pa_order_by_length refuses, before launching anything, a batch beyond PA_MAX_DISPATCH_ORDER,
+    max_blocks < 1, NULL or misaligned arrays and overlapping arrays; an empty batch is a no-op."""
+    lib = pa.lib()
+    v = ctypes.c_void_p
+    F = FAKE
+
+    def call(lens=F, n=4, mb=8, order=F + 4096):
+        return lib.pa_order_by_length(v(lens) if lens else None, n, mb, v(order) if order else None, None)
+
+    assert call(n=-1) == pa.PA_ERR_INVALID_ARG
+    assert call(n=1025) == pa.PA_ERR_INVALID_ARG
+    assert call(mb=0) == pa.PA_ERR_INVALID_ARG
+    assert call(lens=0) == pa.PA_ERR_INVALID_ARG
+    assert call(order=0) == pa.PA_ERR_INVALID_ARG
+    assert call(lens=F + 4) == pa.PA_ERR_INVALID_ARG
+    assert call(order=F + 8) == pa.PA_ERR_INVALID_ARG
+    assert call(order=F) == pa.PA_ERR_INVALID_ARG            # the same array
+    assert call(order=F + 16, n=5) == pa.PA_ERR_INVALID_ARG  # 20 bytes each: they overlap
+    assert call(n=0, lens=0, order=0) == pa.PA_OK
 
 
 def test_dispatch_order_helper(pa):
@@ -178,7 +215,7 @@ def test_i8_validation(pa):
     assert app(B=0) == pa.PA_OK
 
     def dec(out=F, pool=F, B=4, mb=8, ps=16, odt=0, scale=0.125, ws=None, wsb=0):
-        return lib.pa_decode_gqa_i8(out, F, pool, F, F, B, mb, 64, ps, scale, odt, ws, wsb, None, None, None)
+        return lib.pa_decode_gqa_i8(out, F, pool, F, F, B, mb, 64, ps, scale, odt, ws, wsb, None, None, None, None)
 
     assert dec(ps=32) == pa.PA_ERR_UNSUPPORTED
     assert dec(odt=3) == pa.PA_ERR_UNSUPPORTED
@@ -191,7 +228,7 @@ def test_i8_validation(pa):
 
     def fused(rope=F, mp=64):
         return lib.pa_append_decode_gqa_i8(F, F, F, F, F, F, F, rope, 4, 8, 64, 16, mp, 0.125, 0, None, 0, None,
-                                           None, None)
+                                           None, None, None)
 
     assert fused(rope=None) == pa.PA_ERR_INVALID_ARG
     assert fused(mp=0) == pa.PA_ERR_INVALID_ARG
@@ -345,8 +382,15 @@ def test_dispatch_order_length_refused(pa):
             pa.decode_gqa_i8(out, q, i8, bt, lens, dispatch_order=bad)
         with pytest.raises(ValueError, match="exactly num_seqs"):
             pa.append_decode_gqa_i8(out, q, kn, kn, i8, bt, lens, table, dispatch_order=bad)
-    arr, ptr = pa._order(np.array([2, 0, 1], np.int32), B)
-    assert arr.shape == (3,) and ptr.value == arr.ctypes.data
+    arr, ptr, dptr = pa._order(np.array([2, 0, 1], np.int32), B)
+    assert arr.shape == (3,) and ptr.value == arr.ctypes.data and dptr is None
+    # a tensor is a device order: int32 of exactly num_seqs entries on the call's device
+    t = torch.tensor([2, 0, 1], dtype=torch.int32)
+    keep, ptr, dptr = pa._order(t, B, t.device)
+    assert keep is t and ptr is None and dptr.value == t.data_ptr()
+    for bad in (torch.tensor([1, 0], dtype=torch.int32), torch.tensor([2, 0, 1], dtype=torch.int64)):
+        with pytest.raises((ValueError, TypeError)):
+            pa.decode_gqa(out, q, kp, kp, bt, lens, dispatch_order=bad)
 
 
 def test_noalloc_size_limit(pa):
@@ -360,7 +404,7 @@ def test_noalloc_size_limit(pa):
 
     def na(B=4, mb=8, ps=16, mp=64, q=F, rope=F):
         return lib.pa_append_decode_gqa_noalloc(F, q, F, F, F, F, F, F, rope, B, mb, 64, ps, mp, 0.125, 0, None,
-                                                None, None)
+                                                None, None, None)
 
     assert lib.pa_decode_workspace_bytes(64, 16 * pp + 1) > pa.NOALLOC_SCRATCH_BYTES
     assert na(B=64, mb=16 * pp + 1) == pa.PA_ERR_WORKSPACE

@@ -78,5 +78,5 @@ def test_noalloc_refuses_oversize():
     assert binding.decode_workspace_bytes(B, mb) > binding.NOALLOC_SCRATCH_BYTES
     F = ctypes.c_void_p(0x7F0000000000)
     rc = lib.pa_append_decode_gqa_noalloc(F, F, F, F, F, F, F, F, F, B, mb, 1 << 16, 16, 4096, 0.125, 0, None, None,
-                                          None)
+                                          None, None)
     assert rc == binding.PA_ERR_WORKSPACE
