@@ -40,18 +40,25 @@ __global__ __launch_bounds__(kOrderThreads) void k_order_by_length(const int32_t
     const int lane = t & 63;
     const int w = t >> 6;
     const int cw = (max_blocks + kOrderClasses - 1) / kOrderClasses;
-    int cls = -1;
+    int cls = kOrderClasses;  // past the last class: no sequence
     if (t < n) {
         const int64_t L = lens[t];
         cls = (L >= 1 && L <= static_cast<int64_t>(max_blocks) * kPage)
                   ? static_cast<int>(((L + kPage - 1) / kPage - 1) / cw) : 0;
     }
-    int within = 0;  // members of this sequence's class in this wave, below this lane
-    for (int v = 0; v < kOrderClasses; ++v) {
-        const uint64_t m = __ballot(cls == v);
-        if (cls == v) within = lanes_below(m);
-        if (lane == 0) s_cnt[v][w] = __popcll(m);
+    s_cnt[t / kOrderWaves][t % kOrderWaves] = 0;
+    // The lanes of this wave in the same class as this lane, bit-sliced: one
+    // ballot per bit of the class (7 bits: 64 classes and "none"), and this
+    // lane keeps the lanes that agree with it on every bit.
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+        const uint64_t bk = __ballot((cls >> k) & 1);
+        same &= ((cls >> k) & 1) ? bk : ~bk;
     }
+    const int within = lanes_below(same);  // members of its class in this wave, below this lane
+    __syncthreads();
+    if (cls < kOrderClasses && within == 0) s_cnt[cls][w] = __popcll(same);
     __syncthreads();
     // Exclusive scan of the counts in rank order (class descending, wave
     // ascending): thread k holds entry k of that order.  Within a wave the
