@@ -74,8 +74,13 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P,
     // Issue priority starts high and steps down as the wave's pages run out
     // (see the main loop): two workgroups share each CU, and age-ordered
     // arbitration alone lets the older one finish far ahead of the younger,
-    // which then streams alone with half the loads in flight.
-    __builtin_amdgcn_s_setprio(3);
+    // which then streams alone with half the loads in flight.  Launches given
+    // a dispatch order (longest first, for ragged batches) run faster without
+    // it (ragged 256-sequence batch, device order: 59.0 -> 58.1 us), launches
+    // in slot order with it (the same batch 62.9 -> 61.5 us, batch 64 44.2 ->
+    // 44.0 us), so only those level.
+    constexpr bool kLevel = std::is_same_v<Ord, DispatchOrder<false>>;
+    if (kLevel) __builtin_amdgcn_s_setprio(3);
 
     __shared__ int s_app_page;  // fused: page of the appended token (last partition)
     __shared__ float s_m[kWaves][kGroup];
@@ -286,6 +291,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged(DecodeParams P,
     // level and catches up, so both end close together.
     const int span = pg1 - pg0;
     auto level = [&]() {
+        if (!kLevel) return;
         const int done16 = 16 * (p - pg0);
         if (done16 >= 15 * span) __builtin_amdgcn_s_setprio(0);
         else if (done16 >= 13 * span) __builtin_amdgcn_s_setprio(1);
