@@ -5,37 +5,37 @@
 // table names for its position, at the absolute RoPE position.  One workgroup
 // per appended token: it resolves (page, slot) once, rotates the 8 K heads and
 // (optionally) the 32 q heads with the fp64 cos/sin table row of that
-// position (rope_pair_bf16), and copies V verbatim.  The kernel moves ~6 KiB per token, so it is
-// bound by launch latency, not bandwidth; it stays simple and fully coalesced
-// (consecutive lanes touch consecutive bf16 elements).
+// position (rope_pair_bf16), and copies V verbatim.  The kernel moves ~10 KiB per token with q, so
+// it is bound by latency (length, then block table, then stores), not
+// bandwidth; its accesses are fully coalesced (consecutive lanes touch
+// consecutive bf16 elements).
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 
-// Rotate-half pairs i0 .. i0+3 of a row (with their partners i0+32 .. i0+35)
-// by the (cos, sin) entries cs[2i], cs[2i+1] (rope_pair_bf16): 8-byte row loads
-// and stores, 16-byte table loads.
-__device__ __forceinline__ void rope_unit4(const uint16_t *src, uint16_t *dst, int i0, const double *cs) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(src + i0);
-    const uint2 b = *reinterpret_cast<const uint2 *>(src + i0 + kD / 2);
-    const double2 t0 = *reinterpret_cast<const double2 *>(cs + 2 * i0);
-    const double2 t1 = *reinterpret_cast<const double2 *>(cs + 2 * i0 + 2);
-    const double2 t2 = *reinterpret_cast<const double2 *>(cs + 2 * i0 + 4);
-    const double2 t3 = *reinterpret_cast<const double2 *>(cs + 2 * i0 + 6);
+// Rotate-half pairs i0 .. i0+3 of a row held as a = elements i0 .. i0+3 and
+// b = their partners i0+32 .. i0+35 (8 bytes each) by the (cos, sin) entries
+// t[k] of pair i0 + k (rope_pair_bf16); the rotated halves, packed the same way.
+__device__ __forceinline__ void rope4(uint2 a, uint2 b, const double2 (&t)[4], uint2 &lo_out, uint2 &hi_out) {
     uint16_t lo[4], hi[4];
-    rope_pair_bf16(bf16_lo(a.x), bf16_lo(b.x), t0.x, t0.y, lo[0], hi[0]);
-    rope_pair_bf16(bf16_hi(a.x), bf16_hi(b.x), t1.x, t1.y, lo[1], hi[1]);
-    rope_pair_bf16(bf16_lo(a.y), bf16_lo(b.y), t2.x, t2.y, lo[2], hi[2]);
-    rope_pair_bf16(bf16_hi(a.y), bf16_hi(b.y), t3.x, t3.y, lo[3], hi[3]);
-    *reinterpret_cast<uint2 *>(dst + i0) = uint2{lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16)};
-    *reinterpret_cast<uint2 *>(dst + i0 + kD / 2) =
-        uint2{hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16)};
+    rope_pair_bf16(bf16_lo(a.x), bf16_lo(b.x), t[0].x, t[0].y, lo[0], hi[0]);
+    rope_pair_bf16(bf16_hi(a.x), bf16_hi(b.x), t[1].x, t[1].y, lo[1], hi[1]);
+    rope_pair_bf16(bf16_lo(a.y), bf16_lo(b.y), t[2].x, t[2].y, lo[2], hi[2]);
+    rope_pair_bf16(bf16_hi(a.y), bf16_hi(b.y), t[3].x, t[3].y, lo[3], hi[3]);
+    lo_out = uint2{lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16)};
+    hi_out = uint2{hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16)};
 }
 
 // token = blockIdx.x = s * tokens_per_seq + i.
 //   decode (prefix_mode == 0): pos = lens[s] - 1   (tokens_per_seq == 1)
 //   prefill (prefix_mode == 1): pos = lens[s] + i  (lens holds prefix lengths)
+// Work in units of 4 pairs: K is 8 heads x 8 units (threads 0..63), V 8 heads
+// x 8 sixteen-byte chunks copied verbatim (threads 64..127), q 32 heads x 8
+// units in place (one per thread).  The rows depend on the token alone, so
+// their loads go out first, beside the length's; the table row waits for the
+// length and the stores for the page id, and a token that fails either check
+// writes nothing.
 __global__ __launch_bounds__(256) void k_append_rope(uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
                                                      const uint16_t *__restrict__ v_new, uint16_t *__restrict__ k_pool,
                                                      uint16_t *__restrict__ v_pool, const int32_t *__restrict__ bt,
@@ -45,40 +45,53 @@ __global__ __launch_bounds__(256) void k_append_rope(uint16_t *__restrict__ q, c
     const int tok = blockIdx.x;
     const int s = tok / tokens_per_seq;
     const int i = tok - s * tokens_per_seq;
+    const int t = threadIdx.x;
+    const int i0 = 4 * (t & 7);
+    const int j = (t >> 3) & (kHKV - 1);
     const int64_t len = lens[s];
+    uint2 qa{0u, 0u}, qb{0u, 0u}, ka{0u, 0u}, kb{0u, 0u};
+    u32x4 vv{0u, 0u, 0u, 0u};
+    uint16_t *qrow = q ? q + (static_cast<int64_t>(tok) * kHQ + (t >> 3)) * kD : nullptr;
+    if (q) {
+        qa = *reinterpret_cast<const uint2 *>(qrow + i0);
+        qb = *reinterpret_cast<const uint2 *>(qrow + i0 + kD / 2);
+    }
+    const int64_t krow = (static_cast<int64_t>(tok) * kHKV + j) * kD;
+    if (t < 64) {
+        ka = *reinterpret_cast<const uint2 *>(k_new + krow + i0);
+        kb = *reinterpret_cast<const uint2 *>(k_new + krow + i0 + kD / 2);
+    } else if (t < 128) {
+        vv = reinterpret_cast<const u32x4 *>(v_new + krow)[t & 7];
+    }
     const int64_t pos = prefix_mode ? len + i : len - 1;
     const bool bad_len = prefix_mode ? (len < 0) : (len < 1);
     if (bad_len || pos >= static_cast<int64_t>(max_blocks) * kPage || pos >= max_pos) {
-        if (threadIdx.x == 0 && flags) atomicOr(flags, kDevErrContextLen);
+        if (t == 0 && flags) atomicOr(flags, kDevErrContextLen);
         return;
     }
     const int page = bt[static_cast<int64_t>(s) * max_blocks + (pos >> 4)];
+    const double *cs = rope + pos * kD + 2 * i0;  // pairs i0 .. i0+3 of [32][2]
+    const double2 tb[4] = {reinterpret_cast<const double2 *>(cs)[0], reinterpret_cast<const double2 *>(cs)[1],
+                           reinterpret_cast<const double2 *>(cs)[2], reinterpret_cast<const double2 *>(cs)[3]};
     if (page < 0 || page >= num_pages) {
-        if (threadIdx.x == 0 && flags) atomicOr(flags, kDevErrPageId);
+        if (t == 0 && flags) atomicOr(flags, kDevErrPageId);
         return;
     }
     const int slot = static_cast<int>(pos & (kPage - 1));
-    const double *cs = rope + pos * kD;  // [32][2]
-    const int t = threadIdx.x;
-
-    // Work in units of 4 pairs: K is 8 heads x 8 units (threads 0..63), V 8 heads
-    // x 8 sixteen-byte chunks copied verbatim (threads 64..127), q 32 heads x 8
-    // units in place (one per thread).
+    const int64_t prow = ((static_cast<int64_t>(page) * kHKV + j) * kPage + slot) * kD;
     if (t < 64) {
-        const int j = t >> 3, i0 = 4 * (t & 7);
-        const uint16_t *src = k_new + (static_cast<int64_t>(tok) * kHKV + j) * kD;
-        uint16_t *dst = k_pool + ((static_cast<int64_t>(page) * kHKV + j) * kPage + slot) * kD;
-        rope_unit4(src, dst, i0, cs);
+        uint2 lo, hi;
+        rope4(ka, kb, tb, lo, hi);
+        *reinterpret_cast<uint2 *>(k_pool + prow + i0) = lo;
+        *reinterpret_cast<uint2 *>(k_pool + prow + i0 + kD / 2) = hi;
     } else if (t < 128) {
-        const int j = (t - 64) >> 3, c = (t - 64) & 7;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(v_new + (static_cast<int64_t>(tok) * kHKV + j) * kD);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(v_pool + ((static_cast<int64_t>(page) * kHKV + j) * kPage + slot) * kD);
-        dst[c] = src[c];
+        reinterpret_cast<u32x4 *>(v_pool + prow)[t & 7] = vv;
     }
     if (q) {
-        const int h = t >> 3, i0 = 4 * (t & 7);
-        uint16_t *row = q + (static_cast<int64_t>(tok) * kHQ + h) * kD;
-        rope_unit4(row, row, i0, cs);
+        uint2 lo, hi;
+        rope4(qa, qb, tb, lo, hi);
+        *reinterpret_cast<uint2 *>(qrow + i0) = lo;
+        *reinterpret_cast<uint2 *>(qrow + i0 + kD / 2) = hi;
     }
 }
 
