@@ -47,6 +47,10 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0
 # decode workgroups resident at once: 2 per CU (8 waves each, at most 4 waves per SIMD), 256 CUs
 RESIDENT_DECODE_WGS = 512
+# (long_run, short_run) of the ragged steps' device order, per page format: ragged batches of 256
+# sequences over four seeds, us per launch against plain longest first (1, 0): bf16 (3, 2) 2.3-2.6 %
+# faster, (2, 1) 1.2-2.0 %, (1, 1) 7 % slower; INT8 (4, 1) 0-1 % faster, (3, 2) and (3, 1) slower.
+ORDER_RUNS = {"bf16": (3, 2), "int8": (4, 1)}
 # sources each fused decode kernel is compiled from (its traffic figure is tied to them),
 # and the committed rocprofv3 summary that holds that figure
 TRAFFIC = {
@@ -427,12 +431,16 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
     # dispatched longest first, from an order computed on the device from the device-resident
     # lengths once per step (pa_order_by_length, inside the timed step) and read by every
     # layer's launch; a smaller batch starts all its workgroups at once and runs in slot order.
+    # The order deals the ranked sequences in runs from the long and the short end (ORDER_RUNS,
+    # measured per page format on four seeded ragged batches).
     parts = -(-spec.max_blocks * 16 // binding.decode_partition_tokens())
     use_order = spec.num_seqs * 8 * parts > RESIDENT_DECODE_WGS
     order_buf = torch.empty(spec.num_seqs, dtype=torch.int32, device=device)
+    runs = ORDER_RUNS[kv]
 
     def make_order():
-        return binding.order_by_length(lens, spec.max_blocks, order_buf, stream=stream) if use_order else None
+        return (binding.order_by_length(lens, spec.max_blocks, order_buf, *runs, stream=stream)
+                if use_order else None)
 
     def step_fused(order=None):
         for l in range(spec.num_layers):
@@ -516,8 +524,9 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
                             if not separate else
                             "per layer: pa_append_kv_rope%s then pa_decode_gqa%s" % (sfx, sfx)),
                    "decode_partition_tokens": binding.decode_partition_tokens(),
-                   "dispatch": ("longest first: pa_order_by_length on the device once per step (in the timed "
-                                "step), its order passed to every layer's launch" if use_order else "slot order")},
+                   "dispatch": (f"longest first, dealt in runs of {runs[0]} long and {runs[1]} short sequences: "
+                                "pa_order_by_length on the device once per step (in the timed step), its order "
+                                "passed to every layer's launch" if use_order else "slot order")},
         "kv_bytes_per_step": kv_step,
         "roofline": {"bound": "hbm",
                      "kernel": ("k_decode_paged_i8<8,true,nt> (pa_append_decode_gqa_i8)" if i8 else

@@ -115,7 +115,7 @@ int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t s
  * from, so a caller can refuse a library built from another header.  Like the
  * fixed geometry (samir-vllm, section "Limitations et perspectives": changing
  * the architecture means recompiling), a mismatch is refused, not adapted to. */
-#define PA_ABI_VERSION 12
+#define PA_ABI_VERSION 13
 int32_t pa_abi_version(void);
 
 /* Identity of the sources the library was built from: the sha256 (64 hex
@@ -212,19 +212,26 @@ pa_status pa_dispatch_order_longest_first(const int32_t *lengths, int32_t n, int
  * continuous-batching decode batch mixes contexts of very different lengths:
  * samir-vllm, "Gestion de la KV cache et strategies de batching", admission as
  * soon as a request's page budget is free).  Writes order[0 .. num_seqs-1]
- * (DEVICE int32) from context_lens (DEVICE int32[num_seqs]): the sequences by
- * length class, longest class first, index order within a class, where class
- * c of a valid length L (1 <= L <= 16 * max_blocks) is (ceil(L/16) - 1) /
- * ceil(max_blocks/64), 64 classes across the table width; an invalid length
- * has class 0, the last (the decode rejects it as usual).  Pass the result as
- * device_order to every decode of the step: starting the long contexts first
- * keeps them from forming the launch's tail, and changes no result.  One
- * workgroup on `stream`, nothing allocated; the lengths must not change
- * between this call and the decodes that use its order (stream order).
- * PA_ERR_INVALID_ARG for num_seqs outside [0, PA_MAX_DISPATCH_ORDER],
- * max_blocks < 1, a NULL or misaligned array, or arrays that overlap.        */
-pa_status pa_order_by_length(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t *order,
-                             hipStream_t stream);
+ * (DEVICE int32) from context_lens (DEVICE int32[num_seqs]).  The sequences
+ * are ranked by length class, longest class first, index order within a
+ * class, where class c of a valid length L (1 <= L <= 16 * max_blocks) is
+ * (ceil(L/16) - 1) / ceil(max_blocks/64), 64 classes across the table width;
+ * an invalid length has class 0, the last (the decode rejects it as usual).
+ * The ranks are then dealt in runs: long_run sequences from the long end,
+ * short_run from the short end, and again, until the two ends meet (1, 0 is
+ * plain longest first; with 3, 2 a batch of 10 is ranks 0 1 2 9 8 3 4 5 7 6).
+ * Mixing a few short sequences in among the long ones keeps the CUs streaming
+ * while the short ones pay their fixed costs, and the launch still ends on
+ * short sequences.  Pass the result as device_order to every decode of the
+ * step; no result changes.  One workgroup on `stream`, nothing allocated; the
+ * lengths must not change between this call and the decodes that use its
+ * order (stream order).  PA_ERR_INVALID_ARG for num_seqs outside [0,
+ * PA_MAX_DISPATCH_ORDER], max_blocks < 1, long_run outside [1,
+ * PA_MAX_ORDER_RUN], short_run outside [0, PA_MAX_ORDER_RUN], a NULL or
+ * misaligned array, or arrays that overlap.                                  */
+#define PA_MAX_ORDER_RUN 64
+pa_status pa_order_by_length(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t long_run,
+                             int32_t short_run, int32_t *order, hipStream_t stream);
 
 /* Paged GQA decode (samir-vllm, batched-decode paragraph of "Gestion de la KV
  * cache ..."; tiny-vllm ch.2, "One buffer, two roles": the attention output is

@@ -37,7 +37,7 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 
 class PaError(RuntimeError):
@@ -122,7 +122,7 @@ def lib():
     L.pa_dispatch_order_longest_first.restype = ctypes.c_int
     L.pa_dispatch_order_longest_first.argtypes = [P, i32, P]
     L.pa_order_by_length.restype = ctypes.c_int
-    L.pa_order_by_length.argtypes = [P, i32, i32, P, P]
+    L.pa_order_by_length.argtypes = [P, i32, i32, i32, i32, P, P]
     L.pa_probe_stream_read.restype = ctypes.c_int
     L.pa_probe_stream_read.argtypes = [P, u64, P, P]
     L.pa_get_device_error.restype = i32
@@ -574,10 +574,12 @@ def dispatch_order_longest_first(lengths) -> np.ndarray:
 
 
 def order_by_length(context_lens: torch.Tensor, max_blocks: int, order: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
-    """pa_order_by_length: the sequences longest first (64 length classes across max_blocks pages,
-    index order within a class), computed on the device into ``order`` (int32[num_seqs], a new
-    tensor when None).  Pass it as ``dispatch_order`` to the decode calls of the step."""
+                    long_run: int = 1, short_run: int = 0, stream=None) -> torch.Tensor:
+    """pa_order_by_length: the sequences ranked longest first (64 length classes across
+    max_blocks pages, index order within a class) and dealt in runs of ``long_run`` from the
+    long end and ``short_run`` from the short end, computed on the device into ``order``
+    (int32[num_seqs], a new tensor when None).  Pass it as ``dispatch_order`` to the decode calls
+    of the step."""
     _expect(context_lens, "context_lens", torch.int32)
     if context_lens.dim() != 1:
         raise ValueError("context_lens must be [num_seqs]")
@@ -585,8 +587,8 @@ def order_by_length(context_lens: torch.Tensor, max_blocks: int, order: Optional
     if order is None:
         order = torch.empty(n, dtype=torch.int32, device=context_lens.device)
     _expect(order, "order", torch.int32, (n,), context_lens.device)
-    _check(lib().pa_order_by_length(_ptr(context_lens), n, int(max_blocks), _ptr(order), _stream(stream)),
-           "pa_order_by_length")
+    _check(lib().pa_order_by_length(_ptr(context_lens), n, int(max_blocks), int(long_run), int(short_run),
+                                    _ptr(order), _stream(stream)), "pa_order_by_length")
     return order
 
 

@@ -355,16 +355,20 @@ pa_status pa_dispatch_order_longest_first(const int32_t *lengths, int32_t n, int
     return PA_OK;
 }
 
-pa_status pa_order_by_length(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t *order,
-                             hipStream_t stream) {
+pa_status pa_order_by_length(const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t long_run,
+                             int32_t short_run, int32_t *order, hipStream_t stream) {
     if (num_seqs < 0 || num_seqs > PA_MAX_DISPATCH_ORDER || max_blocks < 1) return PA_ERR_INVALID_ARG;
+    if (long_run < 1 || long_run > PA_MAX_ORDER_RUN || short_run < 0 || short_run > PA_MAX_ORDER_RUN)
+        return PA_ERR_INVALID_ARG;
     if (num_seqs == 0) return PA_OK;
     if (!context_lens || !order || !aligned16(context_lens) || !aligned16(order)) return PA_ERR_INVALID_ARG;
     const uintptr_t a = reinterpret_cast<uintptr_t>(context_lens), b = reinterpret_cast<uintptr_t>(order);
     const uintptr_t bytes = static_cast<uintptr_t>(num_seqs) * sizeof(int32_t);
     if (a < b + bytes && b < a + bytes) return PA_ERR_INVALID_ARG;
-    return pa::launch_order_by_length(context_lens, num_seqs, max_blocks, order, stream) == hipSuccess ? PA_OK
-                                                                                                       : PA_ERR_HIP;
+    return pa::launch_order_by_length(context_lens, num_seqs, max_blocks, long_run, short_run, order, stream) ==
+                   hipSuccess
+               ? PA_OK
+               : PA_ERR_HIP;
 }
 
 pa_status pa_probe_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {

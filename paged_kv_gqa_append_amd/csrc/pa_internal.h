@@ -85,8 +85,10 @@ int decode_part_pages();
 hipError_t launch_append_rope(const AppendLaunch &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 // A longest-first dispatch order of n <= kMaxDispatchOrder sequences, written
-// on the device from their device-resident lengths (pa_order_by_length).
-hipError_t launch_order_by_length(const int32_t *lens, int n, int max_blocks, int32_t *order, hipStream_t stream);
+// on the device from their device-resident lengths, dealt in runs of long_run
+// long and short_run short sequences (pa_order_by_length).
+hipError_t launch_order_by_length(const int32_t *lens, int n, int max_blocks, int long_run, int short_run,
+                                  int32_t *order, hipStream_t stream);
 hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream);
 
 // INT8 K/V pages (pa_i8.hip).  The tile pool travels in k_pool; v_pool is unused.

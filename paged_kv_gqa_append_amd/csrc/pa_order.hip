@@ -30,9 +30,19 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // Rank = (longer classes first) + (same class, lower index first).  A class
 // spans cw = ceil(max_blocks / 64) pages: sequence s with 1 <= L <= 16 *
 // max_blocks has class (ceil(L / 16) - 1) / cw; a length outside that range
-// (which the decode rejects) has class 0, the last.  order[rank] = s.
+// (which the decode rejects) has class 0, the last.  The ranks are then dealt
+// in runs: long_run from the long end, short_run from the short end, and so
+// on until the two meet; order[position] = s.
+__device__ __forceinline__ int mixed_position(int r, int n, int k, int m) {
+    const int G = n / (k + m), R = n % (k + m);
+    const int from_long = G * k + min(R, k);  // ranks dealt from the long end
+    if (r < from_long) return (r / k) * (k + m) + r % k;
+    const int t = n - 1 - r;  // 0 = the shortest
+    return (t / m) * (k + m) + k + t % m;
+}
+
 __global__ __launch_bounds__(kOrderThreads) void k_order_by_length(const int32_t *lens, int n, int max_blocks,
-                                                                   int32_t *order) {
+                                                                   int long_run, int short_run, int32_t *order) {
     __shared__ int s_cnt[kOrderClasses][kOrderWaves];   // members of class v among wave w's sequences
     __shared__ int s_base[kOrderClasses][kOrderWaves];  // rank of the first of them
     __shared__ int s_scan_total[kOrderWaves];
@@ -75,14 +85,16 @@ __global__ __launch_bounds__(kOrderThreads) void k_order_by_length(const int32_t
     for (int x = 0; x < w; ++x) pre += s_scan_total[x];
     s_base[v][ww] = pre;
     __syncthreads();
-    if (t < n) order[s_base[cls][w] + within] = t;
+    if (t < n) order[mixed_position(s_base[cls][w] + within, n, long_run, short_run)] = t;
 }
 
 }  // namespace
 
-hipError_t launch_order_by_length(const int32_t *lens, int n, int max_blocks, int32_t *order, hipStream_t stream) {
+hipError_t launch_order_by_length(const int32_t *lens, int n, int max_blocks, int long_run, int short_run,
+                                  int32_t *order, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_order_by_length, dim3(1), dim3(kOrderThreads), 0, stream, lens, n, max_blocks, order);
+    hipLaunchKernelGGL(k_order_by_length, dim3(1), dim3(kOrderThreads), 0, stream, lens, n, max_blocks, long_run,
+                       short_run, order);
     return hipGetLastError();
 }
 

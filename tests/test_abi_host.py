@@ -46,7 +46,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 12
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 13
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -119,15 +119,19 @@ def test_device_order_validation(pa):
 
 def test_order_by_length_validation(pa):
     """pa_order_by_length refuses, before launching anything, a batch beyond PA_MAX_DISPATCH_ORDER,
-    max_blocks < 1, NULL or misaligned arrays and overlapping arrays; an empty batch is a no-op."""
+    max_blocks < 1, runs outside [1, 64] (long) or [0, 64] (short), NULL or misaligned arrays and
+    overlapping arrays; an empty batch is a no-op."""
     lib = pa.lib()
     v = ctypes.c_void_p
     F = FAKE
 
-    def call(lens=F, n=4, mb=8, order=F + 4096):
-        return lib.pa_order_by_length(v(lens) if lens else None, n, mb, v(order) if order else None, None)
+    def call(lens=F, n=4, mb=8, order=F + 4096, k=1, m=0):
+        return lib.pa_order_by_length(v(lens) if lens else None, n, mb, k, m, v(order) if order else None, None)
 
     assert call(n=-1) == pa.PA_ERR_INVALID_ARG
+    for k, m in ((0, 0), (-1, 1), (65, 0), (1, -1), (1, 65)):
+        assert call(k=k, m=m) == pa.PA_ERR_INVALID_ARG, (k, m)
+        assert call(k=k, m=m, n=0, lens=0, order=0) == pa.PA_ERR_INVALID_ARG, (k, m)
     assert call(n=1025) == pa.PA_ERR_INVALID_ARG
     assert call(mb=0) == pa.PA_ERR_INVALID_ARG
     assert call(lens=0) == pa.PA_ERR_INVALID_ARG

@@ -5,7 +5,8 @@ dispatch_order).
 
 The order itself is integer work, checked exactly: it is the unique stable
 ordering by the header's length classes (longest class first, index order
-inside a class), so it equals numpy's stable sort on those classes, for
+inside a class), dealt in the header's runs from the long and the short end,
+so it equals numpy's stable sort on those classes dealt the same way, for
 batches of 1 to 1024 sequences, table widths whose classes hold 1 to 64 pages,
 and lengths that are invalid (placed last).  An order moves work in time and
 nothing else, so decodes dispatched by it give the bits of slot order: out,
@@ -25,19 +26,39 @@ from paged_kv_gqa_append_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def expected_order(lens, max_blocks):
+def expected_order(lens, max_blocks, long_run=1, short_run=0):
     """The order the header defines: 64 classes of ceil(max_blocks / 64) pages; class of a valid
-    length L: (ceil(L / 16) - 1) // width; invalid lengths class 0; stable, longest class first."""
+    length L: (ceil(L / 16) - 1) // width; invalid lengths class 0; stable, longest class first;
+    then dealt long_run from the long end, short_run from the short end, until the ends meet."""
     lens = np.asarray(lens, dtype=np.int64)
     width = -(-max_blocks // 64)
     valid = (lens >= 1) & (lens <= 16 * max_blocks)
     cls = np.where(valid, (-(-lens // 16) - 1) // width, 0)
-    return np.lexsort((np.arange(len(lens)), -cls)).astype(np.int32), cls
+    ranked = np.lexsort((np.arange(len(lens)), -cls)).astype(np.int32)
+    out, a, b = [], 0, len(ranked) - 1
+    while a <= b:
+        for _ in range(long_run):
+            if a <= b:
+                out.append(ranked[a])
+                a += 1
+        for _ in range(short_run):
+            if a <= b:
+                out.append(ranked[b])
+                b -= 1
+    return np.array(out, dtype=np.int32), cls
+
+
+def test_expected_order_runs():
+    """The run rule on the header's own example: with runs 3, 2, ten sequences ranked 0..9 are
+    dealt 0 1 2 9 8 3 4 5 7 6."""
+    lens = 16 * np.arange(10, 0, -1) * 8  # ten distinct classes, longest first
+    assert expected_order(lens, 128, 3, 2)[0].tolist() == [0, 1, 2, 9, 8, 3, 4, 5, 7, 6]
 
 
 @pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 256, 1000, 1024])
 @pytest.mark.parametrize("max_blocks", [1, 8, 64, 65, 128, 129, 4096])
-def test_order_by_length_exact(n, max_blocks):
+@pytest.mark.parametrize("runs", [(1, 0), (3, 2), (1, 1), (4, 1), (64, 64)])
+def test_order_by_length_exact(n, max_blocks, runs):
     rng = np.random.default_rng(n * 7919 + max_blocks)
     top = 16 * max_blocks
     lens = rng.integers(1, top + 1, size=n)
@@ -45,12 +66,13 @@ def test_order_by_length_exact(n, max_blocks):
     lens = np.where(k < 0.1, rng.choice([0, -7, top + 1, 2**31 - 1, -2**31], size=n), lens)  # invalid ones
     lens = np.where((k >= 0.1) & (k < 0.2), rng.choice([1, 16, 17, top], size=n), lens)  # edges
     lens = lens.astype(np.int32)
-    want, cls = expected_order(lens, max_blocks)
+    want, cls = expected_order(lens, max_blocks, *runs)
     order = guarded_empty((n,), torch.int32)
-    binding.order_by_length(to_dev_i32(lens), max_blocks, order)
+    binding.order_by_length(to_dev_i32(lens), max_blocks, order, *runs)
     got = order.cpu().numpy()
     assert np.array_equal(np.sort(got), np.arange(n)), "not a permutation"
-    assert np.all(np.diff(cls[got]) <= 0), "classes not descending"
+    if runs[1] == 0:
+        assert np.all(np.diff(cls[got]) <= 0), "classes not descending"
     assert np.array_equal(got, want)
 
 
@@ -80,7 +102,8 @@ def run(case, kv, fused, order, pool_i8, table, lens=None, noalloc=False):
     ws = guarded_workspace(case.num_seqs, case.max_blocks)
     flags = guarded_flags()
     if isinstance(order, str):  # computed on the device from the lengths the decode reads
-        order = binding.order_by_length(dlens, case.max_blocks, guarded_empty((case.num_seqs,), torch.int32))
+        runs = (3, 2) if order == "device32" else (1, 0)
+        order = binding.order_by_length(dlens, case.max_blocks, guarded_empty((case.num_seqs,), torch.int32), *runs)
     kw = dict(dispatch_order=order, device_flags=flags)
     if noalloc:
         binding.append_decode_gqa_noalloc(out, q, kn, vn, pools[0], pools[1], dbt, dlens, table, case.scale, **kw)
@@ -128,7 +151,7 @@ def test_device_order_equals_slot_order(name, kv, fused):
     base = run(case, kv, fused, None, pool_i8, table)
     assert base[3] == 0
     perm = np.random.default_rng(n).permutation(n).astype(np.int32)
-    for what, order in (("order_by_length", "device"), ("random", to_dev_i32(perm))):
+    for what, order in (("order_by_length", "device"), ("runs 3, 2", "device32"), ("random", to_dev_i32(perm))):
         assert_same(base, run(case, kv, fused, order, pool_i8, table), f"{name} {kv} fused={fused} {what}")
     if not fused:
         if kv == "int8":
