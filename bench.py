@@ -286,18 +286,25 @@ def prefill_flops(prefix_lens, chunk_len):
     return pairs * 32 * 4 * 64, pairs * 32
 
 
-def cpu_baseline_prefill(case, target_s):
+def cpu_baseline_prefill(case, target_s, kv="bf16"):
     """Time the fp64 oracle's chunked prefill on whole sequences of the workload."""
     import oracle
 
     total, done, flops = 0.0, 0, 0
+    pool_i8 = oracle.quantize_pages_i8(case.k_pool, case.v_pool) if kv == "int8" else None
     for s in range(case.num_seqs):
         one = lambda a: np.ascontiguousarray(a[s:s + 1])
         kp, vp = case.k_pool.copy(), case.v_pool.copy()
+        pool = None if pool_i8 is None else pool_i8.copy()
         t0 = time.perf_counter()
-        _, rc = oracle.prefill_chunk(one(case.q).copy(), one(case.k_chunk), one(case.v_chunk), kp, vp,
-                                     one(case.block_tables), one(case.prefix_lens), case.num_pages, case.theta,
-                                     case.scale)
+        if kv == "int8":
+            _, rc = oracle.prefill_chunk_i8(one(case.q).copy(), one(case.k_chunk), one(case.v_chunk), pool,
+                                            one(case.block_tables), one(case.prefix_lens), case.num_pages,
+                                            case.theta, case.scale)
+        else:
+            _, rc = oracle.prefill_chunk(one(case.q).copy(), one(case.k_chunk), one(case.v_chunk), kp, vp,
+                                         one(case.block_tables), one(case.prefix_lens), case.num_pages, case.theta,
+                                         case.scale)
         total += time.perf_counter() - t0
         assert rc == oracle.OK
         done += 1
@@ -306,8 +313,9 @@ def cpu_baseline_prefill(case, target_s):
             break
     return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "cpu_model": host_cpu_model(), "kind": "oracle", "seconds": round(total, 3),
-            "sample": f"fp64 oracle chunked prefill (append + causal attention) of {done} of the {case.num_seqs} "
-                      f"sequences of the workload ({flops} algorithmic flops)"}
+            "sample": f"fp64 oracle chunked prefill{' into INT8 pages' if kv == 'int8' else ''} (append + causal "
+                      f"attention) of {done} of the {case.num_seqs} sequences of the workload ({flops} algorithmic "
+                      "flops)"}
 
 
 
@@ -580,10 +588,11 @@ def run_decode(name, kv, args, torch, binding, device, *, headline, cpu_seconds)
     return res
 
 
-def run_prefill(args, torch, binding, device, *, cpu_seconds):
+def run_prefill(args, torch, binding, device, *, cpu_seconds, kv="bf16"):
     """One step = one pa_prefill_chunk call: append the 4 x 512 chunk rows
     (K rotated into pages, q rotated in place), then causal MFMA attention of
-    every chunk row over its 1536 + i + 1 keys."""
+    every chunk row over its 1536 + i + 1 keys.  kv="int8": pa_prefill_chunk_i8
+    over an INT8 pool quantised from the same pages before timing."""
     from paged_kv_gqa_append_amd import workloads as W
 
     c = W.prefill_config()
@@ -598,10 +607,19 @@ def run_prefill(args, torch, binding, device, *, cpu_seconds):
     table = binding.rope_table(2048 + 64, c.theta, device)
     stream = torch.cuda.current_stream()
 
+    pool = None
+    if kv == "int8":
+        pool = binding.i8_pool(c.num_pages, device)
+        binding.quantize_pages_i8(pool, kp, vp)
+        torch.cuda.synchronize()
+
     # q is rotated in place by every call (a norm-preserving rotation, so its
     # values stay N(0,1)-like); the chunk rows are re-appended at the same slots.
     def step():
-        binding.prefill_chunk(out, q, kc, vc, kp, vp, bt, prefix, table, c.scale, stream=stream)
+        if pool is not None:
+            binding.prefill_chunk_i8(out, q, kc, vc, pool, bt, prefix, table, c.scale, stream=stream)
+        else:
+            binding.prefill_chunk(out, q, kc, vc, kp, vp, bt, prefix, table, c.scale, stream=stream)
 
     warm = warm_up(step, torch, args.warmup)
     calls = []
@@ -622,12 +640,16 @@ def run_prefill(args, torch, binding, device, *, cpu_seconds):
         "steps": args.steps,
         "config": {"workload": "chunked_prefill", "num_seqs": c.num_seqs, "prefix_len": int(c.prefix_lens[0]),
                    "chunk_len": c.chunk_len, "layers": 1, "q_heads": 32, "kv_heads": 8, "head_dim": 64,
-                   "page_size": 16, "num_pages": c.num_pages, "causal": "inclusive",
-                   "step": "pa_prefill_chunk (chunk append + RoPE, then causal paged attention on MFMA)"},
+                   "page_size": 16, "num_pages": c.num_pages, "causal": "inclusive", "kv_format": kv,
+                   "step": ("pa_prefill_chunk_i8 (chunk quantised into INT8 pages + RoPE, then causal attention "
+                            "over the INT8 pages on f16 MFMA, weights as hi + lo halves)" if pool is not None else
+                            "pa_prefill_chunk (chunk append + RoPE, then causal paged attention on MFMA)")},
         "median_ms_per_step": round(float(np.median(per_call)), 5),
         "tokens_per_s": round(c.num_seqs * c.chunk_len / (ms * 1e-3), 1),
         "flops_per_step": flops, "exp_per_step": n_exp,
-        "roofline": {"bound": "mfma", "kernel": "k_append_rope (prefix mode) + k_prefill_attn, one call",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("k_append_rope_i8 (prefix mode) + k_prefill_attn_i8, one call; peak of dense f16 MFMA"
+                                if pool is not None else "k_append_rope (prefix mode) + k_prefill_attn, one call"),
                      "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops, "mean_launch_us": round(ms * 1e3, 2)},
@@ -642,17 +664,24 @@ def run_prefill(args, torch, binding, device, *, cpu_seconds):
         torch.cuda.synchronize()
         got = bf16_bits_to_f64(out)
         refs = []
+        pool_host = oracle.quantize_pages_i8(c.k_pool, c.v_pool) if pool is not None else None
         for s in range(c.num_seqs):
             one = lambda a: np.ascontiguousarray(a[s:s + 1])
-            ref, rc = oracle.prefill_chunk(one(q_before).copy(), one(c.k_chunk), one(c.v_chunk), c.k_pool.copy(),
-                                           c.v_pool.copy(), one(c.block_tables), one(c.prefix_lens), c.num_pages,
-                                           c.theta, c.scale)
+            if pool_host is not None:
+                ref, rc = oracle.prefill_chunk_i8(one(q_before).copy(), one(c.k_chunk), one(c.v_chunk),
+                                                  pool_host.copy(), one(c.block_tables), one(c.prefix_lens),
+                                                  c.num_pages, c.theta, c.scale)
+            else:
+                ref, rc = oracle.prefill_chunk(one(q_before).copy(), one(c.k_chunk), one(c.v_chunk),
+                                               c.k_pool.copy(), c.v_pool.copy(), one(c.block_tables),
+                                               one(c.prefix_lens), c.num_pages, c.theta, c.scale)
             assert rc == oracle.OK
             refs.append(ref[0])
         res["accuracy"] = accuracy_stats(got, np.stack(refs), TOL_BF16_OUT,
                                          f"all {c.num_seqs} x {c.chunk_len} rows, 32 heads x 64 dims, bf16 out")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_prefill(c, cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline_prefill(c, cpu_seconds, kv)
+    del pool
     return res
 
 
@@ -771,8 +800,9 @@ def main():
         return
     dec_dtype = "bf16" if args.kv == "bf16" else "int8 K/V, bf16 q/out, fp32 accumulation"
     if args.config == "prefill":
-        print(json.dumps(line(PREFILL_METRIC, "bf16", run_prefill(args, torch, binding, device,
-                                                                  cpu_seconds=args.cpu_seconds))), flush=True)
+        print(json.dumps(line(PREFILL_METRIC, "bf16" if args.kv == "bf16" else "int8 K/V, f16 MFMA, fp32 accumulation",
+                              run_prefill(args, torch, binding, device, cpu_seconds=args.cpu_seconds,
+                                          kv=args.kv))), flush=True)
         return
     if args.config == "argmax":
         print(json.dumps(line(ARGMAX_METRIC, "bf16", run_argmax(args, torch, binding, device,
@@ -794,6 +824,9 @@ def main():
         t0 = time.perf_counter()
         sec["prefill"] = run_prefill(args, torch, binding, device, cpu_seconds=cs)
         sec["prefill"]["wall_s"] = round(time.perf_counter() - t0, 1)
+        t0 = time.perf_counter()
+        sec["prefill_int8"] = run_prefill(args, torch, binding, device, cpu_seconds=cs, kv="int8")
+        sec["prefill_int8"]["wall_s"] = round(time.perf_counter() - t0, 1)
         t0 = time.perf_counter()
         sec["argmax"] = run_argmax(args, torch, binding, device, cpu_seconds=cs)
         sec["argmax"]["wall_s"] = round(time.perf_counter() - t0, 1)

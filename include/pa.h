@@ -115,7 +115,7 @@ int32_t pa_get_device_error(uint32_t *device_flags, int32_t clear, hipStream_t s
  * from, so a caller can refuse a library built from another header.  Like the
  * fixed geometry (samir-vllm, section "Limitations et perspectives": changing
  * the architecture means recompiling), a mismatch is refused, not adapted to. */
-#define PA_ABI_VERSION 13
+#define PA_ABI_VERSION 14
 int32_t pa_abi_version(void);
 
 /* Identity of the sources the library was built from: the sha256 (64 hex
@@ -376,6 +376,26 @@ pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, con
                            int32_t page_size, float scale, int32_t out_dtype, void *workspace,
                            size_t workspace_bytes, uint32_t *device_flags, const int32_t *dispatch_order,
                            const int32_t *device_order, hipStream_t stream);
+
+/* Chunked prefill into INT8 pages (TinyLoop, "Lifecycle and Memory Model":
+ * section "prefill_chunk and scratch residency" processes the prompt in row
+ * chunks, section "Per-request / handle-owned memory" names the INT8 K/V
+ * mode).  pa_prefill_chunk over an INT8 pool: for each s and chunk token i at
+ * pos = prefix_lens[s] + i, k_chunk[s][i] and v_chunk[s][i] are appended as
+ * pa_append_kv_rope_i8 appends one token (K rotated, rounded to bf16 and
+ * quantised; V quantised; q[s][i] rotated in place); then every chunk query
+ * attends causally (keys 0..pos inclusive) to its sequence's keys, with K_t,
+ * V_t the values code * scale:
+ *   out[s][i][h][:] = softmax_t(scale * <q[s][i][h], K_t>) . V_t,  t <= pos
+ * on f16 MFMAs with the INT8 decode's arithmetic (exact codes, scales in
+ * fp32, f16 hi + lo weights), accumulated in fp32.  Shapes, aliasing (out may
+ * alias q exactly), max_blocks <= 512 and device errors as pa_prefill_chunk;
+ * the pool is the PA_I8_TILE_BYTES tile pool of pa_decode_gqa_i8.            */
+pa_status pa_prefill_chunk_i8(void *out, void *q, const void *k_chunk, const void *v_chunk, void *kv_pool_i8,
+                              const int32_t *block_tables, const int32_t *prefix_lens, const double *rope_cos_sin,
+                              int32_t num_seqs, int32_t chunk_len, int32_t max_blocks, int32_t num_pages,
+                              int32_t page_size, int32_t max_pos, float scale, int32_t out_dtype,
+                              uint32_t *device_flags, hipStream_t stream);
 
 /* pa_append_kv_rope_i8 followed by pa_decode_gqa_i8 in one launch, bitwise equal
  * to the two calls (same rotation, rounding and quantisation); q as in

@@ -14,7 +14,9 @@ and hand-built halfway cases; RoPE against complex multiplication and the
 Hugging Face Llama rotate-half routine; decode against torch's fp64
 ``scaled_dot_product_attention`` on gathered contiguous K/V plus closed forms
 (single token, identical rows, q = 0, two-token logistic, ones column) and
-page-placement invariance; prefill against causal SDPA and decode.
+page-placement invariance; prefill against causal SDPA and decode; the INT8
+prefill (a composition of the INT8 append and decode) against causal SDPA on
+the dequantised pool and against the bf16 prefill's rows quantised.
 """
 from __future__ import annotations
 
@@ -235,6 +237,34 @@ def decode_gqa_i8(q, pool, block_tables, context_lens, num_pages: int, scale: fl
     rc = lib.oracle_decode_gqa_i8(_ptr(out), _ptr(qq), _ptr(pl), _ptr(bt), _ptr(cl), B, int(bt.shape[-1]),
                                   int(num_pages), float(scale))
     return out, int(rc)
+
+
+def prefill_chunk_i8(q, k_chunk, v_chunk, pool, block_tables, prefix_lens, num_pages: int, theta: float,
+                     scale: float):
+    """Chunked prefill into INT8 pages (TinyLoop, "prefill_chunk and scratch residency": the prompt in
+    row chunks; "Per-request / handle-owned memory": the INT8 K/V mode), written as what it is made of:
+    chunk token i of every sequence is appended at position prefix + i exactly as ``append_kv_rope_i8``
+    appends one token (its decode length prefix + i + 1), q row i rotated with it; then chunk row i
+    attends causally, keys 0 .. prefix + i, exactly as ``decode_gqa_i8`` at that length.  In place on
+    ``q`` (uint16 [B][C][32][64]) and ``pool``; returns (out fp64 [B][C][32][64], status)."""
+    if not (q.flags.c_contiguous and q.dtype == np.uint16):
+        raise TypeError("q must be C-contiguous uint16")
+    kc, vc = _u16(k_chunk), _u16(v_chunk)
+    pl = _i32(prefix_lens).astype(np.int64)
+    B, C = int(q.shape[0]), int(q.shape[1])
+    rc = OK
+    for i in range(C):
+        qi = np.ascontiguousarray(q[:, i])
+        r = append_kv_rope_i8(qi, kc[:, i], vc[:, i], pool, block_tables, (pl + i + 1).astype(np.int32), num_pages,
+                              theta)
+        q[:, i] = qi
+        rc = rc if rc != OK else r
+    out = np.zeros((B, C, 32, 64), dtype=np.float64)
+    for i in range(C):
+        o, r = decode_gqa_i8(q[:, i], pool, block_tables, (pl + i + 1).astype(np.int32), num_pages, scale)
+        out[:, i] = o
+        rc = rc if rc != OK else r
+    return out, rc
 
 
 def argmax(logits) -> np.ndarray:

@@ -33,11 +33,11 @@ EXPORTS = ("pa_status_string", "pa_abi_version", "pa_rope_table_fill_host", "pa_
            "pa_kvm_queued", "pa_i8_pool_bytes", "pa_quantize_pages_i8", "pa_append_kv_rope_i8", "pa_decode_gqa_i8",
            "pa_append_decode_gqa_i8", "pa_argmax_workspace_bytes", "pa_argmax", "pa_probe_stream_read",
            "pa_dispatch_order_longest_first", "pa_get_device_error", "pa_build_id",
-           "pa_append_decode_gqa_noalloc", "pa_order_by_length")
+           "pa_append_decode_gqa_noalloc", "pa_order_by_length", "pa_prefill_chunk_i8")
 PA_LOGITS_BF16, PA_LOGITS_FP32 = 0, 1
 PA_I8_TILE_BYTES = 2176
 # PA_ABI_VERSION of the header whose signatures this module declares
-ABI_VERSION = 13
+ABI_VERSION = 14
 
 
 class PaError(RuntimeError):
@@ -104,6 +104,9 @@ def lib():
     L.pa_prefill_chunk.restype = ctypes.c_int
     L.pa_prefill_chunk.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32,
                                    P, P]
+    L.pa_prefill_chunk_i8.restype = ctypes.c_int
+    L.pa_prefill_chunk_i8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, ctypes.c_float, i32, P,
+                                      P]
     L.pa_i8_pool_bytes.restype = u64
     L.pa_i8_pool_bytes.argtypes = [i32]
     L.pa_quantize_pages_i8.restype = ctypes.c_int
@@ -425,6 +428,38 @@ def _i8_pool_checks(pool):
     if pool.dim() != 3 or tuple(pool.shape[1:]) != (_w.NUM_KV_HEADS, PA_I8_TILE_BYTES):
         raise ValueError(f"INT8 pool must be [num_pages][8][2176] uint8, got {tuple(pool.shape)}")
     return int(pool.shape[0])
+
+
+def prefill_chunk_i8(out: torch.Tensor, q: torch.Tensor, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                     kv_pool_i8: torch.Tensor, block_tables: torch.Tensor, prefix_lens: torch.Tensor,
+                     rope_cos_sin: torch.Tensor, scale: float = 0.125, device_flags: Optional[torch.Tensor] = None,
+                     page_size: int = 16, stream=None) -> torch.Tensor:
+    """pa_prefill_chunk_i8: quantise the chunk into the INT8 pool (q rotated in place), then causal
+    attention over the INT8 pages into ``out``."""
+    num_pages = _i8_pool_checks(kv_pool_i8)
+    dev = kv_pool_i8.device
+    _expect(prefix_lens, "prefix_lens", torch.int32, device=dev)
+    B = int(prefix_lens.shape[0])
+    if q.dim() != 4:
+        raise ValueError("q must be [num_seqs][chunk_len][32][64]")
+    C = int(q.shape[1])
+    _expect(q, "q", torch.bfloat16, (B, C, 32, 64), dev)
+    _expect(k_chunk, "k_chunk", torch.bfloat16, (B, C, 8, 64), dev)
+    _expect(v_chunk, "v_chunk", torch.bfloat16, (B, C, 8, 64), dev)
+    _expect(block_tables, "block_tables", torch.int32, device=dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks]")
+    _expect(rope_cos_sin, "rope_cos_sin", torch.float64, device=dev)
+    odt = _out_dtype(out)
+    _expect(out, "out", out.dtype, (B, C, 32, 64), dev)
+    if device_flags is not None:
+        _expect(device_flags, "device_flags", torch.int32, (1,), dev)
+    rc = lib().pa_prefill_chunk_i8(_ptr(out), _ptr(q), _ptr(k_chunk), _ptr(v_chunk), _ptr(kv_pool_i8),
+                                   _ptr(block_tables), _ptr(prefix_lens), _ptr(rope_cos_sin), B, C,
+                                   int(block_tables.shape[1]), num_pages, int(page_size), int(rope_cos_sin.shape[0]),
+                                   float(scale), odt, _ptr(device_flags), _stream(stream))
+    _check(rc, "pa_prefill_chunk_i8")
+    return out
 
 
 def _tables(block_tables, context_lens, dev):

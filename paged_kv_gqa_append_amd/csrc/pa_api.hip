@@ -281,6 +281,32 @@ pa_status pa_quantize_pages_i8(void *kv_pool_i8, const void *k_pool, const void 
                                         stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_prefill_chunk_i8(void *out, void *q, const void *k_chunk, const void *v_chunk, void *kv_pool_i8,
+                              const int32_t *block_tables, const int32_t *prefix_lens, const double *rope_cos_sin,
+                              int32_t num_seqs, int32_t chunk_len, int32_t max_blocks, int32_t num_pages,
+                              int32_t page_size, int32_t max_pos, float scale, int32_t out_dtype,
+                              uint32_t *device_flags, hipStream_t stream) {
+    if (num_seqs < 0 || chunk_len < 0 || max_blocks < 1 || num_pages < 1 || max_pos < 1 || !isfinite(scale))
+        return PA_ERR_INVALID_ARG;
+    if (page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+    if (max_blocks > pa::kMaxBlocksPrefill) return PA_ERR_UNSUPPORTED;
+    if (out_dtype != PA_OUT_BF16 && out_dtype != PA_OUT_FP32) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || chunk_len == 0) return PA_OK;
+    if (!out || !q || !k_chunk || !v_chunk || !kv_pool_i8 || !block_tables || !prefix_lens || !rope_cos_sin)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_chunk) || !aligned16(v_chunk) || !aligned16(kv_pool_i8) ||
+        !aligned16(block_tables) || !aligned16(prefix_lens) || !aligned16(rope_cos_sin))
+        return PA_ERR_INVALID_ARG;
+    // The chunk's rows are quantised into their pages and its q rows rotated
+    // first; the attention kernel reads q rotated and every key from the pool.
+    pa::AppendLaunch a{q, k_chunk, v_chunk, kv_pool_i8, nullptr, block_tables, prefix_lens, rope_cos_sin,
+                       num_seqs, chunk_len, 1, max_blocks, num_pages, max_pos, device_flags};
+    if (pa::launch_append_rope_i8(a, stream) != hipSuccess) return PA_ERR_HIP;
+    pa::PrefillLaunch p{out, q, kv_pool_i8, nullptr, block_tables, prefix_lens, num_seqs, chunk_len,
+                        max_blocks, num_pages, max_pos, scale, out_dtype == PA_OUT_FP32, device_flags};
+    return pa::launch_prefill_attention_i8(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, void *kv_pool_i8,
                                const int32_t *block_tables, const int32_t *context_lens,
                                const double *rope_cos_sin, int32_t num_seqs, int32_t max_blocks,

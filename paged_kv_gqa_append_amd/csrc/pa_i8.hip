@@ -51,90 +51,28 @@
 #include <math.h>
 
 #include "pa_decode_core.h"
+#include "pa_i8_core.h"
 
 namespace pa {
 
-constexpr int kI8Tile = 2176;     // bytes per (page, KV head) tile
-constexpr int kI8VOff = 1024;     // V block offset
-constexpr int kI8KScOff = 2048;   // K scales
-constexpr int kI8VScOff = 2112;   // V scales
-constexpr int kPageBytesI8 = kHKV * kI8Tile;
-constexpr float kOffsetF16 = 1152.0f;  // value of the f16 an INT8 code c becomes, minus c
-
-__device__ __forceinline__ int i8_kpos(int t, int d) { return (((d & 31) >> 3) * 16 + t) * 16 + (d >> 5) * 8 + (d & 7); }
-__device__ __forceinline__ int i8_vpos(int t, int d) {
-    return kI8VOff + ((t >> 2) * 16 + (d & 15)) * 16 + (d >> 4) * 4 + (t & 3);
-}
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Quantise one value against a row scale (binary32 throughout, the decision
-// the format defines): round-half-even(x / scale), clamped to [-127, 127].
-__device__ __forceinline__ int quant_code(float x, float scale) {
-    if (!(scale > 0.0f)) return 0;
-    float c = rintf(x / scale);
-    c = fminf(fmaxf(c, -127.0f), 127.0f);
-    return static_cast<int>(c);
-}
-
-// Max over the 32 lanes of each half-wave (lanes 0-31 and 32-63 separately).
-__device__ __forceinline__ float max_lanes32(float v) {
-#pragma unroll
-    for (int k = 1; k < 32; k <<= 1) v = fmaxf(v, __shfl_xor(v, k, 64));
-    return v;
-}
-// Max over the 8 consecutive lanes of an aligned lane group.
-__device__ __forceinline__ float max_lanes8(float v) {
-    v = fmaxf(v, dpp_f32<0xB1>(v));
-    v = fmaxf(v, dpp_f32<0x4E>(v));
-    v = fmaxf(v, dpp_f32<0x141>(v));
-    return v;
-}
-
-// 4 codes (two's complement bytes of w) -> the f16 values 1152 + code, as two
-// packed pairs (bytes 0,1 and 2,3): code ^ 0x80 = code + 128 under the f16
-// exponent byte 0x64 is 1024 + code + 128, exactly.
-__device__ __forceinline__ void codes_to_f16x4(uint32_t w, uint32_t &p01, uint32_t &p23) {
-    const uint32_t u = w ^ 0x80808080u;
-    p01 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-    p23 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-}
-__device__ __forceinline__ half8 codes8_to_f16(uint32_t w0, uint32_t w1) {
-    uint32_t a, b, c, d;
-    codes_to_f16x4(w0, a, b);
-    codes_to_f16x4(w1, c, d);
-    return __builtin_bit_cast(half8, u32x4{a, b, c, d});
-}
-// 4 codes -> the f16 values of the codes themselves (1152 + code, minus 1152
-// in packed f16: exact, every integer in [-127, 127] being an f16).
-__device__ __forceinline__ half4 codes4_to_f16_signed(uint32_t w) {
-    uint32_t a, b;
-    codes_to_f16x4(w, a, b);
-    const half4 off = {static_cast<_Float16>(-kOffsetF16), static_cast<_Float16>(-kOffsetF16),
-                       static_cast<_Float16>(-kOffsetF16), static_cast<_Float16>(-kOffsetF16)};
-    return __builtin_bit_cast(half4, u32x2{a, b}) + off;
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, half2v));
-}
-
 // ------------------------------------------------------------- append ------
-// One workgroup (256 threads) per sequence: thread t serves KV head j = t/32,
-// rotate-half pair p = t%32 of K and elements 2p, 2p+1 of V, plus 4 q pairs.
+// One workgroup (256 threads) per appended token: thread t serves KV head
+// j = t/32, rotate-half pair p = t%32 of K and elements 2p, 2p+1 of V, plus 4
+// q pairs.  token = blockIdx.x = s * tokens_per_seq + i;
+//   decode (prefix_mode == 0): pos = lens[s] - 1   (tokens_per_seq == 1)
+//   prefill (prefix_mode == 1): pos = lens[s] + i  (lens holds prefix lengths)
 __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
                                                         const uint16_t *__restrict__ v_new, uint8_t *__restrict__ pool,
                                                         const int32_t *__restrict__ bt, const int32_t *__restrict__ lens,
-                                                        const double *__restrict__ rope, int max_blocks, int num_pages,
-                                                        int max_pos, uint32_t *__restrict__ flags) {
-    const int s = blockIdx.x;
+                                                        const double *__restrict__ rope, int tokens_per_seq,
+                                                        int prefix_mode, int max_blocks, int num_pages, int max_pos,
+                                                        uint32_t *__restrict__ flags) {
+    const int tok = blockIdx.x;
+    const int s = tok / tokens_per_seq;
     const int64_t len = lens[s];
-    const int64_t pos = len - 1;
-    if (len < 1 || pos >= static_cast<int64_t>(max_blocks) * kPage || pos >= max_pos) {
+    const int64_t pos = prefix_mode ? len + (tok - s * tokens_per_seq) : len - 1;
+    const bool bad_len = prefix_mode ? (len < 0) : (len < 1);
+    if (bad_len || pos >= static_cast<int64_t>(max_blocks) * kPage || pos >= max_pos) {
         if (threadIdx.x == 0 && flags) atomicOr(flags, kDevErrContextLen);
         return;
     }
@@ -150,7 +88,7 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
     uint8_t *tile = pool + (static_cast<int64_t>(page) * kHKV + j) * kI8Tile;
     {
         // K: rotate the pair, round to bf16 (the stored row of the bf16 format), quantise the row
-        const uint16_t *src = k_new + (static_cast<int64_t>(s) * kHKV + j) * kD;
+        const uint16_t *src = k_new + (static_cast<int64_t>(tok) * kHKV + j) * kD;
         uint16_t b0, b1;
         rope_pair_bf16(bf16_to_f32(src[p]), bf16_to_f32(src[p + 32]), cs[2 * p], cs[2 * p + 1], b0, b1);
         const float y0 = bf16_to_f32(b0);
@@ -162,7 +100,7 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
     }
     {
         // V: elements 2p, 2p+1 verbatim from bf16, quantised with the row's scale
-        const uint32_t wv = reinterpret_cast<const uint32_t *>(v_new + (static_cast<int64_t>(s) * kHKV + j) * kD)[p];
+        const uint32_t wv = reinterpret_cast<const uint32_t *>(v_new + (static_cast<int64_t>(tok) * kHKV + j) * kD)[p];
         const float v0 = bf16_lo(wv), v1 = bf16_hi(wv);
         const float sc = max_lanes32(fmaxf(fabsf(v0), fabsf(v1))) / 127.0f;
         tile[i8_vpos(slot, 2 * p)] = static_cast<uint8_t>(quant_code(v0, sc));
@@ -174,7 +112,7 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
         for (int r = 0; r < 4; ++r) {
             const int idx = t + 256 * r;
             const int h = idx >> 5, pp = idx & 31;
-            uint16_t *row = q + (static_cast<int64_t>(s) * kHQ + h) * kD;
+            uint16_t *row = q + (static_cast<int64_t>(tok) * kHQ + h) * kD;
             uint16_t b0, b1;
             rope_pair_bf16(bf16_to_f32(row[pp]), bf16_to_f32(row[pp + 32]), cs[2 * pp], cs[2 * pp + 1], b0, b1);
             row[pp] = b0;
@@ -236,31 +174,6 @@ __global__ __launch_bounds__(256) void k_quantize_pages_i8(uint8_t *__restrict__
 // workgroup of kWaves waves per (sequence, KV head, context partition), pages
 // dealt round-robin to the waves, the next page's loads always in flight.
 // The pool travels in DecodeParams::k_pool (v_pool is unused).
-struct I8Page {
-    u32x4 k, v;   // the lane's K unit and V unit
-    f32x4 ks, vs; // K and V scales of tokens 4(l/16) .. +3
-};
-
-// The value lane src (wave-uniform) holds, as a scalar.
-__device__ __forceinline__ float lane_value(float v, int src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
-}
-
-// Sum (or max) over the four lanes l, l^16, l^32, l^48.
-__device__ __forceinline__ float sum_quarters(float v) {
-    float lo, hi;
-    xor16_pair(v, lo, hi);
-    v = lo + hi;
-    xor32_pair(v, lo, hi);
-    return lo + hi;
-}
-__device__ __forceinline__ float max_quarters(float v) {
-    float lo, hi;
-    xor16_pair(v, lo, hi);
-    v = fmaxf(lo, hi);
-    xor32_pair(v, lo, hi);
-    return fmaxf(lo, hi);
-}
 
 // kLevel: the wave priority starts high and steps down as the wave's pages run
 // out (as in the bf16 kernel).  The s_setprio instructions also constrain how
@@ -703,11 +616,13 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
 constexpr int kDecodeWavesI8 = 8;
 
 hipError_t launch_append_rope_i8(const AppendLaunch &a, hipStream_t stream) {
-    if (a.num_seqs == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_append_rope_i8, dim3(static_cast<unsigned>(a.num_seqs)), dim3(256), 0, stream,
+    const int64_t tokens = static_cast<int64_t>(a.num_seqs) * a.tokens_per_seq;
+    if (tokens == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_append_rope_i8, dim3(static_cast<unsigned>(tokens)), dim3(256), 0, stream,
                        static_cast<uint16_t *>(a.q), static_cast<const uint16_t *>(a.k_new),
                        static_cast<const uint16_t *>(a.v_new), static_cast<uint8_t *>(a.k_pool), a.block_tables,
-                       a.lens, a.rope, a.max_blocks, a.num_pages, a.max_pos, a.flags);
+                       a.lens, a.rope, a.tokens_per_seq, a.prefix_mode, a.max_blocks, a.num_pages, a.max_pos,
+                       a.flags);
     return hipGetLastError();
 }
 

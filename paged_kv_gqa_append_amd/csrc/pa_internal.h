@@ -90,6 +90,9 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 hipError_t launch_order_by_length(const int32_t *lens, int n, int max_blocks, int long_run, int short_run,
                                   int32_t *order, hipStream_t stream);
 hipError_t launch_prefill_attention(const PrefillLaunch &p, hipStream_t stream);
+// Chunked prefill attention over an INT8 tile pool (PrefillLaunch::k_pool;
+// v_pool unused), after the chunk has been appended into it.
+hipError_t launch_prefill_attention_i8(const PrefillLaunch &p, hipStream_t stream);
 
 // INT8 K/V pages (pa_i8.hip).  The tile pool travels in k_pool; v_pool is unused.
 hipError_t launch_append_rope_i8(const AppendLaunch &a, hipStream_t stream);

@@ -46,7 +46,7 @@ def test_status_strings(pa):
     assert pa.status_string(0) == "PA_OK"
     assert pa.status_string(3) == "PA_ERR_WORKSPACE"
     assert pa.status_string(99) == "PA_ERR_UNKNOWN"
-    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 13
+    assert pa.lib().pa_abi_version() == pa.ABI_VERSION == 14
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
@@ -229,6 +229,19 @@ def test_i8_validation(pa):
     assert dec(B=0, out=None) == pa.PA_OK
     need = lib.pa_decode_workspace_bytes(4, 1000)
     assert need > 0 and dec(mb=1000) == pa.PA_ERR_WORKSPACE
+
+    def pre8(B=2, C=8, ps=16, odt=0, q=F, pool=F, mp=64, mb=4):
+        return lib.pa_prefill_chunk_i8(F, q, F, F, pool, F, F, F, B, C, mb, 16, ps, mp, 0.125, odt, None, None)
+
+    assert pre8(ps=32) == pa.PA_ERR_UNSUPPORTED
+    assert pre8(odt=5) == pa.PA_ERR_UNSUPPORTED
+    assert pre8(mb=513) == pa.PA_ERR_UNSUPPORTED
+    assert pre8(C=-1) == pa.PA_ERR_INVALID_ARG
+    assert pre8(mp=0) == pa.PA_ERR_INVALID_ARG
+    assert pre8(pool=None) == pa.PA_ERR_INVALID_ARG
+    assert pre8(q=v(FAKE + 8)) == pa.PA_ERR_INVALID_ARG
+    assert pre8(B=0, q=None, pool=None) == pa.PA_OK
+    assert pre8(C=0, q=None, pool=None) == pa.PA_OK
 
     def fused(rope=F, mp=64):
         return lib.pa_append_decode_gqa_i8(F, F, F, F, F, F, F, rope, 4, 8, 64, 16, mp, 0.125, 0, None, 0, None,

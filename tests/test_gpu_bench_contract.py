@@ -72,3 +72,11 @@ def test_prefill_line():
     line = run_bench("--config", "prefill", "--steps", "3", "--warmup", "2", "--cpu-seconds", "1")
     check_common(line, 3, "TFLOP/s", "mfma")
     assert line["accuracy"]["elements"] == 4 * 512 * 32 * 64
+
+
+def test_prefill_int8_line():
+    print("bench contract: prefill over INT8 pages", flush=True)
+    line = run_bench("--config", "prefill", "--kv", "int8", "--steps", "3", "--warmup", "2", "--cpu-seconds", "1")
+    check_common(line, 3, "TFLOP/s", "mfma")
+    assert line["config"]["kv_format"] == "int8"
+    assert line["accuracy"]["elements"] == 4 * 512 * 32 * 64
