@@ -13,14 +13,22 @@
 // serves rows row0 + 4w .. +3 over every key they see and finishes them
 // itself (no merge across waves).  The MFMAs are the INT8 decode's with all
 // 16 columns live: column c = 4r + h is row r of the wave's four and query
-// head h of the group.  Per page: S^T[16 tokens][16 columns] = K . Q^T (two
-// v_mfma_f32_16x16x32_f16 on the codes), then O[16 columns][64] += P' . V
-// (four v_mfma_f32_16x16x16_f16 for each half of an f16 hi + lo weight pair).
+// head h of the group.
+//
+// The sequence's pages go through LDS in groups of four, one per wave: each
+// wave loads one page's INT8 tile and writes its codes as the f16 MFMA
+// operands (and its scales) into the group's LDS slot, so a page is converted
+// once per workgroup; two groups alternate, one barrier per group.  The waves
+// take the pages two at a time (32 keys): per page S^T[16 tokens][16 columns]
+// = K . Q^T (two v_mfma_f32_16x16x32_f16 on the codes, the accumulator
+// starting at minus the code offset's contribution), then for the pair
+// O[16 columns][64] += P' . V with four v_mfma_f32_16x16x32_f16 for each half
+// of an f16 hi + lo weight pair, k = 8 quarter + i taking token 4 quarter + i
+// of the first page for i < 4 and of the second for i >= 4 in both operands.
 // The arithmetic per (column, token) is the INT8 decode's (pa_i8.hip): exact
-// codes, the 1152 offset subtracted from the score, the K scale applied to
-// the score, the V scale folded into the weights with the lazy exponent ve,
-// online softmax in log2 units with a lazy running max per column; keys past
-// a column's position get weight 0.
+// codes, the K scale applied to the score, the V scale folded into the
+// weights with the lazy exponent ve, online softmax in log2 units with a lazy
+// running max per column; keys past a column's position get weight 0.
 #include <math.h>
 
 #include <type_traits>
@@ -47,12 +55,26 @@ struct PrefillI8Params {
     float scale_log2;
 };
 
-// Four waves (16 rows) per workgroup, three workgroups per CU: the kernel
-// needs about 160 VGPRs (three waves per SIMD); with eight-wave workgroups at
-// four waves per SIMD the compiler spilled.
+// Four waves (16 rows) per workgroup, three workgroups per CU.
 constexpr int kWavesP8 = 4;
 constexpr int kThreadsP8 = 64 * kWavesP8;
 constexpr int kRowsP8 = 4 * kWavesP8;  // chunk rows per workgroup
+constexpr int kGroupP8 = kWavesP8;     // pages per LDS group: one converted by each wave
+
+// One page's tile as MFMA operands, in LDS (4224 B).  k[h][l]: lane l's K
+// operand for dims 8(l/16)+32h .. +7 of token l%16 (f16 values 1152 + code);
+// sc[0..15] the K scales times the softmax scale (log2 units, q's power of two
+// removed), sc[16..31] the V scales.  vp[n][l] (in the first page of each
+// pair): lane l's V operand for dims 16n + l%16 of the pair, tokens 4(l/16) ..
+// +3 of the first page (low 8 bytes, written by the wave that converts it) and
+// of the second (high 8 bytes), as signed f16 codes.
+struct alignas(16) PageOps {
+    u32x4 k[2][64];
+    float sc[32];
+};
+struct alignas(16) PairV {
+    u32x4 vp[4][64];
+};
 
 __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Params P) {
     // ids -> (sequence, KV head, tile): the 3 low id bits pick the XCD, which is
@@ -64,12 +86,15 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
     const int tile = P.n_tiles - 1 - rank % P.n_tiles;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
     const int hh = lane & 15;  // MFMA column: row hh/4 of the wave's four, head hh%4
     const int qd = lane >> 4;  // quarter: K dims 8qd..+7 and 32+8qd..+7; tokens and scales 4qd..+3
     const int C = P.chunk_len;
 
     __shared__ int s_pages[kMaxBlocksPrefill];
+    __shared__ PageOps s_ops[2][kGroupP8];
+    __shared__ PairV s_v[2][kGroupP8 / 2];
+    __shared__ float s_qmax[kWavesP8];
 
     // ---- prologue: length, block table (into LDS, checked), this lane's q
     const int prefix = P.prefix_lens[s];
@@ -91,6 +116,22 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
     const uint16_t *qrow = P.q + ((static_cast<int64_t>(s) * C + row_c) * kHQ + j * kGroup + (hh & 3)) * kD;
     const u32x4 qraw0 = *reinterpret_cast<const u32x4 *>(qrow + 8 * qd);
     const u32x4 qraw1 = *reinterpret_cast<const u32x4 *>(qrow + 32 + 8 * qd);
+    float qf[16];
+    {
+        const uint32_t a[8] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w, qraw1.x, qraw1.y, qraw1.z, qraw1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            qf[2 * k] = bf16_lo(a[k]);
+            qf[2 * k + 1] = bf16_hi(a[k]);
+        }
+    }
+    {
+        float qm = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) qm = fmaxf(qm, fabsf(qf[k]));
+        qm = max_groups(max_lanes8(qm));
+        if (lane == 0) s_qmax[w] = qm;
+    }
 
     // ---- validation: the whole sequence's pages (the loop above staged them in LDS)
     const bool ok = len_ok && __syncthreads_or(bad) == 0;
@@ -112,29 +153,21 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
             atomicOr(P.flags, len_ok ? kDevErrPageId : kDevErrContextLen);
         return;
     }
-    if (row0 >= C) return;  // a wave past the chunk's end (no barrier follows)
-
+    // a wave past the chunk's end converts its pages and meets the barriers
+    // but attends nothing
+    const bool active = row0 < C;
     // the wave's keys: 0 .. the position of its last row
     const int last_pos = prefix + min(row0 + 3, C - 1);
     const int np_w = last_pos / kPage + 1;
     // pages from which some column's causal limit falls inside (or before) the page
     const int first_masked = (prefix + row0) / kPage;
+    // the workgroup's pages (those of its last row) and groups of four
+    const int np_g = (prefix + min(tile * kRowsP8 + kRowsP8 - 1, C - 1)) / kPage + 1;
+    const int n_groups = (np_g + kGroupP8 - 1) / kGroupP8;
 
     // ---- q as the f16 B operand, scaled by 2^(15 - e) so that its largest
-    // element over the wave's 16 columns lies in [2^14, 2^15)
-    float qf[16];
-    {
-        const uint32_t a[8] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w, qraw1.x, qraw1.y, qraw1.z, qraw1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            qf[2 * k] = bf16_lo(a[k]);
-            qf[2 * k + 1] = bf16_hi(a[k]);
-        }
-    }
-    float qmax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) qmax = fmaxf(qmax, fabsf(qf[k]));
-    qmax = max_groups(max_lanes8(qmax));
+    // element over the workgroup's 64 columns lies in [2^14, 2^15)
+    const float qmax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
     int qe = 0;
     if (qmax > 0.0f) (void)frexpf(qmax, &qe);
     const int qshift = min(15 - qe, 126);
@@ -147,28 +180,45 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
         qb0 = __builtin_bit_cast(half8, u32x4{hq[0], hq[1], hq[2], hq[3]});
         qb1 = __builtin_bit_cast(half8, u32x4{hq[4], hq[5], hq[6], hq[7]});
     }
-    // 1152 * <q', 1> for column hh: the offset the code encoding adds to a score
-    float corr;
+    // -1152 * <q', 1> for column hh: the start of every score accumulator, which
+    // removes the offset the code encoding adds
+    float ncorr;
     {
         const uint32_t c1152 = 0x64806480u;  // f16 1152.0 twice
         const half8 k1152 = __builtin_bit_cast(half8, u32x4{c1152, c1152, c1152, c1152});
         f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qb0, z, 0, 0, 0);
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1152, qb1, z, 0, 0, 0);
-        corr = z[0];
+        ncorr = -z[0];
     }
     const float sc_log2 = P.scale_log2 * ldexpf(1.0f, -qshift);
 
+    // ---- page conversion: one page's INT8 tile -> its PageOps in LDS
+    struct RawPage {
+        u32x4 k, v;   // the lane's K unit and V unit
+        uint32_t sc;  // scale (l % 32): K scales then V scales
+    };
     const int64_t tile_j = static_cast<int64_t>(j) * kI8Tile;
-    auto load_page = [&](int p) {
+    auto load_raw = [&](int p) {
         const int page = __builtin_amdgcn_readfirstlane(s_pages[p]);
         const uint8_t *t = P.pool + static_cast<int64_t>(page) * kPageBytesI8 + tile_j;
-        I8Page r;
+        RawPage r;
         r.k = *reinterpret_cast<const u32x4 *>(t + lane * 16);
         r.v = *reinterpret_cast<const u32x4 *>(t + kI8VOff + lane * 16);
-        r.ks = *reinterpret_cast<const f32x4 *>(t + kI8KScOff + qd * 16);
-        r.vs = *reinterpret_cast<const f32x4 *>(t + kI8VScOff + qd * 16);
+        r.sc = *reinterpret_cast<const uint32_t *>(t + kI8KScOff + 4 * (lane & 31));
         return r;
+    };
+    // the wave's page in its group: slot w, half w % 2 of pair w / 2's V
+    auto store_ops = [&](const RawPage &r, PageOps &d, PairV &pv) {
+        d.k[0][lane] = __builtin_bit_cast(u32x4, codes8_to_f16(r.k.x, r.k.y));
+        d.k[1][lane] = __builtin_bit_cast(u32x4, codes8_to_f16(r.k.z, r.k.w));
+        u32x2 *vh = reinterpret_cast<u32x2 *>(&pv.vp[0][lane]) + (w & 1);
+        vh[0] = __builtin_bit_cast(u32x2, codes4_to_f16_signed(r.v.x));
+        vh[128] = __builtin_bit_cast(u32x2, codes4_to_f16_signed(r.v.y));
+        vh[256] = __builtin_bit_cast(u32x2, codes4_to_f16_signed(r.v.z));
+        vh[384] = __builtin_bit_cast(u32x2, codes4_to_f16_signed(r.v.w));
+        const float sc = __builtin_bit_cast(float, r.sc);
+        if (lane < 32) d.sc[lane] = lane < 16 ? sc * sc_log2 : sc;
     };
 
     float m_run = kNegBig;  // running max (log2 units) of column hh
@@ -181,31 +231,41 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
     float vmul = 1.0f;                                          // 2^-ve
     uint32_t vlim_bits = __builtin_bit_cast(uint32_t, 128.0f);  // 2^(ve + 7), as bits
 
-    // masked: a page in which some column's causal limit falls (the wave's
-    // last one or two pages); the others are live for every column
-    auto process = [&](const I8Page &r, int p, auto masked_c) {
-        constexpr bool masked = decltype(masked_c)::value;
-        f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
-        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(r.k.x, r.k.y), qb0, st, 0, 0, 0);
-        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8_to_f16(r.k.z, r.k.w), qb1, st, 0, 0, 0);
-        float x[4];
+    // pages p, p + 1 (slots A, B); masked: some key of the pair lies past some
+    // column's position (the wave's last one or two pages, and a page past its
+    // last, whose keys are all past)
+    auto process_pair = [&](const PageOps &A, const PageOps &B, const PairV &V, int p, bool masked) {
+        f32x4 sa = {ncorr, ncorr, ncorr, ncorr}, sb = sa;
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A.k[0][lane]), qb0, sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, B.k[0][lane]), qb0, sb, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, A.k[1][lane]), qb1, sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, B.k[1][lane]), qb1, sb, 0, 0, 0);
+        const f32x4 ksa = *reinterpret_cast<const f32x4 *>(&A.sc[4 * qd]);
+        const f32x4 ksb = *reinterpret_cast<const f32x4 *>(&B.sc[4 * qd]);
+        const f32x4 vsa = *reinterpret_cast<const f32x4 *>(&A.sc[16 + 4 * qd]);
+        const f32x4 vsb = *reinterpret_cast<const f32x4 *>(&B.sc[16 + 4 * qd]);
+        float x[8], vsl[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (st[i] - corr) * (r.ks[i] * sc_log2);
-        bool dead[4] = {false, false, false, false};
+        for (int i = 0; i < 4; ++i) {
+            x[i] = sa[i] * ksa[i];
+            x[4 + i] = sb[i] * ksb[i];
+            vsl[i] = vsa[i];
+            vsl[4 + i] = vsb[i];
+        }
+        bool dead[8] = {false, false, false, false, false, false, false, false};
         if (masked) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dead[i] = p * kPage + 4 * qd + i > pos_c;
-                if (dead[i]) x[i] = -INFINITY;
+            for (int i = 0; i < 8; ++i) {
+                dead[i] = (p + (i >> 2)) * kPage + 4 * qd + (i & 3) > pos_c;
+                if (dead[i]) x[i] = -INFINITY, vsl[i] = 0.0f;
             }
         }
-        const float xm = max_quarters(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        const float xm = max_quarters(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
         const bool need = xm > m_run + kRescaleLog2;
-        float vsl[4];
+        uint32_t vmx = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vsl[i] = (masked && dead[i]) ? 0.0f : r.vs[i];
-        const uint32_t vmx = max(max(__builtin_bit_cast(uint32_t, vsl[0]), __builtin_bit_cast(uint32_t, vsl[1])),
-                                 max(__builtin_bit_cast(uint32_t, vsl[2]), __builtin_bit_cast(uint32_t, vsl[3])));
+        for (int i = 0; i < 8; ++i) vmx = max(vmx, __builtin_bit_cast(uint32_t, vsl[i]));
         const bool vneed = vmx > vlim_bits;
         if (__builtin_amdgcn_ballot_w64(need || vneed)) {
             if (__builtin_amdgcn_ballot_w64(need)) {
@@ -241,51 +301,54 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
                 }
             }
         }
-        float pw[4], pv[4];
+        float pw[8], pv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             pw[i] = fast_exp2(x[i] - m_run);
-            pv[i] = (masked && dead[i]) ? 0.0f : pw[i] * (vsl[i] * vmul);
+            pv[i] = pw[i] * (vsl[i] * vmul);
         }
-        l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-        const uint32_t h01 = pack_f16x2(pv[0], pv[1]);
-        const uint32_t h23 = pack_f16x2(pv[2], pv[3]);
-        const half2v e01 = __builtin_bit_cast(half2v, h01), e23 = __builtin_bit_cast(half2v, h23);
-        const uint32_t l01 = pack_f16x2(pv[0] - static_cast<float>(e01[0]), pv[1] - static_cast<float>(e01[1]));
-        const uint32_t l23 = pack_f16x2(pv[2] - static_cast<float>(e23[0]), pv[3] - static_cast<float>(e23[1]));
-        const half4 ph = __builtin_bit_cast(half4, u32x2{h01, h23});
-        const half4 pl = __builtin_bit_cast(half4, u32x2{l01, l23});
-        const half4 vb[4] = {codes4_to_f16_signed(r.v.x), codes4_to_f16_signed(r.v.y),
-                             codes4_to_f16_signed(r.v.z), codes4_to_f16_signed(r.v.w)};
+        l_run += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb[n], acc[n], 0, 0, 0);
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb[n], acc[n], 0, 0, 0);
+        for (int k = 0; k < 4; ++k) {
+            hw[k] = pack_f16x2(pv[2 * k], pv[2 * k + 1]);
+            const half2v e = __builtin_bit_cast(half2v, hw[k]);
+            lw[k] = pack_f16x2(pv[2 * k] - static_cast<float>(e[0]), pv[2 * k + 1] - static_cast<float>(e[1]));
         }
+        const half8 ph = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+        const half8 pl = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+        half8 vo[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) vo[n] = __builtin_bit_cast(half8, V.vp[n][lane]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vo[n], acc[n], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vo[n], acc[n], 0, 0, 0);
     };
 
-    // Pages 0 .. np_w-1, two in flight: at the top of a step cur holds page p
-    // and alt page p + 1, both issued.  The steady loop takes unmasked pages
-    // two at a time and its two loads are known to be needed, so they are
-    // unconditional (see the decode kernels); the rest go one at a time.
-    const std::integral_constant<bool, false> kLive;
-    const std::integral_constant<bool, true> kMasked;
-    int p = 0;
-    I8Page cur = load_page(0);
-    I8Page alt = load_page(min(1, np_w - 1));
-    while (p + 1 < first_masked && p + 3 < np_w) {
-        process(cur, p, kLive);
-        cur = load_page(p + 2);
-        process(alt, p + 1, kLive);
-        alt = load_page(p + 3);
-        p += 2;
-    }
-    while (p < np_w) {
-        if (p < first_masked) process(cur, p, kLive);
-        else process(cur, p, kMasked);
-        ++p;
-        cur = alt;
-        if (p + 1 < np_w) alt = load_page(p + 1);
+    // ---- the page loop.  Group g holds pages 4g .. 4g+3 (wave w converts page
+    // 4g + w; past the last page it converts the last page again, unused).  At
+    // the top of step g the group's slots are written and visible, and raw holds
+    // group g + 1's page, issued.
+    RawPage raw = load_raw(min(w, np_g - 1));
+    store_ops(raw, s_ops[0][w], s_v[0][w >> 1]);
+    raw = load_raw(min(kGroupP8 + w, np_g - 1));
+    __syncthreads();
+    for (int g = 0; g < n_groups; ++g) {
+        const PageOps *grp = s_ops[g & 1];
+        const PairV *gv = s_v[g & 1];
+        if (active) {
+#pragma unroll
+            for (int h = 0; h < kGroupP8 / 2; ++h) {
+                const int p = kGroupP8 * g + 2 * h;
+                if (p < np_w) process_pair(grp[2 * h], grp[2 * h + 1], gv[h], p, p + 1 >= first_masked);
+            }
+        }
+        if (g + 1 < n_groups) {
+            store_ops(raw, s_ops[(g + 1) & 1][w], s_v[(g + 1) & 1][w >> 1]);
+            raw = load_raw(min(kGroupP8 * (g + 2) + w, np_g - 1));
+        }
+        __syncthreads();
     }
 
     // ---- out[s][row][j*4 + h][16n + hh] = O x 2^ve / l of column 4qd + i

@@ -1,8 +1,8 @@
 """GPU parity for softmax scales other than 1/sqrt(64): negative (the scores' order reverses; the
 prefill kernel negates q for its products), zero (every live key weighs the same: the plain
 average of V) and large (4.0: sharply peaked weights, so the running reference moves often).
-Decode over bf16 and INT8 pages, fused append + decode, and chunked prefill, each against the
-oracle evaluated with the same scale, within the fp32 tolerance."""
+Decode over bf16 and INT8 pages, fused append + decode, and chunked prefill into bf16 and INT8
+pages, each against the oracle evaluated with the same scale, within the fp32 tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -88,3 +88,24 @@ def test_prefill_scales(scale):
                                    c.theta, scale)
     assert rc == oracle.OK
     assert_close(to_host_f64(out), ref, TOL_FP32, f"prefill, scale {scale}")
+
+
+@pytest.mark.parametrize("scale", SCALES)
+def test_prefill_i8_scales(scale):
+    """Chunked prefill into INT8 pages: the scale reaches the scores through the per-key K scale
+    products, so a negative scale flips every score's sign there."""
+    c = W.make_prefill_case("scale8", 92, [5, 40, 300], 37, poison=True)
+    pool = oracle.quantize_pages_i8(c.k_pool, c.v_pool)
+    q = to_dev_bf16(c.q)
+    flags = guarded_flags()
+    out = guarded_empty(q.shape, torch.float32)
+    binding.prefill_chunk_i8(out, q, to_dev_bf16(c.k_chunk), to_dev_bf16(c.v_chunk), to_dev_u8(pool),
+                             to_dev_i32(c.block_tables), to_dev_i32(c.prefix_lens), rope(max_pos=4200), scale,
+                             device_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    qh, ph = c.q.copy(), pool.copy()
+    ref, rc = oracle.prefill_chunk_i8(qh, c.k_chunk, c.v_chunk, ph, c.block_tables, c.prefix_lens, c.num_pages,
+                                      c.theta, scale)
+    assert rc == oracle.OK
+    assert_close(to_host_f64(out), ref, TOL_FP32, f"INT8 prefill, scale {scale}")
