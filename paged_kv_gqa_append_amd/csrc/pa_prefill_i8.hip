@@ -221,15 +221,28 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
         if (lane < 32) d.sc[lane] = lane < 16 ? sc * sc_log2 : sc;
     };
 
-    float m_run = kNegBig;  // running max (log2 units) of column hh
-    float l_run = 0.0f;     // sum of 2^(x - m) over the lane's tokens
+    // Softmax state of column hh (the same in its four quarter lanes).  A key's
+    // weight is kept as 2^(x - m - ve): m the column's lazy reference, ve the
+    // wave's lazy V exponent, so that weight times V scale is the f16 operand
+    // directly; l and O carry the same factor 2^-ve, which their ratio drops.
+    float m_run = kNegBig;  // reference (log2 units)
+    float l_run = 0.0f;     // sum of the lane's weights
     // acc[n]: O[column 4qd + i][dim 16n + hh]
     f32x4 acc[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     int ve = 0;
-    float vmul = 1.0f;                                          // 2^-ve
+    float mv = m_run;                                           // m + ve
+    float thr = kRescaleLog2;                                   // x - m - ve above this: move m
     uint32_t vlim_bits = __builtin_bit_cast(uint32_t, 128.0f);  // 2^(ve + 7), as bits
+    auto scale_rows = [&](float f) {  // accumulator row 4qd + i by column 4qd + i's factor
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float fi = __shfl(f, 4 * qd + i, 64);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[n][i] *= fi;
+        }
+    };
 
     // pages p, p + 1 (slots A, B); masked: some key of the pair lies past some
     // column's position (the wave's last one or two pages, and a page past its
@@ -244,42 +257,49 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
         const f32x4 ksb = *reinterpret_cast<const f32x4 *>(&B.sc[4 * qd]);
         const f32x4 vsa = *reinterpret_cast<const f32x4 *>(&A.sc[16 + 4 * qd]);
         const f32x4 vsb = *reinterpret_cast<const f32x4 *>(&B.sc[16 + 4 * qd]);
-        float x[8], vsl[8];
+        float sv[8], ks[8], vsl[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = sa[i] * ksa[i];
-            x[4 + i] = sb[i] * ksb[i];
-            vsl[i] = vsa[i];
-            vsl[4 + i] = vsb[i];
+            sv[i] = sa[i], sv[4 + i] = sb[i];
+            ks[i] = ksa[i], ks[4 + i] = ksb[i];
+            vsl[i] = vsa[i], vsl[4 + i] = vsb[i];
         }
-        bool dead[8] = {false, false, false, false, false, false, false, false};
-        if (masked) {
+        // t = x - m - ve, x = the score in log2 units; a key past the column's
+        // position gets t = -inf and V scale 0
+        float t[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                dead[i] = (p + (i >> 2)) * kPage + 4 * qd + (i & 3) > pos_c;
-                if (dead[i]) x[i] = -INFINITY, vsl[i] = 0.0f;
-            }
+        for (int i = 0; i < 8; ++i) t[i] = __builtin_fmaf(sv[i], ks[i], -mv);
+        auto kill = [&](float *u) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((p + (i >> 2)) * kPage + 4 * qd + (i & 3) > pos_c) u[i] = -INFINITY;
+        };
+        if (masked) {
+            kill(t);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((p + (i >> 2)) * kPage + 4 * qd + (i & 3) > pos_c) vsl[i] = 0.0f;
         }
-        const float xm = max_quarters(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
-        const bool need = xm > m_run + kRescaleLog2;
+        const float tm = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
         uint32_t vmx = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) vmx = max(vmx, __builtin_bit_cast(uint32_t, vsl[i]));
+        const bool need = tm > thr;
         const bool vneed = vmx > vlim_bits;
         if (__builtin_amdgcn_ballot_w64(need || vneed)) {
             if (__builtin_amdgcn_ballot_w64(need)) {
-                const float mn = need ? xm : m_run;
+                // the column's largest score of the pair, from the scores themselves
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = sv[i] * ks[i];
+                if (masked) kill(x);
+                const float xm = max_quarters(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                                    fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+                const float mn = xm > m_run + kRescaleLog2 ? xm : m_run;
                 const float f = fast_exp2(m_run - mn);
                 m_run = mn;
                 l_run *= f;
-                // accumulator row 4qd + i is column 4qd + i: its factor is that column's
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float fi = __shfl(f, 4 * qd + i, 64);
-#pragma unroll
-                    for (int n = 0; n < 4; ++n) acc[n][i] *= fi;
-                }
+                scale_rows(f);
             }
             if (__builtin_amdgcn_ballot_w64(vneed)) {
                 // the largest live scale over the whole wave (columns mask different tokens)
@@ -295,17 +315,22 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
                     for (int n = 0; n < 4; ++n)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) acc[n][i] *= f;
+                    l_run *= f;
                     ve = ve_new;
-                    vmul = ldexpf(1.0f, -ve);
+                    thr = kRescaleLog2 - static_cast<float>(ve);
                     vlim_bits = __builtin_bit_cast(uint32_t, ldexpf(1.0f, ve + 7));
                 }
             }
+            mv = m_run + static_cast<float>(ve);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] = __builtin_fmaf(sv[i], ks[i], -mv);
+            if (masked) kill(t);
         }
         float pw[8], pv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            pw[i] = fast_exp2(x[i] - m_run);
-            pv[i] = pw[i] * (vsl[i] * vmul);
+            pw[i] = fast_exp2(t[i]);
+            pv[i] = pw[i] * vsl[i];
         }
         l_run += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
         uint32_t hw[4], lw[4];
@@ -351,13 +376,12 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
         __syncthreads();
     }
 
-    // ---- out[s][row][j*4 + h][16n + hh] = O x 2^ve / l of column 4qd + i
+    // ---- out[s][row][j*4 + h][16n + hh] = O / l of column 4qd + i (both carry 2^-ve)
     const float l_tot = sum_quarters(l_run);
-    const float vback = ldexpf(1.0f, ve);
     const int r = row0 + qd;  // accumulator rows 4qd .. 4qd+3: row qd of the wave's four, heads 0..3
     float inv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) inv[i] = vback / __shfl(l_tot, 4 * qd + i, 64);
+    for (int i = 0; i < 4; ++i) inv[i] = 1.0f / __shfl(l_tot, 4 * qd + i, 64);
     if (r >= C) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
