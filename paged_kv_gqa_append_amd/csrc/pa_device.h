@@ -13,6 +13,7 @@ constexpr int kD = 64;        // head dim
 constexpr int kPage = 16;     // tokens per page
 constexpr int kTile = kPage * kD;          // elements of one (page, kv head) tile
 constexpr int kPageElems = kHKV * kTile;   // elements of one page (all heads)
+constexpr int kCuPerXcd = 32;  // gfx950: 8 XCDs x 32 CUs; workgroup ids are dealt to XCDs by id mod 8
 
 constexpr uint32_t kDevErrContextLen = 0x1u;
 constexpr uint32_t kDevErrPageId = 0x2u;

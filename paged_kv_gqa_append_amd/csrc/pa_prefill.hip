@@ -292,7 +292,6 @@ __device__ __forceinline__ float slow_path(const float (&t)[16], float &ref, flo
 // LDS layout of one workgroup: two key halves, each with kNBuf K and V block
 // buffers; after the block loop the same bytes hold the partial results the
 // two halves exchange.
-constexpr int kCuPerXcd = 32;                           // gfx950: 8 XCDs x 32 CUs
 constexpr int kThreads = 256;                           // 4 waves: 2 head pairs x 2 key halves
 constexpr int kNBuf = 4;                                // K/V blocks in LDS per key half (3 in flight)
 constexpr int kHalfBytes = 2 * kNBuf * kBlockBytes;     // per key half: K and V, kNBuf buffers each

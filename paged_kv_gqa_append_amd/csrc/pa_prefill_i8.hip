@@ -78,10 +78,16 @@ struct alignas(16) PairV {
 
 __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Params P) {
     // ids -> (sequence, KV head, tile): the 3 low id bits pick the XCD, which is
-    // also the KV head; each (sequence, head) takes its tiles longest first.
+    // also the KV head.  An XCD deals its workgroups to its 32 CUs in turn, so
+    // its p-th, (p+32)-th, ... share a CU: even turns take the work list (rank
+    // r: sequence r / n_tiles, tiles from the highest positions down) forward
+    // and odd turns backward, so each CU pairs long tiles with short ones.
     const int bid = blockIdx.x;
     const int j = bid & (kHKV - 1);
-    const int rank = bid >> 3;
+    const int pslot = bid >> 3;
+    const int base = pslot & ~(kCuPerXcd - 1);
+    const int span = min(static_cast<int>(gridDim.x >> 3) - base, kCuPerXcd);  // a last turn may be short
+    const int rank = ((pslot / kCuPerXcd) & 1) ? base + span - 1 - (pslot - base) : pslot;
     const int s = rank / P.n_tiles;
     const int tile = P.n_tiles - 1 - rank % P.n_tiles;
     const int tid = threadIdx.x;
