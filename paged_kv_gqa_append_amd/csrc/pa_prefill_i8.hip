@@ -61,6 +61,13 @@ constexpr int kThreadsP8 = 64 * kWavesP8;
 constexpr int kRowsP8 = 4 * kWavesP8;  // chunk rows per workgroup
 constexpr int kGroupP8 = kWavesP8;     // pages per LDS group: one converted by each wave
 
+// With bf16 output a pair's weights go to the P.V product as f16 alone (no lo
+// half) when none of its live V scales exceeds 1/4, i.e. every |v| <= 127/4:
+// an f16 weight is within 2^-12 of its value relative, so the output moves by
+// at most 2^-12 * 32 < 8e-3, inside the bf16 output's 1e-2 bound, before its
+// own rounding to bf16 (2^-9 relative).
+constexpr uint32_t kHiOnlyVScaleBits = 0x3E800000u;  // 0.25f
+
 // One page's tile as MFMA operands, in LDS (4224 B).  k[h][l]: lane l's K
 // operand for dims 8(l/16)+32h .. +7 of token l%16 (f16 values 1152 + code);
 // sc[0..15] the K scales times the softmax scale (log2 units, q's power of two
@@ -339,22 +346,28 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
             pv[i] = pw[i] * vsl[i];
         }
         l_run += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
-        uint32_t hw[4], lw[4];
+        uint32_t hw[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            hw[k] = pack_f16x2(pv[2 * k], pv[2 * k + 1]);
-            const half2v e = __builtin_bit_cast(half2v, hw[k]);
-            lw[k] = pack_f16x2(pv[2 * k] - static_cast<float>(e[0]), pv[2 * k + 1] - static_cast<float>(e[1]));
-        }
+        for (int k = 0; k < 4; ++k) hw[k] = pack_f16x2(pv[2 * k], pv[2 * k + 1]);
         const half8 ph = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
-        const half8 pl = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
         half8 vo[4];
 #pragma unroll
         for (int n = 0; n < 4; ++n) vo[n] = __builtin_bit_cast(half8, V.vp[n][lane]);
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vo[n], acc[n], 0, 0, 0);
+        // the lo halves: always for fp32 output; for bf16 output only where some
+        // live V scale of the pair exceeds 1/4 (see kHiOnlyVScale)
+        if (P.out_fp32 || __builtin_amdgcn_ballot_w64(vmx > kHiOnlyVScaleBits)) {
+            uint32_t lw[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vo[n], acc[n], 0, 0, 0);
+            for (int k = 0; k < 4; ++k) {
+                const half2v e = __builtin_bit_cast(half2v, hw[k]);
+                lw[k] = pack_f16x2(pv[2 * k] - static_cast<float>(e[0]), pv[2 * k + 1] - static_cast<float>(e[1]));
+            }
+            const half8 pl = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vo[n], acc[n], 0, 0, 0);
+        }
     };
 
     // ---- the page loop.  Group g holds pages 4g .. 4g+3 (wave w converts page

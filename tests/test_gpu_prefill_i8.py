@@ -95,9 +95,11 @@ def test_prefill_i8_output_may_alias_q():
     assert np.array_equal(to_host_bits(out), sep)
 
 
-def test_prefill_i8_outliers_and_wide_values():
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_prefill_i8_outliers_and_wide_values(out_dtype):
     """Rows scaled x20 (1 % of the pool) and a chunk whose V rows reach 1e4: the scales and the
-    lazy V exponent carry them; outputs within the fp32 bar."""
+    lazy V exponent carry them; outputs within the fp32 bar, or the bf16 one for bf16 output
+    (where pairs of pages with a V scale above 1/4 take the lo weight halves and the rest not)."""
     c = W.make_prefill_case("wide8", 181, [64, 200], 50, poison=True)
     rng = np.random.default_rng(5)
     kp = W.bf16_bits_to_f32(c.k_pool).copy()
@@ -109,10 +111,10 @@ def test_prefill_i8_outliers_and_wide_values():
     c.v_chunk = W.f32_to_bf16_bits(vc)
     pool = oracle.quantize_pages_i8(c.k_pool, c.v_pool)
     d = DevPrefillI8(c, pool)
-    got = to_host_f64(d.run(torch.float32))
+    got = to_host_f64(d.run(out_dtype))
     ref, _, opool = oracle_rows(c, pool)
     assert np.array_equal(d.pool.cpu().numpy(), opool)
-    assert_close(got, ref, TOL_FP32, "outliers and wide V")
+    assert_close(got, ref, TOL_FP32 if out_dtype == torch.float32 else TOL_BF16, "outliers and wide V")
 
 
 def test_prefill_i8_device_errors():
