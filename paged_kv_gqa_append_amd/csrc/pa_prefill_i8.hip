@@ -62,11 +62,11 @@ constexpr int kRowsP8 = 4 * kWavesP8;  // chunk rows per workgroup
 constexpr int kGroupP8 = kWavesP8;     // pages per LDS group: one converted by each wave
 
 // With bf16 output a pair's weights go to the P.V product as f16 alone (no lo
-// half) when none of its live V scales exceeds 1/4, i.e. every |v| <= 127/4:
-// an f16 weight is within 2^-12 of its value relative, so the output moves by
-// at most 2^-12 * 32 < 8e-3, inside the bf16 output's 1e-2 bound, before its
-// own rounding to bf16 (2^-9 relative).
-constexpr uint32_t kHiOnlyVScaleBits = 0x3E800000u;  // 0.25f
+// half) when none of its live V scales exceeds 1/8, i.e. every |v| <= 127/8:
+// an f16 weight is within 2^-11 of its value relative, so the output (a
+// weighted mean of the v) moves by at most 2^-11 * 16 < 8e-3, inside the bf16
+// output's 1e-2 bound, before its own rounding to bf16 (2^-9 relative).
+constexpr uint32_t kHiOnlyVScaleBits = 0x3E000000u;  // 0.125f
 
 // One page's tile as MFMA operands, in LDS (4224 B).  k[h][l]: lane l's K
 // operand for dims 8(l/16)+32h .. +7 of token l%16 (f16 values 1152 + code);
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vo[n], acc[n], 0, 0, 0);
         // the lo halves: always for fp32 output; for bf16 output only where some
-        // live V scale of the pair exceeds 1/4 (see kHiOnlyVScale)
+        // live V scale of the pair exceeds 1/8 (kHiOnlyVScaleBits)
         if (P.out_fp32 || __builtin_amdgcn_ballot_w64(vmx > kHiOnlyVScaleBits)) {
             uint32_t lw[4];
 #pragma unroll

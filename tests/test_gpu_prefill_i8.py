@@ -99,7 +99,7 @@ def test_prefill_i8_output_may_alias_q():
 def test_prefill_i8_outliers_and_wide_values(out_dtype):
     """Rows scaled x20 (1 % of the pool) and a chunk whose V rows reach 1e4: the scales and the
     lazy V exponent carry them; outputs within the fp32 bar, or the bf16 one for bf16 output
-    (where pairs of pages with a V scale above 1/4 take the lo weight halves and the rest not)."""
+    (where pairs of pages with a V scale above 1/8 take the lo weight halves and the rest not)."""
     c = W.make_prefill_case("wide8", 181, [64, 200], 50, poison=True)
     rng = np.random.default_rng(5)
     kp = W.bf16_bits_to_f32(c.k_pool).copy()
