@@ -104,4 +104,17 @@ __device__ __forceinline__ void rope_pair_bf16(float x0, float x1, double c, dou
     hi = f64_to_bf16(p2 + p3);
 }
 
+// Rotate-half pairs i0 .. i0+3 of a row held as a = elements i0 .. i0+3 and
+// b = their partners i0+32 .. i0+35 (8 bytes each) by the (cos, sin) entries
+// t[k] of pair i0 + k (rope_pair_bf16); the rotated halves, packed the same way.
+__device__ __forceinline__ void rope4(uint2 a, uint2 b, const double2 (&t)[4], uint2 &lo_out, uint2 &hi_out) {
+    uint16_t lo[4], hi[4];
+    rope_pair_bf16(bf16_lo(a.x), bf16_lo(b.x), t[0].x, t[0].y, lo[0], hi[0]);
+    rope_pair_bf16(bf16_hi(a.x), bf16_hi(b.x), t[1].x, t[1].y, lo[1], hi[1]);
+    rope_pair_bf16(bf16_lo(a.y), bf16_lo(b.y), t[2].x, t[2].y, lo[2], hi[2]);
+    rope_pair_bf16(bf16_hi(a.y), bf16_hi(b.y), t[3].x, t[3].y, lo[3], hi[3]);
+    lo_out = uint2{lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16)};
+    hi_out = uint2{hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16)};
+}
+
 }  // namespace pa

@@ -56,9 +56,8 @@
 namespace pa {
 
 // ------------------------------------------------------------- append ------
-// One workgroup (256 threads) per appended token: thread t serves KV head
-// j = t/32, rotate-half pair p = t%32 of K and elements 2p, 2p+1 of V, plus 4
-// q pairs.  token = blockIdx.x = s * tokens_per_seq + i;
+// One workgroup (256 threads) per appended token; token = blockIdx.x =
+// s * tokens_per_seq + i;
 //   decode (prefix_mode == 0): pos = lens[s] - 1   (tokens_per_seq == 1)
 //   prefill (prefix_mode == 1): pos = lens[s] + i  (lens holds prefix lengths)
 __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q, const uint16_t *__restrict__ k_new,
@@ -67,57 +66,93 @@ __global__ __launch_bounds__(256) void k_append_rope_i8(uint16_t *__restrict__ q
                                                         const double *__restrict__ rope, int tokens_per_seq,
                                                         int prefix_mode, int max_blocks, int num_pages, int max_pos,
                                                         uint32_t *__restrict__ flags) {
+    // Work in units of 4 pairs, as the bf16 append: K is 8 heads x 8 units
+    // (threads 0..63), V 8 heads x 8 chunks of 8 dims (threads 64..127), q 32
+    // heads x 8 units in place (one per thread).  The rows depend on the token
+    // alone, so their loads go out first, beside the length's; the table row
+    // waits for the length and the stores for the page id, and a token that
+    // fails either check writes nothing.  A row's scale is the maximum |x| over
+    // its 64 dims (the 8 lanes of its head) / 127.
     const int tok = blockIdx.x;
     const int s = tok / tokens_per_seq;
+    const int i = tok - s * tokens_per_seq;
+    const int t = threadIdx.x;
+    const int u = t & 7;
+    const int i0 = 4 * u;
+    const int j = (t >> 3) & (kHKV - 1);
     const int64_t len = lens[s];
-    const int64_t pos = prefix_mode ? len + (tok - s * tokens_per_seq) : len - 1;
+    uint2 qa{0u, 0u}, qb{0u, 0u}, ka{0u, 0u}, kb{0u, 0u};
+    u32x4 vv{0u, 0u, 0u, 0u};
+    uint16_t *qrow = q ? q + (static_cast<int64_t>(tok) * kHQ + (t >> 3)) * kD : nullptr;
+    if (q) {
+        qa = *reinterpret_cast<const uint2 *>(qrow + i0);
+        qb = *reinterpret_cast<const uint2 *>(qrow + i0 + kD / 2);
+    }
+    const int64_t krow = (static_cast<int64_t>(tok) * kHKV + j) * kD;
+    if (t < 64) {
+        ka = *reinterpret_cast<const uint2 *>(k_new + krow + i0);
+        kb = *reinterpret_cast<const uint2 *>(k_new + krow + i0 + kD / 2);
+    } else if (t < 128) {
+        vv = reinterpret_cast<const u32x4 *>(v_new + krow)[u];
+    }
+    const int64_t pos = prefix_mode ? len + i : len - 1;
     const bool bad_len = prefix_mode ? (len < 0) : (len < 1);
     if (bad_len || pos >= static_cast<int64_t>(max_blocks) * kPage || pos >= max_pos) {
-        if (threadIdx.x == 0 && flags) atomicOr(flags, kDevErrContextLen);
+        if (t == 0 && flags) atomicOr(flags, kDevErrContextLen);
         return;
     }
     const int page = bt[static_cast<int64_t>(s) * max_blocks + (pos >> 4)];
+    const double *cs = rope + pos * kD + 2 * i0;  // pairs i0 .. i0+3 of [32][2]
+    const double2 tb[4] = {reinterpret_cast<const double2 *>(cs)[0], reinterpret_cast<const double2 *>(cs)[1],
+                           reinterpret_cast<const double2 *>(cs)[2], reinterpret_cast<const double2 *>(cs)[3]};
     if (page < 0 || page >= num_pages) {
-        if (threadIdx.x == 0 && flags) atomicOr(flags, kDevErrPageId);
+        if (t == 0 && flags) atomicOr(flags, kDevErrPageId);
         return;
     }
     const int slot = static_cast<int>(pos & (kPage - 1));
-    const double *cs = rope + pos * kD;  // [32][2]
-    const int t = threadIdx.x;
-    const int j = t >> 5, p = t & 31;
     uint8_t *tile = pool + (static_cast<int64_t>(page) * kHKV + j) * kI8Tile;
-    {
-        // K: rotate the pair, round to bf16 (the stored row of the bf16 format), quantise the row
-        const uint16_t *src = k_new + (static_cast<int64_t>(tok) * kHKV + j) * kD;
-        uint16_t b0, b1;
-        rope_pair_bf16(bf16_to_f32(src[p]), bf16_to_f32(src[p + 32]), cs[2 * p], cs[2 * p + 1], b0, b1);
-        const float y0 = bf16_to_f32(b0);
-        const float y1 = bf16_to_f32(b1);
-        const float sc = max_lanes32(fmaxf(fabsf(y0), fabsf(y1))) / 127.0f;
-        tile[i8_kpos(slot, p)] = static_cast<uint8_t>(quant_code(y0, sc));
-        tile[i8_kpos(slot, p + 32)] = static_cast<uint8_t>(quant_code(y1, sc));
-        if (p == 0) *reinterpret_cast<float *>(tile + kI8KScOff + 4 * slot) = sc;
-    }
-    {
-        // V: elements 2p, 2p+1 verbatim from bf16, quantised with the row's scale
-        const uint32_t wv = reinterpret_cast<const uint32_t *>(v_new + (static_cast<int64_t>(tok) * kHKV + j) * kD)[p];
-        const float v0 = bf16_lo(wv), v1 = bf16_hi(wv);
-        const float sc = max_lanes32(fmaxf(fabsf(v0), fabsf(v1))) / 127.0f;
-        tile[i8_vpos(slot, 2 * p)] = static_cast<uint8_t>(quant_code(v0, sc));
-        tile[i8_vpos(slot, 2 * p + 1)] = static_cast<uint8_t>(quant_code(v1, sc));
-        if (p == 0) *reinterpret_cast<float *>(tile + kI8VScOff + 4 * slot) = sc;
+    if (t < 64) {
+        // K: rotate, round to bf16 (the stored row of the bf16 format), quantise
+        uint2 lo, hi;
+        rope4(ka, kb, tb, lo, hi);
+        const float y[8] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y),
+                            bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y)};
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(y[k]));
+        const float sc = max_lanes8(a) / 127.0f;
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            w0 |= (static_cast<uint32_t>(quant_code(y[k], sc)) & 0xFFu) << (8 * k);
+            w1 |= (static_cast<uint32_t>(quant_code(y[4 + k], sc)) & 0xFFu) << (8 * k);
+        }
+        // dims i0 .. i0+3 and i0+32 .. i0+35 are 4 consecutive bytes each
+        *reinterpret_cast<uint32_t *>(tile + i8_kpos(slot, i0)) = w0;
+        *reinterpret_cast<uint32_t *>(tile + i8_kpos(slot, i0 + 32)) = w1;
+        if (u == 0) *reinterpret_cast<float *>(tile + kI8KScOff + 4 * slot) = sc;
+    } else if (t < 128) {
+        // V: dims 8u .. 8u+7 verbatim from bf16, quantised with the row's scale
+        const uint32_t wd[4] = {vv.x, vv.y, vv.z, vv.w};
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = bf16_lo(wd[k]);
+            x[2 * k + 1] = bf16_hi(wd[k]);
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(x[k]));
+        const float sc = max_lanes8(a) / 127.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tile[i8_vpos(slot, 8 * u + k)] = static_cast<uint8_t>(quant_code(x[k], sc));
+        if (u == 0) *reinterpret_cast<float *>(tile + kI8VScOff + 4 * slot) = sc;
     }
     if (q) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int idx = t + 256 * r;
-            const int h = idx >> 5, pp = idx & 31;
-            uint16_t *row = q + (static_cast<int64_t>(tok) * kHQ + h) * kD;
-            uint16_t b0, b1;
-            rope_pair_bf16(bf16_to_f32(row[pp]), bf16_to_f32(row[pp + 32]), cs[2 * pp], cs[2 * pp + 1], b0, b1);
-            row[pp] = b0;
-            row[pp + 32] = b1;
-        }
+        uint2 lo, hi;
+        rope4(qa, qb, tb, lo, hi);
+        *reinterpret_cast<uint2 *>(qrow + i0) = lo;
+        *reinterpret_cast<uint2 *>(qrow + i0 + kD / 2) = hi;
     }
 }
 
