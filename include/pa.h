@@ -388,7 +388,10 @@ pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, con
  * V_t the values code * scale:
  *   out[s][i][h][:] = softmax_t(scale * <q[s][i][h], K_t>) . V_t,  t <= pos
  * on f16 MFMAs with the INT8 decode's arithmetic (exact codes, scales in
- * fp32, f16 hi + lo weights), accumulated in fp32.  Shapes, aliasing (out may
+ * fp32), accumulated in fp32.  The weights (softmax weight x V scale) go in as
+ * f16 hi + lo halves for PA_OUT_FP32; for PA_OUT_BF16 the lo half is dropped
+ * for keys taken together (two pages) whose V scales are all <= 1/8, where f16
+ * weights alone keep the output within 2^-11 * 16 < 8e-3 of exact.  Shapes, aliasing (out may
  * alias q exactly), max_blocks <= 512 and device errors as pa_prefill_chunk;
  * the pool is the PA_I8_TILE_BYTES tile pool of pa_decode_gqa_i8.            */
 pa_status pa_prefill_chunk_i8(void *out, void *q, const void *k_chunk, const void *v_chunk, void *kv_pool_i8,
