@@ -22,13 +22,15 @@
 // take the pages two at a time (32 keys): per page S^T[16 tokens][16 columns]
 // = K . Q^T (two v_mfma_f32_16x16x32_f16 on the codes, the accumulator
 // starting at minus the code offset's contribution), then for the pair
-// O[16 columns][64] += P' . V with four v_mfma_f32_16x16x32_f16 for each half
-// of an f16 hi + lo weight pair, k = 8 quarter + i taking token 4 quarter + i
-// of the first page for i < 4 and of the second for i >= 4 in both operands.
-// The arithmetic per (column, token) is the INT8 decode's (pa_i8.hip): exact
-// codes, the K scale applied to the score, the V scale folded into the
-// weights with the lazy exponent ve, online softmax in log2 units with a lazy
-// running max per column; keys past a column's position get weight 0.
+// O[16 columns][64] += P' . V with four v_mfma_f32_16x16x32_f16 on the f16 hi
+// halves of the weights (and four more on the lo halves where the output
+// needs them), k = 8 quarter + i taking token 4 quarter + i of the first page
+// for i < 4 and of the second for i >= 4 in both operands.  Per (column,
+// token) the arithmetic is the INT8 decode's (pa_i8.hip): exact codes, the K
+// scale applied to the score, the V scale folded into the weight, online
+// softmax in log2 units; here a weight is kept as 2^(x - m - ve) with m the
+// column's lazy reference and ve the wave's lazy V exponent, and keys past a
+// column's position get weight 0.
 #include <math.h>
 
 #include <type_traits>
