@@ -507,20 +507,22 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_decode_paged_i8(DecodeParams
             pv[i] = (last && dead[i]) ? 0.0f : pw[i] * (vsl[i] * vmul);
         }
         l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-        // weights as an f16 pair hi + lo (lo = the rounding remainder of hi)
+        // weights as an f16 pair hi + lo (lo = the rounding remainder of hi);
+        // the lo products only where the output needs them (kHiOnlyVScaleBits)
         const uint32_t h01 = pack_f16x2(pv[0], pv[1]);
         const uint32_t h23 = pack_f16x2(pv[2], pv[3]);
-        const half2v e01 = __builtin_bit_cast(half2v, h01), e23 = __builtin_bit_cast(half2v, h23);
-        const uint32_t l01 = pack_f16x2(pv[0] - static_cast<float>(e01[0]), pv[1] - static_cast<float>(e01[1]));
-        const uint32_t l23 = pack_f16x2(pv[2] - static_cast<float>(e23[0]), pv[3] - static_cast<float>(e23[1]));
         const half4 ph = __builtin_bit_cast(half4, u32x2{h01, h23});
-        const half4 pl = __builtin_bit_cast(half4, u32x2{l01, l23});
         const half4 vb[4] = {codes4_to_f16_signed(r.v.x), codes4_to_f16_signed(r.v.y),
                              codes4_to_f16_signed(r.v.z), codes4_to_f16_signed(r.v.w)};
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb[n], acc[n], 0, 0, 0);
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb[n], acc[n], 0, 0, 0);
+        for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb[n], acc[n], 0, 0, 0);
+        if (P.out_fp32 || __builtin_amdgcn_ballot_w64(vmx > kHiOnlyVScaleBits)) {
+            const half2v e01 = __builtin_bit_cast(half2v, h01), e23 = __builtin_bit_cast(half2v, h23);
+            const uint32_t l01 = pack_f16x2(pv[0] - static_cast<float>(e01[0]), pv[1] - static_cast<float>(e01[1]));
+            const uint32_t l23 = pack_f16x2(pv[2] - static_cast<float>(e23[0]), pv[3] - static_cast<float>(e23[1]));
+            const half4 pl = __builtin_bit_cast(half4, u32x2{l01, l23});
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb[n], acc[n], 0, 0, 0);
         }
     };
     auto process_last = [&](I8Page r, int p) {

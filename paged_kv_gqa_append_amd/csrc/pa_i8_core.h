@@ -20,6 +20,14 @@ constexpr int kI8VScOff = 2112;   // V scales
 constexpr int kPageBytesI8 = kHKV * kI8Tile;
 constexpr float kOffsetF16 = 1152.0f;  // value of the f16 an INT8 code c becomes, minus c
 
+// The P.V products take each weight (softmax weight x V scale) as an f16 hi
+// half plus an f16 lo half (its rounding remainder).  With bf16 output the lo
+// half is dropped for keys whose live V scales are all <= 1/8, i.e. every
+// |v| <= 127/8: an f16 weight is within 2^-11 of its value relative, so the
+// output (a weighted mean of the v) moves by at most 2^-11 * 16 < 8e-3, inside
+// the bf16 output's 1e-2 bound, before its own rounding to bf16.
+constexpr uint32_t kHiOnlyVScaleBits = 0x3E000000u;  // 0.125f, as bits
+
 __device__ __forceinline__ int i8_kpos(int t, int d) { return (((d & 31) >> 3) * 16 + t) * 16 + (d >> 5) * 8 + (d & 7); }
 __device__ __forceinline__ int i8_vpos(int t, int d) {
     return kI8VOff + ((t >> 2) * 16 + (d & 15)) * 16 + (d >> 4) * 4 + (t & 3);

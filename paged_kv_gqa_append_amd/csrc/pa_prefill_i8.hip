@@ -63,13 +63,6 @@ constexpr int kThreadsP8 = 64 * kWavesP8;
 constexpr int kRowsP8 = 4 * kWavesP8;  // chunk rows per workgroup
 constexpr int kGroupP8 = kWavesP8;     // pages per LDS group: one converted by each wave
 
-// With bf16 output a pair's weights go to the P.V product as f16 alone (no lo
-// half) when none of its live V scales exceeds 1/8, i.e. every |v| <= 127/8:
-// an f16 weight is within 2^-11 of its value relative, so the output (a
-// weighted mean of the v) moves by at most 2^-11 * 16 < 8e-3, inside the bf16
-// output's 1e-2 bound, before its own rounding to bf16 (2^-9 relative).
-constexpr uint32_t kHiOnlyVScaleBits = 0x3E000000u;  // 0.125f
-
 // One page's tile as MFMA operands, in LDS (4224 B).  k[h][l]: lane l's K
 // operand for dims 8(l/16)+32h .. +7 of token l%16 (f16 values 1152 + code);
 // sc[0..15] the K scales times the softmax scale (log2 units, q's power of two
