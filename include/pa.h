@@ -370,7 +370,10 @@ pa_status pa_append_kv_rope_i8(void *q, const void *k_new, const void *v_new, vo
                                uint32_t *device_flags, hipStream_t stream);
 
 /* pa_decode_gqa over an INT8 pool: K_t, V_t are the values the codes stand for
- * (code * scale); everything else as pa_decode_gqa, out may alias q.        */
+ * (code * scale); everything else as pa_decode_gqa, out may alias q.  The
+ * weights (softmax weight x V scale) enter the products as f16 hi + lo halves;
+ * with PA_OUT_BF16 a page whose live V scales are all <= 1/8 takes the hi
+ * halves alone (within 2^-11 * 16 < 8e-3 of exact).                          */
 pa_status pa_decode_gqa_i8(void *out, const void *q, const void *kv_pool_i8, const int32_t *block_tables,
                            const int32_t *context_lens, int32_t num_seqs, int32_t max_blocks, int32_t num_pages,
                            int32_t page_size, float scale, int32_t out_dtype, void *workspace,
