@@ -9,13 +9,13 @@
 //     out[s][i][h] = sum_t softmax_t(scale <q, K_t>) V_t,   t <= pos,
 // with K_t, V_t the values code * scale the INT8 format stands for.
 //
-// A workgroup of 4 waves serves (sequence, KV head j, 16 chunk rows); wave w
+// A workgroup of 8 waves serves (sequence, KV head j, 32 chunk rows); wave w
 // serves rows row0 + 4w .. +3 over every key they see and finishes them
 // itself (no merge across waves).  The MFMAs are the INT8 decode's with all
 // 16 columns live: column c = 4r + h is row r of the wave's four and query
 // head h of the group.
 //
-// The sequence's pages go through LDS in groups of four, one per wave: each
+// The sequence's pages go through LDS in groups of eight, one per wave: each
 // wave loads one page's INT8 tile and writes its codes as the f16 MFMA
 // operands (and its scales) into the group's LDS slot, so a page is converted
 // once per workgroup; two groups alternate, one barrier per group.  The waves
@@ -57,8 +57,8 @@ struct PrefillI8Params {
     float scale_log2;
 };
 
-// Four waves (16 rows) per workgroup, three workgroups per CU.
-constexpr int kWavesP8 = 4;
+// Eight waves (32 rows) per workgroup, two workgroups per CU.
+constexpr int kWavesP8 = 8;
 constexpr int kThreadsP8 = 64 * kWavesP8;
 constexpr int kRowsP8 = 4 * kWavesP8;  // chunk rows per workgroup
 constexpr int kGroupP8 = kWavesP8;     // pages per LDS group: one converted by each wave
@@ -78,7 +78,7 @@ struct alignas(16) PairV {
     u32x4 vp[4][64];
 };
 
-__global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Params P) {
+__global__ __launch_bounds__(kThreadsP8, 2) void k_prefill_attn_i8(PrefillI8Params P) {
     // ids -> (sequence, KV head, tile): the 3 low id bits pick the XCD, which is
     // also the KV head.  An XCD deals its workgroups to its 32 CUs in turn, so
     // its p-th, (p+32)-th, ... share a CU: even turns take the work list (rank
@@ -169,13 +169,15 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
     const int np_w = last_pos / kPage + 1;
     // pages from which some column's causal limit falls inside (or before) the page
     const int first_masked = (prefix + row0) / kPage;
-    // the workgroup's pages (those of its last row) and groups of four
+    // the workgroup's pages (those of its last row) and groups of eight
     const int np_g = (prefix + min(tile * kRowsP8 + kRowsP8 - 1, C - 1)) / kPage + 1;
     const int n_groups = (np_g + kGroupP8 - 1) / kGroupP8;
 
     // ---- q as the f16 B operand, scaled by 2^(15 - e) so that its largest
-    // element over the workgroup's 64 columns lies in [2^14, 2^15)
-    const float qmax = fmaxf(fmaxf(s_qmax[0], s_qmax[1]), fmaxf(s_qmax[2], s_qmax[3]));
+    // element over the workgroup's 128 columns lies in [2^14, 2^15)
+    float qmax = s_qmax[0];
+#pragma unroll
+    for (int v = 1; v < kWavesP8; ++v) qmax = fmaxf(qmax, s_qmax[v]);
     int qe = 0;
     if (qmax > 0.0f) (void)frexpf(qmax, &qe);
     const int qshift = min(15 - qe, 126);
@@ -365,8 +367,8 @@ __global__ __launch_bounds__(kThreadsP8, 3) void k_prefill_attn_i8(PrefillI8Para
         }
     };
 
-    // ---- the page loop.  Group g holds pages 4g .. 4g+3 (wave w converts page
-    // 4g + w; past the last page it converts the last page again, unused).  At
+    // ---- the page loop.  Group g holds pages 8g .. 8g+7 (wave w converts page
+    // 8g + w; past the last page it converts the last page again, unused).  At
     // the top of step g the group's slots are written and visible, and raw holds
     // group g + 1's page, issued.
     RawPage raw = load_raw(min(w, np_g - 1));
